@@ -1,0 +1,329 @@
+"""CPU oracle for the forward pass of one top-K routed mixture-of-experts FFN layer.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The product library never calls it and
+shares no code with it: the HIP path and this oracle have only the seeded input
+generator in common.
+
+Plain, slow, obviously correct. Everything after the router logits is float64
+(numpy matmul serves as the library primitive). The router logits are float32
+in the canonical sequential-fmaf order (router_fp32.c), because the router is
+kept in float32 (Arjun Jaggi, "Mixture of Experts in LLMs: How Sparse Models
+Scale", section "Switch Transformers") and the expert choice must agree bit
+for bit with any implementation that follows the same order.
+
+Page references (title, site, section):
+  [MTA]   "Mixture of Experts", maptheai.com tutorial
+  [GLO]   "Mixture of Experts (MoE)", ai-and-cloud.com glossary
+  [CUR]   "Mixture of Experts.", llm.curionode.com, Vol. VII Plate 4
+  [LENSA] "Mixture of Experts", Lensa ML explainer (Steps 1-6, FAQ)
+  [AJ]    "Mixture of Experts in LLMs: How Sparse Models Scale", arjunjaggi.com
+
+Function -> passage it follows -> what pins it (tests/test_oracle_pins.py):
+  router_logits_f32   [LENSA] Step 2; [CUR] "Parameters you hold..." (linear
+                      router + softmax); [AJ] "Switch Transformers" (float32)
+                      -> exact correctly-rounded fma chain recomputed with
+                         rational arithmetic; float64 error bound.
+  select_topk         [MTA] "The mechanism"; [LENSA] Step 3 (top-k)
+                      -> brute force over all K-subsets, with ties.
+  router_probs        [LENSA] Step 2 (softmax over experts)
+                      -> sums to 1; the page's illustrative distribution.
+  gates               [LENSA] Step 3 (softmax over the chosen logits; the
+                      Mixtral formula; Switch scales by p_i)
+                      -> the page's worked gates 0.61 / 0.39; sum to 1.
+  expert_counts,
+  stable_permutation  [LENSA] Step 4 (T*K routing slots counted per expert);
+                      Step 5 (experts that take any number of tokens)
+                      -> Python's stable sorted(); the page's histogram stats.
+  expert_ffn          [LENSA] Step 1 (each expert is a full FFN, 3 x d x w);
+                      [CUR] intro (E separate MLPs)
+                      -> E=1, K=1 equals a dense FFN built from torch's own
+                         gelu/silu and matmul.
+  combine             [MTA] "The mechanism"; [LENSA] Step 3 (y = sum g E(h))
+                      -> the page's worked 4-dim example.
+  aux_loss            [LENSA] Step 4 (E * sum f * P; equals 1 when routing is
+                      uniform) -> uniform-P and uniform-f closed forms.
+  param_counts        [CUR] "Parameters you hold..."; [LENSA] Steps 1 and 6
+                      -> the printed 4.46M / 1.32M / 3.39x / 25.2x,
+                         37.0B / 11.1B / 3.3x and 176M / 45.1B.
+"""
+from __future__ import annotations
+
+import ctypes
+import itertools
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf as _erf
+
+ACT_GELU = 0
+ACT_SWIGLU = 1
+GATE_RENORM = 0
+GATE_RAW = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle_router.so")
+_SRC_PATH = os.path.join(_HERE, "router_fp32.c")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile router_fp32.c with gcc (no fast-math, no fp contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                               "-shared", "-fPIC", _SRC_PATH, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_router_logits_f32.restype = None
+        lib.oracle_router_logits_f32.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+        _lib = lib
+    return _lib
+
+
+# ----------------------------------------------------------------------------- router
+
+def router_logits_f32(h32: np.ndarray, W_r: np.ndarray, b_r: Optional[np.ndarray]) -> np.ndarray:
+    """logit[t,e] = (h . W_r)[t,e] (+ b_r[e]) in float32, canonical fmaf order ([LENSA] Step 2)."""
+    h32 = np.ascontiguousarray(h32, dtype=np.float32)
+    W_r = np.ascontiguousarray(W_r, dtype=np.float32)
+    T, d = h32.shape
+    d2, E = W_r.shape
+    assert d == d2
+    out = np.empty((T, E), dtype=np.float32)
+    if b_r is not None:
+        b_r = np.ascontiguousarray(b_r, dtype=np.float32)
+        assert b_r.shape == (E,)
+    if T > 0:
+        _load().oracle_router_logits_f32(h32.ctypes.data, W_r.ctypes.data,
+                                         None if b_r is None else b_r.ctypes.data,
+                                         T, d, E, out.ctypes.data)
+    return out
+
+
+def router_logits_f64(h: np.ndarray, W_r: np.ndarray, b_r: Optional[np.ndarray]) -> np.ndarray:
+    """The same logits in float64 (used only to bound the float32 rounding)."""
+    l = np.asarray(h, np.float64) @ np.asarray(W_r, np.float64)
+    if b_r is not None:
+        l = l + np.asarray(b_r, np.float64)[None, :]
+    return l
+
+
+def select_topk(logits: np.ndarray, K: int) -> np.ndarray:
+    """The K chosen experts per token, largest logit first; equal logits: lower index first.
+
+    Selecting on the logits is the same as selecting on the softmax
+    probabilities, since the softmax is increasing ([LENSA] Step 3).
+    """
+    T, E = logits.shape
+    idx = np.empty((T, K), dtype=np.int32)
+    experts = np.arange(E)
+    for t in range(T):
+        # lexsort: last key is primary -> logit descending, then expert ascending
+        order = np.lexsort((experts, -logits[t].astype(np.float64)))
+        idx[t] = order[:K]
+    return idx
+
+
+def router_probs(logits: np.ndarray) -> np.ndarray:
+    """p[t,e] = softmax over all E experts of the logits, in float64 ([LENSA] Step 2)."""
+    l = np.asarray(logits, np.float64)
+    m = l.max(axis=1, keepdims=True)
+    ex = np.exp(l - m)
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def gates(logits: np.ndarray, idx: np.ndarray, mode: int) -> np.ndarray:
+    """Gate weight of each chosen expert ([LENSA] Step 3).
+
+    RENORM: a softmax over the K chosen logits only (the Mixtral form
+            softmax(TopK(h W_g))), so the K gates sum to 1.
+    RAW:    the full-softmax probability p_i of the chosen expert, not
+            renormalised (Switch top-1).
+    """
+    l = np.asarray(logits, np.float64)
+    chosen = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+    if mode == GATE_RENORM:
+        ex = np.exp(chosen - chosen[:, :1])
+        return ex / ex.sum(axis=1, keepdims=True)
+    if mode == GATE_RAW:
+        return np.take_along_axis(router_probs(logits), idx.astype(np.int64), axis=1)
+    raise ValueError(mode)
+
+
+# ----------------------------------------------------------------------------- grouping
+
+def expert_counts(idx: np.ndarray, E: int) -> np.ndarray:
+    """Routing slots per expert: T*K slots in all ([LENSA] Step 4)."""
+    return np.bincount(idx.reshape(-1).astype(np.int64), minlength=E).astype(np.int32)
+
+
+def stable_permutation(idx: np.ndarray, E: int):
+    """Group the T*K slots by expert, keeping token order inside each group.
+
+    Returns (offsets[E+1], slot_token[S], token_slot[T,K]): group e occupies
+    rows offsets[e] .. offsets[e+1]-1; row s holds token slot_token[s]; the
+    j-th choice of token t sits in row token_slot[t, j].
+    """
+    T, K = idx.shape
+    counts = expert_counts(idx, E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    tok = np.repeat(np.arange(T, dtype=np.int64), K)
+    ch = np.tile(np.arange(K, dtype=np.int64), T)
+    ex = idx.reshape(-1).astype(np.int64)
+    order = np.lexsort((tok, ex))  # primary: expert, then token (stable)
+    slot_token = tok[order].astype(np.int32)
+    token_slot = np.empty((T, K), dtype=np.int32)
+    token_slot[tok[order], ch[order]] = np.arange(T * K, dtype=np.int32)
+    return offsets, slot_token, token_slot
+
+
+# ----------------------------------------------------------------------------- experts
+
+def gelu(z: np.ndarray) -> np.ndarray:
+    """Exact (erf) GELU."""
+    return 0.5 * z * (1.0 + _erf(z / np.sqrt(2.0)))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x: np.ndarray, e: int, params: Dict[str, Optional[np.ndarray]], act: int) -> np.ndarray:
+    """Expert e's feed-forward block on rows x, float64 ([LENSA] Step 1; [CUR] intro).
+
+    Stored weights are output-major: params["W1"][e] is width x d, i.e. the
+    transpose of the d x width matrix of the math, so x . W1 = x @ W1[e].T.
+      GELU:   o = GELU(x W1 + b1) W2 + b2
+      SwiGLU: o = (SiLU(x W1) * (x W3)) W2     (three d x width matrices, no bias)
+    """
+    x = np.asarray(x, np.float64)
+    W1 = np.asarray(params["W1"][e], np.float64)
+    W2 = np.asarray(params["W2"][e], np.float64)
+    if act == ACT_GELU:
+        z = x @ W1.T
+        if params.get("b1") is not None:
+            z = z + np.asarray(params["b1"][e], np.float64)
+        o = gelu(z) @ W2.T
+        if params.get("b2") is not None:
+            o = o + np.asarray(params["b2"][e], np.float64)
+        return o
+    if act == ACT_SWIGLU:
+        W3 = np.asarray(params["W3"][e], np.float64)
+        return (silu(x @ W1.T) * (x @ W3.T)) @ W2.T
+    raise ValueError(act)
+
+
+def combine(o: np.ndarray, token_slot: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """y[t] = sum_j g[t,j] * o[token_slot[t,j]] ([MTA] "The mechanism"; [LENSA] Step 3)."""
+    T, K = token_slot.shape
+    y = np.zeros((T, o.shape[1]), dtype=np.float64)
+    for j in range(K):
+        y += g[:, j:j + 1] * o[token_slot[:, j]]
+    return y
+
+
+def aux_loss(counts: np.ndarray, p: np.ndarray, K: int) -> float:
+    """E * sum_e f_e * P_e ([LENSA] Step 4).
+
+    f_e = share of the T*K routing slots that go to expert e;
+    P_e = mean over tokens of the full-softmax probability of expert e.
+    """
+    T, E = p.shape
+    if T == 0:
+        return 0.0
+    f = np.asarray(counts, np.float64) / float(T * K)
+    P = p.mean(axis=0)
+    return float(E * np.sum(f * P))
+
+
+# ----------------------------------------------------------------------------- layer
+
+def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int,
+                act: int, gate: int, tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """The whole layer. `inp` holds float32 arrays of the exact input values.
+
+    Routing, grouping and the aux loss cover all T tokens. The expert FFNs and
+    y are computed for all tokens, or only for the rows listed in `tokens`
+    (y then has len(tokens) rows, in that order).
+    """
+    h32 = np.asarray(inp["h"], np.float32).reshape(T, d)
+    logits = router_logits_f32(h32, inp["W_r"], inp.get("b_r"))
+    idx = select_topk(logits, K)
+    p = router_probs(logits)
+    g = gates(logits, idx, gate)
+    counts = expert_counts(idx, E)
+    offsets, slot_token, token_slot = stable_permutation(idx, E)
+    aux = aux_loss(counts, p, K)
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y = np.zeros((len(rows), d), dtype=np.float64)
+    h64 = h32.astype(np.float64)
+    for e in range(E):
+        sel_r, sel_j = np.nonzero(idx[rows] == e)
+        if len(sel_r) == 0:
+            continue
+        o = expert_ffn(h64[rows[sel_r]], e, inp, act)
+        # y[t] += g[t,j] * E_e(h[t]); each token meets each expert at most once
+        y[sel_r] += g[rows[sel_r], sel_j][:, None] * o
+    return {"logits": logits, "topk_idx": idx, "topk_gate": g, "probs": p, "counts": counts,
+            "offsets": offsets, "slot_token": slot_token, "token_slot": token_slot,
+            "aux": aux, "y": y, "rows": rows}
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+def param_counts_micro(d: int, layers: int, E: int, K: int, width: int) -> Dict[str, int]:
+    """Non-embedding parameters of the micro model ([CUR] Workshop and "Parameters you hold").
+
+    Per layer: attention 4 d^2, two LayerNorms (gain + bias: 4 d), the router
+    d E, and E experts of two bias-free d x width matrices; plus a final
+    LayerNorm (2 d). Active counts K experts instead of E.
+    """
+    shared = layers * (4 * d * d + 4 * d + d * E) + 2 * d
+    expert = 2 * d * width
+    return {"total": shared + layers * E * expert, "active": shared + layers * K * expert,
+            "attention_plus_active_experts": layers * (4 * d * d + K * expert)}
+
+
+def param_counts_swiglu_model(d: int, layers: int, E: int, K: int, width: int,
+                              vocab: int = 32000) -> Dict[str, int]:
+    """A 7B-style model with SwiGLU experts ([LENSA] Step 1).
+
+    Per layer: attention 4 d^2, two RMSNorm gains (2 d), the router d E, and E
+    experts of 3 d width parameters; plus a final norm (d) and untied input and
+    output embeddings (2 vocab d). Active counts K experts instead of E.
+    """
+    shared = layers * (4 * d * d + 2 * d + d * E) + d + 2 * vocab * d
+    expert = 3 * d * width
+    return {"expert": expert, "total": shared + layers * E * expert,
+            "active": shared + layers * K * expert, "routed_total": layers * E * expert}
+
+
+def load_stats(counts: Sequence[int], T: int, K: int) -> Dict[str, float]:
+    """Histogram statistics of the Step 4 widget ([LENSA] Step 4)."""
+    c = np.asarray(counts, np.int64)
+    S = T * K
+    top2 = np.sort(c)[::-1][:2].sum()
+    return {"slots": int(c.sum()), "balanced": S / len(c), "busiest_share": float(c.max() / S),
+            "top2_share": float(top2 / S), "idle": int((c == 0).sum())}
+
+
+def brute_force_topk_set(logits_row: np.ndarray, K: int):
+    """The K-subset with the largest logit sum; ties -> lexicographically smallest index set."""
+    best, best_sum = None, None
+    for sub in itertools.combinations(range(len(logits_row)), K):  # lexicographic order
+        s = float(sum(float(logits_row[i]) for i in sub))
+        if best_sum is None or s > best_sum:
+            best, best_sum = sub, s
+    return best

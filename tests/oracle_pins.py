@@ -1,0 +1,367 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each check_* function raises AssertionError when the oracle disagrees with a
+printed value, a closed form, an invariant, a textbook routine or brute force.
+tests/test_oracle_pins.py runs them; tests/test_oracle_mutations.py plants
+plausible mistakes in the oracle and requires that at least one check fails.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- exact fp32 fma
+
+def _round_f32(x: Fraction) -> np.float32:
+    """Correctly rounded (nearest, ties to even) float32 of an exact rational."""
+    c = np.float32(float(x))
+    cands = {np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))}
+    best = None
+    for v in cands:
+        err = abs(Fraction(float(v)) - x)
+        key = (err, int(np.array(v, np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, v)
+    return np.float32(best[1])
+
+
+def _fma_f32(a: np.float32, b: np.float32, c: np.float32) -> np.float32:
+    exact = Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c))
+    if exact == 0:
+        neg = (math.copysign(1.0, float(a) * float(b)) < 0) and (math.copysign(1.0, float(c)) < 0)
+        return np.float32(-0.0 if neg else 0.0)
+    return _round_f32(exact)
+
+
+def check_router_logits_exact(seed=0):
+    """Bit-exact: the C chain equals a rational-arithmetic fma chain, with and without bias."""
+    rng = np.random.default_rng(seed)
+    T, d, E = 5, 24, 6
+    h = rng.standard_normal((T, d)).astype(np.float32)
+    W = (rng.standard_normal((d, E)) * 0.02).astype(np.float32)
+    # cancellation-heavy token: exercises rounding of small results
+    h[3] = np.float32(1e3) * np.sign(h[3])
+    W[:, 2] = np.float32(1e-3) * (np.arange(d) % 2 * 2 - 1)
+    b = rng.standard_normal(E).astype(np.float32)
+    for bias in (None, b):
+        got = O.router_logits_f32(h, W, bias)
+        for t in range(T):
+            for e in range(E):
+                acc = np.float32(0.0)
+                for k in range(d):
+                    acc = _fma_f32(h[t, k], W[k, e], acc)
+                if bias is not None:
+                    acc = _round_f32(Fraction(float(acc)) + Fraction(float(bias[e])))
+                assert np.array(got[t, e]).view(np.uint32) == np.array(acc).view(np.uint32), \
+                    (t, e, got[t, e], acc, bias is not None)
+
+
+def check_router_logits_bound(seed=1):
+    """|l32 - l| <= gamma_(d+1) (sum_k |h_k W_k| + |b|) for d = 4096 (float32 error bound)."""
+    rng = np.random.default_rng(seed)
+    T, d, E = 32, 4096, 8
+    h = rng.standard_normal((T, d)).astype(np.float32)
+    W = (rng.standard_normal((d, E)) * 0.02).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    l32 = O.router_logits_f32(h, W, b).astype(np.float64)
+    h64, W64, b64 = h.astype(np.float64), W.astype(np.float64), b.astype(np.float64)
+    exact = h64 @ W64 + b64
+    u = 2.0 ** -24
+    gamma = (d + 1) * u / (1 - (d + 1) * u)
+    mag = np.abs(h64) @ np.abs(W64) + np.abs(b64)
+    bound = gamma * mag + 1e-12 * mag  # float64 reference error is far below this margin
+    assert np.all(np.abs(l32 - exact) <= bound)
+    assert np.any(l32 != exact)  # genuinely float32
+
+
+def check_topk_bruteforce(seed=2):
+    """Top-K set and order vs brute force over all K-subsets, including forced ties."""
+    rng = np.random.default_rng(seed)
+    for E in range(1, 9):
+        for K in range(1, min(4, E) + 1):
+            for tie in (False, True):
+                T = 24
+                l = rng.standard_normal((T, E)).astype(np.float32)
+                if tie:
+                    l = np.round(l * 2) / 2  # many equal logits
+                    l[0] = 0.0
+                idx = O.select_topk(l, K)
+                assert idx.shape == (T, K) and idx.dtype == np.int32
+                for t in range(T):
+                    best = None
+                    for sub in itertools.combinations(range(E), K):
+                        s = sum(Fraction(float(l[t, i])) for i in sub)
+                        if best is None or s > best[0]:
+                            best = (s, sub)
+                    assert tuple(sorted(idx[t].tolist())) == best[1], (E, K, t, l[t], idx[t])
+                    order = sorted(best[1], key=lambda i: (-float(l[t, i]), i))
+                    assert idx[t].tolist() == order
+
+
+def check_probs(seed=3):
+    """Full softmax: rows sum to 1; matches scipy's softmax; shift invariance."""
+    from scipy.special import softmax as sp_softmax
+    rng = np.random.default_rng(seed)
+    l = (rng.standard_normal((50, 8)) * 3).astype(np.float32)
+    p = O.router_probs(l)
+    assert np.allclose(p.sum(1), 1.0, atol=1e-15, rtol=0)
+    assert np.allclose(p, sp_softmax(l.astype(np.float64), axis=1), atol=1e-15, rtol=0)
+    assert np.allclose(O.router_probs(l.astype(np.float64) + 7.0), p, atol=1e-15, rtol=0)  # exact shift
+
+
+def check_gates_worked_example():
+    """Lensa ML Step 3: unchosen p's as printed, chosen gates 0.61 / 0.39, chosen mass 56%."""
+    g = _golden("lensa_step3_topk_combine.json")
+    mass = g["chosen_mass_percent"] / 100.0
+    p = np.zeros(8)
+    for k, v in g["unchosen_p"].items():
+        p[int(k[1:]) - 1] = v
+    p[2] = mass * g["chosen_gates"]["E3"]
+    p[3] = mass * g["chosen_gates"]["E4"]
+    assert abs(p.sum() - 1.0) < 1e-12  # the printed numbers are consistent
+    logits = np.log(p).astype(np.float32)[None, :]
+    idx = O.select_topk(logits, 2)
+    assert idx[0].tolist() == [2, 3]
+    gr = O.gates(logits, idx, O.GATE_RENORM)[0]
+    assert round(gr[0], 2) == 0.61 and round(gr[1], 2) == 0.39
+    pr = O.router_probs(logits)[0]
+    for k, v in g["unchosen_p"].items():
+        assert round(pr[int(k[1:]) - 1], 2) == v
+    assert round(100 * (pr[2] + pr[3])) == g["chosen_mass_percent"]
+    graw = O.gates(logits, idx, O.GATE_RAW)[0]
+    assert np.allclose(graw, pr[[2, 3]], rtol=0, atol=1e-15)
+
+
+def check_gates_invariants(seed=4):
+    """RENORM gates sum to 1, K=1 RENORM is exactly 1, K=E gives the full softmax."""
+    rng = np.random.default_rng(seed)
+    E = 8
+    l = (rng.standard_normal((40, E)) * 2).astype(np.float32)
+    for K in (1, 2, 3, 8):
+        idx = O.select_topk(l, K)
+        g = O.gates(l, idx, O.GATE_RENORM)
+        assert np.all(np.abs(g.sum(1) - 1.0) < 1e-15)
+        assert np.all(np.diff(g, axis=1) <= 0)  # largest logit first -> largest gate first
+        if K == 1:
+            assert np.all(g == 1.0)
+        if K == E:
+            p = O.router_probs(l)
+            assert np.allclose(g, np.take_along_axis(p, idx.astype(np.int64), 1), rtol=0, atol=1e-15)
+            assert np.allclose(O.gates(l, idx, O.GATE_RAW), g, rtol=0, atol=1e-15)
+
+
+def check_combine_worked_example():
+    """Lensa ML Step 3: 0.61 E3(h) + 0.39 E4(h) printed as [0.27, 0.30, -0.53, -0.52]."""
+    g = _golden("lensa_step3_topk_combine.json")
+    o = np.array([g["E3_h"], g["E4_h"]], dtype=np.float64)
+    gates = np.array([[g["chosen_gates"]["E3"], g["chosen_gates"]["E4"]]])
+    y = O.combine(o, np.array([[0, 1]], dtype=np.int32), gates)[0]
+    assert [round(v, g["printed_decimals"]) for v in y] == g["y_printed"], y
+
+
+def check_permutation_sorted(seed=5):
+    """Grouping equals Python's stable sorted() of the slots by (expert, token)."""
+    rng = np.random.default_rng(seed)
+    for T, E, K in ((1, 1, 1), (37, 5, 2), (64, 8, 3), (200, 64, 1), (0, 4, 2)):
+        l = rng.standard_normal((T, E)).astype(np.float32)
+        idx = O.select_topk(l, K)
+        offsets, slot_token, token_slot = O.stable_permutation(idx, E)
+        slots = sorted(((int(idx[t, j]), t, j) for t in range(T) for j in range(K)),
+                       key=lambda s: (s[0], s[1]))
+        assert slot_token.tolist() == [s[1] for s in slots]
+        for s, (e, t, j) in enumerate(slots):
+            assert token_slot[t, j] == s
+        cnt = [sum(1 for s in slots if s[0] == e) for e in range(E)]
+        assert offsets.tolist() == [sum(cnt[:e]) for e in range(E + 1)]
+        assert O.expert_counts(idx, E).tolist() == cnt
+
+
+def check_load_stats_page():
+    """Lensa ML Step 4: 512 slots, balanced 64, busiest 44.7%, top two 77%, two idle."""
+    g = _golden("lensa_step4_load.json")
+    s = O.load_stats(g["counts"], g["T"], g["K"])
+    assert s["slots"] == g["T"] * g["K"]
+    assert s["balanced"] == g["balanced_printed"]
+    assert round(100 * s["busiest_share"], 1) == g["busiest_share_percent_printed"]
+    assert round(100 * s["top2_share"]) == g["top2_share_percent_printed"]
+    assert s["idle"] == g["idle_printed"]
+
+
+def check_aux_uniform_probs():
+    """W_r = 0, no bias: every p = 1/E exactly, so E * sum f P = sum f = 1 exactly, for any K."""
+    rng = np.random.default_rng(6)
+    for E, K, T in ((8, 2, 40), (4, 1, 9), (64, 2, 33), (2, 2, 5), (1, 1, 7)):
+        d = 16
+        inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+               "W_r": np.zeros((d, E), np.float32), "b_r": None}
+        l = O.router_logits_f32(inp["h"], inp["W_r"], None)
+        idx = O.select_topk(l, K)
+        assert idx[:, :].tolist() == [list(range(K))] * T  # all ties: lowest indices win
+        aux = O.aux_loss(O.expert_counts(idx, E), O.router_probs(l), K)
+        assert aux == 1.0, (E, K, aux)
+
+
+def check_aux_uniform_load():
+    """Every expert gets exactly T*K/E slots: E * sum f P = sum P = 1 whatever p is."""
+    E, K, T, d = 4, 1, 12, 4
+    h = np.zeros((T, d), np.float32)
+    for t in range(T):
+        h[t, t % E] = 1.0 + 0.1 * t  # token t points at expert t % E
+    W = np.eye(d, E, dtype=np.float32) * 3.0
+    l = O.router_logits_f32(h, W, None)
+    idx = O.select_topk(l, K)
+    counts = O.expert_counts(idx, E)
+    assert counts.tolist() == [T * K // E] * E
+    aux = O.aux_loss(counts, O.router_probs(l), K)
+    assert abs(aux - 1.0) < 1e-14
+    # sharply peaked router with one-hot routing: P -> f, so aux -> E * sum f^2
+    W2 = np.eye(d, E, dtype=np.float32) * 200.0
+    h2 = np.zeros((T, d), np.float32)
+    h2[:, 0] = 1.0
+    h2[: T // 2, 1] = 2.0
+    l2 = O.router_logits_f32(h2, W2, None)
+    idx2 = O.select_topk(l2, 1)
+    c2 = O.expert_counts(idx2, E)
+    f = c2 / T
+    assert abs(O.aux_loss(c2, O.router_probs(l2), 1) - E * np.sum(f * f)) < 1e-12
+
+
+def _torch_dense_ffn(x, W1, b1, W3, W2, b2, act):
+    xt = torch.from_numpy(x)
+    z = xt @ torch.from_numpy(W1).T
+    if act == O.ACT_GELU:
+        if b1 is not None:
+            z = z + torch.from_numpy(b1)
+        o = torch.nn.functional.gelu(z, approximate="none") @ torch.from_numpy(W2).T
+        if b2 is not None:
+            o = o + torch.from_numpy(b2)
+        return o.numpy()
+    z3 = xt @ torch.from_numpy(W3).T
+    return ((torch.nn.functional.silu(z) * z3) @ torch.from_numpy(W2).T).numpy()
+
+
+def check_dense_reduction(seed=7):
+    """E = 1, K = 1: the layer is exactly the dense FFN (gate 1.0), checked against torch."""
+    rng = np.random.default_rng(seed)
+    T, d, w = 19, 24, 40
+    for act in (O.ACT_GELU, O.ACT_SWIGLU):
+        for gate in (O.GATE_RENORM, O.GATE_RAW):
+            inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+                   "W_r": rng.standard_normal((d, 1)).astype(np.float32),
+                   "b_r": rng.standard_normal(1).astype(np.float32),
+                   "W1": rng.standard_normal((1, w, d)) * d ** -0.5,
+                   "W2": rng.standard_normal((1, d, w)) * w ** -0.5}
+            if act == O.ACT_GELU:
+                inp.update(b1=rng.standard_normal((1, w)) * 0.3, b2=rng.standard_normal((1, d)) * 0.3, W3=None)
+            else:
+                inp.update(W3=rng.standard_normal((1, w, d)) * d ** -0.5, b1=None, b2=None)
+            r = O.moe_forward(inp, T, d, 1, 1, act, gate)
+            assert np.all(r["topk_gate"] == 1.0) and np.all(r["topk_idx"] == 0)
+            ref = _torch_dense_ffn(inp["h"].astype(np.float64), inp["W1"][0],
+                                   None if inp["b1"] is None else inp["b1"][0],
+                                   None if inp["W3"] is None else inp["W3"][0], inp["W2"][0],
+                                   None if inp["b2"] is None else inp["b2"][0], act)
+            assert np.max(np.abs(r["y"] - ref)) < 1e-12
+            assert r["aux"] == 1.0
+
+
+def check_soft_mixture_K_equals_E(seed=8):
+    """K = E: top-K keeps every expert and y = sum_e p_e E_e(h) (the dense soft mixture)."""
+    rng = np.random.default_rng(seed)
+    T, d, w, E = 7, 12, 20, 4
+    inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+           "W_r": rng.standard_normal((d, E)).astype(np.float32), "b_r": None,
+           "W1": rng.standard_normal((E, w, d)) * d ** -0.5,
+           "W3": rng.standard_normal((E, w, d)) * d ** -0.5,
+           "W2": rng.standard_normal((E, d, w)) * w ** -0.5, "b1": None, "b2": None}
+    r = O.moe_forward(inp, T, d, E, E, O.ACT_SWIGLU, O.GATE_RENORM)
+    p = r["probs"]
+    x = inp["h"].astype(np.float64)
+    ref = np.zeros((T, d))
+    for e in range(E):
+        ref += p[:, e:e + 1] * _torch_dense_ffn(x, inp["W1"][e], None, inp["W3"][e], inp["W2"][e],
+                                                None, O.ACT_SWIGLU)
+    assert np.max(np.abs(r["y"] - ref)) < 1e-12
+
+
+def check_forward_subset_consistency(seed=9):
+    """Computing only some rows of y gives the same rows as the full layer."""
+    rng = np.random.default_rng(seed)
+    T, d, w, E, K = 30, 16, 24, 5, 2
+    inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+           "W_r": rng.standard_normal((d, E)).astype(np.float32),
+           "b_r": rng.standard_normal(E).astype(np.float32),
+           "W1": rng.standard_normal((E, w, d)), "W2": rng.standard_normal((E, d, w)),
+           "b1": rng.standard_normal((E, w)), "b2": rng.standard_normal((E, d)), "W3": None}
+    full = O.moe_forward(inp, T, d, E, K, O.ACT_GELU, O.GATE_RENORM)
+    rows = [29, 0, 13, 13, 7]
+    part = O.moe_forward(inp, T, d, E, K, O.ACT_GELU, O.GATE_RENORM, tokens=rows)
+    assert np.array_equal(part["y"], full["y"][rows])
+    # the grouped formulation (permute -> per-expert FFN -> combine) gives the same y
+    o = np.zeros((T * K, d))
+    for e in range(E):
+        s0, s1 = full["offsets"][e], full["offsets"][e + 1]
+        if s1 > s0:
+            o[s0:s1] = O.expert_ffn(inp["h"][full["slot_token"][s0:s1]], e, inp, O.ACT_GELU)
+    y2 = O.combine(o, full["token_slot"], full["topk_gate"])
+    assert np.max(np.abs(y2 - full["y"])) < 1e-12
+
+
+def check_param_counts():
+    """Printed parameter counts of the micro model, the 7B shape and Mixtral."""
+    g = _golden("param_counts.json")
+    m = g["micro"]
+    c = O.param_counts_micro(m["d"], m["layers"], m["E"], m["K"], m["width"])
+    assert round(c["total"] / 1e6, 2) == m["total_millions_printed"]
+    assert round(c["active"] / 1e6, 2) == m["active_millions_printed"]
+    assert round(c["total"] / c["active"], 2) == m["ratio_printed"]
+    c64 = O.param_counts_micro(m["d"], m["layers"], 64, m["K"], m["width"])
+    assert round(c64["total"] / c64["active"], 1) == m["ratio_E64_printed"]
+    assert round(c["attention_plus_active_experts"] / 1e6, 2) == m["text_active_millions_printed"]
+
+    s = g["seven_b_shape"]
+    c7 = O.param_counts_swiglu_model(s["d"], s["layers"], s["E"], s["K"], s["width"])
+    assert round(c7["expert"] / 1e6) == s["expert_millions_printed"]
+    assert round(c7["total"] / 1e9, 1) == s["total_billions_printed"]
+    assert round(c7["active"] / 1e9, 1) == s["active_billions_printed"]
+    assert round(c7["total"] / c7["active"], 1) == s["ratio_printed"]
+    # convention-free: the difference is exactly L (E - K) experts
+    assert c7["total"] - c7["active"] == s["layers"] * (s["E"] - s["K"]) * c7["expert"]
+    assert abs((c7["total"] - c7["active"]) / 1e9
+               - (s["total_billions_printed"] - s["active_billions_printed"])) <= 0.1
+
+    x = g["mixtral"]
+    cm = O.param_counts_swiglu_model(x["d"], x["layers"], x["E"], x["K"], x["width"])
+    assert round(cm["expert"] / 1e6) == x["expert_millions_printed"]
+    assert round(cm["routed_total"] / 1e9, 1) == x["routed_billions_printed"]
+    assert round(100 * cm["routed_total"] / (x["total_billions_printed"] * 1e9)) == \
+        x["routed_share_percent_printed"]
+    # active = shared + routed * K / E with shared = printed total - routed
+    shared = x["total_billions_printed"] * 1e9 - cm["routed_total"]
+    active = shared + cm["routed_total"] * x["K"] / x["E"]
+    assert round(active / 1e9, 1) == x["active_billions_printed"]
+    assert round(x["total_billions_printed"] * 2) == x["held_GB_fp16_printed"]
+    assert round(x["active_billions_printed"] * 2) == x["read_per_token_GB_fp16_printed"]
+
+
+ALL_CHECKS = [check_router_logits_exact, check_router_logits_bound, check_topk_bruteforce,
+              check_probs, check_gates_worked_example, check_gates_invariants,
+              check_combine_worked_example, check_permutation_sorted, check_load_stats_page,
+              check_aux_uniform_probs, check_aux_uniform_load, check_dense_reduction,
+              check_soft_mixture_K_equals_E, check_forward_subset_consistency, check_param_counts]

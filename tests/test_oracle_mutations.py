@@ -1,0 +1,154 @@
+"""Plant plausible mistakes in the oracle and require that the pins catch each one.
+
+Every mutation is applied to the oracle module on the CPU only (monkeypatch);
+the pins of tests/oracle_pins.py must then fail at least once.
+"""
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import moe_oracle as O
+
+_orig = {name: getattr(O, name) for name in
+         ("router_logits_f32", "select_topk", "router_probs", "gates", "stable_permutation",
+          "aux_loss", "gelu", "silu", "expert_ffn", "combine", "param_counts_micro",
+          "param_counts_swiglu_model", "expert_counts")}
+
+
+def _logits_no_bias(h, W, b):
+    return _orig["router_logits_f32"](h, W, None)
+
+
+def _logits_reverse_k(h, W, b):
+    h = np.ascontiguousarray(np.asarray(h, np.float32)[:, ::-1])
+    W = np.ascontiguousarray(np.asarray(W, np.float32)[::-1, :])
+    return _orig["router_logits_f32"](h, W, b)
+
+
+def _logits_bias_first(h, W, b):
+    # bias folded in at the start of the chain instead of added at the end
+    if b is None:
+        return _orig["router_logits_f32"](h, W, None)
+    h = np.asarray(h, np.float32)
+    h1 = np.concatenate([np.ones((h.shape[0], 1), np.float32), h], axis=1)
+    W1 = np.concatenate([np.asarray(b, np.float32)[None, :], np.asarray(W, np.float32)], axis=0)
+    return _orig["router_logits_f32"](h1, W1, None)
+
+
+def _topk_high_index_wins(l, K):
+    E = l.shape[1]
+    idx = _orig["select_topk"](l[:, ::-1], K)
+    return (E - 1 - idx).astype(np.int32)
+
+
+def _topk_smallest(l, K):
+    return _orig["select_topk"](-np.asarray(l), K)
+
+
+def _gates_no_renorm(l, idx, mode):
+    return np.take_along_axis(_orig["router_probs"](l), idx.astype(np.int64), axis=1)
+
+
+def _probs_wrong_sign(l):
+    l = np.asarray(l, np.float64)
+    ex = np.exp(l.min(axis=1, keepdims=True) - l)
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def _perm_token_descending(idx, E):
+    T, K = idx.shape
+    off, st, ts = _orig["stable_permutation"](idx[::-1].copy(), E)
+    st = (T - 1 - st).astype(np.int32)
+    ts = ts[::-1].copy()
+    return off, st, ts
+
+
+def _aux_missing_K(counts, p, K):
+    return _orig["aux_loss"](counts, p, 1)
+
+
+def _aux_missing_E(counts, p, K):
+    return _orig["aux_loss"](counts, p, K) / p.shape[1]
+
+
+def _aux_sum_not_mean(counts, p, K):
+    return _orig["aux_loss"](counts, p, K) * p.shape[0]
+
+
+def _gelu_tanh(z):
+    return 0.5 * z * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _ffn_silu_on_w3(x, e, params, act):
+    if act != O.ACT_SWIGLU:
+        return _orig["expert_ffn"](x, e, params, act)
+    x = np.asarray(x, np.float64)
+    W1, W3, W2 = (np.asarray(params[k][e], np.float64) for k in ("W1", "W3", "W2"))
+    return ((x @ W1.T) * O.silu(x @ W3.T)) @ W2.T
+
+
+def _ffn_no_b2(x, e, params, act):
+    p = dict(params)
+    p["b2"] = None
+    return _orig["expert_ffn"](x, e, p, act)
+
+
+def _combine_swapped(o, ts, g):
+    return _orig["combine"](o, ts, g[:, ::-1])
+
+
+def _micro_three_matrices(d, layers, E, K, width):
+    c = _orig["param_counts_micro"](d, layers, E, K, width)
+    extra = layers * d * width
+    return {"total": c["total"] + E * extra, "active": c["active"] + K * extra,
+            "attention_plus_active_experts": c["attention_plus_active_experts"] + K * extra}
+
+
+def _swiglu_two_matrices(d, layers, E, K, width, vocab=32000):
+    c = _orig["param_counts_swiglu_model"](d, layers, E, K, width, vocab)
+    e2 = 2 * d * width
+    shared = c["total"] - c["routed_total"]
+    return {"expert": e2, "total": shared + layers * E * e2, "active": shared + layers * K * e2,
+            "routed_total": layers * E * e2}
+
+
+def _counts_off_by_one(idx, E):
+    c = _orig["expert_counts"](idx, E).copy()
+    if len(c):
+        c[0] += 1
+    return c
+
+
+MUTATIONS = {
+    "router_drops_bias": ("router_logits_f32", _logits_no_bias),
+    "router_reverse_k_order": ("router_logits_f32", _logits_reverse_k),
+    "router_bias_first": ("router_logits_f32", _logits_bias_first),
+    "topk_high_index_wins_ties": ("select_topk", _topk_high_index_wins),
+    "topk_smallest": ("select_topk", _topk_smallest),
+    "gates_not_renormalised": ("gates", _gates_no_renorm),
+    "softmax_wrong_sign": ("router_probs", _probs_wrong_sign),
+    "permutation_tokens_descending": ("stable_permutation", _perm_token_descending),
+    "aux_f_over_T": ("aux_loss", _aux_missing_K),
+    "aux_missing_E": ("aux_loss", _aux_missing_E),
+    "aux_sum_not_mean": ("aux_loss", _aux_sum_not_mean),
+    "gelu_tanh_approx": ("gelu", _gelu_tanh),
+    "swiglu_silu_on_w3": ("expert_ffn", _ffn_silu_on_w3),
+    "expert_drops_b2": ("expert_ffn", _ffn_no_b2),
+    "combine_swaps_gates": ("combine", _combine_swapped),
+    "micro_counts_three_matrices": ("param_counts_micro", _micro_three_matrices),
+    "swiglu_counts_two_matrices": ("param_counts_swiglu_model", _swiglu_two_matrices),
+    "counts_off_by_one": ("expert_counts", _counts_off_by_one),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception as exc:  # an assertion, or a crash caused by the planted mistake
+            failed.append((check.__name__, type(exc).__name__))
+    assert failed, "mutation %s slipped past every pin" % name
