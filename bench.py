@@ -1,0 +1,212 @@
+"""Benchmark of the MoE FFN layer forward pass on one MI355X.
+
+One step = one moe_forward call (route, group, expert GEMMs, combine, aux) over
+one batch of seeded synthetic input already resident in HBM.
+
+Headline (`value`): tokens/s on the Mixtral-shaped prefill layer (T=4096,
+d=4096, E=8, top-2, SwiGLU width 14336, bf16). The decode-shaped layer (T=16)
+and the Switch-style top-1 layer (T=8192, E=64, width 1376) are reported in
+extra objects of the same JSON line. Each carries a roofline for its dominant
+kernel: algorithmic flops or bytes per launch divided by that kernel's mean
+duration, measured with HIP events that the library records on the launch
+stream during the timed region.
+
+cpu_baseline: the CPU oracle (never tuned) on a bounded sample of the
+prefill workload: the same layer restricted to its first tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_mixture_experts_48_amd as moe  # noqa: E402
+from sparse_mixture_experts_48_amd import workloads as W  # noqa: E402
+
+METRIC = "MoE-layer tokens/s + TFLOP/s (% MFMA peak) prefill; HBM GB/s (% peak) decode"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def bpe(cfg):
+    return 2 if cfg.dtype == W.DT_BF16 else 4
+
+
+def algorithmic(cfg, counts):
+    """Flops and bytes the method itself needs (only experts that are hit are read)."""
+    n_mat = 3 if cfg.act == W.ACT_SWIGLU else 2
+    hit = int((counts > 0).sum())
+    flops_router = 2.0 * cfg.T * cfg.d * cfg.E
+    flops_g1 = 2.0 * cfg.S * cfg.d * cfg.width * (n_mat - 1)
+    flops_g2 = 2.0 * cfg.S * cfg.width * cfg.d
+    b = bpe(cfg)
+    w_g1 = hit * (n_mat - 1) * cfg.width * cfg.d * b + (hit * cfg.width * b if cfg.act == W.ACT_GELU else 0)
+    w_g2 = hit * cfg.d * cfg.width * b + (hit * cfg.d * b if cfg.act == W.ACT_GELU else 0)
+    bytes_total = cfg.T * cfg.d * b * 2 + cfg.d * cfg.E * 4 + w_g1 + w_g2
+    return {"flops": flops_router + flops_g1 + flops_g2, "flops_gemm1": flops_g1, "flops_gemm2": flops_g2,
+            "bytes": bytes_total, "weight_bytes_gemm1": w_g1, "weight_bytes_gemm2": w_g2, "experts_hit": hit}
+
+
+def time_workload(cfg, steps, warmup, label):
+    sys.stderr.write("[bench] %s: generating inputs %s\n" % (label, cfg))
+    sys.stderr.flush()
+    inp = W.make_inputs(cfg)
+    layer = moe.MoELayer(cfg, inp)
+    del inp
+    for _ in range(warmup):
+        layer.forward()
+    torch.cuda.synchronize()
+    counts = layer.counts.cpu().numpy()
+    sys.stderr.write("[bench] %s: timing %d steps\n" % (label, steps))
+    sys.stderr.flush()
+    with moe.Trace(capacity=16 * steps + 16) as tr:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            layer.forward()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        events = tr.read()
+    ms = (t1 - t0) * 1e3 / steps
+    per_kernel = {}
+    for name, dur in events:
+        per_kernel.setdefault(name, []).append(dur)
+    kernels = {k: {"mean_ms": float(np.mean(v)), "launches_per_step": len(v) / steps}
+               for k, v in per_kernel.items()}
+    alg = algorithmic(cfg, counts)
+    aux = float(layer.aux.cpu()[0])
+    del layer
+    torch.cuda.empty_cache()
+    return ms, kernels, alg, counts, aux
+
+
+def roofline_mfma(flops, mean_ms, peak):
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None}
+
+
+def roofline_hbm(nbytes, mean_ms):
+    achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+
+
+def cpu_baseline(cfg, n_tokens):
+    """The CPU oracle on the first n_tokens tokens of the workload (same weights)."""
+    from oracle import moe_oracle as O
+    sub = cfg.with_(T=n_tokens)
+    inp = W.make_inputs(cfg)
+    p = {"h": W.as_float32(inp["h"][:n_tokens]), "W_r": W.as_float32(inp["W_r"]),
+         "b_r": W.as_float32(inp["b_r"])}
+
+    class PerExpert:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return W.as_float32(self.t[e])
+
+    for k in ("W1", "W3", "W2", "b1", "b2"):
+        p[k] = None if inp[k] is None else PerExpert(inp[k])
+    O.build()
+    t0 = time.perf_counter()
+    O.moe_forward(p, sub.T, sub.d, sub.E, sub.K, sub.act, sub.gate)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d of %d tokens of %s (full layer: routing, %d experts' float64 FFNs, combine, "
+                      "aux); %.1f s wall" % (n_tokens, cfg.T, cfg.name, cfg.E, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="time only the prefill workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X only: this layer's path is built and measured on a single GPU "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.lib()  # fail loudly if the HIP library is missing
+
+    cfg = W.WORKLOADS["mixtral_prefill"]
+    ms, kernels, alg, counts, aux = time_workload(cfg, args.steps, args.warmup, "prefill")
+    g1 = kernels["gemm1"]["mean_ms"]
+    out = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs, random-init weights; no dataset)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "K": cfg.K, "width": cfg.width,
+                   "act": "swiglu", "gate": "renorm", "router": "float32", "parallelism": "single GPU"},
+        "roofline": dict(roofline_mfma(alg["flops_gemm1"], g1, PEAK_BF16_TFLOPS), kernel="gemm1"),
+        "layer_tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
+        "layer_mfma_frac": round(alg["flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "aux_loss": round(aux, 6),
+        "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in kernels.items()},
+    }
+    if not args.no_extra:
+        dcfg = W.WORKLOADS["mixtral_decode"]
+        dsteps = max(args.steps, 50)
+        dms, dk, dalg, dcounts, _ = time_workload(dcfg, dsteps, args.warmup, "decode")
+        out["decode"] = {
+            "workload": dcfg.name, "steps": dsteps, "ms_per_step": round(dms, 4),
+            "tokens_per_s": round(dcfg.T / (dms * 1e-3), 1),
+            "layer_hbm_GBps": round(dalg["bytes"] / (dms * 1e-3) / 1e9, 1),
+            "layer_hbm_frac": round(dalg["bytes"] / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "experts_hit": dalg["experts_hit"],
+            "roofline": dict(roofline_hbm(dalg["weight_bytes_gemm1"], dk["gemm1"]["mean_ms"]), kernel="gemm1"),
+            "roofline_gemm2": dict(roofline_hbm(dalg["weight_bytes_gemm2"], dk["gemm2"]["mean_ms"]),
+                                   kernel="gemm2"),
+            "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in dk.items()},
+        }
+        scfg = W.WORKLOADS["switch_top1"]
+        sms, sk, salg, scounts, saux = time_workload(scfg, args.steps, args.warmup, "switch")
+        out["switch_top1"] = {
+            "workload": scfg.name, "ms_per_step": round(sms, 4),
+            "tokens_per_s": round(scfg.T / (sms * 1e-3), 1),
+            "layer_tflops": round(salg["flops"] / (sms * 1e-3) / 1e12, 2),
+            "layer_hbm_GBps": round(salg["bytes"] / (sms * 1e-3) / 1e9, 1),
+            "layer_hbm_frac": round(salg["bytes"] / (sms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "roofline": dict(roofline_hbm(salg["weight_bytes_gemm1"], sk["gemm1"]["mean_ms"]), kernel="gemm1"),
+            "aux_loss": round(saux, 6), "experts_hit": salg["experts_hit"],
+            "max_expert_rows": int(scounts.max()),
+            "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in sk.items()},
+        }
+    if not args.no_cpu:
+        sys.stderr.write("[bench] cpu baseline: oracle on %d tokens\n" % args.cpu_tokens)
+        sys.stderr.flush()
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

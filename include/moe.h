@@ -1,0 +1,187 @@
+/*
+ * moe.h — C-ABI of a top-K routed mixture-of-experts FFN layer (forward pass)
+ * for the AMD MI355X (gfx950).
+ *
+ * The layer (Lensa ML explainer "Mixture of Experts", Steps 2-4; maptheai.com
+ * "Mixture of Experts", section "The mechanism"; Curionode "Mixture of
+ * Experts." Plate VII.4, introduction):
+ *   logits = h . W_r (+ b_r)         a linear router, kept in float32
+ *   p      = softmax over the E experts
+ *   choose the K experts with the largest logits
+ *   gates  = softmax over the K chosen logits (renormalised, Mixtral form)
+ *            or p_i itself (Switch top-1 form)
+ *   y      = sum over the chosen experts of gate * Expert_e(h)
+ *   aux    = E * sum_e f_e * P_e     (f_e = share of the T*K routing slots on e,
+ *                                     P_e = mean of p over tokens; Step 4)
+ * Only the chosen experts run, each on the rows routed to it.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Every pointer argument is a DEVICE pointer (memory owned by the caller,
+ *    e.g. a torch tensor), except `desc`, which is a host pointer read during
+ *    the call only. All tensors are contiguous, row-major, 16-byte aligned.
+ *  - The library never allocates device memory and never synchronises the
+ *    host. Scratch comes from the caller's workspace `ws` (`ws_bytes` long,
+ *    256-byte aligned), sized by moe_workspace_size(). All work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and is complete once the
+ *    stream is; outputs are not valid before that.
+ *  - Arguments are validated on the host before anything is enqueued. On any
+ *    error nothing is enqueued, no output is touched, and a nonzero moe_status
+ *    is returned. Nothing aborts, throws or prints.
+ *  - Results are bitwise identical from run to run on the same device (no
+ *    floating-point atomics anywhere).
+ *  - T = 0 is valid: routing outputs become zeros, aux becomes 0.
+ *  - Inputs must be finite; behaviour on NaN/Inf is unspecified.
+ *  - Calls keep no state between them (apart from the trace switch below) and
+ *    may run concurrently on different streams with disjoint buffers.
+ *
+ * Tensor layouts (S = T*K routing slots, bpe = 4 for MOE_F32, 2 for MOE_BF16)
+ *  h        [T][d]          dtype    token representations
+ *  W_r      [d][E]          float32  router weight (always float32)
+ *  b_r      [E]             float32  optional router bias, added to the logits
+ *  W1, W3   [E][width][d]   dtype    row n of expert e = column n of the d x width
+ *                                    matrix of the math (output-major: the reduction
+ *                                    dimension d is contiguous)
+ *  b1       [E][width]      dtype    GELU experts only (optional)
+ *  W2       [E][d][width]   dtype    row j of expert e = column j of the width x d matrix
+ *  b2       [E][d]          dtype    GELU experts only (optional)
+ *  topk_idx [T][K]          int32    chosen experts, largest logit first; equal
+ *                                    logits: lower expert index first
+ *  topk_gate[T][K]          float32  gate of each choice
+ *  expert_counts [E]        int32    routing slots per expert (sum = S)
+ *  expert_offsets[E+1]      int32    exclusive prefix sum of the counts
+ *  slot_token [S]           int32    token held by grouped row s
+ *  token_slot [T][K]        int32    grouped row of the j-th choice of token t
+ *  h_perm   [S][d]          dtype    h grouped by expert: rows of expert e are
+ *                                    offsets[e] .. offsets[e+1]-1, tokens ascending
+ *  o_perm   [S][d]          float32  ungated expert output of each grouped row
+ *  y        [T][d]          dtype    layer output
+ *
+ * Expert MLPs (Lensa ML Step 1: each expert is a full FFN):
+ *  MOE_ACT_GELU:   o = GELU(x W1 + b1) W2 + b2   (exact erf GELU; biases optional)
+ *  MOE_ACT_SWIGLU: o = (SiLU(x W1) * (x W3)) W2  (no biases; W3 required)
+ *
+ * Numerics: router logits are float32, accumulated for each (token, expert)
+ * as one sequential fused-multiply-add chain over k = 0..d-1 starting from +0,
+ * with the bias added afterwards; expert selection therefore depends on no
+ * summation-order choice. Softmax, gates and aux are float32. Expert GEMMs
+ * accumulate in float32 (bf16 inputs use bf16 MFMA); the hidden activation
+ * is stored in the input dtype; o_perm is float32; y is rounded once.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,        /* T < 0, d or width < 1, E < 1, K < 1 or K > E */
+  MOE_ERR_UNSUPPORTED = 3,  /* E > 64, K > 8, d or width not a multiple of 8, S or
+                               tensor sizes beyond 2^31 - 1 elements, an unknown
+                               act/gate/dtype, a misaligned pointer, or W3 missing
+                               for SwiGLU */
+  MOE_ERR_WORKSPACE = 4,    /* ws_bytes smaller than moe_workspace_size(), or ws misaligned */
+  MOE_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum moe_act { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
+typedef enum moe_gate { MOE_GATE_RENORM = 0, MOE_GATE_RAW = 1 } moe_gate;
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Shape of one layer, in the pages' terms: T tokens of width d, E experts of
+ * width `width`, K chosen per token (Lensa ML Steps 1 and 3). */
+typedef struct moe_desc {
+  int64_t T;
+  int64_t d;
+  int64_t E;
+  int64_t K;
+  int64_t width;
+  int32_t act;    /* moe_act */
+  int32_t gate;   /* moe_gate */
+  int32_t dtype;  /* moe_dtype: h, W1, W3, W2, b1, b2, h_perm, y */
+  int32_t reserved; /* must be 0 */
+} moe_desc;
+
+/* Human-readable name of a moe_status value (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* Bytes of workspace that any entry point below needs for this layer shape.
+ * Host-only; enqueues nothing. */
+int moe_workspace_size(const moe_desc* desc, size_t* bytes);
+
+/* Router (Lensa ML Step 2: a linear layer and a softmax; Step 3: top-k and
+ * gates; Step 4: slot counts and the load-balance loss).
+ * In:  h, W_r, b_r (nullable).
+ * Out: topk_idx, topk_gate, expert_counts, prob_mean [E] (P_e, nullable),
+ *      aux_loss [1] (nullable), logits [T][E] float32 (nullable).
+ * Returns a moe_status. */
+int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
+              int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
+              float* prob_mean, float* aux_loss, float* logits,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Grouping of the routing slots by expert (Lensa ML Step 5: experts take any
+ * number of tokens; no token is dropped). Stable: inside each expert's group
+ * tokens keep their order.
+ * In:  topk_idx, h.
+ * Out: expert_offsets, slot_token, token_slot, h_perm (gathered rows of h).
+ * Returns a moe_status. */
+int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h,
+                int32_t* expert_offsets, int32_t* slot_token, int32_t* token_slot,
+                void* h_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Each expert's FFN on its own grouped rows only (maptheai.com "The mechanism":
+ * only the chosen experts run; Lensa ML Step 1: each expert is a full FFN).
+ * In:  h_perm, expert_offsets, W1, b1 (nullable), W3 (SwiGLU), W2, b2 (nullable).
+ * Out: o_perm (ungated float32 expert outputs, one row per grouped slot).
+ * Returns a moe_status. */
+int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expert_offsets,
+                   const void* W1, const void* b1, const void* W3, const void* W2,
+                   const void* b2, float* o_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Gated combine y[t] = sum_j gate[t][j] * o_perm[token_slot[t][j]] (Lensa ML
+ * Step 3; maptheai.com "The mechanism"), accumulated in float32 in ascending j
+ * and rounded once to dtype. A gather: each y row is written by one owner.
+ * Needs no workspace. Returns a moe_status. */
+int moe_combine(const moe_desc* desc, const float* o_perm, const int32_t* token_slot,
+                const float* topk_gate, void* y, void* stream);
+
+/* The whole layer: route -> group -> experts -> combine, plus the aux loss.
+ * In:  h, W_r, b_r (nullable), W1, b1 (nullable), W3 (SwiGLU), W2, b2 (nullable).
+ * Out: y, aux_loss [1] (nullable), expert_counts [E] (nullable).
+ * For K = 1 the second expert GEMM writes gate * o straight into y.
+ * Returns a moe_status. */
+int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
+                const void* W1, const void* b1, const void* W3, const void* W2,
+                const void* b2, void* y, float* aux_loss, int32_t* expert_counts,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Instrumentation (not part of the layer). While enabled, every kernel the
+ * library launches is bracketed by two hipEvents recorded on its launch
+ * stream, for up to `capacity` launches (later launches are not traced).
+ * moe_trace_enable creates the events (host-side HIP calls); moe_trace_read
+ * waits for the recorded events, writes up to `max` entries of kernel id
+ * (moe_kernel_id) and duration in milliseconds, sets *n, and rewinds the
+ * buffer; moe_trace_disable frees the events. Not thread-safe. */
+typedef enum moe_kernel_id {
+  MOE_K_ROUTE = 0, MOE_K_FINALIZE = 1, MOE_K_HIST = 2, MOE_K_PERMUTE = 3,
+  MOE_K_GEMM1 = 4, MOE_K_GEMM2 = 5, MOE_K_COMBINE = 6, MOE_K_ZERO = 7
+} moe_kernel_id;
+int moe_trace_enable(int capacity);
+int moe_trace_read(int32_t* kernel_id, float* ms, int max, int* n);
+int moe_trace_disable(void);
+
+/* Name of a kernel id for reports (static string, never NULL). */
+const char* moe_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,417 @@
+// C-ABI of the MoE layer (declared in include/moe.h): argument validation,
+// workspace carving and kernel launches on the caller's stream.
+//
+// Nothing here allocates device memory or synchronises the host (the trace
+// functions aside). Every entry point validates all arguments before its first
+// HIP call, so an invalid call leaves outputs and the stream untouched.
+#include <vector>
+
+#include "moe.h"
+#include "kernels.h"
+
+namespace moe {
+hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st);
+hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st);
+hipError_t launch_gemm1_f32(const FfnArgs& f, hipStream_t st);
+hipError_t launch_gemm2_f32(const FfnArgs& f, hipStream_t st);
+
+hipError_t launch_gemm1(const FfnArgs& f, hipStream_t st) {
+  return f.bf16 ? launch_gemm1_bf16(f, st) : launch_gemm1_f32(f, st);
+}
+hipError_t launch_gemm2(const FfnArgs& f, hipStream_t st) {
+  return f.bf16 ? launch_gemm2_bf16(f, st) : launch_gemm2_f32(f, st);
+}
+}  // namespace moe
+
+namespace {
+
+using moe::RouteTiling;
+
+constexpr int64_t kMaxInt = 2147483647;
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Plan {
+  RouteTiling rt;
+  size_t blk_hist, blk_psum, blk_base;
+  size_t topk_idx, topk_gate, token_slot, slot_token;
+  size_t counts, offsets, pmean, aux;
+  size_t h_perm, act, o_perm;
+  size_t total;
+};
+
+Plan make_plan(const moe_desc& d) {
+  Plan p{};
+  p.rt = moe::route_tiling(d.T, d.E);
+  const size_t S = static_cast<size_t>(d.T) * d.K;
+  const size_t bpe = d.dtype == MOE_BF16 ? 2 : 4;
+  const size_t nbe = static_cast<size_t>(p.rt.NB) * d.E;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  p.blk_hist = take(nbe * 4);
+  p.blk_psum = take(nbe * 4);
+  p.blk_base = take(nbe * 4);
+  p.topk_idx = take(S * 4);
+  p.topk_gate = take(S * 4);
+  p.token_slot = take(S * 4);
+  p.slot_token = take(S * 4);
+  p.counts = take(d.E * 4);
+  p.offsets = take((d.E + 1) * 4);
+  p.pmean = take(d.E * 4);
+  p.aux = take(4);
+  p.h_perm = take(S * d.d * bpe);
+  p.act = take(S * d.width * bpe);
+  p.o_perm = take(d.K > 1 ? S * d.d * 4 : 0);
+  p.total = off;
+  return p;
+}
+
+int check_desc(const moe_desc* d) {
+  if (d == nullptr) return MOE_ERR_NULL;
+  if (d->T < 0 || d->d < 1 || d->width < 1 || d->E < 1 || d->K < 1 || d->K > d->E) return MOE_ERR_SHAPE;
+  if (d->E > 64 || d->K > 8 || d->d % 8 != 0 || d->width % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->act != MOE_ACT_GELU && d->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (d->gate != MOE_GATE_RENORM && d->gate != MOE_GATE_RAW) return MOE_ERR_UNSUPPORTED;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->reserved != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->T > kMaxInt / d->K || d->d > kMaxInt || d->width > kMaxInt) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// A tensor pointer: NULL only when the tensor has no elements; 16-byte aligned.
+int check_ptr(const void* p, bool has_elements) {
+  if (p == nullptr) return has_elements ? MOE_ERR_NULL : MOE_OK;
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_ws(const Plan& pl, const void* ws, size_t ws_bytes) {
+  if (ws_bytes < pl.total) return MOE_ERR_WORKSPACE;
+  if (pl.total > 0 && ws == nullptr) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+#define MOE_CHECK(expr)              \
+  do {                               \
+    const int _s = (expr);           \
+    if (_s != MOE_OK) return _s;     \
+  } while (0)
+
+int check_experts(const moe_desc& d, const void* W1, const void* b1, const void* W3, const void* W2,
+                  const void* b2) {
+  MOE_CHECK(check_ptr(W1, true));
+  MOE_CHECK(check_ptr(W2, true));
+  if (d.act == MOE_ACT_SWIGLU) {
+    if (W3 == nullptr) return MOE_ERR_UNSUPPORTED;
+    MOE_CHECK(check_ptr(W3, true));
+  }
+  MOE_CHECK(check_ptr(b1, false));
+  MOE_CHECK(check_ptr(b2, false));
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ---------------------------------------------------------------------------- tracing
+
+struct TraceState {
+  bool on = false;
+  int cap = 0;
+  int n = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<int32_t> kid;
+};
+TraceState g_trace;
+
+template <typename F>
+hipError_t traced(int kid, hipStream_t st, F&& launch) {
+  if (!g_trace.on || g_trace.n >= g_trace.cap) return launch();
+  const int i = g_trace.n++;
+  g_trace.kid[i] = kid;
+  (void)hipEventRecord(g_trace.ev[2 * i], st);
+  const hipError_t err = launch();
+  (void)hipEventRecord(g_trace.ev[2 * i + 1], st);
+  return err;
+}
+
+
+#define MOE_LAUNCH(kid, st, call)                                 \
+  do {                                                            \
+    const hipError_t _e = traced((kid), (st), [&] { return call; }); \
+    if (_e != hipSuccess) return MOE_ERR_HIP;                     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: invalid layer shape";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape, type or alignment not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small or misaligned";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_kernel_name(int kernel_id) {
+  switch (kernel_id) {
+    case MOE_K_ROUTE: return "route";
+    case MOE_K_FINALIZE: return "finalize";
+    case MOE_K_HIST: return "hist";
+    case MOE_K_PERMUTE: return "permute";
+    case MOE_K_GEMM1: return "gemm1";
+    case MOE_K_GEMM2: return "gemm2";
+    case MOE_K_COMBINE: return "combine";
+    case MOE_K_ZERO: return "zero";
+    default: return "unknown";
+  }
+}
+
+int moe_workspace_size(const moe_desc* desc, size_t* bytes) {
+  MOE_CHECK(check_desc(desc));
+  if (bytes == nullptr) return MOE_ERR_NULL;
+  *bytes = make_plan(*desc).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, int32_t* topk_idx,
+              float* topk_gate, int32_t* expert_counts, float* prob_mean, float* aux_loss, float* logits,
+              void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_desc(desc));
+  const moe_desc& d = *desc;
+  const bool any = d.T > 0;
+  MOE_CHECK(check_ptr(h, any));
+  MOE_CHECK(check_ptr(W_r, true));
+  MOE_CHECK(check_ptr(b_r, false));
+  MOE_CHECK(check_ptr(topk_idx, any));
+  MOE_CHECK(check_ptr(topk_gate, any));
+  MOE_CHECK(check_ptr(expert_counts, true));
+  MOE_CHECK(check_ptr(prob_mean, false));
+  MOE_CHECK(check_ptr(aux_loss, false));
+  MOE_CHECK(check_ptr(logits, false));
+  const Plan pl = make_plan(d);
+  MOE_CHECK(check_ws(pl, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!any) {
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, expert_counts, nullptr, prob_mean, aux_loss, st));
+    return MOE_OK;
+  }
+  moe::RouteArgs ra{h, W_r, b_r, static_cast<int>(d.T), static_cast<int>(d.d), static_cast<int>(d.E),
+                    static_cast<int>(d.K), d.gate, topk_idx, topk_gate, logits,
+                    at<int32_t>(ws, pl.blk_hist), at<float>(ws, pl.blk_psum)};
+  MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, d.dtype == MOE_BF16, st));
+  MOE_LAUNCH(MOE_K_FINALIZE, st,
+             moe::launch_finalize(ra.blk_hist, ra.blk_psum, pl.rt.NB, ra.T, ra.E, ra.K, nullptr, expert_counts,
+                                  nullptr, prob_mean, aux_loss, st));
+  return MOE_OK;
+}
+
+int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h, int32_t* expert_offsets,
+                int32_t* slot_token, int32_t* token_slot, void* h_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+  MOE_CHECK(check_desc(desc));
+  const moe_desc& d = *desc;
+  const bool any = d.T > 0;
+  MOE_CHECK(check_ptr(topk_idx, any));
+  MOE_CHECK(check_ptr(h, any));
+  MOE_CHECK(check_ptr(expert_offsets, true));
+  MOE_CHECK(check_ptr(slot_token, any));
+  MOE_CHECK(check_ptr(token_slot, any));
+  MOE_CHECK(check_ptr(h_perm, any));
+  const Plan pl = make_plan(d);
+  MOE_CHECK(check_ws(pl, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!any) {
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, nullptr, expert_offsets, nullptr, nullptr, st));
+    return MOE_OK;
+  }
+  const int T = static_cast<int>(d.T), E = static_cast<int>(d.E), K = static_cast<int>(d.K);
+  int32_t* blk_hist = at<int32_t>(ws, pl.blk_hist);
+  int32_t* blk_base = at<int32_t>(ws, pl.blk_base);
+  const size_t row_bytes = static_cast<size_t>(d.d) * (d.dtype == MOE_BF16 ? 2 : 4);
+  MOE_LAUNCH(MOE_K_HIST, st, moe::launch_hist(topk_idx, T, E, K, pl.rt, blk_hist, st));
+  MOE_LAUNCH(MOE_K_FINALIZE, st,
+             moe::launch_finalize(blk_hist, nullptr, pl.rt.NB, T, E, K, blk_base, nullptr, expert_offsets,
+                                  nullptr, nullptr, st));
+  MOE_LAUNCH(MOE_K_PERMUTE, st,
+             moe::launch_permute(topk_idx, blk_base, T, E, K, pl.rt, h, row_bytes, h_perm, slot_token,
+                                 token_slot, st));
+  return MOE_OK;
+}
+
+int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expert_offsets, const void* W1,
+                   const void* b1, const void* W3, const void* W2, const void* b2, float* o_perm, void* ws,
+                   size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_desc(desc));
+  const moe_desc& d = *desc;
+  const bool any = d.T > 0;
+  MOE_CHECK(check_ptr(h_perm, any));
+  MOE_CHECK(check_ptr(expert_offsets, true));
+  MOE_CHECK(check_experts(d, W1, b1, W3, W2, b2));
+  MOE_CHECK(check_ptr(o_perm, any));
+  const Plan pl = make_plan(d);
+  MOE_CHECK(check_ws(pl, ws, ws_bytes));
+  if (!any) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe::FfnArgs f{};
+  f.S = static_cast<int>(d.T * d.K);
+  f.d = static_cast<int>(d.d);
+  f.E = static_cast<int>(d.E);
+  f.K = static_cast<int>(d.K);
+  f.width = static_cast<int>(d.width);
+  f.act = d.act;
+  f.bf16 = d.dtype == MOE_BF16;
+  f.x = h_perm;
+  f.offsets = expert_offsets;
+  f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
+  f.a = at<char>(ws, pl.act);
+  f.o_perm = o_perm;
+  f.fused_y = false;
+  f.max_rows_per_expert = static_cast<int>(d.T);
+  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_gemm1(f, st));
+  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_gemm2(f, st));
+  return MOE_OK;
+}
+
+int moe_combine(const moe_desc* desc, const float* o_perm, const int32_t* token_slot, const float* topk_gate,
+                void* y, void* stream) {
+  MOE_CHECK(check_desc(desc));
+  const moe_desc& d = *desc;
+  const bool any = d.T > 0;
+  MOE_CHECK(check_ptr(o_perm, any));
+  MOE_CHECK(check_ptr(token_slot, any));
+  MOE_CHECK(check_ptr(topk_gate, any));
+  MOE_CHECK(check_ptr(y, any));
+  if (!any) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MOE_LAUNCH(MOE_K_COMBINE, st,
+             moe::launch_combine(o_perm, token_slot, topk_gate, static_cast<int>(d.T), static_cast<int>(d.d),
+                                 static_cast<int>(d.K), d.dtype == MOE_BF16, y, st));
+  return MOE_OK;
+}
+
+int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, const void* W1,
+                const void* b1, const void* W3, const void* W2, const void* b2, void* y, float* aux_loss,
+                int32_t* expert_counts, void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_desc(desc));
+  const moe_desc& d = *desc;
+  const bool any = d.T > 0;
+  MOE_CHECK(check_ptr(h, any));
+  MOE_CHECK(check_ptr(W_r, true));
+  MOE_CHECK(check_ptr(b_r, false));
+  MOE_CHECK(check_experts(d, W1, b1, W3, W2, b2));
+  MOE_CHECK(check_ptr(y, any));
+  MOE_CHECK(check_ptr(aux_loss, false));
+  MOE_CHECK(check_ptr(expert_counts, false));
+  const Plan pl = make_plan(d);
+  MOE_CHECK(check_ws(pl, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!any) {
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, expert_counts, nullptr, nullptr, aux_loss, st));
+    return MOE_OK;
+  }
+  const int T = static_cast<int>(d.T), E = static_cast<int>(d.E), K = static_cast<int>(d.K);
+  const bool bf16 = d.dtype == MOE_BF16;
+  int32_t* topk_idx = at<int32_t>(ws, pl.topk_idx);
+  float* topk_gate = at<float>(ws, pl.topk_gate);
+  int32_t* blk_hist = at<int32_t>(ws, pl.blk_hist);
+  float* blk_psum = at<float>(ws, pl.blk_psum);
+  int32_t* blk_base = at<int32_t>(ws, pl.blk_base);
+  int32_t* offsets = at<int32_t>(ws, pl.offsets);
+  int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
+  int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
+  void* h_perm = at<char>(ws, pl.h_perm);
+  int32_t* counts = expert_counts != nullptr ? expert_counts : at<int32_t>(ws, pl.counts);
+
+  moe::RouteArgs ra{h, W_r, b_r, T, static_cast<int>(d.d), E, K, d.gate, topk_idx, topk_gate, nullptr,
+                    blk_hist, blk_psum};
+  MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
+  MOE_LAUNCH(MOE_K_FINALIZE, st,
+             moe::launch_finalize(blk_hist, blk_psum, pl.rt.NB, T, E, K, blk_base, counts, offsets, nullptr,
+                                  aux_loss, st));
+  const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
+  MOE_LAUNCH(MOE_K_PERMUTE, st,
+             moe::launch_permute(topk_idx, blk_base, T, E, K, pl.rt, h, row_bytes, h_perm, slot_token,
+                                 token_slot, st));
+  moe::FfnArgs f{};
+  f.S = T * K;
+  f.d = static_cast<int>(d.d);
+  f.E = E;
+  f.K = K;
+  f.width = static_cast<int>(d.width);
+  f.act = d.act;
+  f.bf16 = bf16;
+  f.x = h_perm;
+  f.offsets = offsets;
+  f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
+  f.a = at<char>(ws, pl.act);
+  f.o_perm = at<float>(ws, pl.o_perm);
+  f.fused_y = K == 1;
+  f.y = y;
+  f.slot_token = slot_token;
+  f.topk_gate = topk_gate;
+  f.max_rows_per_expert = T;
+  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_gemm1(f, st));
+  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_gemm2(f, st));
+  if (K > 1) {
+    MOE_LAUNCH(MOE_K_COMBINE, st, moe::launch_combine(f.o_perm, token_slot, topk_gate, T, f.d, K, bf16, y, st));
+  }
+  return MOE_OK;
+}
+
+int moe_trace_enable(int capacity) {
+  if (capacity < 1) return MOE_ERR_SHAPE;
+  moe_trace_disable();
+  g_trace.ev.assign(2 * static_cast<size_t>(capacity), nullptr);
+  g_trace.kid.assign(capacity, -1);
+  for (auto& e : g_trace.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      moe_trace_disable();
+      return MOE_ERR_HIP;
+    }
+  }
+  g_trace.cap = capacity;
+  g_trace.n = 0;
+  g_trace.on = true;
+  return MOE_OK;
+}
+
+int moe_trace_read(int32_t* kernel_id, float* ms, int max, int* n) {
+  if (kernel_id == nullptr || ms == nullptr || n == nullptr) return MOE_ERR_NULL;
+  const int cnt = g_trace.n < max ? g_trace.n : max;
+  if (g_trace.n > 0 && hipEventSynchronize(g_trace.ev[2 * (g_trace.n - 1) + 1]) != hipSuccess) return MOE_ERR_HIP;
+  for (int i = 0; i < cnt; ++i) {
+    kernel_id[i] = g_trace.kid[i];
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]) != hipSuccess) return MOE_ERR_HIP;
+    ms[i] = t;
+  }
+  *n = cnt;
+  g_trace.n = 0;
+  return MOE_OK;
+}
+
+int moe_trace_disable(void) {
+  for (auto& e : g_trace.ev)
+    if (e != nullptr) (void)hipEventDestroy(e);
+  g_trace.ev.clear();
+  g_trace.kid.clear();
+  g_trace.cap = 0;
+  g_trace.n = 0;
+  g_trace.on = false;
+  return MOE_OK;
+}
+
+}  // extern "C"

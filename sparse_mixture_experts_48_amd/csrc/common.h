@@ -1,0 +1,69 @@
+// Device helpers shared by the layer's HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits in memory
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round to nearest even; inputs are finite.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Exact GELU, 0.5 z (1 + erf(z / sqrt 2)), with the device erff.
+__device__ __forceinline__ float gelu_exact(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Which expert owns global m-tile `mt` when every expert's rows are cut into
+// tiles of `bm` rows. Returns false if `mt` is past the last tile.
+// offsets: [E+1] exclusive prefix of the per-expert row counts.
+__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int bm,
+                                            int mt, int* expert, int* row0, int* rows) {
+  int acc = 0;
+  for (int e = 0; e < E; ++e) {
+    const int beg = offsets[e];
+    const int cnt = offsets[e + 1] - beg;
+    const int nt = (cnt + bm - 1) / bm;
+    if (mt < acc + nt) {
+      const int local = mt - acc;
+      *expert = e;
+      *row0 = beg + local * bm;
+      *rows = min(bm, cnt - local * bm);
+      return true;
+    }
+    acc += nt;
+  }
+  return false;
+}
+
+}  // namespace moe

@@ -1,0 +1,68 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Token tiling of the router; the grouping kernels reuse it so that the
+// router's per-block histograms line up with the grouping blocks.
+struct RouteTiling {
+  int EP;   // experts padded to 8, 16, 32 or 64
+  int TPT;  // tokens per thread
+  int TB;   // tokens per block
+  int NB;   // blocks
+};
+RouteTiling route_tiling(int64_t T, int64_t E);
+
+struct RouteArgs {
+  const void* h;
+  const float* Wr;
+  const float* br;
+  int T, d, E, K, gate;
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* logits;      // nullable
+  int32_t* blk_hist;  // [NB][E]
+  float* blk_psum;    // [NB][E]
+};
+
+hipError_t launch_route(const RouteArgs& a, const RouteTiling& rt, bool bf16, hipStream_t st);
+hipError_t launch_hist(const int32_t* topk_idx, int T, int E, int K, const RouteTiling& rt,
+                       int32_t* blk_hist, hipStream_t st);
+hipError_t launch_finalize(const int32_t* blk_hist, const float* blk_psum, int NB, int T, int E, int K,
+                           int32_t* blk_base, int32_t* counts, int32_t* offsets, float* prob_mean,
+                           float* aux, hipStream_t st);
+hipError_t launch_zero_outputs(int E, int32_t* counts, int32_t* offsets, float* prob_mean, float* aux,
+                               hipStream_t st);
+
+// Stable grouping: slot ranks, token_slot, slot_token and the gathered rows.
+hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, int T, int E, int K,
+                          const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
+                          int32_t* slot_token, int32_t* token_slot, hipStream_t st);
+
+// Expert GEMMs over the grouped rows.
+struct FfnArgs {
+  int S, d, E, K, width, act;  // S = T*K grouped rows
+  bool bf16;
+  const void* x;               // h_perm [S][d]
+  const int32_t* offsets;      // [E+1]
+  const void* W1; const void* b1; const void* W3; const void* W2; const void* b2;
+  void* a;                     // hidden activations [S][width], dtype (workspace)
+  float* o_perm;               // [S][d] float32; unused when fused_y
+  // K = 1 fused gated scatter: y[slot_token[s]] = gate[slot_token[s]] * o[s]
+  bool fused_y;
+  void* y;
+  const int32_t* slot_token;
+  const float* topk_gate;
+  int max_rows_per_expert;     // host-known bound (T) used to pick the kernel family
+};
+hipError_t launch_gemm1(const FfnArgs& f, hipStream_t st);
+hipError_t launch_gemm2(const FfnArgs& f, hipStream_t st);
+
+hipError_t launch_combine(const float* o_perm, const int32_t* token_slot, const float* topk_gate,
+                          int T, int d, int K, bool bf16, void* y, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,101 @@
+// Stable grouping of the T*K routing slots by expert.
+//
+// Lensa ML explainer "Mixture of Experts", Step 5: instead of fixed capacity
+// buffers, experts take any number of tokens (dropless). Each expert's rows
+// are contiguous; inside a group tokens keep their order, so the result is
+// the stable sort of the slots by (expert, token).
+//
+// Block b owns the same token range as router block b. Its base row for
+// expert e is offsets[e] + (slots of e in blocks before b), computed by the
+// finalize kernel. Inside the block, wave w counts its 64 tokens per expert
+// with a ballot; a token's rank is the popcount of the lanes below it that
+// chose the same expert, plus the counts of earlier waves.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPermThreads = 256;  // 4 waves x 64 tokens
+constexpr int kMaxK = 8;
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_base, int T, int E, int K,
+    int TB, const char* __restrict__ h, size_t row_bytes, char* __restrict__ h_perm,
+    int32_t* __restrict__ slot_token, int32_t* __restrict__ token_slot) {
+  __shared__ int cnt_s[kPermThreads / 64][64];
+  __shared__ int slots_s[kPermThreads][kMaxK];
+  const int wave = threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const int t0 = blockIdx.x * TB;
+  const int lt = threadIdx.x;
+  const int t = t0 + lt;
+  const bool ok = lt < TB && t < T;
+  int ids[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) ids[j] = (ok && j < K) ? topk_idx[static_cast<size_t>(t) * K + j] : -1;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  for (int e = 0; e < E; ++e) {
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) has |= (ids[j] == e);
+    const uint64_t m = __ballot(has);
+    if (lane == 0) cnt_s[wave][e] = __popcll(m);
+  }
+  __syncthreads();
+
+  for (int e = 0; e < E; ++e) {
+    int base = blk_base[static_cast<size_t>(blockIdx.x) * E + e];
+    for (int w = 0; w < wave; ++w) base += cnt_s[w][e];
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) has |= (ids[j] == e);
+    const uint64_t m = __ballot(has);
+    if (has) {
+      const int slot = base + __popcll(m & below);
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (ids[j] == e) {
+          token_slot[static_cast<size_t>(t) * K + j] = slot;
+          slots_s[lt][j] = slot;
+        }
+      }
+      slot_token[slot] = t;
+    }
+  }
+
+  if (h_perm == nullptr) return;
+  __syncthreads();
+  // Gather: each token row is read once and written to its K grouped rows.
+  const int ntok = min(TB, T - t0);
+  const int nvec = static_cast<int>(row_bytes / 16);
+  for (int r = wave; r < ntok; r += kPermThreads / 64) {
+    const uint4* src = reinterpret_cast<const uint4*>(h + static_cast<size_t>(t0 + r) * row_bytes);
+    int sl[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) sl[j] = (j < K) ? slots_s[r][j] : 0;
+    for (int c = lane; c < nvec; c += 64) {
+      const uint4 v = src[c];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j < K) reinterpret_cast<uint4*>(h_perm + static_cast<size_t>(sl[j]) * row_bytes)[c] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, int T, int E, int K,
+                          const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
+                          int32_t* slot_token, int32_t* token_slot, hipStream_t st) {
+  if (rt.TB > kPermThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_kernel, dim3(rt.NB), dim3(kPermThreads), 0, st, topk_idx, blk_base, T, E, K,
+                     rt.TB, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
+                     slot_token, token_slot);
+  return hipGetLastError();
+}
+
+}  // namespace moe

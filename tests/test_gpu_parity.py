@@ -1,0 +1,236 @@
+"""Parity of the HIP path (through the C-ABI) against the CPU oracle.
+
+Bars: bit-exact expert choice, router logits, counts, offsets, grouping and
+gathered rows; gates within 1e-6; P and aux within 1e-5 relative; the float32
+expert outputs within max|d|/rms <= 1e-5 (float32 layers) or 2e-2 (bfloat16
+layers); y within the same bars once each element's own output rounding (half
+an ulp of the output dtype) is discounted; the combine stage within one
+rounding of its float32 sum.
+
+Small cases run the whole oracle and span several tiles with ragged tails;
+the five full-size workloads compare all routing outputs and a sample of y
+rows (every used expert is represented), in the same launch configuration as
+the benchmark.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import sparse_mixture_experts_48_amd as moe
+from oracle import moe_oracle as O
+from sparse_mixture_experts_48_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - the CPU suite deselects these
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+L = W.LayerShape
+SMALL = {
+    # name: shape (T, d, E, K, width, act, gate, dtype, router_bias, seed)
+    "f32_gelu_ragged": L("f32_gelu_ragged", 300, 128, 8, 2, 512, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "none", 11),
+    "f32_swiglu_k1_fused": L("f32_swiglu_k1_fused", 201, 64, 4, 1, 200, W.ACT_SWIGLU, W.GATE_RAW, W.DT_F32,
+                             "normal2", 12),
+    "f32_swiglu_k2": L("f32_swiglu_k2", 97, 72, 6, 2, 136, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_F32, "none", 24),
+    "bf16_gelu_skewed_e64": L("bf16_gelu_skewed_e64", 700, 128, 64, 2, 512, W.ACT_GELU, W.GATE_RENORM,
+                              W.DT_BF16, "normal2", 13),
+    "bf16_swiglu_tails": L("bf16_swiglu_tails", 333, 256, 8, 2, 680, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16,
+                           "none", 14),
+    "bf16_switch_k1": L("bf16_switch_k1", 517, 512, 16, 1, 344, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
+                        "zipf1.1", 15),
+    "bf16_k3_e12": L("bf16_k3_e12", 150, 192, 12, 3, 256, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 16),
+    "bf16_k_equals_e": L("bf16_k_equals_e", 100, 128, 4, 4, 128, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16,
+                         "none", 17),
+    "bf16_e1_k1": L("bf16_e1_k1", 64, 128, 1, 1, 256, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "none", 18),
+    "bf16_raw_k2_e40": L("bf16_raw_k2_e40", 260, 136, 40, 2, 264, W.ACT_GELU, W.GATE_RAW, W.DT_BF16,
+                         "normal2", 19),
+    "bf16_many_tiles": L("bf16_many_tiles", 2048, 256, 8, 2, 384, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16,
+                         "none", 25),
+    "stream_T16": L("stream_T16", 16, 512, 8, 2, 1376, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 20),
+    "stream_T32_tails": L("stream_T32_tails", 32, 264, 8, 2, 520, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16,
+                          "none", 21),
+    "stream_T5_k1_e64": L("stream_T5_k1_e64", 5, 256, 64, 1, 128, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
+                          "zipf1.1", 22),
+    "stream_gelu_T24": L("stream_gelu_T24", 24, 128, 8, 2, 512, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16,
+                         "normal2", 23),
+    "T1": L("T1", 1, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 26),
+    "f32_T1": L("f32_T1", 1, 64, 8, 2, 64, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2", 27),
+}
+
+
+def _case(cfg, zero_router=False):
+    inp = W.make_inputs(cfg)
+    if zero_router:  # every logit ties: experts 0..K-1 take every token
+        inp["W_r"] = torch.zeros_like(inp["W_r"])
+        inp["b_r"] = None
+    return inp
+
+
+def _check_route(cfg, dev, r):
+    desc = moe.desc_of(cfg)
+    g = moe.route(desc, dev["h"], dev["W_r"], dev["b_r"], want_logits=True)
+    torch.cuda.synchronize()
+    H.check_logits_bits(H.to_np(g["logits"]), r["logits"])
+    H.check_bits_equal("topk_idx", H.to_np(g["topk_idx"]), r["topk_idx"])
+    H.check_bits_equal("expert_counts", H.to_np(g["counts"]), r["counts"])
+    gate_err = float(np.max(np.abs(H.to_np(g["topk_gate"]) - r["topk_gate"]))) if cfg.T else 0.0
+    assert gate_err <= H.GATE_ATOL, gate_err
+    P = r["probs"].mean(axis=0) if cfg.T else np.zeros(cfg.E)
+    assert np.max(np.abs(H.to_np(g["prob_mean"]) - P)) <= H.PROB_RTOL * max(P.max(), 1e-30) + 1e-7
+    aux = float(H.to_np(g["aux"])[0])
+    assert abs(aux - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0), (aux, r["aux"])
+
+
+def _check_permute(cfg, dev, r):
+    desc = moe.desc_of(cfg)
+    idx = torch.from_numpy(r["topk_idx"]).cuda()
+    g = moe.permute(desc, idx, dev["h"])
+    torch.cuda.synchronize()
+    H.check_bits_equal("expert_offsets", H.to_np(g["offsets"]), r["offsets"])
+    H.check_bits_equal("slot_token", H.to_np(g["slot_token"]), r["slot_token"])
+    H.check_bits_equal("token_slot", H.to_np(g["token_slot"]), r["token_slot"])
+    want = dev["h"][torch.from_numpy(r["slot_token"].astype(np.int64)).cuda()]
+    assert torch.equal(g["h_perm"].view(torch.int16) if want.dtype == torch.bfloat16 else g["h_perm"],
+                       want.view(torch.int16) if want.dtype == torch.bfloat16 else want), "h_perm rows differ"
+
+
+def _check_expert_ffn(cfg, inp, dev, r, slots=None):
+    desc = moe.desc_of(cfg)
+    h_perm = dev["h"][torch.from_numpy(r["slot_token"].astype(np.int64)).cuda()].contiguous()
+    offs = torch.from_numpy(r["offsets"]).cuda()
+    o = moe.expert_ffn(desc, h_perm, offs, dev["W1"], dev["b1"], dev["W3"], dev["W2"], dev["b2"])
+    torch.cuda.synchronize()
+    o = H.to_np(o)
+    p = H.oracle_params(inp)
+    slots = np.arange(cfg.S) if slots is None else np.asarray(slots)
+    ref = np.zeros((len(slots), cfg.d))
+    got = o[slots]
+    expert_of_slot = np.searchsorted(r["offsets"], slots, side="right") - 1
+    for e in np.unique(expert_of_slot):
+        sel = np.nonzero(expert_of_slot == e)[0]
+        x = p["h"][r["slot_token"][slots[sel]]]
+        ref[sel] = O.expert_ffn(x, int(e), p, cfg.act)
+    err = H.rel_err(got, ref)
+    assert err <= H.Y_TOL[cfg.dtype], err
+
+
+def _check_combine(cfg, r):
+    desc = moe.desc_of(cfg)
+    # feed float32-rounded oracle expert outputs and gates; compare against the
+    # oracle combine of exactly those float32 values
+    rng = np.random.default_rng(cfg.seed)
+    o32 = rng.standard_normal((cfg.S, cfg.d)).astype(np.float32)
+    g32 = r["topk_gate"].astype(np.float32)
+    y = moe.combine(desc, torch.from_numpy(o32).cuda(), torch.from_numpy(r["token_slot"]).cuda(),
+                    torch.from_numpy(g32).cuda(), cfg.torch_dtype)
+    torch.cuda.synchronize()
+    ref = O.combine(o32.astype(np.float64), r["token_slot"], g32.astype(np.float64))
+    # elementwise bound: K float32 fmas (each within 2^-24 of the running sum
+    # of |g o|), then for bfloat16 one round-to-nearest (2^-8 relative)
+    mag = O.combine(np.abs(o32.astype(np.float64)), r["token_slot"], np.abs(g32.astype(np.float64)))
+    bound = (cfg.K + 1) * 2.0 ** -24 * mag
+    if cfg.dtype == W.DT_BF16:
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    diff = np.abs(H.to_np(y).astype(np.float64) - ref)
+    worst = np.unravel_index(np.argmax(diff - bound), diff.shape)
+    assert np.all(diff <= bound), ("combine outside one-rounding bound", worst, diff[worst], bound[worst])
+
+
+def _check_forward(cfg, dev, r, rows=None, repeats=3):
+    layer_desc = moe.desc_of(cfg)
+    ws = moe.workspace(layer_desc)
+    outs = []
+    for _ in range(repeats):
+        y, aux, counts = moe.forward(layer_desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"],
+                                     dev["W3"], dev["W2"], dev["b2"], ws=ws)
+        torch.cuda.synchronize()
+        outs.append((y.clone(), aux.clone(), counts.clone()))
+    for y2, a2, c2 in outs[1:]:  # bitwise run-to-run determinism
+        assert torch.equal(y2.view(torch.int16) if y2.dtype == torch.bfloat16 else y2,
+                           outs[0][0].view(torch.int16) if y2.dtype == torch.bfloat16 else outs[0][0])
+        assert torch.equal(a2, outs[0][1]) and torch.equal(c2, outs[0][2])
+    y, aux, counts = outs[0]
+    H.check_bits_equal("expert_counts", H.to_np(counts), r["counts"])
+    assert abs(float(H.to_np(aux)[0]) - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0)
+    yg = H.to_np(y)
+    if rows is not None:
+        yg = yg[rows]
+    raw, net = H.layer_err(yg, r["y"], cfg.dtype)
+    H.say("[gpu] %s y: max|d|/rms = %.4f (raw), %.4f (net of output rounding)" % (cfg.name, raw, net))
+    assert net <= H.Y_TOL[cfg.dtype], (raw, net)
+    assert raw <= H.Y_TOL[cfg.dtype] + (2.0 ** -8) * np.abs(r["y"]).max() / np.sqrt(np.mean(r["y"] ** 2))
+    return raw
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_all_stages(name):
+    cfg = SMALL[name]
+    H.say("[gpu] small case %s %s" % (name, cfg))
+    inp = _case(cfg)
+    r = H.run_oracle(cfg, inp)
+    dev = H.to_dev(inp)
+    _check_route(cfg, dev, r)
+    _check_permute(cfg, dev, r)
+    _check_expert_ffn(cfg, inp, dev, r)
+    _check_combine(cfg, r)
+    _check_forward(cfg, dev, r)
+
+
+@pytest.mark.parametrize("dtype,act", [(W.DT_BF16, W.ACT_SWIGLU), (W.DT_F32, W.ACT_GELU), (W.DT_BF16, W.ACT_GELU)])
+def test_all_slots_on_first_experts(dtype, act):
+    """W_r = 0: all logits tie, so experts 0..K-1 each take all T tokens (huge groups, idle rest)."""
+    cfg = L("ties", 600, 128, 8, 2, 256, act, W.GATE_RENORM, dtype, "none", 31)
+    H.say("[gpu] tie case %s" % (cfg,))
+    inp = _case(cfg, zero_router=True)
+    r = H.run_oracle(cfg, inp)
+    assert r["counts"].tolist() == [600, 600, 0, 0, 0, 0, 0, 0]
+    dev = H.to_dev(inp)
+    _check_route(cfg, dev, r)
+    _check_forward(cfg, dev, r)
+
+
+def test_empty_batch():
+    cfg = L("empty", 0, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 32)
+    H.say("[gpu] T=0")
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    desc = moe.desc_of(cfg)
+    aux = torch.full((1,), 7.0, device="cuda")
+    counts = torch.full((8,), 7, dtype=torch.int32, device="cuda")
+    moe.forward(desc, dev["h"], dev["W_r"], None, dev["W1"], None, dev["W3"], dev["W2"], None, aux=aux,
+                counts=counts)
+    g = moe.route(desc, dev["h"], dev["W_r"], None)
+    p = moe.permute(desc, g["topk_idx"], dev["h"])
+    torch.cuda.synchronize()
+    assert float(aux[0]) == 0.0 and counts.sum().item() == 0
+    assert float(g["aux"][0]) == 0.0 and g["counts"].sum().item() == 0
+    assert p["offsets"].tolist() == [0] * 9
+
+
+FULL = ["micro", "skewed", "mixtral_prefill", "mixtral_decode", "switch_top1"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload(name):
+    cfg = W.WORKLOADS[name]
+    H.say("[gpu] full workload %s %s" % (name, cfg))
+    inp = W.make_inputs(cfg)
+    rows = None
+    r = H.run_oracle(cfg, inp, tokens=[])  # routing for every token; y below
+    if cfg.T * cfg.d * cfg.width > 2 ** 31:
+        rows = H.sample_tokens(r, cfg.T)
+    r = H.run_oracle(cfg, inp, tokens=rows)
+    dev = H.to_dev(inp)
+    _check_route(cfg, dev, r)
+    _check_permute(cfg, dev, r)
+    slots = None
+    if rows is not None:
+        slots = np.unique(r["token_slot"][rows].reshape(-1))
+    _check_expert_ffn(cfg, inp, dev, r, slots=slots)
+    _check_combine(cfg, r)
+    err = _check_forward(cfg, dev, r, rows=rows)
+    H.say("[gpu] %s y max|d|/rms = %.3e, aux = %.6f, idle experts = %d, max share = %.3f" % (
+        name, err, r["aux"], int((r["counts"] == 0).sum()), r["counts"].max() / cfg.S))
+    del dev
+    torch.cuda.empty_cache()
