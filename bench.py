@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="time only the prefill workload")
+    ap.add_argument("--only", choices=["prefill", "decode", "switch"], default=None,
+                    help="time one workload only (for per-workload profiles); prints its own JSON object")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=128)
     args = ap.parse_args()
@@ -148,6 +150,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     moe.lib()  # fail loudly if the HIP library is missing
+    if args.only is not None:
+        name = {"prefill": "mixtral_prefill", "decode": "mixtral_decode", "switch": "switch_top1"}[args.only]
+        c = W.WORKLOADS[name]
+        ms, kernels, alg, counts, aux = time_workload(c, args.steps, args.warmup, args.only)
+        print(json.dumps({"workload": name, "ms_per_step": round(ms, 4), "tokens_per_s": round(c.T / (ms * 1e-3), 1),
+                          "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in kernels.items()}}))
+        return
 
     cfg = W.WORKLOADS["mixtral_prefill"]
     ms, kernels, alg, counts, aux = time_workload(cfg, args.steps, args.warmup, "prefill")

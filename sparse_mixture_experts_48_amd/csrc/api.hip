@@ -36,7 +36,7 @@ struct Plan {
   size_t blk_hist, blk_psum, blk_base;
   size_t topk_idx, topk_gate, token_slot, slot_token;
   size_t counts, offsets, pmean, aux;
-  size_t h_perm, act, o_perm;
+  size_t act, o_perm;
   size_t total;
 };
 
@@ -63,7 +63,6 @@ Plan make_plan(const moe_desc& d) {
   p.offsets = take((d.E + 1) * 4);
   p.pmean = take(d.E * 4);
   p.aux = take(4);
-  p.h_perm = take(S * d.d * bpe);
   p.act = take(S * d.width * bpe);
   p.o_perm = take(d.K > 1 ? S * d.d * 4 : 0);
   p.total = off;
@@ -79,6 +78,11 @@ int check_desc(const moe_desc* d) {
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->reserved != 0) return MOE_ERR_UNSUPPORTED;
   if (d->T > kMaxInt / d->K || d->d > kMaxInt || d->width > kMaxInt) return MOE_ERR_UNSUPPORTED;
+  // every operand matrix (h, grouped rows, hidden activations, one expert's
+  // weight matrix) must have fewer than 2^31 elements: kernels use 32-bit offsets
+  const int64_t S = d->T * d->K;
+  if (S > 0 && (S > kMaxInt / d->d || S > kMaxInt / d->width)) return MOE_ERR_UNSUPPORTED;
+  if (d->d > kMaxInt / d->width) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -332,7 +336,6 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
   int32_t* offsets = at<int32_t>(ws, pl.offsets);
   int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
   int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
-  void* h_perm = at<char>(ws, pl.h_perm);
   int32_t* counts = expert_counts != nullptr ? expert_counts : at<int32_t>(ws, pl.counts);
 
   moe::RouteArgs ra{h, W_r, b_r, T, static_cast<int>(d.d), E, K, d.gate, topk_idx, topk_gate, nullptr,
@@ -343,8 +346,9 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
                                   aux_loss, st));
   const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
   MOE_LAUNCH(MOE_K_PERMUTE, st,
-             moe::launch_permute(topk_idx, blk_base, T, E, K, pl.rt, h, row_bytes, h_perm, slot_token,
+             moe::launch_permute(topk_idx, blk_base, T, E, K, pl.rt, h, row_bytes, nullptr, slot_token,
                                  token_slot, st));
+  // GEMM1 reads the rows of h through slot_token: the grouped copy of h is never written.
   moe::FfnArgs f{};
   f.S = T * K;
   f.d = static_cast<int>(d.d);
@@ -353,7 +357,8 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
   f.width = static_cast<int>(d.width);
   f.act = d.act;
   f.bf16 = bf16;
-  f.x = h_perm;
+  f.x = h;
+  f.x_rows = slot_token;
   f.offsets = offsets;
   f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
   f.a = at<char>(ws, pl.act);

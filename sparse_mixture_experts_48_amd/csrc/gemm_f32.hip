@@ -17,7 +17,8 @@ enum { F_G1_SWIGLU = 0, F_G1_GELU = 1, F_G2_OPERM = 2, F_G2_FUSED_Y = 3 };
 constexpr int kFBM = 64, kFBN = 64, kFBK = 16, kFPad = 4;
 
 struct F32Params {
-  const float* x;          // [S][Kd]
+  const float* x;          // [S][Kd] grouped rows (or h, through x_rows)
+  const int32_t* x_rows;   // nullable: grouped row s is row x_rows[s] of x
   const int32_t* offsets;  // [E+1]
   const float* B;          // [E][N][Kd]
   const float* B3;         // [E][N][Kd] or null
@@ -45,7 +46,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
 
   // loader: thread -> (row = tid / 4, k = (tid % 4) * 4), four consecutive k
   const int lrow = tid / 4, lk = (tid % 4) * 4;
-  const float* a_src = p.x + static_cast<size_t>(row0 + min(lrow, rows - 1)) * Kd + lk;
+  const int arow = row0 + min(lrow, rows - 1);
+  const float* a_src = p.x + static_cast<size_t>(p.x_rows != nullptr ? p.x_rows[arow] : arow) * Kd + lk;
   const int bn = min(n0 + lrow, N - 1);
   const float* b_src[NMAT];
   b_src[0] = p.B + (static_cast<size_t>(e) * N + bn) * Kd + lk;
@@ -135,6 +137,7 @@ hipError_t launch_f32(F32Params p, int S, hipStream_t st) {
 hipError_t launch_gemm1_f32(const FfnArgs& f, hipStream_t st) {
   F32Params p{};
   p.x = static_cast<const float*>(f.x);
+  p.x_rows = f.x_rows;
   p.offsets = f.offsets;
   p.B = static_cast<const float*>(f.W1);
   p.B3 = static_cast<const float*>(f.W3);

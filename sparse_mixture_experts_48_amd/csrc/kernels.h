@@ -47,7 +47,8 @@ hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, int 
 struct FfnArgs {
   int S, d, E, K, width, act;  // S = T*K grouped rows
   bool bf16;
-  const void* x;               // h_perm [S][d]
+  const void* x;               // grouped rows [S][d], or h [T][d] read through x_rows
+  const int32_t* x_rows;       // nullable: GEMM1 reads row x_rows[s] of x for grouped row s
   const int32_t* offsets;      // [E+1]
   const void* W1; const void* b1; const void* W3; const void* W2; const void* b2;
   void* a;                     // hidden activations [S][width], dtype (workspace)

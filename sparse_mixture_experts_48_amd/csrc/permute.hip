@@ -68,7 +68,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
   if (h_perm == nullptr) return;
   __syncthreads();
-  // Gather: each token row is read once and written to its K grouped rows.
+  // Gather: each token row is read once (up to 8 x 16 bytes per lane in flight)
+  // and written to its K grouped rows.
+  constexpr int kU = 8;
   const int ntok = min(TB, T - t0);
   const int nvec = static_cast<int>(row_bytes / 16);
   for (int r = wave; r < ntok; r += kPermThreads / 64) {
@@ -76,11 +78,23 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int sl[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) sl[j] = (j < K) ? slots_s[r][j] : 0;
-    for (int c = lane; c < nvec; c += 64) {
-      const uint4 v = src[c];
+    for (int c0 = 0; c0 < nvec; c0 += 64 * kU) {
+      uint4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < nvec) v[u] = src[c];
+      }
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j) {
-        if (j < K) reinterpret_cast<uint4*>(h_perm + static_cast<size_t>(sl[j]) * row_bytes)[c] = v;
+        if (j < K) {
+          uint4* dst = reinterpret_cast<uint4*>(h_perm + static_cast<size_t>(sl[j]) * row_bytes);
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int c = c0 + u * 64 + lane;
+            if (c < nvec) dst[c] = v[u];
+          }
+        }
       }
     }
   }

@@ -23,26 +23,32 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteBK = 64;           // k values staged in LDS per step
-constexpr int kRoutePad = kRouteBK + 4; // row stride in floats (16-byte aligned, bank-skewed)
+constexpr int kRouteTB = 32;  // tokens per block
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-template <typename Tin> struct Vec8;
-template <> struct Vec8<float> {
-  __device__ __forceinline__ static void load(const float* p, float* out) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+// 8 consecutive h values of one token as raw bits (bf16: one 16-byte load).
+template <typename Tin> struct HVec;
+template <> struct HVec<float> {
+  typedef float4 raw[2];
+  __device__ __forceinline__ static void load(const float* p, raw& r) {
+    r[0] = *reinterpret_cast<const float4*>(p);
+    r[1] = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ static void zero(raw& r) { r[0] = r[1] = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ static void to_f32(const raw& r, float* out) {
+    out[0] = r[0].x; out[1] = r[0].y; out[2] = r[0].z; out[3] = r[0].w;
+    out[4] = r[1].x; out[5] = r[1].y; out[6] = r[1].z; out[7] = r[1].w;
   }
 };
-template <> struct Vec8<bf16_t> {
-  __device__ __forceinline__ static void load(const bf16_t* p, float* out) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+template <> struct HVec<bf16_t> {
+  typedef uint4 raw[1];
+  __device__ __forceinline__ static void load(const bf16_t* p, raw& r) { r[0] = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static void zero(raw& r) { r[0] = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ static void to_f32(const raw& r, float* out) {
+    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = __uint_as_float(w[i] << 16);
@@ -51,7 +57,10 @@ template <> struct Vec8<bf16_t> {
   }
 };
 
-template <typename Tin, int EP, int TE, int TPT>
+// EP: experts padded to a power of two; TE experts and TPT tokens per thread;
+// BK: k values per LDS stage; NS: pipeline depth (NS - 1 stages of global
+// loads in flight in registers while one stage is consumed from LDS).
+template <typename Tin, int EP, int TE, int TPT, int BK, int NS>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
     int T, int d, int E, int K, int gate_mode,
@@ -61,9 +70,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   constexpr int G = kRouteThreads / LE;   // token groups per block
   constexpr int TB = G * TPT;             // tokens per block
   static_assert(LE >= 1 && LE <= 64 && (64 % LE) == 0, "token lanes must tile a wave");
+  static_assert(TB == kRouteTB, "router tiling");
+  constexpr int HP = BK + 4;              // h_s row stride (floats)
+  constexpr int WP = EP + 4;              // w_s row stride (floats)
+  constexpr int HV = TB * (BK / 8) / kRouteThreads;       // 8-value h vectors per thread per stage
+  constexpr int WV = (BK * EP / 4 + kRouteThreads - 1) / kRouteThreads;  // W_r float4s per thread
+  static_assert(HV >= 1 && HV * kRouteThreads == TB * (BK / 8), "h staging");
 
-  __shared__ __align__(16) float h_s[TB][kRoutePad];
-  __shared__ __align__(16) float w_s[EP][kRoutePad];
+  __shared__ __align__(16) float h_s[2][TB][HP];
+  __shared__ __align__(16) float w_s[2][BK][WP];
   __shared__ float psum_s[G][EP];
   __shared__ int hist_s[EP];
 
@@ -72,6 +87,63 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int el = tid % LE;
   const int t0 = blockIdx.x * TB;
   if (tid < EP) hist_s[tid] = 0;
+  const int nc = (d + BK - 1) / BK;
+
+  typename HVec<Tin>::raw hreg[NS][HV];
+  float4 wreg[NS][WV];
+
+  // Issue the global loads of stage c into register slot `slot`.
+  auto load_stage = [&](int c, int slot) {
+    const int k0 = c * BK;
+    const int kn = min(BK, d - k0);
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int i = tid + v * kRouteThreads;
+      const int r = i / (BK / 8);
+      const int cc = (i % (BK / 8)) * 8;
+      const int t = t0 + r;
+      if (t < T && cc < kn) HVec<Tin>::load(h + static_cast<size_t>(t) * d + k0 + cc, hreg[slot][v]);
+      else HVec<Tin>::zero(hreg[slot][v]);
+    }
+    // rows k0 .. k0+kn of W_r are one contiguous run of kn*E floats
+    const float4* wsrc = reinterpret_cast<const float4*>(Wr + static_cast<size_t>(k0) * E);
+    const int n4 = kn * E / 4;
+#pragma unroll
+    for (int v = 0; v < WV; ++v) {
+      const int i = tid + v * kRouteThreads;
+      wreg[slot][v] = (i < n4) ? wsrc[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  // Move register slot `slot` (stage c) into LDS buffer `buf`.
+  auto store_stage = [&](int c, int slot, int buf) {
+    const int kn = min(BK, d - c * BK);
+#pragma unroll
+    for (int v = 0; v < HV; ++v) {
+      const int i = tid + v * kRouteThreads;
+      const int r = i / (BK / 8);
+      const int cc = (i % (BK / 8)) * 8;
+      float x[8];
+      HVec<Tin>::to_f32(hreg[slot][v], x);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) h_s[buf][r][cc + u] = x[u];
+    }
+    const int n4 = kn * E / 4;
+#pragma unroll
+    for (int v = 0; v < WV; ++v) {
+      const int i = tid + v * kRouteThreads;
+      if (i < n4) {
+        const float x[4] = {wreg[slot][v].x, wreg[slot][v].y, wreg[slot][v].z, wreg[slot][v].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int f = 4 * i + u;
+          w_s[buf][f / E][f % E] = x[u];
+        }
+      }
+    }
+    if (E < EP) {  // padded experts read zeros
+      for (int i = tid; i < BK * (EP - E); i += kRouteThreads) w_s[buf][i / (EP - E)][E + i % (EP - E)] = 0.0f;
+    }
+  };
 
   float acc[TPT][TE];
 #pragma unroll
@@ -79,49 +151,57 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 #pragma unroll
     for (int q = 0; q < TE; ++q) acc[i][q] = 0.0f;
 
-  for (int k0 = 0; k0 < d; k0 += kRouteBK) {
-    const int kn = min(kRouteBK, d - k0);  // a multiple of 8
-    // h rows of this block, converted to float32, 8 values per load
-    for (int v = tid; v < TB * (kRouteBK / 8); v += kRouteThreads) {
-      const int r = v / (kRouteBK / 8);
-      const int c = (v % (kRouteBK / 8)) * 8;
-      const int t = t0 + r;
-      float x[8];
-      if (t < T && c < kn) {
-        Vec8<Tin>::load(h + static_cast<size_t>(t) * d + k0 + c, x);
+  auto compute4 = [&](int buf, int kk) {
+    float4 hv[TPT];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) hv[i] = *reinterpret_cast<const float4*>(&h_s[buf][tg + i * G][kk]);
+    float wv[4][TE];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (TE == 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&w_s[buf][kk + s][el * TE]);
+        wv[s][0] = w4.x; wv[s][1] = w4.y; wv[s][2] = w4.z; wv[s][3] = w4.w;
       } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = 0.0f;
+        for (int q = 0; q < TE; ++q) wv[s][q] = w_s[buf][kk + s][el * TE + q];
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) h_s[r][c + u] = x[u];
     }
-    // W_r[k0 .. k0+kn)[0 .. E) transposed into w_s[e][k]
-    for (int v = tid; v < kRouteBK * EP; v += kRouteThreads) {
-      const int r = v / EP;
-      const int c = v % EP;
-      float x = 0.0f;
-      if (r < kn && c < E) x = Wr[static_cast<size_t>(k0 + r) * E + c];
-      w_s[c][r] = x;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const float hk[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int q = 0; q < TE; ++q) acc[i][q] = fmaf(hk[s], wv[s][q], acc[i][q]);
     }
-    __syncthreads();
-    for (int kk = 0; kk < kn; kk += 4) {
-      float4 hv[TPT], wv[TE];
+  };
+  auto compute_stage = [&](int c, int buf) {
+    const int kn = min(BK, d - c * BK);  // a multiple of 8
+    if (kn == BK) {
+      // fully unrolled so that LDS reads run ahead of the dependent fma chain
 #pragma unroll
-      for (int i = 0; i < TPT; ++i) hv[i] = *reinterpret_cast<const float4*>(&h_s[tg + i * G][kk]);
-#pragma unroll
-      for (int q = 0; q < TE; ++q) wv[q] = *reinterpret_cast<const float4*>(&w_s[el * TE + q][kk]);
-#pragma unroll
-      for (int i = 0; i < TPT; ++i)
-#pragma unroll
-        for (int q = 0; q < TE; ++q) {
-          acc[i][q] = fmaf(hv[i].x, wv[q].x, acc[i][q]);
-          acc[i][q] = fmaf(hv[i].y, wv[q].y, acc[i][q]);
-          acc[i][q] = fmaf(hv[i].z, wv[q].z, acc[i][q]);
-          acc[i][q] = fmaf(hv[i].w, wv[q].w, acc[i][q]);
-        }
+      for (int kk = 0; kk < BK; kk += 4) compute4(buf, kk);
+    } else {
+      for (int kk = 0; kk < kn; kk += 4) compute4(buf, kk);
     }
-    __syncthreads();
+  };
+
+  // Pipeline: stage c is loaded into registers NS-1 steps before it is
+  // stored to LDS buffer c&1 and consumed; one barrier per stage.
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nc) load_stage(s, s);
+  for (int c0 = 0; c0 < nc; c0 += NS) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = c0 + s;
+      if (c < nc) {
+        store_stage(c, s, c & 1);
+        __syncthreads();
+        if (c + NS - 1 < nc) load_stage(c + NS - 1, (s + NS - 1) % NS);
+        compute_stage(c, c & 1);
+      }
+    }
   }
 
   float psum_local[TE];
@@ -254,12 +334,13 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     int32_t* __restrict__ offsets_out, float* __restrict__ prob_mean, float* __restrict__ aux_out) {
   __shared__ int part_cnt[kFinParts][64];
   __shared__ float part_p[kFinParts][64];
+  __shared__ int tot_s[64];
   __shared__ int off_s[65];
   __shared__ float P_s[64];
   const int e = threadIdx.x % 64;
   const int part = threadIdx.x / 64;
   const int per = (NB + kFinParts - 1) / kFinParts;
-  const int b0 = part * per;
+  const int b0 = min(NB, part * per);
   const int b1 = min(NB, b0 + per);
   int c = 0;
   float ps = 0.0f;
@@ -275,11 +356,11 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   if (threadIdx.x < 64) {
     int tot = 0;
     float ptot = 0.0f;
-    for (int p = 0; p < kFinParts; ++p) {
+    for (int p = 0; p < kFinParts; ++p) {  // fixed order
       tot += part_cnt[p][e];
       ptot += part_p[p][e];
     }
-    part_cnt[0][e] = tot;  // reuse row 0 for totals after the read above (same thread)
+    tot_s[e] = tot;
     P_s[e] = (T > 0) ? ptot / static_cast<float>(T) : 0.0f;
   }
   __syncthreads();
@@ -287,33 +368,29 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     int run = 0;
     for (int x = 0; x < E; ++x) {
       off_s[x] = run;
-      run += part_cnt[0][x];
+      run += tot_s[x];
     }
     off_s[E] = run;
   }
   __syncthreads();
   if (threadIdx.x < E) {
-    if (counts_out != nullptr) counts_out[e] = part_cnt[0][e];
+    if (counts_out != nullptr) counts_out[e] = tot_s[e];
     if (prob_mean != nullptr) prob_mean[e] = P_s[e];
   }
   if (threadIdx.x <= E && offsets_out != nullptr) offsets_out[threadIdx.x] = off_s[threadIdx.x];
   if (threadIdx.x == 0 && aux_out != nullptr) {
     float a = 0.0f;
     const float S = static_cast<float>(T) * static_cast<float>(K);
-    for (int x = 0; x < E; ++x) a += (static_cast<float>(part_cnt[0][x]) / S) * P_s[x];
+    for (int x = 0; x < E; ++x) a += (static_cast<float>(tot_s[x]) / S) * P_s[x];
     *aux_out = (T > 0) ? static_cast<float>(E) * a : 0.0f;
   }
-  if (blk_base != nullptr) {
-    // base[b][e] = offsets[e] + sum_{b' < b} hist[b'][e]; the part prefix is
-    // recomputed from blk_hist (part_cnt row 0 now holds totals).
-    __syncthreads();
-    if (e < E) {
-      int pre = off_s[e];
-      for (int b = 0; b < b0; ++b) pre += blk_hist[static_cast<size_t>(b) * E + e];
-      for (int b = b0; b < b1; ++b) {
-        blk_base[static_cast<size_t>(b) * E + e] = pre;
-        pre += blk_hist[static_cast<size_t>(b) * E + e];
-      }
+  if (blk_base != nullptr && e < E) {
+    // base[b][e] = offsets[e] + slots of e in blocks before b
+    int pre = off_s[e];
+    for (int p = 0; p < part; ++p) pre += part_cnt[p][e];
+    for (int b = b0; b < b1; ++b) {
+      blk_base[static_cast<size_t>(b) * E + e] = pre;
+      pre += blk_hist[static_cast<size_t>(b) * E + e];
     }
   }
 }
@@ -327,33 +404,22 @@ __global__ void zero_outputs_kernel(int E, int32_t* counts, int32_t* offsets, fl
   if (aux != nullptr && i == 0) *aux = 0.0f;
 }
 
-template <typename Tin, int EP, int TE>
-hipError_t launch_route_tpt(const RouteArgs& a, int tpt, hipStream_t st) {
-  const int LE = EP / TE;
-  const int G = kRouteThreads / LE;
-  const int TB = G * tpt;
-  const int nb = (a.T + TB - 1) / TB;
-  const Tin* h = static_cast<const Tin*>(a.h);
-#define MOE_ROUTE_LAUNCH(TPTV)                                                                    \
-  hipLaunchKernelGGL((route_kernel<Tin, EP, TE, TPTV>), dim3(nb), dim3(kRouteThreads), 0, st, h, \
-                     a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx, a.topk_gate,             \
-                     a.logits, a.blk_hist, a.blk_psum)
-  switch (tpt) {
-    case 1: MOE_ROUTE_LAUNCH(1); break;
-    case 2: MOE_ROUTE_LAUNCH(2); break;
-    default: MOE_ROUTE_LAUNCH(4); break;
-  }
-#undef MOE_ROUTE_LAUNCH
+template <typename Tin, int EP, int TE, int TPT, int BK, int NS>
+hipError_t launch_route_cfg(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
+  hipLaunchKernelGGL((route_kernel<Tin, EP, TE, TPT, BK, NS>), dim3(rt.NB), dim3(kRouteThreads), 0, st,
+                     static_cast<const Tin*>(a.h), a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
+                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum);
   return hipGetLastError();
 }
 
+// Thread tiles: 32 tokens x EP experts per block of 256 threads.
 template <typename Tin>
 hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
   switch (rt.EP) {
-    case 8: return launch_route_tpt<Tin, 8, 1>(a, rt.TPT, st);
-    case 16: return launch_route_tpt<Tin, 16, 2>(a, rt.TPT, st);
-    case 32: return launch_route_tpt<Tin, 32, 2>(a, rt.TPT, st);
-    default: return launch_route_tpt<Tin, 64, 4>(a, rt.TPT, st);
+    case 8: return launch_route_cfg<Tin, 8, 1, 1, 128, 4>(a, rt, st);
+    case 16: return launch_route_cfg<Tin, 16, 2, 1, 128, 4>(a, rt, st);
+    case 32: return launch_route_cfg<Tin, 32, 2, 2, 64, 4>(a, rt, st);
+    default: return launch_route_cfg<Tin, 64, 4, 2, 64, 4>(a, rt, st);
   }
 }
 
@@ -362,16 +428,8 @@ hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStre
 RouteTiling route_tiling(int64_t T, int64_t E) {
   RouteTiling rt;
   rt.EP = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
-  const int TE = rt.EP == 8 ? 1 : rt.EP == 64 ? 4 : 2;
-  const int LE = rt.EP / TE;
-  const int G = kRouteThreads / LE;
-  // Prefer more tokens per thread (more independent chains, fewer LDS reads
-  // per fma) while the grid still has about two blocks per compute unit.
-  rt.TPT = 1;
-  for (int tpt = 4; tpt >= 2; tpt /= 2) {
-    if ((T + G * tpt - 1) / (G * tpt) >= 512) { rt.TPT = tpt; break; }
-  }
-  rt.TB = G * rt.TPT;
+  rt.TPT = rt.EP >= 32 ? 2 : 1;
+  rt.TB = kRouteTB;
   rt.NB = static_cast<int>((T + rt.TB - 1) / rt.TB);
   return rt;
 }
