@@ -77,6 +77,24 @@ def time_workload(cfg, steps, warmup, label):
         t1 = time.perf_counter()
         events = tr.read()
     ms = (t1 - t0) * 1e3 / steps
+    # the same step replayed from a captured HIP graph (no per-kernel launch gaps)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer.forward()
+    g.replay()
+    torch.cuda.synchronize()
+    tg0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - tg0) * 1e3 / steps
+    del g
     per_kernel = {}
     for name, dur in events:
         per_kernel.setdefault(name, []).append(dur)
@@ -86,7 +104,7 @@ def time_workload(cfg, steps, warmup, label):
     aux = float(layer.aux.cpu()[0])
     del layer
     torch.cuda.empty_cache()
-    return ms, kernels, alg, counts, aux
+    return ms, kernels, alg, counts, aux, ms_graph
 
 
 def roofline_mfma(flops, mean_ms, peak):
@@ -141,6 +159,8 @@ def main():
                     help="time one workload only (for per-workload profiles); prints its own JSON object")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="also run a plain device-to-device copy of this many MiB (a reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X only: this layer's path is built and measured on a single GPU "
@@ -150,16 +170,24 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     moe.lib()  # fail loudly if the HIP library is missing
+    if args.calibrate_copy > 0:
+        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.only is not None:
         name = {"prefill": "mixtral_prefill", "decode": "mixtral_decode", "switch": "switch_top1"}[args.only]
         c = W.WORKLOADS[name]
-        ms, kernels, alg, counts, aux = time_workload(c, args.steps, args.warmup, args.only)
-        print(json.dumps({"workload": name, "ms_per_step": round(ms, 4), "tokens_per_s": round(c.T / (ms * 1e-3), 1),
+        ms, kernels, alg, counts, aux, msg = time_workload(c, args.steps, args.warmup, args.only)
+        print(json.dumps({"workload": name, "ms_per_step": round(ms, 4), "ms_per_step_graph": round(msg, 4),
+                          "tokens_per_s": round(c.T / (ms * 1e-3), 1),
                           "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in kernels.items()}}))
         return
 
     cfg = W.WORKLOADS["mixtral_prefill"]
-    ms, kernels, alg, counts, aux = time_workload(cfg, args.steps, args.warmup, "prefill")
+    ms, kernels, alg, counts, aux, ms_g = time_workload(cfg, args.steps, args.warmup, "prefill")
     g1 = kernels["gemm1"]["mean_ms"]
     out = {
         "metric": METRIC,
@@ -169,6 +197,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_graph": round(ms_g, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -185,9 +214,11 @@ def main():
     if not args.no_extra:
         dcfg = W.WORKLOADS["mixtral_decode"]
         dsteps = max(args.steps, 50)
-        dms, dk, dalg, dcounts, _ = time_workload(dcfg, dsteps, args.warmup, "decode")
+        dms, dk, dalg, dcounts, _, dms_g = time_workload(dcfg, dsteps, args.warmup, "decode")
         out["decode"] = {
             "workload": dcfg.name, "steps": dsteps, "ms_per_step": round(dms, 4),
+            "ms_per_step_graph": round(dms_g, 4), "tokens_per_s_graph": round(dcfg.T / (dms_g * 1e-3), 1),
+            "layer_hbm_frac_graph": round(dalg["bytes"] / (dms_g * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "tokens_per_s": round(dcfg.T / (dms * 1e-3), 1),
             "layer_hbm_GBps": round(dalg["bytes"] / (dms * 1e-3) / 1e9, 1),
             "layer_hbm_frac": round(dalg["bytes"] / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
@@ -198,9 +229,9 @@ def main():
             "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in dk.items()},
         }
         scfg = W.WORKLOADS["switch_top1"]
-        sms, sk, salg, scounts, saux = time_workload(scfg, args.steps, args.warmup, "switch")
+        sms, sk, salg, scounts, saux, sms_g = time_workload(scfg, args.steps, args.warmup, "switch")
         out["switch_top1"] = {
-            "workload": scfg.name, "ms_per_step": round(sms, 4),
+            "workload": scfg.name, "ms_per_step": round(sms, 4), "ms_per_step_graph": round(sms_g, 4),
             "tokens_per_s": round(scfg.T / (sms * 1e-3), 1),
             "layer_tflops": round(salg["flops"] / (sms * 1e-3) / 1e12, 2),
             "layer_hbm_GBps": round(salg["bytes"] / (sms * 1e-3) / 1e9, 1),

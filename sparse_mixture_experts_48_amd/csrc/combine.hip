@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int c = static_cast<int>(i % d4) * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < K; ++j) {
-      const int s = token_slot[static_cast<size_t>(t) * K + j];
+      const int s = min(max(token_slot[static_cast<size_t>(t) * K + j], 0), T * K - 1);  // stay inside o_perm
       const float g = gate[static_cast<size_t>(t) * K + j];
       const float4 o = *reinterpret_cast<const float4*>(o_perm + static_cast<size_t>(s) * d + c);
       acc.x = fmaf(g, o.x, acc.x);

@@ -44,15 +44,26 @@ __device__ __forceinline__ float gelu_exact(float z) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Rows [*beg, *end) of expert e, clamped into [0, S): offsets that do not
+// describe a grouping of S rows give wrong results but never an access
+// outside the S-row buffers.
+__device__ __forceinline__ void expert_rows(const int32_t* __restrict__ offsets, int e, int S, int* beg,
+                                            int* end) {
+  const int b = min(max(offsets[e], 0), S);
+  *beg = b;
+  *end = min(max(offsets[e + 1], b), S);
+}
+
 // Which expert owns global m-tile `mt` when every expert's rows are cut into
 // tiles of `bm` rows. Returns false if `mt` is past the last tile.
-// offsets: [E+1] exclusive prefix of the per-expert row counts.
-__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int bm,
+// offsets: [E+1] exclusive prefix of the per-expert row counts (clamped to [0, S)).
+__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int S, int bm,
                                             int mt, int* expert, int* row0, int* rows) {
   int acc = 0;
   for (int e = 0; e < E; ++e) {
-    const int beg = offsets[e];
-    const int cnt = offsets[e + 1] - beg;
+    int beg, end;
+    expert_rows(offsets, e, S, &beg, &end);
+    const int cnt = end - beg;
     const int nt = (cnt + bm - 1) / bm;
     if (mt < acc + nt) {
       const int local = mt - acc;

@@ -48,6 +48,7 @@ struct GemmParams {
   const int32_t* slot_token;
   const float* gate;        // topk_gate [T] (K = 1)
   int E, N, Kd;
+  int S;                    // grouped rows (bound of every grouped-row index)
   int n_mt;                 // m-tile slots in the grid (upper bound)
 };
 
@@ -63,22 +64,27 @@ __device__ __forceinline__ float epilogue_g1(int mode, float v1, float v3, const
 
 // ---------------------------------------------------------------------------- tiled kernel
 //
-// Block: 256 threads = 2 x 2 waves; tile = BM grouped rows x BN weight rows;
-// k staged 64 at a time in a double-buffered LDS tile that is filled by
-// direct global-to-LDS loads (global_load_lds_dwordx4): no staging
-// registers, no LDS store instructions. One stage per iteration:
-//   barrier (this stage's loads have landed in every wave)
-//   -> read all of this stage's MFMA fragments into registers
-//   -> issue the loads of the next stage into the other buffer
-//   -> 64 MFMAs per wave.
-// Nothing reads LDS between issuing a stage's loads and the next barrier.
+// Block: 256 threads = 2 x 2 waves; tile = BM grouped rows x BN weight rows.
+// k is staged 32 at a time through a ring of four LDS buffers filled by
+// direct global-to-LDS loads (global_load_lds_dwordx4: no staging registers,
+// no LDS store instructions), three stages ahead of the MFMAs: the loads are
+// latency-bound, so several stages must be in flight per compute unit.
+// Per stage:
+//   wait until this wave's loads of the stage have landed (the two newer
+//   stages stay in flight), barrier (so have every wave's)
+//   -> read the stage's MFMA fragments
+//   -> issue the loads of the stage three ahead into the buffer freed by the
+//      previous stage
+//   -> 32 MFMAs per wave (reads of the second 16-k step overlap the first).
+// Every stage issues the same number of loads (past the end of the reduction
+// they read a 16-byte zero constant into the freed buffer), so the wait count
+// is the same at every stage; the kernel drains them before its epilogue.
 //
-// LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r sits at
-// c ^ ((r & 7) ^ ((r >> 3) & 1)), so the 16-byte fragment reads of 8 or 16
-// consecutive rows fall in distinct bank groups. A direct load fills 64
-// consecutive chunk slots (8 rows) per wave instruction; each lane fetches
-// the global chunk that belongs in its slot. Chunks past the end of the
-// reduction come from a 16-byte zero constant.
+// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at
+// c ^ (((r >> 1) ^ (r >> 3)) & 3): fragment reads of 8 or 16 consecutive rows
+// fall in distinct bank groups. A direct load fills 64 consecutive chunk
+// slots (16 rows) per wave instruction; each lane fetches the global chunk
+// that belongs in its slot.
 //
 // The weights are the MFMA M operand and the tokens the N operand, so lane l
 // of a 32x32 accumulator holds token l % 32 and four consecutive output
@@ -88,12 +94,13 @@ __device__ __forceinline__ float epilogue_g1(int mode, float v1, float v3, const
 // followed by the same WTN/2 rows of W3, so the two products that meet in
 // SiLU(x W1) * (x W3) sit in the same lane and register.
 
-constexpr int kBK = 64;   // k per stage: 8 chunks of 8 bf16
+constexpr int kBK = 32;   // k per stage: 4 chunks of 8 bf16
+constexpr int kTileGroupN = 4;  // n-tiles per group in the XCD-aware block order
 
 __device__ const u32x4_t kZeroChunk = {0u, 0u, 0u, 0u};
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 8 + (chunk ^ ((row & 7) ^ ((row >> 3) & 1)));
+  return row * 4 + (chunk ^ (((row >> 1) ^ (row >> 3)) & 3));
 }
 
 __device__ __forceinline__ void lds_dma16(const void* gsrc, u32x4_t* lds_wave_base) {
@@ -101,25 +108,43 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, u32x4_t* lds_wave_ba
                                    (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 template <int BM, int BN, int MODE>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
   constexpr int WM = 2, WN = 2;
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int A_IN = BM / 32;        // direct-load instructions per wave per stage (8 rows each)
-  constexpr int B_IN = BN / 32;
+  constexpr int A_IN = BM / 64;        // direct-load instructions per wave per stage (16 rows each)
+  constexpr int B_IN = BN / 64;
+  constexpr int DI = A_IN + B_IN;
   constexpr int NCOLS = BN / NMAT;     // output columns per block
   static_assert(TM >= 1 && TN >= NMAT && A_IN >= 1 && B_IN >= 1, "tile too small");
+  static_assert(2 * DI <= 63, "vmcnt range");
 
-  // One array per buffer, so that reads of one buffer are known not to alias
-  // the direct loads that fill the other.
-  __shared__ u32x4_t A0[BM * 8], B0[BN * 8], A1[BM * 8], B1[BN * 8];
+  // One array per ring slot, so that reads of one slot are known not to alias
+  // the direct loads that fill another.
+  __shared__ u32x4_t A0[BM * 4], A1[BM * 4], A2[BM * 4], A3[BM * 4];
+  __shared__ u32x4_t B0[BN * 4], B1[BN * 4], B2[BN * 4], B3[BN * 4];
 
-  const int mt = blockIdx.x % p.n_mt;
-  const int nt = blockIdx.x / p.n_mt;
+  // XCD-aware order. Hardware sends block b to XCD b % 8; give each XCD a
+  // contiguous run of logical tiles, ordered (n-tile group of kNG) x (m-tile)
+  // x (n-tile in group), so the blocks that run together on one XCD share
+  // their token and weight slices in that XCD's L2.
+  constexpr int kNG = kTileGroupN;
+  const int n_nt = (p.N + NCOLS - 1) / NCOLS;
+  const int n_ntg = (n_nt + kNG - 1) / kNG;
+  const int total = n_ntg * p.n_mt * kNG;
+  const int per_xcd = (total + 7) / 8;
+  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (t >= total) return;
+  const int nt = (t / (kNG * p.n_mt)) * kNG + t % kNG;
+  const int mt = (t / kNG) % p.n_mt;
+  if (nt >= n_nt) return;
   int e, row0, rows;
-  if (!find_m_tile(p.offsets, p.E, BM, mt, &e, &row0, &rows)) return;
+  if (!find_m_tile(p.offsets, p.E, p.S, BM, mt, &e, &row0, &rows)) return;
   const int n0 = nt * NCOLS;
 
   const int tid = threadIdx.x;
@@ -140,17 +165,17 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
     }
   };
 
-  // Direct-load sources. Wave wid, instruction u fills slots
-  // [(wid*A_IN + u)*64, +64): rows (wid*A_IN + u)*8 + lane/8, physical chunk
-  // lane%8, i.e. logical chunk (lane%8) ^ f(row).
-  // 32-bit element offsets (every operand matrix has fewer than 2^31 elements).
-  // The logical chunk of instruction u depends only on the parity of u.
-  const int kc_even = ((lane % 8) ^ ((lane / 8) & 7)) * 8;
-  const int kc_odd = ((lane % 8) ^ ((lane / 8) & 7) ^ 1) * 8;
+  // Direct-load sources. Wave wid, instruction u fills slots [(wid*IN + u)*64, +64):
+  // rows (wid*IN + u)*16 + lane/4, physical chunk lane%4, i.e. logical chunk
+  // (lane%4) ^ f(row); f depends on the lane and on the parity of wid*IN + u.
+  // Offsets are 32-bit element offsets (every operand matrix has < 2^31 elements).
+  const int lr = lane / 4;
+  const int kc_even = ((lane % 4) ^ (((lr >> 1) ^ (lr >> 3)) & 3)) * 8;
+  const int kc_odd = ((lane % 4) ^ (((lr >> 1) ^ ((lr >> 3) | 2)) & 3)) * 8;
   int a_off[A_IN];
 #pragma unroll
   for (int u = 0; u < A_IN; ++u) {
-    const int r = (wid * A_IN + u) * 8 + lane / 8;
+    const int r = (wid * A_IN + u) * 16 + lr;
     const int s = row0 + min(r, rows - 1);
     const int src_row = (p.x_rows != nullptr) ? p.x_rows[s] : s;
     a_off[u] = src_row * Kd + (((wid * A_IN + u) & 1) ? kc_odd : kc_even);
@@ -160,13 +185,11 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
   int b_off[B_IN];
 #pragma unroll
   for (int u = 0; u < B_IN; ++u) {
-    const int j = (wid * B_IN + u) * 8 + lane / 8;
     int mat;
-    const int n = min(brow_col(j, &mat), N - 1);
-    // SwiGLU: a wave's B instructions alternate between W1 and W3 row blocks
+    const int n = min(brow_col((wid * B_IN + u) * 16 + lr, &mat), N - 1);
     b_off[u] = n * Kd + (((wid * B_IN + u) & 1) ? kc_odd : kc_even);
-    (void)mat;
   }
+  // Loads of the stage starting at k0 (or zeros if k0 is past the end).
   auto issue_stage = [&](int k0, u32x4_t* As, u32x4_t* Bs) {
 #pragma unroll
     for (int u = 0; u < A_IN; ++u) {
@@ -177,9 +200,8 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
     }
 #pragma unroll
     for (int u = 0; u < B_IN; ++u) {
-      const int j0 = (wid * B_IN + u) * 8;
       int mat;
-      (void)brow_col(j0, &mat);  // all 8 rows of one instruction come from the same matrix
+      (void)brow_col((wid * B_IN + u) * 16, &mat);  // the 16 rows of one instruction share a matrix
       const int kc = ((wid * B_IN + u) & 1) ? kc_odd : kc_even;
       const bf16_t* base = (NMAT == 2 && mat) ? B3exp : Bexp;
       const void* g = (k0 + kc < Kd) ? static_cast<const void*>(base + b_off[u] + k0)
@@ -200,11 +222,11 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
   const int fsub = lane / 32;  // which of the two 8-wide k chunks of a 16-k step
   const int nk = (Kd + kBK - 1) / kBK;
 
-  // One stage: barrier (stage kt landed everywhere), first fragments, loads of
-  // stage kt+1 into the other buffer pair, then MFMAs of k-step ks while the
-  // fragments of ks+1 are read.
   auto run_stage = [&](int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* An, u32x4_t* Bn) {
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DI));  // this wave's loads of stage kt have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();                   // ... and every other wave's
+    asm volatile("" ::: "memory");
     bf16x8_t wf[kBK / 16][TN], xf[kBK / 16][TM];
     auto read = [&](int ks) {
       const int c = ks * 2 + fsub;
@@ -214,7 +236,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
       for (int i = 0; i < TM; ++i) xf[ks][i] = as_bf16x8(As[swz(wm * WTM + i * 32 + frow, c)]);
     };
     read(0);
-    if (kt + 1 < nk) issue_stage((kt + 1) * kBK, An, Bn);
+    issue_stage((kt + 3) * kBK, An, Bn);  // zeros once past the end: keeps the wait count uniform
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       if (ks + 1 < kBK / 16) read(ks + 1);
@@ -227,12 +249,20 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
   };
 
   issue_stage(0, A0, B0);
+  issue_stage(kBK, A1, B1);
+  issue_stage(2 * kBK, A2, B2);
   int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {  // straight-line pair of stages: no merge point for acc
-    run_stage(kt, A0, B0, A1, B1);
+  for (; kt + 4 <= nk; kt += 4) {  // straight-line ring: no merge point for acc inside the loop
+    run_stage(kt, A0, B0, A3, B3);
     run_stage(kt + 1, A1, B1, A0, B0);
+    run_stage(kt + 2, A2, B2, A1, B1);
+    run_stage(kt + 3, A3, B3, A2, B2);
   }
-  if (kt < nk) run_stage(kt, A0, B0, A1, B1);
+  if (kt < nk) run_stage(kt, A0, B0, A3, B3);
+  if (kt + 1 < nk) run_stage(kt + 1, A1, B1, A0, B0);
+  if (kt + 2 < nk) run_stage(kt + 2, A2, B2, A1, B1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
+  asm volatile("" ::: "memory");
 
   // Epilogue. Accumulator (j, i), register r: token = i*32 + lane%32 of the
   // wave's rows; weight row = j*32 + (r/4)*8 + (lane/32)*4 + r%4.
@@ -280,13 +310,14 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
 constexpr int kStreamWaves = 4;
 constexpr int kKS = 128;  // k per step: 4 loads of 32 contiguous k (8 per lane group) per row
 
-template <int MODE, int NR, int MC>
+template <int MODE, int NR, int MC, int NBUF>
 __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmParams p, int n_groups) {
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
   const int e = blockIdx.x / n_groups;
   const int grp = blockIdx.x % n_groups;
-  const int beg = p.offsets[e];
-  const int rows = p.offsets[e + 1] - beg;
+  int beg, end_row;
+  expert_rows(p.offsets, e, p.S, &beg, &end_row);
+  const int rows = min(end_row - beg, MC * 16);  // the host guarantees <= MC * 16 rows per expert
   if (rows <= 0) return;
   const int lane = threadIdx.x % 64;
   const int wave = threadIdx.x / 64;
@@ -321,8 +352,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmPara
 #pragma unroll
       for (int c = 0; c < MC; ++c) acc[m][q][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t wreg[2][NMAT][NR][4];
-  u32x4_t xreg[2][MC][4];
+  u32x4_t wreg[NBUF][NMAT][NR][4];
+  u32x4_t xreg[NBUF][MC][4];
   auto load = [&](int slot, int k0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -353,15 +384,24 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmPara
   };
 
   const int nk = (Kd + kKS - 1) / kKS;
-  load(0, 0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    load(1, (kt + 1) * kKS);
-    compute(0);
-    if (kt + 2 < nk) load(0, (kt + 2) * kKS);
-    compute(1);
+  if constexpr (NBUF == 2) {
+    // explicit register double buffer: one k-step in flight per wave
+    load(0, 0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      load(1, (kt + 1) * kKS);
+      compute(0);
+      if (kt + 2 < nk) load(0, (kt + 2) * kKS);
+      compute(1);
+    }
+    if (kt < nk) compute(0);
+  } else {
+    // single buffer: fewer registers, more waves per SIMD to keep loads in flight
+    for (int kt = 0; kt < nk; ++kt) {
+      load(0, kt * kKS);
+      compute(0);
+    }
   }
-  if (kt < nk) compute(0);
 
   // 16x16 accumulator layout: lane l holds column l%16 (a token row) and
   // rows (l/16)*4 + r (four consecutive output columns n).
@@ -407,35 +447,48 @@ hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
   p.n_mt = (S + BM - 1) / BM + min(p.E, S);
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
-  const size_t grid = static_cast<size_t>(p.n_mt) * n_nt;
+  const size_t total = static_cast<size_t>((n_nt + kTileGroupN - 1) / kTileGroupN) * p.n_mt * kTileGroupN;
+  const size_t grid = (total + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, MODE>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-// Large tiles when the grid still covers the chip a few times over.
+// Tile shape from the mean rows per expert (S / E): with about 1k rows per
+// expert, 256 x 256 tiles (the largest accumulator tile a compute unit's
+// registers hold, and the fewest bytes moved per flop); with about 100 rows
+// per expert, 128-row tiles waste less of each weight tile on padding rows.
+// Small grids fall back to 128 x 128 so that the chip is still covered.
 template <int MODE>
 hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
+  constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU);
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
-  const long big = static_cast<long>((S + 255) / 256 + min(p.E, S)) * ((p.N + 256 / NMAT - 1) / (256 / NMAT));
-  if (big >= 4 * 256) return launch_tile<256, 256, MODE>(p, S, st);
-  const long mid = static_cast<long>((S + 255) / 256 + min(p.E, S)) * ((p.N + 128 / NMAT - 1) / (128 / NMAT));
-  if (mid >= 2 * 256) return launch_tile<256, 128, MODE>(p, S, st);
+  const int mean_rows = S / max(p.E, 1);
+  auto blocks = [&](int bm, int bn) {
+    return static_cast<long>((S + bm - 1) / bm + min(p.E, S)) * ((p.N + bn / NMAT - 1) / (bn / NMAT));
+  };
+  if (mean_rows >= 512 && blocks(256, 256) >= 2 * 256) return launch_tile<256, 256, MODE>(p, S, st);
+  if (G1 && blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, MODE>(p, S, st);
   return launch_tile<128, 128, MODE>(p, S, st);
 }
 
-template <int MODE, int NR>
+template <int MODE, int NR, int NBUF>
 hipError_t launch_stream(GemmParams p, int max_rows, hipStream_t st) {
   const int n_groups = (p.N + kStreamWaves * NR * 16 - 1) / (kStreamWaves * NR * 16);
   const dim3 grid(static_cast<unsigned>(p.E * n_groups));
   if (max_rows <= 16) {
-    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 1>), grid, dim3(kStreamWaves * 64), 0, st, p, n_groups);
+    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 1, NBUF>), grid, dim3(kStreamWaves * 64), 0, st, p, n_groups);
   } else {
-    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 2>), grid, dim3(kStreamWaves * 64), 0, st, p, n_groups);
+    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 2, NBUF>), grid, dim3(kStreamWaves * 64), 0, st, p, n_groups);
   }
   return hipGetLastError();
 }
 
 constexpr int kStreamMaxRows = 32;
+// Measured on the Mixtral-shaped decode layer: one 16-row weight fragment per
+// wave (many waves, no second round) with a register double buffer for GEMM1
+// and a single buffer (more waves per SIMD) for GEMM2.
+constexpr int kStreamNR1 = 1, kStreamBuf1 = 2;  // weight fragments per wave, register buffers
+constexpr int kStreamNR2 = 1, kStreamBuf2 = 1;
 
 }  // namespace
 
@@ -451,10 +504,11 @@ hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st) {
   p.E = f.E;
   p.N = f.width;
   p.Kd = f.d;
+  p.S = f.S;
   const bool swiglu = f.act == 1;
   if (f.max_rows_per_expert <= kStreamMaxRows) {
-    return swiglu ? launch_stream<G1_SWIGLU, 2>(p, f.max_rows_per_expert, st)
-                  : launch_stream<G1_GELU, 2>(p, f.max_rows_per_expert, st);
+    return swiglu ? launch_stream<G1_SWIGLU, kStreamNR1, kStreamBuf1>(p, f.max_rows_per_expert, st)
+                  : launch_stream<G1_GELU, kStreamNR1, kStreamBuf1>(p, f.max_rows_per_expert, st);
   }
   return swiglu ? launch_tile_auto<G1_SWIGLU>(p, f.S, st) : launch_tile_auto<G1_GELU>(p, f.S, st);
 }
@@ -469,6 +523,7 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
   p.E = f.E;
   p.N = f.d;
   p.Kd = f.width;
+  p.S = f.S;
   if (f.fused_y) {
     p.out = f.y;
     p.slot_token = f.slot_token;
@@ -477,8 +532,8 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
     p.out = f.o_perm;
   }
   if (f.max_rows_per_expert <= kStreamMaxRows) {
-    return f.fused_y ? launch_stream<G2_FUSED_Y, 1>(p, f.max_rows_per_expert, st)
-                     : launch_stream<G2_OPERM, 1>(p, f.max_rows_per_expert, st);
+    return f.fused_y ? launch_stream<G2_FUSED_Y, kStreamNR2, kStreamBuf2>(p, f.max_rows_per_expert, st)
+                     : launch_stream<G2_OPERM, kStreamNR2, kStreamBuf2>(p, f.max_rows_per_expert, st);
   }
   return f.fused_y ? launch_tile_auto<G2_FUSED_Y>(p, f.S, st) : launch_tile_auto<G2_OPERM>(p, f.S, st);
 }

@@ -26,7 +26,7 @@ struct F32Params {
   void* out;
   const int32_t* slot_token;
   const float* gate;
-  int E, N, Kd, n_mt;
+  int E, N, Kd, S, n_mt;
 };
 
 template <int MODE>
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
   const int mt = blockIdx.x % p.n_mt;
   const int nt = blockIdx.x / p.n_mt;
   int e, row0, rows;
-  if (!find_m_tile(p.offsets, p.E, kFBM, mt, &e, &row0, &rows)) return;
+  if (!find_m_tile(p.offsets, p.E, p.S, kFBM, mt, &e, &row0, &rows)) return;
   const int n0 = nt * kFBN;
   const int tid = threadIdx.x;
   const int tx = tid % 16, ty = tid / 16;
@@ -146,6 +146,7 @@ hipError_t launch_gemm1_f32(const FfnArgs& f, hipStream_t st) {
   p.E = f.E;
   p.N = f.width;
   p.Kd = f.d;
+  p.S = f.S;
   return f.act == 1 ? launch_f32<F_G1_SWIGLU>(p, f.S, st) : launch_f32<F_G1_GELU>(p, f.S, st);
 }
 
@@ -158,6 +159,7 @@ hipError_t launch_gemm2_f32(const FfnArgs& f, hipStream_t st) {
   p.E = f.E;
   p.N = f.d;
   p.Kd = f.width;
+  p.S = f.S;
   if (f.fused_y) {
     p.out = f.y;
     p.slot_token = f.slot_token;
