@@ -18,8 +18,8 @@
 //
 // Two kernel families; the host picks one from T (an upper bound on the rows
 // of any expert):
-//  * gemm_tile_kernel: BM x BN tiles on v_mfma_f32_32x32x16_bf16, LDS double
-//    buffer, tiles enumerated over (expert m-tiles) x (n-tiles) on the device
+//  * gemm_tile_kernel: BM x BN tiles on v_mfma_f32_32x32x16_bf16, LDS rings
+//    fed by direct loads, tiles enumerated over (expert m-tiles) x (n-tiles) on the device
 //    from expert_offsets, so no host synchronisation is needed.
 //  * gemm_stream_kernel (rows per expert <= 32): every wave streams NR x 16
 //    weight rows over the whole reduction with v_mfma_f32_16x16x32_bf16, the
@@ -64,44 +64,50 @@ __device__ __forceinline__ float epilogue_g1(int mode, float v1, float v3, const
 
 // ---------------------------------------------------------------------------- tiled kernel
 //
-// Block: 256 threads = 2 x 2 waves; tile = BM grouped rows x BN weight rows.
-// k is staged 32 at a time through a ring of four LDS buffers filled by
-// direct global-to-LDS loads (global_load_lds_dwordx4: no staging registers,
-// no LDS store instructions), three stages ahead of the MFMAs: the loads are
-// latency-bound, so several stages must be in flight per compute unit.
+// Block: WM x WN waves; tile = BM grouped rows x BN weight rows. k is staged
+// 64 at a time (one 128-byte line of every row) through LDS filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4: no staging registers, no LDS
+// store instructions). The token tile has a ring of three LDS slots and the
+// weight tile a ring of two, which is what 160 KB of LDS holds for a 256 x 256
+// tile: token rows are loaded two stages ahead, weight rows one stage ahead.
 // Per stage:
-//   wait until this wave's loads of the stage have landed (the two newer
-//   stages stay in flight), barrier (so have every wave's)
-//   -> read the stage's MFMA fragments
-//   -> issue the loads of the stage three ahead into the buffer freed by the
-//      previous stage
-//   -> 32 MFMAs per wave (reads of the second 16-k step overlap the first).
+//   wait until this wave's loads of the stage have landed (its newest batch of
+//   token loads stays in flight), barrier (so have every wave's)
+//   -> for each of the four 16-k steps: issue a quarter of the loads of the
+//      following stages (weights of stage kt+1 first, then tokens of stage
+//      kt+2, into the slots freed by stage kt-1), read the next step's MFMA
+//      fragments, run this step's MFMAs.
+// The loads are spread over the MFMAs because a wave issues in order: a load
+// that waits for room in the memory pipeline holds up every MFMA behind it.
+// A compiler fence after each batch keeps the compiler from sinking the loads
+// below later fragment reads (it may, since they target other LDS arrays).
 // Every stage issues the same number of loads (past the end of the reduction
-// they read a 16-byte zero constant into the freed buffer), so the wait count
-// is the same at every stage; the kernel drains them before its epilogue.
+// they read a 16-byte zero constant), so the wait count is the same at every
+// stage; the kernel drains them before its epilogue.
 //
-// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r sits at
-// c ^ (((r >> 1) ^ (r >> 3)) & 3): fragment reads of 8 or 16 consecutive rows
-// fall in distinct bank groups. A direct load fills 64 consecutive chunk
-// slots (16 rows) per wave instruction; each lane fetches the global chunk
-// that belongs in its slot.
+// LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r sits at
+// c ^ ((r & 7) ^ ((r >> 3) & 1)): the fragment reads of 8 or 16 consecutive
+// rows fall in distinct bank groups. One direct load fills 64 consecutive
+// chunk slots (8 rows) per wave instruction; each lane fetches the global
+// chunk that belongs in its slot, so 8 lanes cover one row's 128-byte line.
 //
 // The weights are the MFMA M operand and the tokens the N operand, so lane l
 // of a 32x32 accumulator holds token l % 32 and four consecutive output
 // columns per register group; the epilogue stores 4 values at once.
 //
-// SwiGLU: the BN weight rows of a block are, per wave, WTN/2 rows of W1
+// SwiGLU: the BN weight rows of a block are, per wave column, WTN/2 rows of W1
 // followed by the same WTN/2 rows of W3, so the two products that meet in
 // SiLU(x W1) * (x W3) sit in the same lane and register.
 
-constexpr int kBK = 32;   // k per stage: 4 chunks of 8 bf16
-constexpr int kTileGroupN = 4;  // n-tiles per group in the XCD-aware block order
+constexpr int kBK = 64;          // k per stage
+constexpr int kCH = kBK / 8;     // 16-byte chunks per LDS row
+constexpr int kRPI = 64 / kCH;   // rows filled by one direct-load wave instruction
+constexpr int kTileGroupN = 4;   // n-tiles per group in the XCD-aware block order
 
 __device__ const u32x4_t kZeroChunk = {0u, 0u, 0u, 0u};
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 4 + (chunk ^ (((row >> 1) ^ (row >> 3)) & 3));
-}
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kCH + (chunk ^ swz_key(row)); }
 
 __device__ __forceinline__ void lds_dma16(const void* gsrc, u32x4_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gsrc),
@@ -111,23 +117,26 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, u32x4_t* lds_wave_ba
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
-  constexpr int WM = 2, WN = 2;
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
+  constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int A_IN = BM / 64;        // direct-load instructions per wave per stage (16 rows each)
-  constexpr int B_IN = BN / 64;
-  constexpr int DI = A_IN + B_IN;
-  constexpr int NCOLS = BN / NMAT;     // output columns per block
+  constexpr int A_IN = BM / (NW * kRPI);  // token-row loads per wave per stage
+  constexpr int B_IN = BN / (NW * kRPI);  // weight-row loads per wave per stage
+  constexpr int NKS = kBK / 16;           // MFMA k-steps per stage
+  constexpr int PER = (A_IN + B_IN + NKS - 1) / NKS;  // loads issued per k-step
+  constexpr int NCOLS = BN / NMAT;        // output columns per block
   static_assert(TM >= 1 && TN >= NMAT && A_IN >= 1 && B_IN >= 1, "tile too small");
-  static_assert(2 * DI <= 63, "vmcnt range");
+  static_assert(WTM % 32 == 0 && WTN % (32 * NMAT) == 0, "wave tile");
+  static_assert(2 * A_IN + B_IN <= 63, "vmcnt range");
+  static_assert((3 * BM + 2 * BN) * kCH * 16 <= 160 * 1024, "LDS");
 
   // One array per ring slot, so that reads of one slot are known not to alias
   // the direct loads that fill another.
-  __shared__ u32x4_t A0[BM * 4], A1[BM * 4], A2[BM * 4], A3[BM * 4];
-  __shared__ u32x4_t B0[BN * 4], B1[BN * 4], B2[BN * 4], B3[BN * 4];
+  __shared__ u32x4_t A0[BM * kCH], A1[BM * kCH], A2[BM * kCH];
+  __shared__ u32x4_t B0[BN * kCH], B1[BN * kCH];
 
   // XCD-aware order. Hardware sends block b to XCD b % 8; give each XCD a
   // contiguous run of logical tiles, ordered (n-tile group of kNG) x (m-tile)
@@ -165,49 +174,43 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
     }
   };
 
-  // Direct-load sources. Wave wid, instruction u fills slots [(wid*IN + u)*64, +64):
-  // rows (wid*IN + u)*16 + lane/4, physical chunk lane%4, i.e. logical chunk
-  // (lane%4) ^ f(row); f depends on the lane and on the parity of wid*IN + u.
-  // Offsets are 32-bit element offsets (every operand matrix has < 2^31 elements).
-  const int lr = lane / 4;
-  const int kc_even = ((lane % 4) ^ (((lr >> 1) ^ (lr >> 3)) & 3)) * 8;
-  const int kc_odd = ((lane % 4) ^ (((lr >> 1) ^ ((lr >> 3) | 2)) & 3)) * 8;
-  int a_off[A_IN];
+  // Direct-load sources. Wave wid, instruction u fills chunk slots
+  // [(wid*IN + u)*64, +64): row (wid*IN + u)*8 + lane/8, physical chunk
+  // lane%8, i.e. logical chunk (lane%8) ^ swz_key(row). Offsets are 32-bit
+  // element offsets (every operand matrix has < 2^31 elements).
+  int a_off[A_IN], a_kc[A_IN];
 #pragma unroll
   for (int u = 0; u < A_IN; ++u) {
-    const int r = (wid * A_IN + u) * 16 + lr;
+    const int r = (wid * A_IN + u) * kRPI + lane / kCH;
+    a_kc[u] = ((lane % kCH) ^ swz_key(r)) * 8;
     const int s = row0 + min(r, rows - 1);
     const int src_row = (p.x_rows != nullptr) ? p.x_rows[s] : s;
-    a_off[u] = src_row * Kd + (((wid * A_IN + u) & 1) ? kc_odd : kc_even);
+    a_off[u] = src_row * Kd + a_kc[u];
   }
   const bf16_t* Bexp = p.B + static_cast<size_t>(e) * N * Kd;
   const bf16_t* B3exp = (NMAT == 2) ? p.B3 + static_cast<size_t>(e) * N * Kd : Bexp;
-  int b_off[B_IN];
+  int b_off[B_IN], b_kc[B_IN];
 #pragma unroll
   for (int u = 0; u < B_IN; ++u) {
     int mat;
-    const int n = min(brow_col((wid * B_IN + u) * 16 + lr, &mat), N - 1);
-    b_off[u] = n * Kd + (((wid * B_IN + u) & 1) ? kc_odd : kc_even);
+    const int r = (wid * B_IN + u) * kRPI + lane / kCH;
+    b_kc[u] = ((lane % kCH) ^ swz_key(r)) * 8;
+    const int n = min(brow_col(r, &mat), N - 1);
+    b_off[u] = n * Kd + b_kc[u];
   }
-  // Loads of the stage starting at k0 (or zeros if k0 is past the end).
-  auto issue_stage = [&](int k0, u32x4_t* As, u32x4_t* Bs) {
-#pragma unroll
-    for (int u = 0; u < A_IN; ++u) {
-      const int kc = ((wid * A_IN + u) & 1) ? kc_odd : kc_even;
-      const void* g = (k0 + kc < Kd) ? static_cast<const void*>(p.x + a_off[u] + k0)
-                                     : static_cast<const void*>(&kZeroChunk);
-      lds_dma16(g, As + (wid * A_IN + u) * 64);
-    }
-#pragma unroll
-    for (int u = 0; u < B_IN; ++u) {
-      int mat;
-      (void)brow_col((wid * B_IN + u) * 16, &mat);  // the 16 rows of one instruction share a matrix
-      const int kc = ((wid * B_IN + u) & 1) ? kc_odd : kc_even;
-      const bf16_t* base = (NMAT == 2 && mat) ? B3exp : Bexp;
-      const void* g = (k0 + kc < Kd) ? static_cast<const void*>(base + b_off[u] + k0)
-                                     : static_cast<const void*>(&kZeroChunk);
-      lds_dma16(g, Bs + (wid * B_IN + u) * 64);
-    }
+  // Load u of the token rows of the stage starting at k0 (zeros past the end).
+  auto load_a = [&](int u, int k0, u32x4_t* As) {
+    const void* g = (k0 + a_kc[u] < Kd) ? static_cast<const void*>(p.x + a_off[u] + k0)
+                                        : static_cast<const void*>(&kZeroChunk);
+    lds_dma16(g, As + (wid * A_IN + u) * 64);
+  };
+  auto load_b = [&](int u, int k0, u32x4_t* Bs) {
+    int mat;
+    (void)brow_col((wid * B_IN + u) * kRPI, &mat);  // the 8 rows of one instruction share a matrix
+    const bf16_t* base = (NMAT == 2 && mat) ? B3exp : Bexp;
+    const void* g = (k0 + b_kc[u] < Kd) ? static_cast<const void*>(base + b_off[u] + k0)
+                                        : static_cast<const void*>(&kZeroChunk);
+    lds_dma16(g, Bs + (wid * B_IN + u) * 64);
   };
 
   f32x16_t acc[TN][TM];
@@ -222,12 +225,14 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
   const int fsub = lane / 32;  // which of the two 8-wide k chunks of a 16-k step
   const int nk = (Kd + kBK - 1) / kBK;
 
-  auto run_stage = [&](int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* An, u32x4_t* Bn) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DI));  // this wave's loads of stage kt have landed
+  // Stage kt: MFMAs on slots (As, Bs); loads of weights (kt+1) into Bn and of
+  // tokens (kt+2) into An2, weights first.
+  auto run_stage = [&](int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* Bn, u32x4_t* An2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(A_IN));  // all but this wave's newest token batch landed
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();                   // ... and every other wave's
+    __builtin_amdgcn_s_barrier();                 // ... for every wave
     asm volatile("" ::: "memory");
-    bf16x8_t wf[kBK / 16][TN], xf[kBK / 16][TM];
+    bf16x8_t wf[NKS][TN], xf[NKS][TM];
     auto read = [&](int ks) {
       const int c = ks * 2 + fsub;
 #pragma unroll
@@ -236,10 +241,16 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
       for (int i = 0; i < TM; ++i) xf[ks][i] = as_bf16x8(As[swz(wm * WTM + i * 32 + frow, c)]);
     };
     read(0);
-    issue_stage((kt + 3) * kBK, An, Bn);  // zeros once past the end: keeps the wait count uniform
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      if (ks + 1 < kBK / 16) read(ks + 1);
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const int idx = ks * PER + q;
+        if (idx < B_IN) load_b(idx, (kt + 1) * kBK, Bn);
+        else if (idx < A_IN + B_IN) load_a(idx - B_IN, (kt + 2) * kBK, An2);
+      }
+      asm volatile("" ::: "memory");  // keep the loads ahead of the later fragment reads
+      if (ks + 1 < NKS) read(ks + 1);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -248,19 +259,29 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
     }
   };
 
-  issue_stage(0, A0, B0);
-  issue_stage(kBK, A1, B1);
-  issue_stage(2 * kBK, A2, B2);
+  // Prologue: tokens of stages 0 and 1, weights of stage 0 (in the order the
+  // stage waits expect: the newest token batch may stay in flight).
+#pragma unroll
+  for (int u = 0; u < A_IN; ++u) load_a(u, 0, A0);
+#pragma unroll
+  for (int u = 0; u < B_IN; ++u) load_b(u, 0, B0);
+#pragma unroll
+  for (int u = 0; u < A_IN; ++u) load_a(u, kBK, A1);
+  // Straight-line ring over lcm(3, 2) = 6 stages: no merge point for acc inside the loop.
   int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {  // straight-line ring: no merge point for acc inside the loop
-    run_stage(kt, A0, B0, A3, B3);
-    run_stage(kt + 1, A1, B1, A0, B0);
-    run_stage(kt + 2, A2, B2, A1, B1);
-    run_stage(kt + 3, A3, B3, A2, B2);
+  for (; kt + 6 <= nk; kt += 6) {
+    run_stage(kt, A0, B0, B1, A2);
+    run_stage(kt + 1, A1, B1, B0, A0);
+    run_stage(kt + 2, A2, B0, B1, A1);
+    run_stage(kt + 3, A0, B1, B0, A2);
+    run_stage(kt + 4, A1, B0, B1, A0);
+    run_stage(kt + 5, A2, B1, B0, A1);
   }
-  if (kt < nk) run_stage(kt, A0, B0, A3, B3);
-  if (kt + 1 < nk) run_stage(kt + 1, A1, B1, A0, B0);
-  if (kt + 2 < nk) run_stage(kt + 2, A2, B2, A1, B1);
+  if (kt < nk) run_stage(kt, A0, B0, B1, A2);
+  if (kt + 1 < nk) run_stage(kt + 1, A1, B1, B0, A0);
+  if (kt + 2 < nk) run_stage(kt + 2, A2, B0, B1, A1);
+  if (kt + 3 < nk) run_stage(kt + 3, A0, B1, B0, A2);
+  if (kt + 4 < nk) run_stage(kt + 4, A1, B0, B1, A0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
   asm volatile("" ::: "memory");
 
@@ -442,22 +463,24 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmPara
 
 // ---------------------------------------------------------------------------- launch
 
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE>
 hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
   p.n_mt = (S + BM - 1) / BM + min(p.E, S);
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
   const size_t total = static_cast<size_t>((n_nt + kTileGroupN - 1) / kTileGroupN) * p.n_mt * kTileGroupN;
   const size_t grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, MODE>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE>), dim3(static_cast<unsigned>(grid)),
+                     dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
 }
 
 // Tile shape from the mean rows per expert (S / E): with about 1k rows per
-// expert, 256 x 256 tiles (the largest accumulator tile a compute unit's
-// registers hold, and the fewest bytes moved per flop); with about 100 rows
-// per expert, 128-row tiles waste less of each weight tile on padding rows.
-// Small grids fall back to 128 x 128 so that the chip is still covered.
+// expert, 256 x 256 tiles (the fewest bytes moved per flop) on 8 waves, two
+// per SIMD, so that one wave's MFMAs run while the other waits; with about
+// 100 rows per expert, 128-row tiles waste less of each weight tile on
+// padding rows. Small grids fall back to 128 x 128 so that the chip is still
+// covered.
 template <int MODE>
 hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
   constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU);
@@ -466,9 +489,9 @@ hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
   auto blocks = [&](int bm, int bn) {
     return static_cast<long>((S + bm - 1) / bm + min(p.E, S)) * ((p.N + bn / NMAT - 1) / (bn / NMAT));
   };
-  if (mean_rows >= 512 && blocks(256, 256) >= 2 * 256) return launch_tile<256, 256, MODE>(p, S, st);
-  if (G1 && blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, MODE>(p, S, st);
-  return launch_tile<128, 128, MODE>(p, S, st);
+  if (mean_rows >= 512 && blocks(256, 256) >= 2 * 256) return launch_tile<256, 256, 4, 2, MODE>(p, S, st);
+  if (G1 && blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, 4, 2, MODE>(p, S, st);
+  return launch_tile<128, 128, 2, 2, MODE>(p, S, st);
 }
 
 template <int MODE, int NR, int NBUF>
