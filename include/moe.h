@@ -82,10 +82,11 @@ typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,         /* a required pointer is NULL */
   MOE_ERR_SHAPE = 2,        /* T < 0, d or width < 1, E < 1, K < 1 or K > E */
-  MOE_ERR_UNSUPPORTED = 3,  /* E > 64, K > 8, d or width not a multiple of 8, S or
-                               tensor sizes beyond 2^31 - 1 elements, an unknown
-                               act/gate/dtype, a misaligned pointer, or W3 missing
-                               for SwiGLU */
+  MOE_ERR_UNSUPPORTED = 3,  /* E > 64, K > 8, d or width not a multiple of 8,
+                               d or width above 2^20, T*K above 2^31 - 1, an operand
+                               matrix (S x d, S x width or d x width) of more than
+                               2^31 - 2^22 elements, an unknown act/gate/dtype, a
+                               misaligned pointer, or W3 missing for SwiGLU */
   MOE_ERR_WORKSPACE = 4,    /* ws_bytes smaller than moe_workspace_size(), or ws misaligned */
   MOE_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } moe_status;

@@ -28,6 +28,12 @@ namespace {
 using moe::RouteTiling;
 
 constexpr int64_t kMaxInt = 2147483647;
+// Operand matrices (h, grouped rows, hidden activations, one expert's weight
+// matrix) hold at most 2^31 - 2^22 elements and d, width are at most 2^20, so that
+// 32-bit element offsets, and the byte offsets of the bfloat16 GEMMs' buffer
+// loads (row offset + k offset), never wrap.
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - (int64_t{1} << 22);
+constexpr int64_t kMaxDim = int64_t{1} << 20;
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -77,12 +83,10 @@ int check_desc(const moe_desc* d) {
   if (d->gate != MOE_GATE_RENORM && d->gate != MOE_GATE_RAW) return MOE_ERR_UNSUPPORTED;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->reserved != 0) return MOE_ERR_UNSUPPORTED;
-  if (d->T > kMaxInt / d->K || d->d > kMaxInt || d->width > kMaxInt) return MOE_ERR_UNSUPPORTED;
-  // every operand matrix (h, grouped rows, hidden activations, one expert's
-  // weight matrix) must have fewer than 2^31 elements: kernels use 32-bit offsets
+  if (d->T > kMaxInt / d->K || d->d > kMaxDim || d->width > kMaxDim) return MOE_ERR_UNSUPPORTED;
   const int64_t S = d->T * d->K;
-  if (S > 0 && (S > kMaxInt / d->d || S > kMaxInt / d->width)) return MOE_ERR_UNSUPPORTED;
-  if (d->d > kMaxInt / d->width) return MOE_ERR_UNSUPPORTED;
+  if (S > 0 && (S > kMaxElems / d->d || S > kMaxElems / d->width)) return MOE_ERR_UNSUPPORTED;
+  if (d->d > kMaxElems / d->width) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

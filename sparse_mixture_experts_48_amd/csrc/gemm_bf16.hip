@@ -49,6 +49,7 @@ struct GemmParams {
   const float* gate;        // topk_gate [T] (K = 1)
   int E, N, Kd;
   int S;                    // grouped rows (bound of every grouped-row index)
+  int x_nrows;              // rows of x
   int n_mt;                 // m-tile slots in the grid (upper bound)
 };
 
@@ -66,7 +67,7 @@ __device__ __forceinline__ float epilogue_g1(int mode, float v1, float v3, const
 //
 // Block: WM x WN waves; tile = BM grouped rows x BN weight rows. k is staged
 // 64 at a time (one 128-byte line of every row) through LDS filled by direct
-// global-to-LDS loads (global_load_lds_dwordx4: no staging registers, no LDS
+// global-to-LDS loads (buffer_load_dwordx4 ... lds: no staging registers, no LDS
 // store instructions). The token tile has a ring of three LDS slots and the
 // weight tile a ring of two, which is what 160 KB of LDS holds for a 256 x 256
 // tile: token rows are loaded two stages ahead, weight rows one stage ahead.
@@ -81,9 +82,14 @@ __device__ __forceinline__ float epilogue_g1(int mode, float v1, float v3, const
 // that waits for room in the memory pipeline holds up every MFMA behind it.
 // A compiler fence after each batch keeps the compiler from sinking the loads
 // below later fragment reads (it may, since they target other LDS arrays).
-// Every stage issues the same number of loads (past the end of the reduction
-// they read a 16-byte zero constant), so the wait count is the same at every
-// stage; the kernel drains them before its epilogue.
+// The loads are buffer loads: the k offset of a stage is a scalar added to a
+// per-lane byte offset fixed for the whole reduction, so a load costs no
+// vector instructions. In the last stage the lanes whose chunk lies past the
+// end of the reduction use an offset past the end of the buffer, which the
+// range check turns into zeros. Every stage issues the same number of loads
+// (stages past the last reload the last one into slots no stage reads), so
+// the wait count is the same at every stage; the kernel drains them before
+// its epilogue.
 //
 // LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r sits at
 // c ^ ((r & 7) ^ ((r >> 3) & 1)): the fragment reads of 8 or 16 consecutive
@@ -104,14 +110,22 @@ constexpr int kCH = kBK / 8;     // 16-byte chunks per LDS row
 constexpr int kRPI = 64 / kCH;   // rows filled by one direct-load wave instruction
 constexpr int kTileGroupN = 4;   // n-tiles per group in the XCD-aware block order
 
-__device__ const u32x4_t kZeroChunk = {0u, 0u, 0u, 0u};
-
 __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kCH + (chunk ^ swz_key(row)); }
 
-__device__ __forceinline__ void lds_dma16(const void* gsrc, u32x4_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gsrc),
-                                   (__attribute__((address_space(3))) void*)(lds_wave_base), 16, 0, 0);
+// Buffer resource over `bytes` bytes at `base` (raw dword buffer; loads at
+// byte offsets >= bytes return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes per lane at byte offset voff + soff of the buffer into LDS: the
+// wave writes 64 x 16 consecutive bytes at lds_wave_base.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff,
+                                           u32x4_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16,
+                                           static_cast<int>(voff), soff, 0, 0);
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid % 64;
-  const int wid = tid / 64;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform: LDS bases stay scalar
   const int wm = wid / WN, wn = wid % WN;
   const int Kd = p.Kd, N = p.N;
 
@@ -176,41 +190,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 
   // Direct-load sources. Wave wid, instruction u fills chunk slots
   // [(wid*IN + u)*64, +64): row (wid*IN + u)*8 + lane/8, physical chunk
-  // lane%8, i.e. logical chunk (lane%8) ^ swz_key(row). Offsets are 32-bit
-  // element offsets (every operand matrix has < 2^31 elements).
-  int a_off[A_IN], a_kc[A_IN];
+  // lane%8, i.e. logical chunk (lane%8) ^ swz_key(row). Byte offsets are
+  // 32-bit: the host keeps every operand matrix at or below 2^32 - 2^23 bytes
+  // and d, width at or below 2^20, so row offset + k offset never wraps.
+  const int nk = (Kd + kBK - 1) / kBK;
+  const int k_last = (nk - 1) * kBK;  // first k of the last stage
+  const uint32_t a_bytes = static_cast<uint32_t>(p.x_nrows) * static_cast<uint32_t>(Kd) * 2u;
+  const uint32_t b_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(Kd) * 2u;
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.x, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb1 = buffer_rsrc(p.B + static_cast<size_t>(e) * N * Kd, b_bytes);
+  const __amdgpu_buffer_rsrc_t rb3 =
+      (NMAT == 2) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * N * Kd, b_bytes) : rb1;
+  // per lane: offset for every stage, and for the last one (out of range past the end of k)
+  uint32_t a_vo[A_IN], a_vl[A_IN], b_vo[B_IN], b_vl[B_IN];
 #pragma unroll
   for (int u = 0; u < A_IN; ++u) {
     const int r = (wid * A_IN + u) * kRPI + lane / kCH;
-    a_kc[u] = ((lane % kCH) ^ swz_key(r)) * 8;
+    const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
     const int s = row0 + min(r, rows - 1);
     const int src_row = (p.x_rows != nullptr) ? p.x_rows[s] : s;
-    a_off[u] = src_row * Kd + a_kc[u];
+    a_vo[u] = (static_cast<uint32_t>(src_row) * static_cast<uint32_t>(Kd) + static_cast<uint32_t>(kc)) * 2u;
+    a_vl[u] = (k_last + kc < Kd) ? a_vo[u] : a_bytes;
   }
-  const bf16_t* Bexp = p.B + static_cast<size_t>(e) * N * Kd;
-  const bf16_t* B3exp = (NMAT == 2) ? p.B3 + static_cast<size_t>(e) * N * Kd : Bexp;
-  int b_off[B_IN], b_kc[B_IN];
 #pragma unroll
   for (int u = 0; u < B_IN; ++u) {
     int mat;
     const int r = (wid * B_IN + u) * kRPI + lane / kCH;
-    b_kc[u] = ((lane % kCH) ^ swz_key(r)) * 8;
+    const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
     const int n = min(brow_col(r, &mat), N - 1);
-    b_off[u] = n * Kd + b_kc[u];
+    b_vo[u] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(Kd) + static_cast<uint32_t>(kc)) * 2u;
+    b_vl[u] = (k_last + kc < Kd) ? b_vo[u] : b_bytes;
   }
-  // Load u of the token rows of the stage starting at k0 (zeros past the end).
+  // Load u of the token rows of the stage starting at k0.
   auto load_a = [&](int u, int k0, u32x4_t* As) {
-    const void* g = (k0 + a_kc[u] < Kd) ? static_cast<const void*>(p.x + a_off[u] + k0)
-                                        : static_cast<const void*>(&kZeroChunk);
-    lds_dma16(g, As + (wid * A_IN + u) * 64);
+    lds_load16(ra, k0 >= k_last ? a_vl[u] : a_vo[u], min(k0, k_last) * 2, As + (wid * A_IN + u) * 64);
   };
   auto load_b = [&](int u, int k0, u32x4_t* Bs) {
     int mat;
     (void)brow_col((wid * B_IN + u) * kRPI, &mat);  // the 8 rows of one instruction share a matrix
-    const bf16_t* base = (NMAT == 2 && mat) ? B3exp : Bexp;
-    const void* g = (k0 + b_kc[u] < Kd) ? static_cast<const void*>(base + b_off[u] + k0)
-                                        : static_cast<const void*>(&kZeroChunk);
-    lds_dma16(g, Bs + (wid * B_IN + u) * 64);
+    lds_load16((NMAT == 2 && mat) ? rb3 : rb1, k0 >= k_last ? b_vl[u] : b_vo[u], min(k0, k_last) * 2,
+               Bs + (wid * B_IN + u) * 64);
   };
 
   f32x16_t acc[TN][TM];
@@ -223,7 +242,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 
   const int frow = lane % 32;
   const int fsub = lane / 32;  // which of the two 8-wide k chunks of a 16-k step
-  const int nk = (Kd + kBK - 1) / kBK;
 
   // Stage kt: MFMAs on slots (As, Bs); loads of weights (kt+1) into Bn and of
   // tokens (kt+2) into An2, weights first.
@@ -519,6 +537,7 @@ hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st) {
   GemmParams p{};
   p.x = static_cast<const bf16_t*>(f.x);
   p.x_rows = f.x_rows;
+  p.x_nrows = f.x_rows != nullptr ? f.S / f.K : f.S;
   p.offsets = f.offsets;
   p.B = static_cast<const bf16_t*>(f.W1);
   p.B3 = static_cast<const bf16_t*>(f.W3);
@@ -539,6 +558,7 @@ hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st) {
 hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
   GemmParams p{};
   p.x = static_cast<const bf16_t*>(f.a);
+  p.x_nrows = f.S;
   p.offsets = f.offsets;
   p.B = static_cast<const bf16_t*>(f.W2);
   p.B3 = nullptr;

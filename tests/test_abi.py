@@ -42,6 +42,9 @@ def test_status_strings():
     (dict(K=0), SHAPE), (dict(K=9, E=8), SHAPE), (dict(E=65, K=2), UNSUP), (dict(E=64, K=9), UNSUP),
     (dict(d=100), UNSUP), (dict(w=1372), UNSUP), (dict(act=2), UNSUP), (dict(gate=5), UNSUP),
     (dict(dtype=7), UNSUP), (dict(reserved=1), UNSUP), (dict(T=2 ** 30, K=2), UNSUP),
+    (dict(d=2 ** 20 + 8, w=8), UNSUP), (dict(w=2 ** 20 + 8, d=8), UNSUP), (dict(d=2 ** 20, w=8), OK),
+    # operand matrices hold at most 2^31 - 2^22 elements: T*K*d = 2^31 - 2^22 exactly is the largest
+    (dict(T=261632, d=4096, K=2, w=512), OK), (dict(T=261633, d=4096, K=2, w=512), UNSUP),
 ])
 def test_bad_descriptors(kw, status):
     n = ctypes.c_size_t(0)

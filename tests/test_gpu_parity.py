@@ -54,6 +54,8 @@ SMALL = {
                           "zipf1.1", 22),
     "stream_gelu_T24": L("stream_gelu_T24", 24, 128, 8, 2, 512, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16,
                          "normal2", 23),
+    # both reductions shorter than one 64-k stage of the tiled kernel
+    "bf16_short_k": L("bf16_short_k", 300, 40, 4, 2, 48, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 28),
     "T1": L("T1", 1, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 26),
     "f32_T1": L("f32_T1", 1, 64, 8, 2, 64, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2", 27),
 }
