@@ -107,16 +107,24 @@ def time_workload(cfg, steps, warmup, label):
     return ms, kernels, alg, counts, aux, ms_graph
 
 
-def roofline_mfma(flops, mean_ms, peak):
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of `workload` (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy);
+    None if there is none or the kernel source changed since it was taken."""
+    from sparse_mixture_experts_48_amd import profiling
+    return profiling.traffic_bytes(os.path.join(ROOT, "profiles", "hbm_traffic_%s.md" % workload), kernel, ROOT)
+
+
+def roofline_mfma(flops, mean_ms, peak, traffic=None):
     achieved = flops / (mean_ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None}
+            "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-def roofline_hbm(nbytes, mean_ms):
+def roofline_hbm(nbytes, mean_ms, traffic=None):
     achieved = nbytes / (mean_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic}
 
 
 def cpu_baseline(cfg, n_tokens):
@@ -205,7 +213,10 @@ def main():
         "data": "synthetic (seeded normal inputs, random-init weights; no dataset)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "K": cfg.K, "width": cfg.width,
                    "act": "swiglu", "gate": "renorm", "router": "float32", "parallelism": "single GPU"},
-        "roofline": dict(roofline_mfma(alg["flops_gemm1"], g1, PEAK_BF16_TFLOPS), kernel="gemm1"),
+        "roofline": dict(roofline_mfma(alg["flops_gemm1"], g1, PEAK_BF16_TFLOPS,
+                                       measured_traffic(cfg.name, "gemm1")), kernel="gemm1",
+                         algorithmic_bytes=int(alg["weight_bytes_gemm1"] + cfg.T * cfg.d * bpe(cfg)
+                                               + cfg.S * cfg.width * bpe(cfg))),
         "layer_tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
         "layer_mfma_frac": round(alg["flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "aux_loss": round(aux, 6),
@@ -223,9 +234,10 @@ def main():
             "layer_hbm_GBps": round(dalg["bytes"] / (dms * 1e-3) / 1e9, 1),
             "layer_hbm_frac": round(dalg["bytes"] / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "experts_hit": dalg["experts_hit"],
-            "roofline": dict(roofline_hbm(dalg["weight_bytes_gemm1"], dk["gemm1"]["mean_ms"]), kernel="gemm1"),
-            "roofline_gemm2": dict(roofline_hbm(dalg["weight_bytes_gemm2"], dk["gemm2"]["mean_ms"]),
-                                   kernel="gemm2"),
+            "roofline": dict(roofline_hbm(dalg["weight_bytes_gemm1"], dk["gemm1"]["mean_ms"],
+                                          measured_traffic(dcfg.name, "gemm1")), kernel="gemm1"),
+            "roofline_gemm2": dict(roofline_hbm(dalg["weight_bytes_gemm2"], dk["gemm2"]["mean_ms"],
+                                                measured_traffic(dcfg.name, "gemm2")), kernel="gemm2"),
             "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in dk.items()},
         }
         scfg = W.WORKLOADS["switch_top1"]
@@ -236,7 +248,8 @@ def main():
             "layer_tflops": round(salg["flops"] / (sms * 1e-3) / 1e12, 2),
             "layer_hbm_GBps": round(salg["bytes"] / (sms * 1e-3) / 1e9, 1),
             "layer_hbm_frac": round(salg["bytes"] / (sms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "roofline": dict(roofline_hbm(salg["weight_bytes_gemm1"], sk["gemm1"]["mean_ms"]), kernel="gemm1"),
+            "roofline": dict(roofline_hbm(salg["weight_bytes_gemm1"], sk["gemm1"]["mean_ms"],
+                                          measured_traffic(scfg.name, "gemm1")), kernel="gemm1"),
             "aux_loss": round(saux, 6), "experts_hit": salg["experts_hit"],
             "max_expert_rows": int(scounts.max()),
             "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in sk.items()},

@@ -1,0 +1,156 @@
+"""Summaries of rocprofv3 output for the layer's kernels.
+
+Two kinds of summary, both short Markdown files:
+
+* kernel trace (``rocprofv3 --kernel-trace --stats``): calls, mean and total
+  duration of every kernel of a run;
+* HBM traffic (two ``rocprofv3 --pmc`` runs, ``FETCH_SIZE`` then
+  ``WRITE_SIZE``): bytes per launch of chosen kernels. Both counters are
+  scaled by what they read for a plain device-to-device copy of known size
+  taken in the same run (``bench.py --calibrate-copy MB``), so the figures are
+  bytes, whatever unit the counters count in. The summary records the SHA-256
+  of the source file of the kernels it measured; ``traffic_bytes`` returns
+  nothing once that file has changed.
+
+Command line::
+
+    python -m sparse_mixture_experts_48_amd.profiling trace STATS_CSV --command "..." > out.md
+    python -m sparse_mixture_experts_48_amd.profiling traffic FETCH_CSV WRITE_CSV --copy-mib 1024 \\
+        --kernel gemm1=PATTERN --source FILE --workload NAME --command "..." > out.md
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+from collections import OrderedDict
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+TRAFFIC_TAG = "traffic-json:"
+
+
+def short_name(kernel: str) -> str:
+    """Kernel name without namespaces, argument list and return type."""
+    k = kernel.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    k = re.sub(r"\((moe::)?(\(anonymous namespace\)::)?[A-Za-z_][^()]*\)$", "", k)
+    return k.strip()
+
+
+def summarize_trace(stats_csv: str, command: str, title: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = ["# %s" % title, "", "Command:", "", "```", command, "```", "",
+           "| kernel | calls | mean (us) | min (us) | max (us) | share of GPU time |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f %% |" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(counter_csv: str, counter: str):
+    """{dispatch id: (kernel name, summed counter value)} in dispatch order."""
+    per = OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = per.get(d, (r["Kernel_Name"], 0.0))
+        per[d] = (name, v + float(r["Counter_Value"]))
+    return per
+
+
+def _copy_factor(per, copy_bytes: int) -> float:
+    """Bytes per counter unit, from the largest copy kernel of the run."""
+    vals = [v for name, v in per.values() if COPY_KERNEL in name]
+    if not vals or max(vals) <= 0:
+        raise ValueError("no calibration copy in the counter file")
+    return copy_bytes / max(vals)
+
+
+def file_sha256(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int, kernels: dict, source: str,
+                      workload: str, command: str, repo_root: str) -> str:
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib << 20
+    ff, wf = _copy_factor(fetch, copy_bytes), _copy_factor(write, copy_bytes)
+    result = {}
+    lines = []
+    for label, pattern in kernels.items():
+        rx = re.compile(pattern)
+        fv = [v for name, v in fetch.values() if rx.search(name)]
+        wv = [v for name, v in write.values() if rx.search(name)]
+        if not fv or not wv:
+            raise ValueError("kernel %s (%s) not found" % (label, pattern))
+        f_b = sum(fv) / len(fv) * ff
+        w_b = sum(wv) / len(wv) * wf
+        result[label] = {"read_bytes": round(f_b), "write_bytes": round(w_b), "bytes": round(f_b + w_b),
+                         "launches": [len(fv), len(wv)]}
+        lines.append("| %s | `%s` | %d / %d | %.4f | %.4f | %.4f |" % (
+            label, pattern, len(fv), len(wv), f_b / 1e9, w_b / 1e9, (f_b + w_b) / 1e9))
+    src_rel = os.path.relpath(source, repo_root)
+    payload = {"workload": workload, "source": src_rel, "source_sha256": file_sha256(source),
+               "fetch_bytes_per_unit": ff, "write_bytes_per_unit": wf, "kernels": result}
+    out = ["# HBM traffic per launch: %s" % workload, "",
+           "Commands (one counter pass each; the run also copies %d MiB device to device, whose counts "
+           "give the scale of each counter):" % copy_mib, "", "```", command, "```", "",
+           "Scale: FETCH_SIZE x %.1f bytes per unit, WRITE_SIZE x %.1f bytes per unit." % (ff, wf), "",
+           "| kernel | name pattern | launches (fetch/write pass) | read GB | written GB | total GB |",
+           "|---|---|---:|---:|---:|---:|"] + lines + [
+           "", "Source measured: `%s` (sha256 %s). The benchmark reports these bytes only while that "
+           "file is unchanged." % (src_rel, payload["source_sha256"][:16]), "",
+           "%s %s" % (TRAFFIC_TAG, json.dumps(payload, sort_keys=True))]
+    return "\n".join(out) + "\n"
+
+
+def traffic_bytes(summary_md: str, label: str, repo_root: str):
+    """HBM bytes per launch of kernel `label` from a traffic summary, or None
+    when the summary is missing or its kernel source has changed since."""
+    if not os.path.exists(summary_md):
+        return None
+    for line in open(summary_md):
+        if line.startswith(TRAFFIC_TAG):
+            payload = json.loads(line[len(TRAFFIC_TAG):])
+            src = os.path.join(repo_root, payload["source"])
+            if not os.path.exists(src) or file_sha256(src) != payload["source_sha256"]:
+                return None
+            k = payload["kernels"].get(label)
+            return None if k is None else k["bytes"]
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("--command", required=True)
+    t.add_argument("--title", default="Kernel trace")
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch_csv")
+    f.add_argument("write_csv")
+    f.add_argument("--copy-mib", type=int, required=True)
+    f.add_argument("--kernel", action="append", required=True, metavar="LABEL=REGEX")
+    f.add_argument("--source", required=True)
+    f.add_argument("--workload", required=True)
+    f.add_argument("--command", required=True)
+    a = ap.parse_args()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if a.what == "trace":
+        print(summarize_trace(a.stats_csv, a.command, a.title), end="")
+    else:
+        kernels = OrderedDict(kv.split("=", 1) for kv in a.kernel)
+        print(summarize_traffic(a.fetch_csv, a.write_csv, a.copy_mib, kernels, a.source, a.workload, a.command,
+                                root), end="")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,43 @@
+"""rocprofv3 summaries: counter scaling by the calibration copy, and traffic
+figures that disappear once the measured kernel source changes (CPU only)."""
+import csv
+
+from sparse_mixture_experts_48_amd import profiling
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _counters(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d, name, value in rows:
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_traffic_scaled_by_copy_and_tied_to_source(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    gemm = "void moe::(anonymous namespace)::gemm_tile_kernel<256, 256, 4, 2, 0>(moe::GemmParams)"
+    # 1 MiB copy: fetch counts in 64-byte units here (two rows per dispatch, summed), write in KiB
+    _counters(tmp_path / "f.csv", "FETCH_SIZE", [(1, copy, 8192), (1, copy, 8192), (2, gemm, 100), (3, gemm, 300)])
+    _counters(tmp_path / "w.csv", "WRITE_SIZE", [(1, copy, 1024), (2, gemm, 10), (3, gemm, 30)])
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    md = profiling.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 1,
+                                     {"gemm1": r"gemm_tile_kernel<256, 256, 4, 2, 0>"}, str(src), "w",
+                                     "rocprofv3 ...", str(tmp_path))
+    out = tmp_path / "hbm.md"
+    out.write_text(md)
+    # fetch: 1 MiB / 16384 units = 64 B per unit -> mean 200 units = 12800 B; write: 1024 B per unit -> 20480 B
+    assert profiling.traffic_bytes(str(out), "gemm1", str(tmp_path)) == 12800 + 20480
+    assert profiling.traffic_bytes(str(out), "gemm2", str(tmp_path)) is None
+    src.write_text("kernel v2\n")
+    assert profiling.traffic_bytes(str(out), "gemm1", str(tmp_path)) is None
+    assert profiling.traffic_bytes(str(tmp_path / "missing.md"), "gemm1", str(tmp_path)) is None
+
+
+def test_short_kernel_names():
+    assert profiling.short_name(
+        "void moe::(anonymous namespace)::gemm_tile_kernel<256, 256, 4, 2, 0>(moe::(anonymous namespace)::GemmParams)"
+    ) == "gemm_tile_kernel<256, 256, 4, 2, 0>"
+    assert profiling.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
