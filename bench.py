@@ -166,7 +166,7 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "switch"], default=None,
                     help="time one workload only (for per-workload profiles); prints its own JSON object")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="also run a plain device-to-device copy of this many MiB (a reference for HBM counters)")
     args = ap.parse_args()
