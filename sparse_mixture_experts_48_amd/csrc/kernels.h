@@ -11,8 +11,9 @@ namespace moe {
 // router's per-block histograms line up with the grouping blocks.
 struct RouteTiling {
   int EP;   // experts padded to 8, 16, 32 or 64
-  int TPT;  // tokens per thread
-  int TB;   // tokens per block
+  int TPT;  // tokens per thread (wide layout) or per wave (narrow layout)
+  int NW;   // waves per block of the narrow layout; 0 selects the wide layout
+  int TB;   // tokens per block (at most 32)
   int NB;   // blocks
 };
 RouteTiling route_tiling(int64_t T, int64_t E);

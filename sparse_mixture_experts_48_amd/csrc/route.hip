@@ -11,10 +11,18 @@
 //
 // Numeric contract: each logit is one fmaf chain over k = 0..d-1 from +0,
 // bias added afterwards, so the expert choice is independent of any
-// parallel-reduction order. A thread owns TPT tokens x TE experts and walks k
-// upward; lanes are laid out as [token group][expert lane], so the experts of
-// one token sit in LE = EP/TE adjacent lanes of one wave and the per-token
-// max / argmax / sum reductions are xor-butterflies inside those lanes.
+// parallel-reduction order.
+//
+// Two layouts of the same chains:
+//  * wide (E > 16): a thread owns TPT tokens x TE experts and walks k upward;
+//    lanes are laid out as [token group][expert lane], so the experts of one
+//    token sit in LE = EP/TE adjacent lanes of one wave and the per-token
+//    max / argmax / sum reductions are xor-butterflies inside those lanes.
+//  * narrow (E <= 16, T <= 256): one token per wave, lane = expert. The wave turns its
+//    token's h into float32 once per chunk of k (its own LDS row), the block
+//    stages W_r chunks in LDS, and each of the E active lanes runs its chain
+//    reading h as a broadcast and its W_r column: no conversion in the chain,
+//    and many more waves in flight for small batches.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,7 +31,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteTB = 32;  // tokens per block
+constexpr int kRouteTB = 32;  // tokens per block (wide layout)
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
@@ -61,7 +69,7 @@ template <> struct HVec<bf16_t> {
 // BK: k values per LDS stage; NS: pipeline depth (NS - 1 stages of global
 // loads in flight in registers while one stage is consumed from LDS).
 template <typename Tin, int EP, int TE, int TPT, int BK, int NS>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+__global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
     int T, int d, int E, int K, int gate_mode,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
@@ -307,6 +315,195 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
 }
 
+// Narrow layout: NW waves per block, one token per wave; chunks of kNarrowKC k.
+constexpr int kNarrowKC = 512;
+
+template <typename Tin, int EP, int NW>
+__global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
+    const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
+    int T, int d, int E, int K, int gate_mode,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
+    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum) {
+  constexpr int KC = kNarrowKC;
+  constexpr int NT = NW * 64;
+  constexpr int WF4 = KC * EP / 4;         // float4 slots of a W_r chunk buffer
+  constexpr int WI = (WF4 + NT - 1) / NT;  // W_r float4 loads per thread per chunk
+  static_assert(KC == 8 * 64, "one 8-value h vector per lane per chunk");
+  // Separate arrays per buffer, so that reads of one chunk are known not to
+  // alias the writes of the next.
+  constexpr int RD = 8;                     // ring depth of the chain (steps of 4 k)
+  constexpr int HP = KC + 4 * RD;           // h row stride: the ring may read 4*RD past the chunk
+  __shared__ __align__(16) float hA[NW][HP];
+  __shared__ __align__(16) float hB[NW][HP];
+  constexpr int KP = KC + 4 * RD + 4;       // row stride of the transposed chunk (floats)
+  __shared__ __align__(16) float wA[EP * KP];  // W_r chunk transposed: [e][k - k0]
+  __shared__ __align__(16) float wB[EP * KP];
+  __shared__ float psum_s[NW][EP];
+  __shared__ int hist_s[EP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  if (tid < EP) hist_s[tid] = 0;
+  const int t = blockIdx.x * NW + wave;
+  const bool tok_ok = t < T;                                 // wave-uniform
+  const Tin* hrow = h + static_cast<size_t>(min(t, T - 1)) * d;  // rows past T are dropped
+  const int nc = (d + KC - 1) / KC;
+
+  typename HVec<Tin>::raw hreg;
+  float4 wreg[WI];
+  // Registers <- chunk c: this lane's 8 h values, and the block's share of W_r.
+  auto load_chunk = [&](int c) {
+    const int k0 = c * KC;
+    const int kh = k0 + 8 * lane;
+    if (kh < d) HVec<Tin>::load(hrow + kh, hreg);  // d is a multiple of 8
+    else HVec<Tin>::zero(hreg);
+    const int n4 = min(KC, d - k0) * E / 4;        // W_r rows k0.. are one run of floats
+    const float4* src = reinterpret_cast<const float4*>(Wr + static_cast<size_t>(k0) * E);
+#pragma unroll
+    for (int v = 0; v < WI; ++v) {
+      const int i = tid + v * NT;
+      wreg[v] = (i < n4) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  // LDS <- registers: h as float32 in this wave's row; W_r transposed into the
+  // block's buffer (element f of the chunk run is row f / E, expert f % E; the
+  // quotient is (f * ceil(2^32 / E)) >> 32 in 64 bits, exact for f < 2^16).
+  const uint64_t e_recip = (0x100000000ull + E - 1) / E;
+  auto store_chunk = [&](float (*hs)[HP], float* ws) {
+    float x[8];
+    HVec<Tin>::to_f32(hreg, x);
+    *reinterpret_cast<float4*>(&hs[wave][8 * lane]) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(&hs[wave][8 * lane + 4]) = make_float4(x[4], x[5], x[6], x[7]);
+#pragma unroll
+    for (int v = 0; v < WI; ++v) {
+      const int i = tid + v * NT;
+      if (i < WF4) {
+        const float q[4] = {wreg[v].x, wreg[v].y, wreg[v].z, wreg[v].w};
+        int k = static_cast<int>((static_cast<uint64_t>(4 * i) * e_recip) >> 32);
+        int e = 4 * i - k * E;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (k < KC) ws[e * KP + k] = q[u];
+          if (++e == E) { e = 0; ++k; }
+        }
+      }
+    }
+  };
+
+  float acc = 0.0f;
+  // The chain of lane e reads h (broadcast) and its W_r row four k at a time,
+  // from a register ring filled D steps ahead of the fmas. Both LDS buffers
+  // hold zeros past the end of the reduction (h loads past d are zeroed; W_r
+  // slots past the run are written with the zeros loaded for them), so the
+  // chain runs to kn rounded up to 4*D: the extra steps add exact zeros (acc
+  // starts at +0 and a round-to-nearest sum is never -0 unless both terms are).
+  auto compute = [&](int c, const float (*hs)[HP], const float* ws) {
+    if (lane >= E) return;
+    constexpr int D = RD;
+    static_assert(KC % (4 * D) == 0, "ring");
+    const int kn = min(KC, d - c * KC);
+    const int kn_pad = (kn + 4 * D - 1) / (4 * D) * (4 * D);
+    const float4* hw = reinterpret_cast<const float4*>(hs[wave]);         // HP % 4 == 0
+    const float4* wc = reinterpret_cast<const float4*>(ws + lane * KP);  // KP % 4 == 0
+    float4 rh[D], rw[D];
+    auto fetch = [&](int slot, int k) {  // reads up to 4*D past kn_pad land in the row padding, unused
+      rh[slot] = hw[k / 4];              // same address in every lane
+      rw[slot] = wc[k / 4];
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u) fetch(u, 4 * u);
+    for (int k = 0; k < kn_pad; k += 4 * D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        acc = fmaf(rh[u].x, rw[u].x, acc);
+        acc = fmaf(rh[u].y, rw[u].y, acc);
+        acc = fmaf(rh[u].z, rw[u].z, acc);
+        acc = fmaf(rh[u].w, rw[u].w, acc);
+        fetch(u, k + 4 * (u + D));
+      }
+    }
+  };
+
+  load_chunk(0);
+  int c = 0;
+  for (; c + 2 <= nc; c += 2) {
+    store_chunk(hA, wA);
+    __syncthreads();  // chunk c in LDS; buffers B no longer read (chunk c-1 done)
+    load_chunk(c + 1);
+    compute(c, hA, wA);
+    store_chunk(hB, wB);
+    __syncthreads();
+    if (c + 2 < nc) load_chunk(c + 2);
+    compute(c + 1, hB, wB);
+  }
+  if (c < nc) {
+    store_chunk(hA, wA);
+    __syncthreads();
+    compute(c, hA, wA);
+  }
+
+  // logits, top-K by (logit descending, expert ascending), softmax, gates
+  float l = -INFINITY;
+  if (lane < E) {
+    l = acc;
+    if (br != nullptr) l = l + br[lane];
+  }
+  if (tok_ok && logits_out != nullptr && lane < E) logits_out[static_cast<size_t>(t) * E + lane] = l;
+  bool taken = false;
+  int cidx[8];
+  float cval[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < K) {
+      float bv = (!taken && lane < E) ? l : -INFINITY;
+      int bi = (!taken && lane < E) ? lane : 0x7fffffff;
+#pragma unroll
+      for (int off = 1; off < EP; off <<= 1) {
+        const float ov = __shfl_xor(bv, off, EP);
+        const int oi = __shfl_xor(bi, off, EP);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      cidx[j] = bi;
+      cval[j] = bv;
+      if (lane == bi) taken = true;
+    }
+  }
+  const float m = cval[0];
+  const float ex = (lane < E) ? expf(l - m) : 0.0f;
+  float s = ex;
+#pragma unroll
+  for (int off = 1; off < EP; off <<= 1) s += __shfl_xor(s, off, EP);
+  if (lane < EP) psum_s[wave][lane] = tok_ok ? ex / s : 0.0f;
+  if (tok_ok && lane == 0) {
+    float ec[8];
+    float se = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < K) {
+        ec[j] = expf(cval[j] - m);
+        se += ec[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < K) {
+        const float g = (gate_mode == 0) ? ec[j] / se : ec[j] / s;
+        topk_idx[static_cast<size_t>(t) * K + j] = cidx[j];
+        topk_gate[static_cast<size_t>(t) * K + j] = g;
+        atomicAdd(&hist_s[cidx[j]], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+    float sum = 0.0f;
+    for (int w = 0; w < NW; ++w) sum += psum_s[w][tid];  // fixed order
+    blk_psum[static_cast<size_t>(blockIdx.x) * E + tid] = sum;
+    blk_hist[static_cast<size_t>(blockIdx.x) * E + tid] = hist_s[tid];
+  }
+}
+
 // Per-block expert histogram of topk_idx, with the router's token tiling.
 __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ topk_idx, int T, int E,
                                                    int K, int TB, int32_t* __restrict__ blk_hist) {
@@ -405,31 +602,58 @@ __global__ void zero_outputs_kernel(int E, int32_t* counts, int32_t* offsets, fl
 }
 
 template <typename Tin, int EP, int TE, int TPT, int BK, int NS>
-hipError_t launch_route_cfg(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
-  hipLaunchKernelGGL((route_kernel<Tin, EP, TE, TPT, BK, NS>), dim3(rt.NB), dim3(kRouteThreads), 0, st,
+hipError_t launch_route_wide(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
+  hipLaunchKernelGGL((route_wide_kernel<Tin, EP, TE, TPT, BK, NS>), dim3(rt.NB), dim3(kRouteThreads), 0, st,
                      static_cast<const Tin*>(a.h), a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
                      a.topk_gate, a.logits, a.blk_hist, a.blk_psum);
   return hipGetLastError();
 }
 
-// Thread tiles: 32 tokens x EP experts per block of 256 threads.
+template <typename Tin, int EP, int NW>
+hipError_t launch_route_narrow(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
+  hipLaunchKernelGGL((route_narrow_kernel<Tin, EP, NW>), dim3(rt.NB), dim3(NW * 64), 0, st,
+                     static_cast<const Tin*>(a.h), a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
+                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum);
+  return hipGetLastError();
+}
+
+template <typename Tin, int EP>
+hipError_t launch_route_narrow_nw(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
+  return launch_route_narrow<Tin, EP, 4>(a, rt, st);
+}
+
 template <typename Tin>
 hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
-  switch (rt.EP) {
-    case 8: return launch_route_cfg<Tin, 8, 1, 1, 128, 4>(a, rt, st);
-    case 16: return launch_route_cfg<Tin, 16, 2, 1, 128, 4>(a, rt, st);
-    case 32: return launch_route_cfg<Tin, 32, 2, 2, 64, 4>(a, rt, st);
-    default: return launch_route_cfg<Tin, 64, 4, 2, 64, 4>(a, rt, st);
+  if (rt.NW > 0) {  // narrow layout
+    return rt.EP == 8 ? launch_route_narrow_nw<Tin, 8>(a, rt, st) : launch_route_narrow_nw<Tin, 16>(a, rt, st);
+  }
+  switch (rt.EP) {  // wide layout: 32 tokens x EP experts per block of 256 threads
+    case 8: return launch_route_wide<Tin, 8, 1, 1, 128, 4>(a, rt, st);
+    case 16: return launch_route_wide<Tin, 16, 2, 1, 128, 4>(a, rt, st);
+    case 32: return launch_route_wide<Tin, 32, 2, 2, 64, 4>(a, rt, st);
+    default: return launch_route_wide<Tin, 64, 4, 2, 64, 4>(a, rt, st);
   }
 }
 
 }  // namespace
 
+// Narrow layout for small batches of few experts (T <= 256, E <= 16), where the
+// wide layout leaves most compute units idle: one token per wave, 4 waves per
+// block. Otherwise the wide layout, 32 tokens per block.
+constexpr int64_t kNarrowMaxT = 256;
+
 RouteTiling route_tiling(int64_t T, int64_t E) {
   RouteTiling rt;
   rt.EP = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
-  rt.TPT = rt.EP >= 32 ? 2 : 1;
-  rt.TB = kRouteTB;
+  if (rt.EP <= 16 && T <= kNarrowMaxT) {
+    rt.TPT = 1;
+    rt.NW = 4;
+    rt.TB = 4;
+  } else {
+    rt.TPT = rt.EP >= 32 ? 2 : 1;
+    rt.NW = 0;  // wide layout
+    rt.TB = kRouteTB;
+  }
   rt.NB = static_cast<int>((T + rt.TB - 1) / rt.TB);
   return rt;
 }
