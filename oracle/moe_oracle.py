@@ -43,6 +43,15 @@ Function -> passage it follows -> what pins it (tests/test_oracle_pins.py):
                       -> the page's worked 4-dim example.
   aux_loss            [LENSA] Step 4 (E * sum f * P; equals 1 when routing is
                       uniform) -> uniform-P and uniform-f closed forms.
+  capacity_slots,
+  capacity_keep,
+  drop_stats          [LENSA] Step 5 (C = factor x tokens x k / E slots per
+                      expert; slots past C are skipped; a token with no
+                      expert keeps its residual)
+                      -> the page's C = 64 and 94 dropped slots (18.4 %);
+                         a sort-based restatement of "first C in token order"
+                         on small random routings; C >= T equals the dropless
+                         layer; C = 0 gives y = 0.
   param_counts        [CUR] "Parameters you hold..."; [LENSA] Steps 1 and 6
                       -> the printed 4.46M / 1.32M / 3.39x / 25.2x,
                          37.0B / 11.1B / 3.3x and 176M / 45.1B.
@@ -51,7 +60,9 @@ from __future__ import annotations
 
 import ctypes
 import itertools
+import math
 import os
+from fractions import Fraction
 import subprocess
 from typing import Dict, Optional, Sequence
 
@@ -248,15 +259,56 @@ def aux_loss(counts: np.ndarray, p: np.ndarray, K: int) -> float:
     return float(E * np.sum(f * P))
 
 
+# ----------------------------------------------------------------------------- capacity
+
+def capacity_slots(factor, T: int, K: int, E: int) -> int:
+    """Slots per expert, C = factor * T * K / E ([LENSA] Step 5), rounded up
+    when fractional (the page prints only integer cases; rounding up keeps
+    C * E >= factor * T * K). The factor is read as the decimal it is written as."""
+    return int(math.ceil(Fraction(str(factor)) * T * K / E))
+
+
+def capacity_keep(idx: np.ndarray, E: int, C: int) -> np.ndarray:
+    """Which routing slots are processed when every expert has C slots ([LENSA] Step 5).
+
+    Tokens are taken in order; each of a token's choices fills a free slot of
+    its expert or is dropped. (A token never picks one expert twice, so the
+    order of its K choices does not matter.)
+    """
+    T, K = idx.shape
+    keep = np.zeros((T, K), dtype=bool)
+    used = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for j in range(K):
+            e = int(idx[t, j])
+            if used[e] < C:
+                keep[t, j] = True
+                used[e] += 1
+    return keep
+
+
+def drop_stats(counts: Sequence[int], C: int) -> Dict[str, float]:
+    """Dropped slots and their share when every expert has C slots ([LENSA] Step 5)."""
+    c = np.asarray(counts, np.int64)
+    dropped = int(np.maximum(c - C, 0).sum())
+    return {"dropped": dropped, "percent": 100.0 * dropped / max(int(c.sum()), 1)}
+
+
 # ----------------------------------------------------------------------------- layer
 
 def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int,
-                act: int, gate: int, tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+                act: int, gate: int, tokens: Optional[Sequence[int]] = None,
+                capacity: Optional[int] = None) -> Dict[str, np.ndarray]:
     """The whole layer. `inp` holds float32 arrays of the exact input values.
 
     Routing, grouping and the aux loss cover all T tokens. The expert FFNs and
     y are computed for all tokens, or only for the rows listed in `tokens`
     (y then has len(tokens) rows, in that order).
+
+    capacity: slots per expert ([LENSA] Step 5), or None for dropless. Dropped
+    slots contribute nothing; kept slots keep their gates; a token with every
+    slot dropped has y = 0 (the layer adds nothing to its residual). Counts and
+    the aux loss describe the router's choices, before any drop.
     """
     h32 = np.asarray(inp["h"], np.float32).reshape(T, d)
     logits = router_logits_f32(h32, inp["W_r"], inp.get("b_r"))
@@ -266,11 +318,12 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
     counts = expert_counts(idx, E)
     offsets, slot_token, token_slot = stable_permutation(idx, E)
     aux = aux_loss(counts, p, K)
+    keep = np.ones((T, K), dtype=bool) if capacity is None else capacity_keep(idx, E, capacity)
     rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     y = np.zeros((len(rows), d), dtype=np.float64)
     h64 = h32.astype(np.float64)
     for e in range(E):
-        sel_r, sel_j = np.nonzero(idx[rows] == e)
+        sel_r, sel_j = np.nonzero((idx[rows] == e) & keep[rows])
         if len(sel_r) == 0:
             continue
         o = expert_ffn(h64[rows[sel_r]], e, inp, act)
@@ -278,6 +331,7 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
         y[sel_r] += g[rows[sel_r], sel_j][:, None] * o
     return {"logits": logits, "topk_idx": idx, "topk_gate": g, "probs": p, "counts": counts,
             "offsets": offsets, "slot_token": slot_token, "token_slot": token_slot,
+            "token_slot_kept": np.where(keep, token_slot, -1).astype(np.int32), "keep": keep,
             "aux": aux, "y": y, "rows": rows}
 
 

@@ -360,8 +360,94 @@ def check_param_counts():
     assert round(x["active_billions_printed"] * 2) == x["read_per_token_GB_fp16_printed"]
 
 
+# ----------------------------------------------------------------------------- capacity
+
+def _routing_with_counts(counts, T, K, seed):
+    """A T x K routing (distinct experts per token) whose per-expert counts are `counts`."""
+    slots = [e for e, c in enumerate(counts) for _ in range(c)]
+    assert len(slots) == T * K
+    idx = np.array([[slots[t + j * T] for j in range(K)] for t in range(T)], np.int32)
+    assert all(len(set(r)) == K for r in idx.tolist())
+    return idx[np.random.default_rng(seed).permutation(T)]  # any token order
+
+
+def check_capacity_widget():
+    """Lensa ML Step 5: C = 1.00 x 256 x 2 / 8 = 64; 94 slots dropped (18.4 %)."""
+    g = _golden("lensa_step5_capacity.json")
+    C = O.capacity_slots(g["factor"], g["T"], g["K"], g["E"])
+    assert C == g["capacity_printed"]
+    st = O.drop_stats(g["counts"], C)
+    assert st["dropped"] == g["dropped_printed"]
+    assert round(st["percent"], 1) == g["percent_dropped_printed"]
+    # the same through the slot-level rule, on a routing with the page's counts
+    idx = _routing_with_counts(g["counts"], g["T"], g["K"], seed=11)
+    keep = O.capacity_keep(idx, g["E"], C)
+    assert int((~keep).sum()) == g["dropped_printed"]
+    kept_per_expert = np.bincount(idx[keep].astype(np.int64), minlength=g["E"])
+    assert kept_per_expert.tolist() == [min(c, C) for c in g["counts"]]
+
+
+def check_capacity_order(seed=12):
+    """'First C slots in token order', restated by sorting: for each expert, the C
+    smallest token indices among the tokens that chose it are kept."""
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        T, E = int(rng.integers(1, 13)), int(rng.integers(1, 6))
+        K = int(rng.integers(1, E + 1))
+        idx = np.array([rng.permutation(E)[:K] for _ in range(T)], np.int32)
+        for C in range(0, T + 2):
+            keep = O.capacity_keep(idx, E, C)
+            ref = np.zeros_like(keep)
+            for e in range(E):
+                toks = sorted({t for t in range(T) for j in range(K) if idx[t, j] == e})
+                for t in toks[:C]:
+                    ref[t, list(idx[t]).index(e)] = True
+            assert np.array_equal(keep, ref), (T, E, K, C)
+            if C >= T:
+                assert keep.all()
+
+
+def check_capacity_slots_rounding():
+    """C is the smallest integer with C * E >= factor * T * K (exact for the page's integer case)."""
+    for factor in ("0.5", "0.75", "1.0", "1.1", "1.25", "2.0", "0.3"):
+        for T, K, E in ((256, 2, 8), (80, 1, 8), (7, 2, 3), (4096, 2, 8), (8192, 1, 64)):
+            C = O.capacity_slots(factor, T, K, E)
+            need = Fraction(factor) * T * K
+            assert C * E >= need and (C - 1) * E < need, (factor, T, K, E, C)
+
+
+def check_capacity_layer(seed=13):
+    """C >= T is the dropless layer; C = 0 gives y = 0; tokens that keep every slot
+    match the dropless rows and tokens that keep none are 0; routing outputs
+    (counts, aux) describe the router's choices and do not change."""
+    rng = np.random.default_rng(seed)
+    T, d, w, E, K = 40, 12, 16, 4, 2
+    inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+           "W_r": rng.standard_normal((d, E)).astype(np.float32),
+           "b_r": (rng.standard_normal(E) * 2).astype(np.float32),
+           "W1": rng.standard_normal((E, w, d)) * d ** -0.5, "W3": rng.standard_normal((E, w, d)) * d ** -0.5,
+           "W2": rng.standard_normal((E, d, w)) * w ** -0.5, "b1": None, "b2": None}
+    free = O.moe_forward(inp, T, d, E, K, O.ACT_SWIGLU, O.GATE_RENORM)
+    big = O.moe_forward(inp, T, d, E, K, O.ACT_SWIGLU, O.GATE_RENORM, capacity=T)
+    assert np.array_equal(big["y"], free["y"]) and big["keep"].all()
+    zero = O.moe_forward(inp, T, d, E, K, O.ACT_SWIGLU, O.GATE_RENORM, capacity=0)
+    assert not zero["y"].any() and not zero["keep"].any()
+    assert np.all(zero["token_slot_kept"] == -1)
+    C = O.capacity_slots("0.75", T, K, E)
+    cap = O.moe_forward(inp, T, d, E, K, O.ACT_SWIGLU, O.GATE_RENORM, capacity=C)
+    keep = cap["keep"]
+    assert 0 < (~keep).sum() < T * K  # some, not all, slots dropped
+    full_rows, none_rows = keep.all(axis=1), ~keep.any(axis=1)
+    assert np.array_equal(cap["y"][full_rows], free["y"][full_rows])
+    assert not cap["y"][none_rows].any()
+    assert np.array_equal(cap["counts"], free["counts"]) and cap["aux"] == free["aux"]
+    assert np.array_equal(cap["token_slot_kept"][keep], free["token_slot"][keep])
+
+
 ALL_CHECKS = [check_router_logits_exact, check_router_logits_bound, check_topk_bruteforce,
               check_probs, check_gates_worked_example, check_gates_invariants,
               check_combine_worked_example, check_permutation_sorted, check_load_stats_page,
               check_aux_uniform_probs, check_aux_uniform_load, check_dense_reduction,
-              check_soft_mixture_K_equals_E, check_forward_subset_consistency, check_param_counts]
+              check_soft_mixture_K_equals_E, check_forward_subset_consistency, check_param_counts,
+              check_capacity_widget, check_capacity_order, check_capacity_slots_rounding,
+              check_capacity_layer]

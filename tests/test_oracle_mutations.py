@@ -12,7 +12,7 @@ from oracle import moe_oracle as O
 _orig = {name: getattr(O, name) for name in
          ("router_logits_f32", "select_topk", "router_probs", "gates", "stable_permutation",
           "aux_loss", "gelu", "silu", "expert_ffn", "combine", "param_counts_micro",
-          "param_counts_swiglu_model", "expert_counts")}
+          "param_counts_swiglu_model", "expert_counts", "capacity_keep", "capacity_slots", "drop_stats")}
 
 
 def _logits_no_bias(h, W, b):
@@ -119,7 +119,30 @@ def _counts_off_by_one(idx, E):
     return c
 
 
+def _keep_later_tokens_win(idx, E, C):
+    # slots taken from the last token backwards
+    return _orig["capacity_keep"](idx[::-1].copy(), E, C)[::-1].copy()
+
+
+def _keep_off_by_one(idx, E, C):
+    return _orig["capacity_keep"](idx, E, C + 1)
+
+
+def _capacity_floor(factor, T, K, E):
+    from fractions import Fraction
+    return int(Fraction(str(factor)) * T * K / E)
+
+
+def _drop_stats_over_T(counts, C):
+    st = _orig["drop_stats"](counts, C)
+    return {"dropped": st["dropped"], "percent": 100.0 * st["dropped"] / max(int(sum(counts)) // 2, 1)}
+
+
 MUTATIONS = {
+    "capacity_later_tokens_win": ("capacity_keep", _keep_later_tokens_win),
+    "capacity_off_by_one": ("capacity_keep", _keep_off_by_one),
+    "capacity_rounded_down": ("capacity_slots", _capacity_floor),
+    "drop_percent_of_tokens": ("drop_stats", _drop_stats_over_T),
     "router_drops_bias": ("router_logits_f32", _logits_no_bias),
     "router_reverse_k_order": ("router_logits_f32", _logits_reverse_k),
     "router_bias_first": ("router_logits_f32", _logits_bias_first),
