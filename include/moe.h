@@ -106,11 +106,28 @@ typedef struct moe_desc {
   int32_t act;    /* moe_act */
   int32_t gate;   /* moe_gate */
   int32_t dtype;  /* moe_dtype: h, W1, W3, W2, b1, b2, h_perm, y */
-  int32_t reserved; /* must be 0 */
+  int32_t capacity; /* slots per expert (Lensa ML Step 5, "Capacity & Dropped
+                       Tokens"); 0 = dropless (every slot is processed). With
+                       C > 0 each expert processes its first C slots in token
+                       order and drops the rest: a dropped slot adds nothing
+                       to y and its token_slot entry is -1; a token with no
+                       kept slot gets y = 0 (the layer adds nothing to its
+                       residual). Counts, offsets and the aux loss describe
+                       the router's choices before any drop. Negative values
+                       are MOE_ERR_SHAPE. moe_capacity_slots() gives C for a
+                       capacity factor. */
 } moe_desc;
 
 /* Human-readable name of a moe_status value (static string, never NULL). */
 const char* moe_status_string(int status);
+
+/* Slots per expert for a capacity factor (Lensa ML Step 5): C = factor * T * K / E,
+ * rounded up when fractional (the product is taken in double precision; a
+ * value within 1e-9 relative of an integer counts as that integer). Host-only.
+ * Writes *slots; returns MOE_ERR_NULL for a NULL `slots`, MOE_ERR_SHAPE for
+ * factor < 0, T < 0, K < 1 or E < 1 (or a non-finite factor), and
+ * MOE_ERR_UNSUPPORTED if C would exceed 2^31 - 1. */
+int moe_capacity_slots(double factor, int64_t T, int64_t K, int64_t E, int32_t* slots);
 
 /* Bytes of workspace that any entry point below needs for this layer shape.
  * Host-only; enqueues nothing. */
@@ -128,10 +145,11 @@ int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float
               void* ws, size_t ws_bytes, void* stream);
 
 /* Grouping of the routing slots by expert (Lensa ML Step 5: experts take any
- * number of tokens; no token is dropped). Stable: inside each expert's group
- * tokens keep their order.
+ * number of tokens). Stable: inside each expert's group tokens keep their order.
  * In:  topk_idx, h.
  * Out: expert_offsets, slot_token, token_slot, h_perm (gathered rows of h).
+ * With desc->capacity = C > 0, token_slot is -1 for every slot at rank C or
+ * more in its expert's group (dropped); the groups themselves keep every slot.
  * Returns a moe_status. */
 int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h,
                 int32_t* expert_offsets, int32_t* slot_token, int32_t* token_slot,
@@ -141,6 +159,8 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h,
  * only the chosen experts run; Lensa ML Step 1: each expert is a full FFN).
  * In:  h_perm, expert_offsets, W1, b1 (nullable), W3 (SwiGLU), W2, b2 (nullable).
  * Out: o_perm (ungated float32 expert outputs, one row per grouped slot).
+ * With desc->capacity = C > 0 only the first C rows of each group are
+ * computed; the o_perm rows of dropped slots are left as they were.
  * Returns a moe_status. */
 int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expert_offsets,
                    const void* W1, const void* b1, const void* W3, const void* W2,
@@ -149,14 +169,16 @@ int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expe
 /* Gated combine y[t] = sum_j gate[t][j] * o_perm[token_slot[t][j]] (Lensa ML
  * Step 3; maptheai.com "The mechanism"), accumulated in float32 in ascending j
  * and rounded once to dtype. A gather: each y row is written by one owner.
- * Needs no workspace. Returns a moe_status. */
+ * Entries of token_slot that are negative (slots dropped at capacity) are
+ * skipped. Needs no workspace. Returns a moe_status. */
 int moe_combine(const moe_desc* desc, const float* o_perm, const int32_t* token_slot,
                 const float* topk_gate, void* y, void* stream);
 
 /* The whole layer: route -> group -> experts -> combine, plus the aux loss.
  * In:  h, W_r, b_r (nullable), W1, b1 (nullable), W3 (SwiGLU), W2, b2 (nullable).
  * Out: y, aux_loss [1] (nullable), expert_counts [E] (nullable).
- * For K = 1 the second expert GEMM writes gate * o straight into y.
+ * For K = 1 and no capacity the second expert GEMM writes gate * o straight
+ * into y; with a capacity (desc->capacity > 0) dropped slots add nothing.
  * Returns a moe_status. */
 int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
                 const void* W1, const void* b1, const void* W3, const void* W2,

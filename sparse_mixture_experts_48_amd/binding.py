@@ -29,7 +29,7 @@ KERNEL_IDS = {0: "route", 1: "finalize", 2: "hist", 3: "permute", 4: "gemm1", 5:
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
                 ("K", ctypes.c_int64), ("width", ctypes.c_int64), ("act", ctypes.c_int32),
-                ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -48,6 +48,8 @@ _SIGS = {
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 4 + [_vp]),
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]),
+    "moe_capacity_slots": (ctypes.c_int, [ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.POINTER(ctypes.c_int32)]),
     "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_trace_read": (ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
     "moe_trace_disable": (ctypes.c_int, []),
@@ -80,8 +82,17 @@ def header_symbols() -> List[str]:
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
-def desc_of(cfg: W.LayerShape, T: Optional[int] = None) -> MoeDesc:
-    return MoeDesc(cfg.T if T is None else T, cfg.d, cfg.E, cfg.K, cfg.width, cfg.act, cfg.gate, cfg.dtype, 0)
+def desc_of(cfg: W.LayerShape, T: Optional[int] = None, capacity: int = 0) -> MoeDesc:
+    """Descriptor of a layer shape; capacity = slots per expert (0: dropless)."""
+    return MoeDesc(cfg.T if T is None else T, cfg.d, cfg.E, cfg.K, cfg.width, cfg.act, cfg.gate, cfg.dtype,
+                   capacity)
+
+
+def capacity_slots(factor: float, T: int, K: int, E: int) -> int:
+    """Slots per expert for a capacity factor (moe_capacity_slots)."""
+    c = ctypes.c_int32(0)
+    _check("moe_capacity_slots", lib().moe_capacity_slots(float(factor), T, K, E, ctypes.byref(c)))
+    return c.value
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

@@ -4,6 +4,9 @@
 // Nothing here allocates device memory or synchronises the host (the trace
 // functions aside). Every entry point validates all arguments before its first
 // HIP call, so an invalid call leaves outputs and the stream untouched.
+#include <algorithm>
+#include <climits>
+#include <cmath>
 #include <vector>
 
 #include "moe.h"
@@ -70,10 +73,13 @@ Plan make_plan(const moe_desc& d) {
   p.pmean = take(d.E * 4);
   p.aux = take(4);
   p.act = take(S * d.width * bpe);
-  p.o_perm = take(d.K > 1 ? S * d.d * 4 : 0);
+  p.o_perm = take(d.K > 1 || d.capacity > 0 ? S * d.d * 4 : 0);  // K = 1 dropless writes y directly
   p.total = off;
   return p;
 }
+
+// Rows an expert processes at most: its capacity, or every row when dropless.
+int cap_of(const moe_desc& d) { return d.capacity > 0 ? d.capacity : INT_MAX; }
 
 int check_desc(const moe_desc* d) {
   if (d == nullptr) return MOE_ERR_NULL;
@@ -82,7 +88,7 @@ int check_desc(const moe_desc* d) {
   if (d->act != MOE_ACT_GELU && d->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (d->gate != MOE_GATE_RENORM && d->gate != MOE_GATE_RAW) return MOE_ERR_UNSUPPORTED;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  if (d->reserved != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->capacity < 0) return MOE_ERR_SHAPE;
   if (d->T > kMaxInt / d->K || d->d > kMaxDim || d->width > kMaxDim) return MOE_ERR_UNSUPPORTED;
   const int64_t S = d->T * d->K;
   if (S > 0 && (S > kMaxElems / d->d || S > kMaxElems / d->width)) return MOE_ERR_UNSUPPORTED;
@@ -187,6 +193,17 @@ const char* moe_kernel_name(int kernel_id) {
   }
 }
 
+int moe_capacity_slots(double factor, int64_t T, int64_t K, int64_t E, int32_t* slots) {
+  if (slots == nullptr) return MOE_ERR_NULL;
+  if (!std::isfinite(factor) || factor < 0.0 || T < 0 || K < 1 || E < 1) return MOE_ERR_SHAPE;
+  const double x = factor * static_cast<double>(T) * static_cast<double>(K) / static_cast<double>(E);
+  const double r = std::nearbyint(x);
+  const double c = (std::fabs(x - r) <= 1e-9 * std::max(1.0, std::fabs(x))) ? r : std::ceil(x);
+  if (c > static_cast<double>(kMaxInt)) return MOE_ERR_UNSUPPORTED;
+  *slots = static_cast<int32_t>(c);
+  return MOE_OK;
+}
+
 int moe_workspace_size(const moe_desc* desc, size_t* bytes) {
   MOE_CHECK(check_desc(desc));
   if (bytes == nullptr) return MOE_ERR_NULL;
@@ -254,8 +271,8 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h, in
              moe::launch_finalize(blk_hist, nullptr, pl.rt.NB, T, E, K, blk_base, nullptr, expert_offsets,
                                   nullptr, nullptr, st));
   MOE_LAUNCH(MOE_K_PERMUTE, st,
-             moe::launch_permute(topk_idx, blk_base, T, E, K, pl.rt, h, row_bytes, h_perm, slot_token,
-                                 token_slot, st));
+             moe::launch_permute(topk_idx, blk_base, expert_offsets, T, E, K, cap_of(d), pl.rt, h, row_bytes,
+                                 h_perm, slot_token, token_slot, st));
   return MOE_OK;
 }
 
@@ -287,7 +304,8 @@ int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expe
   f.a = at<char>(ws, pl.act);
   f.o_perm = o_perm;
   f.fused_y = false;
-  f.max_rows_per_expert = static_cast<int>(d.T);
+  f.cap = cap_of(d);
+  f.max_rows_per_expert = static_cast<int>(std::min<int64_t>(d.T, f.cap));
   MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_gemm1(f, st));
   MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_gemm2(f, st));
   return MOE_OK;
@@ -349,9 +367,10 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
              moe::launch_finalize(blk_hist, blk_psum, pl.rt.NB, T, E, K, blk_base, counts, offsets, nullptr,
                                   aux_loss, st));
   const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
+  const int cap = cap_of(d);
   MOE_LAUNCH(MOE_K_PERMUTE, st,
-             moe::launch_permute(topk_idx, blk_base, T, E, K, pl.rt, h, row_bytes, nullptr, slot_token,
-                                 token_slot, st));
+             moe::launch_permute(topk_idx, blk_base, offsets, T, E, K, cap, pl.rt, h, row_bytes, nullptr,
+                                 slot_token, token_slot, st));
   // GEMM1 reads the rows of h through slot_token: the grouped copy of h is never written.
   moe::FfnArgs f{};
   f.S = T * K;
@@ -367,14 +386,15 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
   f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
   f.a = at<char>(ws, pl.act);
   f.o_perm = at<float>(ws, pl.o_perm);
-  f.fused_y = K == 1;
+  f.fused_y = K == 1 && d.capacity == 0;  // with drops, the combine writes the tokens that lost their slot
   f.y = y;
   f.slot_token = slot_token;
   f.topk_gate = topk_gate;
-  f.max_rows_per_expert = T;
+  f.cap = cap;
+  f.max_rows_per_expert = std::min(T, cap);
   MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_gemm1(f, st));
   MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_gemm2(f, st));
-  if (K > 1) {
+  if (!f.fused_y) {
     MOE_LAUNCH(MOE_K_COMBINE, st, moe::launch_combine(f.o_perm, token_slot, topk_gate, T, f.d, K, bf16, y, st));
   }
   return MOE_OK;

@@ -1,4 +1,6 @@
-// Gated combine: y[t] = sum_j gate[t][j] * o_perm[token_slot[t][j]].
+// Gated combine: y[t] = sum_j gate[t][j] * o_perm[token_slot[t][j]], over the
+// slots that were not dropped (token_slot = -1; Lensa ML explainer "Mixture of
+// Experts", Step 5: a token whose every slot is dropped gets 0 from the layer).
 //
 // maptheai.com "Mixture of Experts", section "The mechanism": the chosen
 // experts' outputs are added, weighted by the router's scores; Lensa ML
@@ -27,7 +29,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int c = static_cast<int>(i % d4) * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < K; ++j) {
-      const int s = min(max(token_slot[static_cast<size_t>(t) * K + j], 0), T * K - 1);  // stay inside o_perm
+      const int s_raw = token_slot[static_cast<size_t>(t) * K + j];
+      if (s_raw < 0) continue;  // a slot dropped at its expert's capacity adds nothing
+      const int s = min(s_raw, T * K - 1);  // stay inside o_perm
       const float g = gate[static_cast<size_t>(t) * K + j];
       const float4 o = *reinterpret_cast<const float4*>(o_perm + static_cast<size_t>(s) * d + c);
       acc.x = fmaf(g, o.x, acc.x);

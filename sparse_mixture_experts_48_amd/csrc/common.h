@@ -44,25 +44,29 @@ __device__ __forceinline__ float gelu_exact(float z) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Rows [*beg, *end) of expert e, clamped into [0, S): offsets that do not
-// describe a grouping of S rows give wrong results but never an access
-// outside the S-row buffers.
-__device__ __forceinline__ void expert_rows(const int32_t* __restrict__ offsets, int e, int S, int* beg,
-                                            int* end) {
+// Rows [*beg, *end) of expert e that its FFN processes: at most `cap` rows
+// (the expert's capacity; the grouping is stable, so these are its first cap
+// tokens in token order), clamped into [0, S): offsets that do not describe a
+// grouping of S rows give wrong results but never an access outside the
+// S-row buffers.
+__device__ __forceinline__ void expert_rows(const int32_t* __restrict__ offsets, int e, int S, int cap,
+                                            int* beg, int* end) {
   const int b = min(max(offsets[e], 0), S);
+  const int n = min(max(offsets[e + 1], b), S) - b;
   *beg = b;
-  *end = min(max(offsets[e + 1], b), S);
+  *end = b + min(n, cap);  // cap may be INT_MAX: never form b + cap
 }
 
 // Which expert owns global m-tile `mt` when every expert's rows are cut into
 // tiles of `bm` rows. Returns false if `mt` is past the last tile.
-// offsets: [E+1] exclusive prefix of the per-expert row counts (clamped to [0, S)).
-__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int S, int bm,
-                                            int mt, int* expert, int* row0, int* rows) {
+// offsets: [E+1] exclusive prefix of the per-expert row counts (clamped to [0, S));
+// each expert contributes at most cap rows.
+__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int S, int cap,
+                                            int bm, int mt, int* expert, int* row0, int* rows) {
   int acc = 0;
   for (int e = 0; e < E; ++e) {
     int beg, end;
-    expert_rows(offsets, e, S, &beg, &end);
+    expert_rows(offsets, e, S, cap, &beg, &end);
     const int cnt = end - beg;
     const int nt = (cnt + bm - 1) / bm;
     if (mt < acc + nt) {

@@ -49,6 +49,7 @@ struct GemmParams {
   const float* gate;        // topk_gate [T] (K = 1)
   int E, N, Kd;
   int S;                    // grouped rows (bound of every grouped-row index)
+  int cap;                  // rows each expert processes at most
   int x_nrows;              // rows of x
   int n_mt;                 // m-tile slots in the grid (upper bound)
 };
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const int mt = (t / kNG) % p.n_mt;
   if (nt >= n_nt) return;
   int e, row0, rows;
-  if (!find_m_tile(p.offsets, p.E, p.S, BM, mt, &e, &row0, &rows)) return;
+  if (!find_m_tile(p.offsets, p.E, p.S, p.cap, BM, mt, &e, &row0, &rows)) return;
   const int n0 = nt * NCOLS;
 
   const int tid = threadIdx.x;
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmPara
   const int e = blockIdx.x / n_groups;
   const int grp = blockIdx.x % n_groups;
   int beg, end_row;
-  expert_rows(p.offsets, e, p.S, &beg, &end_row);
+  expert_rows(p.offsets, e, p.S, p.cap, &beg, &end_row);
   const int rows = min(end_row - beg, MC * 16);  // the host guarantees <= MC * 16 rows per expert
   if (rows <= 0) return;
   const int lane = threadIdx.x % 64;
@@ -538,6 +539,7 @@ hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st) {
   p.x = static_cast<const bf16_t*>(f.x);
   p.x_rows = f.x_rows;
   p.x_nrows = f.x_rows != nullptr ? f.S / f.K : f.S;
+  p.cap = f.cap;
   p.offsets = f.offsets;
   p.B = static_cast<const bf16_t*>(f.W1);
   p.B3 = static_cast<const bf16_t*>(f.W3);
@@ -559,6 +561,7 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
   GemmParams p{};
   p.x = static_cast<const bf16_t*>(f.a);
   p.x_nrows = f.S;
+  p.cap = f.cap;
   p.offsets = f.offsets;
   p.B = static_cast<const bf16_t*>(f.W2);
   p.B3 = nullptr;

@@ -27,6 +27,7 @@ struct F32Params {
   const int32_t* slot_token;
   const float* gate;
   int E, N, Kd, S, n_mt;
+  int cap;                 // rows each expert processes at most
 };
 
 template <int MODE>
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
   const int mt = blockIdx.x % p.n_mt;
   const int nt = blockIdx.x / p.n_mt;
   int e, row0, rows;
-  if (!find_m_tile(p.offsets, p.E, p.S, kFBM, mt, &e, &row0, &rows)) return;
+  if (!find_m_tile(p.offsets, p.E, p.S, p.cap, kFBM, mt, &e, &row0, &rows)) return;
   const int n0 = nt * kFBN;
   const int tid = threadIdx.x;
   const int tx = tid % 16, ty = tid / 16;
@@ -147,6 +148,7 @@ hipError_t launch_gemm1_f32(const FfnArgs& f, hipStream_t st) {
   p.N = f.width;
   p.Kd = f.d;
   p.S = f.S;
+  p.cap = f.cap;
   return f.act == 1 ? launch_f32<F_G1_SWIGLU>(p, f.S, st) : launch_f32<F_G1_GELU>(p, f.S, st);
 }
 
@@ -160,6 +162,7 @@ hipError_t launch_gemm2_f32(const FfnArgs& f, hipStream_t st) {
   p.N = f.d;
   p.Kd = f.width;
   p.S = f.S;
+  p.cap = f.cap;
   if (f.fused_y) {
     p.out = f.y;
     p.slot_token = f.slot_token;

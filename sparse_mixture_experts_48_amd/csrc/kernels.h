@@ -40,9 +40,11 @@ hipError_t launch_zero_outputs(int E, int32_t* counts, int32_t* offsets, float* 
                                hipStream_t st);
 
 // Stable grouping: slot ranks, token_slot, slot_token and the gathered rows.
-hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, int T, int E, int K,
-                          const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
-                          int32_t* slot_token, int32_t* token_slot, hipStream_t st);
+// With cap < INT_MAX, a slot whose rank in its expert's group is cap or more is
+// dropped: its token_slot entry is -1.
+hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, const int32_t* offsets, int T,
+                          int E, int K, int cap, const RouteTiling& rt, const void* h, size_t row_bytes,
+                          void* h_perm, int32_t* slot_token, int32_t* token_slot, hipStream_t st);
 
 // Expert GEMMs over the grouped rows.
 struct FfnArgs {
@@ -59,7 +61,8 @@ struct FfnArgs {
   void* y;
   const int32_t* slot_token;
   const float* topk_gate;
-  int max_rows_per_expert;     // host-known bound (T) used to pick the kernel family
+  int max_rows_per_expert;     // host-known bound (min(T, cap)) used to pick the kernel family
+  int cap;                     // rows each expert processes at most (INT_MAX: dropless)
 };
 hipError_t launch_gemm1(const FfnArgs& f, hipStream_t st);
 hipError_t launch_gemm2(const FfnArgs& f, hipStream_t st);

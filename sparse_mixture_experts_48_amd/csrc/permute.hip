@@ -3,7 +3,9 @@
 // Lensa ML explainer "Mixture of Experts", Step 5: instead of fixed capacity
 // buffers, experts take any number of tokens (dropless). Each expert's rows
 // are contiguous; inside a group tokens keep their order, so the result is
-// the stable sort of the slots by (expert, token).
+// the stable sort of the slots by (expert, token). With a capacity of C slots
+// per expert (Step 5), a slot whose rank in its group is C or more is dropped
+// (token_slot = -1): each expert keeps its first C tokens in token order.
 //
 // Block b owns the same token range as router block b. Its base row for
 // expert e is offsets[e] + (slots of e in blocks before b), computed by the
@@ -21,7 +23,8 @@ constexpr int kPermThreads = 256;  // 4 waves x 64 tokens
 constexpr int kMaxK = 8;
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_base, int T, int E, int K,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_base,
+    const int32_t* __restrict__ offsets, int T, int E, int K, int cap,
     int TB, const char* __restrict__ h, size_t row_bytes, char* __restrict__ h_perm,
     int32_t* __restrict__ slot_token, int32_t* __restrict__ token_slot) {
   __shared__ int cnt_s[kPermThreads / 64][64];
@@ -55,10 +58,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const uint64_t m = __ballot(has);
     if (has) {
       const int slot = base + __popcll(m & below);
+      const bool kept = slot - offsets[e] < cap;  // rank in the expert's group, token order
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j) {
         if (ids[j] == e) {
-          token_slot[static_cast<size_t>(t) * K + j] = slot;
+          token_slot[static_cast<size_t>(t) * K + j] = kept ? slot : -1;
           slots_s[lt][j] = slot;
         }
       }
@@ -102,12 +106,12 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
 }  // namespace
 
-hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, int T, int E, int K,
-                          const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
-                          int32_t* slot_token, int32_t* token_slot, hipStream_t st) {
+hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, const int32_t* offsets, int T,
+                          int E, int K, int cap, const RouteTiling& rt, const void* h, size_t row_bytes,
+                          void* h_perm, int32_t* slot_token, int32_t* token_slot, hipStream_t st) {
   if (rt.TB > kPermThreads) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(permute_kernel, dim3(rt.NB), dim3(kPermThreads), 0, st, topk_idx, blk_base, T, E, K,
-                     rt.TB, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
+  hipLaunchKernelGGL(permute_kernel, dim3(rt.NB), dim3(kPermThreads), 0, st, topk_idx, blk_base, offsets, T,
+                     E, K, cap, rt.TB, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
                      slot_token, token_slot);
   return hipGetLastError();
 }

@@ -44,8 +44,9 @@ def oracle_params(inp: Dict[str, Optional[torch.Tensor]]) -> Dict[str, object]:
     return p
 
 
-def run_oracle(cfg: W.LayerShape, inp, tokens: Optional[Sequence[int]] = None):
-    return O.moe_forward(oracle_params(inp), cfg.T, cfg.d, cfg.E, cfg.K, cfg.act, cfg.gate, tokens=tokens)
+def run_oracle(cfg: W.LayerShape, inp, tokens: Optional[Sequence[int]] = None, capacity: Optional[int] = None):
+    return O.moe_forward(oracle_params(inp), cfg.T, cfg.d, cfg.E, cfg.K, cfg.act, cfg.gate, tokens=tokens,
+                         capacity=capacity)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -11,8 +11,8 @@ OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
 FAKE = 0x10000  # a 256-byte aligned, never dereferenced address
 
 
-def _d(T=64, d=128, E=8, K=2, w=512, act=1, gate=0, dtype=1, reserved=0):
-    return MoeDesc(T, d, E, K, w, act, gate, dtype, reserved)
+def _d(T=64, d=128, E=8, K=2, w=512, act=1, gate=0, dtype=1, capacity=0):
+    return MoeDesc(T, d, E, K, w, act, gate, dtype, capacity)
 
 
 def _ws(desc):
@@ -41,7 +41,7 @@ def test_status_strings():
     (dict(T=-1), SHAPE), (dict(d=0), SHAPE), (dict(w=0), SHAPE), (dict(E=0), SHAPE),
     (dict(K=0), SHAPE), (dict(K=9, E=8), SHAPE), (dict(E=65, K=2), UNSUP), (dict(E=64, K=9), UNSUP),
     (dict(d=100), UNSUP), (dict(w=1372), UNSUP), (dict(act=2), UNSUP), (dict(gate=5), UNSUP),
-    (dict(dtype=7), UNSUP), (dict(reserved=1), UNSUP), (dict(T=2 ** 30, K=2), UNSUP),
+    (dict(dtype=7), UNSUP), (dict(capacity=-1), SHAPE), (dict(capacity=5), OK), (dict(T=2 ** 30, K=2), UNSUP),
     (dict(d=2 ** 20 + 8, w=8), UNSUP), (dict(w=2 ** 20 + 8, d=8), UNSUP), (dict(d=2 ** 20, w=8), OK),
     # operand matrices hold at most 2^31 - 2^22 elements: T*K*d = 2^31 - 2^22 exactly is the largest
     (dict(T=261632, d=4096, K=2, w=512), OK), (dict(T=261633, d=4096, K=2, w=512), UNSUP),
@@ -49,6 +49,24 @@ def test_status_strings():
 def test_bad_descriptors(kw, status):
     n = ctypes.c_size_t(0)
     assert moe.lib().moe_workspace_size(ctypes.byref(_d(**kw)), ctypes.byref(n)) == status
+
+
+def test_capacity_slots_helper():
+    """C = factor * T * K / E rounded up; the page's case (Lensa ML Step 5) is 64."""
+    from fractions import Fraction
+    assert moe.capacity_slots(1.0, 256, 2, 8) == 64
+    for factor in (0.5, 0.75, 1.0, 1.1, 1.25, 2.0, 0.3):
+        for T, K, E in ((256, 2, 8), (80, 1, 8), (7, 2, 3), (4096, 2, 8), (8192, 1, 64), (0, 1, 4)):
+            need = Fraction(str(factor)) * T * K / E
+            c = moe.capacity_slots(factor, T, K, E)
+            assert Fraction(c) >= need and Fraction(c - 1) < need or (need == 0 and c == 0), (factor, T, K, E, c)
+    L = moe.lib()
+    out = ctypes.c_int32(0)
+    assert L.moe_capacity_slots(1.0, 256, 2, 8, None) == NULL
+    assert L.moe_capacity_slots(-1.0, 256, 2, 8, ctypes.byref(out)) == SHAPE
+    assert L.moe_capacity_slots(float("nan"), 256, 2, 8, ctypes.byref(out)) == SHAPE
+    assert L.moe_capacity_slots(1.0, 256, 0, 8, ctypes.byref(out)) == SHAPE
+    assert L.moe_capacity_slots(1e12, 2 ** 30, 8, 1, ctypes.byref(out)) == UNSUP
 
 
 def test_workspace_size_and_null_desc():
