@@ -61,10 +61,12 @@
  *  MOE_ACT_GELU:   o = GELU(x W1 + b1) W2 + b2   (exact erf GELU; biases optional)
  *  MOE_ACT_SWIGLU: o = (SiLU(x W1) * (x W3)) W2  (no biases; W3 required)
  *
- * Numerics: router logits are float32, accumulated for each (token, expert)
- * as one sequential fused-multiply-add chain over k = 0..d-1 starting from +0,
- * with the bias added afterwards; expert selection therefore depends on no
- * summation-order choice. Softmax, gates and aux are float32. Expert GEMMs
+ * Numerics: router logits are float32 in one fixed order, so expert selection
+ * depends on no implementation choice: k is cut into groups of four
+ * consecutive values, group g = k / 4 feeds chain g mod 4, each of the four
+ * chains is a fused-multiply-add chain from +0 over its k in ascending order,
+ * logit = (c0 + c1) + (c2 + c3), and the bias is added afterwards. Softmax,
+ * gates and aux are float32. Expert GEMMs
  * accumulate in float32 (bf16 inputs use bf16 MFMA); the hidden activation
  * is stored in the input dtype; o_perm is float32; y is rounded once.
  */

@@ -7,7 +7,7 @@ generator in common.
 
 Plain, slow, obviously correct. Everything after the router logits is float64
 (numpy matmul serves as the library primitive). The router logits are float32
-in the canonical sequential-fmaf order (router_fp32.c), because the router is
+in the canonical order of four interleaved fmaf chains (router_fp32.c), because the router is
 kept in float32 (Arjun Jaggi, "Mixture of Experts in LLMs: How Sparse Models
 Scale", section "Switch Transformers") and the expert choice must agree bit
 for bit with any implementation that follows the same order.
@@ -22,8 +22,9 @@ Page references (title, site, section):
 Function -> passage it follows -> what pins it (tests/test_oracle_pins.py):
   router_logits_f32   [LENSA] Step 2; [CUR] "Parameters you hold..." (linear
                       router + softmax); [AJ] "Switch Transformers" (float32)
-                      -> exact correctly-rounded fma chain recomputed with
-                         rational arithmetic; float64 error bound.
+                      -> exact correctly-rounded fma chains and sums
+                         recomputed with rational arithmetic; float64
+                         error bound.
   select_topk         [MTA] "The mechanism"; [LENSA] Step 3 (top-k)
                       -> brute force over all K-subsets, with ties.
   router_probs        [LENSA] Step 2 (softmax over experts)

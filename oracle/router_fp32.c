@@ -10,10 +10,15 @@
  * LLMs: How Sparse Models Scale", section "Switch Transformers").
  *
  * The pages do not fix a summation order. Expert selection must agree bit for
- * bit between implementations, so the layer's numeric contract fixes one:
- *   acc = +0.0f;  for k = 0 .. d-1 ascending:  acc = fmaf(h[t][k], W_r[k][e], acc);
- *   logit[t][e] = acc (+ b_r[e], one separate float32 addition, if a bias is given).
- * fmaf is correctly rounded, so this defines every bit of every logit.
+ * bit between implementations, so the layer's numeric contract fixes one. The
+ * reduction index k is cut into groups of four consecutive values; group g =
+ * k / 4 belongs to chain j = g mod 4. Each chain starts at +0 and takes its
+ * terms in ascending k:
+ *   c[j] = fmaf(h[t][k], W_r[k][e], c[j])   for every k with (k / 4) mod 4 == j
+ *   logit[t][e] = (c[0] + c[1]) + (c[2] + c[3])   (float32 additions)
+ *   (+ b_r[e], one more float32 addition, if a bias is given).
+ * fmaf and the additions are correctly rounded, so this defines every bit of
+ * every logit.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math, no
  * contraction: every rounding is the one written here).
@@ -26,17 +31,17 @@ void oracle_router_logits_f32(const float* h, const float* W_r, const float* b_r
                               int64_t T, int64_t d, int64_t E, float* logits) {
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
-    float* acc = logits + t * E;
-    for (int64_t e = 0; e < E; ++e) acc[e] = 0.0f;
+    float* out = logits + t * E;
     const float* ht = h + t * d;
-    /* k outermost so that each (t, e) chain still runs k = 0, 1, 2, ... in order. */
-    for (int64_t k = 0; k < d; ++k) {
-      const float hk = ht[k];
-      const float* wk = W_r + k * E;
-      for (int64_t e = 0; e < E; ++e) acc[e] = fmaf(hk, wk[e], acc[e]);
-    }
-    if (b_r != NULL) {
-      for (int64_t e = 0; e < E; ++e) acc[e] = acc[e] + b_r[e];
+    for (int64_t e = 0; e < E; ++e) {
+      float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int64_t k = 0; k < d; ++k) {
+        const int j = (int)((k / 4) % 4);
+        c[j] = fmaf(ht[k], W_r[k * E + e], c[j]);
+      }
+      float l = (c[0] + c[1]) + (c[2] + c[3]);
+      if (b_r != NULL) l = l + b_r[e];
+      out[e] = l;
     }
   }
 }

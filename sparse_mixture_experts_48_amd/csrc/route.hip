@@ -9,20 +9,26 @@
 // Arjun Jaggi, "Mixture of Experts in LLMs", section "Switch Transformers":
 //   the router runs in float32.
 //
-// Numeric contract: each logit is one fmaf chain over k = 0..d-1 from +0,
-// bias added afterwards, so the expert choice is independent of any
-// parallel-reduction order.
+// Numeric contract (the pages leave the summation order open; this one is
+// fixed so that the expert choice never depends on how the work is split):
+// k is cut into groups of four consecutive values, group g belongs to chain
+// g mod 4, each chain is an fmaf chain from +0 over its k in ascending order,
+// and logit = (c0 + c1) + (c2 + c3), bias added afterwards. Four independent
+// chains per logit instead of one quarter the dependent-latency floor of a
+// small batch and give a large batch four times the independent fmas.
 //
 // Two layouts of the same chains:
-//  * wide (E > 16): a thread owns TPT tokens x TE experts and walks k upward;
-//    lanes are laid out as [token group][expert lane], so the experts of one
-//    token sit in LE = EP/TE adjacent lanes of one wave and the per-token
-//    max / argmax / sum reductions are xor-butterflies inside those lanes.
-//  * narrow (E <= 16, T <= 256): one token per wave, lane = expert. The wave turns its
-//    token's h into float32 once per chunk of k (its own LDS row), the block
-//    stages W_r chunks in LDS, and each of the E active lanes runs its chain
-//    reading h as a broadcast and its W_r column: no conversion in the chain,
-//    and many more waves in flight for small batches.
+//  * wide (E > 16): a thread owns TPT tokens x TE experts, all four chains of
+//    each, and walks k upward; lanes are laid out as [token group][expert
+//    lane], so the experts of one token sit in LE = EP/TE adjacent lanes of
+//    one wave and the per-token max / argmax / sum reductions are
+//    xor-butterflies inside those lanes.
+//  * narrow (E <= 16, T <= 256): one token per wave, lane = chain * EP + expert.
+//    The wave turns its token's h into float32 once per chunk of k (its own
+//    LDS row), the block stages W_r chunks in LDS transposed, and each active
+//    lane runs one chain reading four h values and four W_r values per step:
+//    no conversion in the chain, and many more waves in flight for small
+//    batches. Two butterflies over the chain index form the sums.
 #include "common.h"
 #include "kernels.h"
 
@@ -153,13 +159,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     }
   };
 
-  float acc[TPT][TE];
+  float acc[TPT][TE][4];  // the four chains of each logit
 #pragma unroll
   for (int i = 0; i < TPT; ++i)
 #pragma unroll
-    for (int q = 0; q < TE; ++q) acc[i][q] = 0.0f;
+    for (int q = 0; q < TE; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][q][j] = 0.0f;
 
-  auto compute4 = [&](int buf, int kk) {
+  // k = kk .. kk+3 of the stage: one group, chain j = (kk / 4) mod 4 (BK is a
+  // multiple of 16, so the stage offset does not move the round-robin)
+  auto compute4 = [&](int buf, int kk, int j) {
     float4 hv[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) hv[i] = *reinterpret_cast<const float4*>(&h_s[buf][tg + i * G][kk]);
@@ -180,17 +190,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int q = 0; q < TE; ++q) acc[i][q] = fmaf(hk[s], wv[s][q], acc[i][q]);
+        for (int q = 0; q < TE; ++q) acc[i][q][j] = fmaf(hk[s], wv[s][q], acc[i][q][j]);
     }
   };
+  static_assert(BK % 16 == 0, "a stage holds whole rounds of the four chains");
   auto compute_stage = [&](int c, int buf) {
     const int kn = min(BK, d - c * BK);  // a multiple of 8
     if (kn == BK) {
-      // fully unrolled so that LDS reads run ahead of the dependent fma chain
+      // fully unrolled so that LDS reads run ahead of the fma chains
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += 4) compute4(buf, kk);
+      for (int kk = 0; kk < BK; kk += 4) compute4(buf, kk, (kk / 4) % 4);
     } else {
-      for (int kk = 0; kk < kn; kk += 4) compute4(buf, kk);
+      for (int kk = 0; kk < kn; kk += 16) {  // kn - kk >= 8: the first two groups always exist
+        compute4(buf, kk, 0);
+        compute4(buf, kk + 4, 1);
+        if (kk + 8 < kn) {
+          compute4(buf, kk + 8, 2);
+          compute4(buf, kk + 12, 3);
+        }
+      }
     }
   };
 
@@ -225,7 +243,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     for (int q = 0; q < TE; ++q) {
       const int e = el * TE + q;
       if (e < E) {
-        l[q] = acc[i][q];
+        l[q] = (acc[i][q][0] + acc[i][q][1]) + (acc[i][q][2] + acc[i][q][3]);
         if (br != nullptr) l[q] = l[q] + br[e];
       } else {
         l[q] = -INFINITY;
@@ -315,8 +333,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   }
 }
 
-// Narrow layout: NW waves per block, one token per wave; chunks of kNarrowKC k.
+// Narrow layout: kNarrowNW waves per block, one token per wave; chunks of kNarrowKC k.
 constexpr int kNarrowKC = 512;
+constexpr int kNarrowNW = 4;
 
 template <typename Tin, int EP, int NW>
 __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
@@ -331,11 +350,11 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
   static_assert(KC == 8 * 64, "one 8-value h vector per lane per chunk");
   // Separate arrays per buffer, so that reads of one chunk are known not to
   // alias the writes of the next.
-  constexpr int RD = 8;                     // ring depth of the chain (steps of 4 k)
-  constexpr int HP = KC + 4 * RD;           // h row stride: the ring may read 4*RD past the chunk
+  constexpr int RD = 4;                     // ring depth of a chain (steps of one group of 4 k)
+  constexpr int HP = KC + 16 * RD;          // h row stride: the ring may read RD rounds past the chunk
   __shared__ __align__(16) float hA[NW][HP];
   __shared__ __align__(16) float hB[NW][HP];
-  constexpr int KP = KC + 4 * RD + 4;       // row stride of the transposed chunk (floats)
+  constexpr int KP = KC + 16 * RD + 4;      // row stride of the transposed chunk (floats)
   __shared__ __align__(16) float wA[EP * KP];  // W_r chunk transposed: [e][k - k0]
   __shared__ __align__(16) float wB[EP * KP];
   __shared__ float psum_s[NW][EP];
@@ -392,35 +411,50 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
   };
 
   float acc = 0.0f;
-  // The chain of lane e reads h (broadcast) and its W_r row four k at a time,
-  // from a register ring filled D steps ahead of the fmas. Both LDS buffers
-  // hold zeros past the end of the reduction (h loads past d are zeroed; W_r
-  // slots past the run are written with the zeros loaded for them), so the
-  // chain runs to kn rounded up to 4*D: the extra steps add exact zeros (acc
+  // Lane (j, e) = (lane / EP, lane % EP) runs chain j of expert e: the groups
+  // of four k whose index within the chunk is j mod 4 (KC is a multiple of 16,
+  // so chunk boundaries keep the round-robin). One step reads one group of h
+  // (the j-lanes of a token read the same address) and of its W_r row into a
+  // register ring filled RD steps ahead of the fmas. Both LDS buffers hold
+  // zeros past the end of the reduction (h loads past d are zeroed; W_r slots
+  // past the run are written with the zeros loaded for them), so a chain runs
+  // to a whole number of rings: the extra steps add exact zeros (a chain
   // starts at +0 and a round-to-nearest sum is never -0 unless both terms are).
+  const int cj = lane / EP;
+  const int ce = lane % EP;
   auto compute = [&](int c, const float (*hs)[HP], const float* ws) {
-    if (lane >= E) return;
+    if (cj >= 4 || ce >= E) return;
     constexpr int D = RD;
-    static_assert(KC % (4 * D) == 0, "ring");
+    static_assert(KC % (16 * D) == 0, "ring");
     const int kn = min(KC, d - c * KC);
-    const int kn_pad = (kn + 4 * D - 1) / (4 * D) * (4 * D);
-    const float4* hw = reinterpret_cast<const float4*>(hs[wave]);         // HP % 4 == 0
-    const float4* wc = reinterpret_cast<const float4*>(ws + lane * KP);  // KP % 4 == 0
+    const int steps = (kn + 16 * D - 1) / (16 * D) * D;  // rounds of 4 groups, whole rings
+    const float4* hw = reinterpret_cast<const float4*>(hs[wave]) + cj;       // HP % 4 == 0
+    const float4* wc = reinterpret_cast<const float4*>(ws + ce * KP) + cj;   // KP % 4 == 0
     float4 rh[D], rw[D];
-    auto fetch = [&](int slot, int k) {  // reads up to 4*D past kn_pad land in the row padding, unused
-      rh[slot] = hw[k / 4];              // same address in every lane
-      rw[slot] = wc[k / 4];
+    auto fetch = [&](int slot, int m) {  // reads up to D rounds past `steps` land in the row padding, unused
+      rh[slot] = hw[4 * m];
+      rw[slot] = wc[4 * m];
     };
+    // The ring is filled in slot order (pinned, as the refills below): the
+    // wait at the top of the loop then only needs the oldest reads, on entry
+    // as on every later pass.
 #pragma unroll
-    for (int u = 0; u < D; ++u) fetch(u, 4 * u);
-    for (int k = 0; k < kn_pad; k += 4 * D) {
+    for (int u = 0; u < D; ++u) {
+      fetch(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int m = 0; m < steps; m += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         acc = fmaf(rh[u].x, rw[u].x, acc);
         acc = fmaf(rh[u].y, rw[u].y, acc);
         acc = fmaf(rh[u].z, rw[u].z, acc);
         acc = fmaf(rh[u].w, rw[u].w, acc);
-        fetch(u, k + 4 * (u + D));
+        fetch(u, m + u + D);
+        // keep the refill here: left to itself the compiler moves every read of
+        // the ring to the top of the loop and waits for them, so no read would
+        // be in flight while the fmas run
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -443,10 +477,14 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
     compute(c, hA, wA);
   }
 
-  // logits, top-K by (logit descending, expert ascending), softmax, gates
+  // logit = (c0 + c1) + (c2 + c3) on the lanes of chain 0 (lane = expert);
+  // lanes of inactive chains or experts hold +0 and are not used
+  float part = acc + __shfl_xor(acc, EP);  // chains 0/1: c0 + c1; chains 2/3: c2 + c3
+  part = part + __shfl_xor(part, 2 * EP);
+  // top-K by (logit descending, expert ascending), softmax, gates
   float l = -INFINITY;
   if (lane < E) {
-    l = acc;
+    l = part;
     if (br != nullptr) l = l + br[lane];
   }
   if (tok_ok && logits_out != nullptr && lane < E) logits_out[static_cast<size_t>(t) * E + lane] = l;
@@ -619,7 +657,7 @@ hipError_t launch_route_narrow(const RouteArgs& a, const RouteTiling& rt, hipStr
 
 template <typename Tin, int EP>
 hipError_t launch_route_narrow_nw(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
-  return launch_route_narrow<Tin, EP, 4>(a, rt, st);
+  return launch_route_narrow<Tin, EP, kNarrowNW>(a, rt, st);
 }
 
 template <typename Tin>
@@ -647,8 +685,8 @@ RouteTiling route_tiling(int64_t T, int64_t E) {
   rt.EP = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
   if (rt.EP <= 16 && T <= kNarrowMaxT) {
     rt.TPT = 1;
-    rt.NW = 4;
-    rt.TB = 4;
+    rt.NW = kNarrowNW;
+    rt.TB = kNarrowNW;
   } else {
     rt.TPT = rt.EP >= 32 ? 2 : 1;
     rt.NW = 0;  // wide layout

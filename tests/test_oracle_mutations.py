@@ -35,6 +35,30 @@ def _logits_bias_first(h, W, b):
     return _orig["router_logits_f32"](h1, W1, None)
 
 
+def _logits_single_chain(h, W, b):
+    # one sequential chain per logit instead of four interleaved chains
+    h = np.asarray(h, np.float32).astype(np.float64)
+    W = np.asarray(W, np.float32).astype(np.float64)
+    acc = np.zeros((h.shape[0], W.shape[1]), np.float32)
+    for k in range(h.shape[1]):
+        acc = (acc.astype(np.float64) + np.outer(h[:, k], W[k])).astype(np.float32)
+    if b is not None:
+        acc = acc + np.asarray(b, np.float32)[None, :]
+    return acc
+
+
+def _logits_pairs_swapped(h, W, b):
+    # (c0 + c2) + (c1 + c3): relabel the groups of chains 1 and 2
+    h = np.asarray(h, np.float32)
+    d = h.shape[1]
+    k = np.arange(d)
+    g, j = k // 4, (k // 4) % 4
+    partner = g - j + np.where(j == 1, 2, np.where(j == 2, 1, j))
+    src = np.where(4 * partner < d, 4 * partner + k % 4, k)  # a group without partner stays
+    return _orig["router_logits_f32"](np.ascontiguousarray(h[:, src]),
+                                      np.ascontiguousarray(np.asarray(W, np.float32)[src, :]), b)
+
+
 def _topk_high_index_wins(l, K):
     E = l.shape[1]
     idx = _orig["select_topk"](l[:, ::-1], K)
@@ -146,6 +170,8 @@ MUTATIONS = {
     "router_drops_bias": ("router_logits_f32", _logits_no_bias),
     "router_reverse_k_order": ("router_logits_f32", _logits_reverse_k),
     "router_bias_first": ("router_logits_f32", _logits_bias_first),
+    "router_single_chain": ("router_logits_f32", _logits_single_chain),
+    "router_pairs_swapped": ("router_logits_f32", _logits_pairs_swapped),
     "topk_high_index_wins_ties": ("select_topk", _topk_high_index_wins),
     "topk_smallest": ("select_topk", _topk_smallest),
     "gates_not_renormalised": ("gates", _gates_no_renorm),
