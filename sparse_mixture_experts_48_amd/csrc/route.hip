@@ -37,7 +37,16 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteTB = 32;  // tokens per block (wide layout)
+
+// Wide layout per padded expert count: TE experts and TPT tokens per thread,
+// BK k per LDS stage. A block holds kRouteThreads / (EP / TE) * TPT tokens.
+template <int EP> struct WideCfg;
+template <> struct WideCfg<8> { static constexpr int TE = 1, TPT = 1, BK = 128; };
+template <> struct WideCfg<16> { static constexpr int TE = 2, TPT = 1, BK = 128; };
+template <> struct WideCfg<32> { static constexpr int TE = 2, TPT = 2, BK = 64; };
+template <> struct WideCfg<64> { static constexpr int TE = 4, TPT = 2, BK = 64; };
+template <int EP>
+constexpr int wide_tb() { return kRouteThreads / (EP / WideCfg<EP>::TE) * WideCfg<EP>::TPT; }
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
@@ -84,12 +93,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   constexpr int G = kRouteThreads / LE;   // token groups per block
   constexpr int TB = G * TPT;             // tokens per block
   static_assert(LE >= 1 && LE <= 64 && (64 % LE) == 0, "token lanes must tile a wave");
-  static_assert(TB == kRouteTB, "router tiling");
   constexpr int HP = BK + 4;              // h_s row stride (floats)
   constexpr int WP = EP + 4;              // w_s row stride (floats)
-  constexpr int HV = TB * (BK / 8) / kRouteThreads;       // 8-value h vectors per thread per stage
+  constexpr int HN = TB * (BK / 8);                        // 8-value h vectors per stage
+  constexpr int HV = (HN + kRouteThreads - 1) / kRouteThreads;  // ... per thread
   constexpr int WV = (BK * EP / 4 + kRouteThreads - 1) / kRouteThreads;  // W_r float4s per thread
-  static_assert(HV >= 1 && HV * kRouteThreads == TB * (BK / 8), "h staging");
 
   __shared__ __align__(16) float h_s[2][TB][HP];
   __shared__ __align__(16) float w_s[2][BK][WP];
@@ -116,7 +124,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
       const int r = i / (BK / 8);
       const int cc = (i % (BK / 8)) * 8;
       const int t = t0 + r;
-      if (t < T && cc < kn) HVec<Tin>::load(h + static_cast<size_t>(t) * d + k0 + cc, hreg[slot][v]);
+      const bool mine = HN % kRouteThreads == 0 || i < HN;
+      if (mine && t < T && cc < kn) HVec<Tin>::load(h + static_cast<size_t>(t) * d + k0 + cc, hreg[slot][v]);
       else HVec<Tin>::zero(hreg[slot][v]);
     }
     // rows k0 .. k0+kn of W_r are one contiguous run of kn*E floats
@@ -136,6 +145,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
       const int i = tid + v * kRouteThreads;
       const int r = i / (BK / 8);
       const int cc = (i % (BK / 8)) * 8;
+      if (HN % kRouteThreads != 0 && i >= HN) continue;
       float x[8];
       HVec<Tin>::to_f32(hreg[slot][v], x);
 #pragma unroll
@@ -176,9 +186,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     float wv[4][TE];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if constexpr (TE == 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(&w_s[buf][kk + s][el * TE]);
-        wv[s][0] = w4.x; wv[s][1] = w4.y; wv[s][2] = w4.z; wv[s][3] = w4.w;
+      if constexpr (TE % 4 == 0) {
+#pragma unroll
+        for (int q4 = 0; q4 < TE; q4 += 4) {
+          const float4 w4 = *reinterpret_cast<const float4*>(&w_s[buf][kk + s][el * TE + q4]);
+          wv[s][q4] = w4.x; wv[s][q4 + 1] = w4.y; wv[s][q4 + 2] = w4.z; wv[s][q4 + 3] = w4.w;
+        }
       } else {
 #pragma unroll
         for (int q = 0; q < TE; ++q) wv[s][q] = w_s[buf][kk + s][el * TE + q];
@@ -665,11 +678,11 @@ hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStre
   if (rt.NW > 0) {  // narrow layout
     return rt.EP == 8 ? launch_route_narrow_nw<Tin, 8>(a, rt, st) : launch_route_narrow_nw<Tin, 16>(a, rt, st);
   }
-  switch (rt.EP) {  // wide layout: 32 tokens x EP experts per block of 256 threads
-    case 8: return launch_route_wide<Tin, 8, 1, 1, 128, 4>(a, rt, st);
-    case 16: return launch_route_wide<Tin, 16, 2, 1, 128, 4>(a, rt, st);
-    case 32: return launch_route_wide<Tin, 32, 2, 2, 64, 4>(a, rt, st);
-    default: return launch_route_wide<Tin, 64, 4, 2, 64, 4>(a, rt, st);
+  switch (rt.EP) {  // wide layout: wide_tb<EP>() tokens x EP experts per block of 256 threads
+    case 8: return launch_route_wide<Tin, 8, WideCfg<8>::TE, WideCfg<8>::TPT, WideCfg<8>::BK, 4>(a, rt, st);
+    case 16: return launch_route_wide<Tin, 16, WideCfg<16>::TE, WideCfg<16>::TPT, WideCfg<16>::BK, 4>(a, rt, st);
+    case 32: return launch_route_wide<Tin, 32, WideCfg<32>::TE, WideCfg<32>::TPT, WideCfg<32>::BK, 4>(a, rt, st);
+    default: return launch_route_wide<Tin, 64, WideCfg<64>::TE, WideCfg<64>::TPT, WideCfg<64>::BK, 4>(a, rt, st);
   }
 }
 
@@ -690,7 +703,7 @@ RouteTiling route_tiling(int64_t T, int64_t E) {
   } else {
     rt.TPT = rt.EP >= 32 ? 2 : 1;
     rt.NW = 0;  // wide layout
-    rt.TB = kRouteTB;
+    rt.TB = rt.EP == 8 ? wide_tb<8>() : rt.EP == 16 ? wide_tb<16>() : rt.EP == 32 ? wide_tb<32>() : wide_tb<64>();
   }
   rt.NB = static_cast<int>((T + rt.TB - 1) / rt.TB);
   return rt;
