@@ -42,7 +42,14 @@ __device__ __forceinline__ float gelu_exact(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (each about
+// 1 ulp): 4 instructions instead of the ~25 of expf and an IEEE division. The
+// relative error stays near 1e-7, far below the bfloat16 rounding of the
+// hidden activation and within the float32 layer tolerance. For z below about
+// -88 the exponential overflows to +inf and the result is -0 (exact: ~-z e^z).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
 
 // Rows [*beg, *end) of expert e that its FFN processes: at most `cap` rows
 // (the expert's capacity; the grouping is stable, so these are its first cap
