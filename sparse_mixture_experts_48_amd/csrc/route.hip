@@ -18,11 +18,14 @@
 // small batch and give a large batch four times the independent fmas.
 //
 // Two layouts of the same chains:
-//  * wide (E > 16): a thread owns TPT tokens x TE experts, all four chains of
-//    each, and walks k upward; lanes are laid out as [token group][expert
-//    lane], so the experts of one token sit in LE = EP/TE adjacent lanes of
-//    one wave and the per-token max / argmax / sum reductions are
-//    xor-butterflies inside those lanes.
+//  * wide (E > 16 or T > 256): a thread owns one chain of TPT tokens x TE
+//    experts and walks that chain's k upward; lanes are laid out as [token
+//    group][chain][expert lane], so the four chains of a logit sit LE = EP/TE
+//    lanes apart (two xor-butterflies form the sums, identical in all four)
+//    and the experts of one token sit in LE adjacent lanes, where the
+//    per-token max / argmax / sum reductions are xor-butterflies. Keeping one
+//    chain per thread leaves the registers for a larger token x expert tile,
+//    which sets the LDS bytes read per fma.
 //  * narrow (E <= 16, T <= 256): one token per wave, lane = chain * EP + expert.
 //    The wave turns its token's h into float32 once per chunk of k (its own
 //    LDS row), the block stages W_r chunks in LDS transposed, and each active
@@ -38,15 +41,16 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 
-// Wide layout per padded expert count: TE experts and TPT tokens per thread,
-// BK k per LDS stage. A block holds kRouteThreads / (EP / TE) * TPT tokens.
+// Wide layout per padded expert count: TE experts and TPT tokens per thread
+// (one chain of each), BK k per LDS stage. A token group takes 4 * EP / TE
+// lanes; a block holds kRouteThreads / (4 * EP / TE) * TPT tokens.
 template <int EP> struct WideCfg;
-template <> struct WideCfg<8> { static constexpr int TE = 1, TPT = 1, BK = 128; };
-template <> struct WideCfg<16> { static constexpr int TE = 2, TPT = 1, BK = 128; };
-template <> struct WideCfg<32> { static constexpr int TE = 2, TPT = 2, BK = 64; };
-template <> struct WideCfg<64> { static constexpr int TE = 4, TPT = 2, BK = 64; };
+template <> struct WideCfg<8> { static constexpr int TE = 2, TPT = 1, BK = 128; };
+template <> struct WideCfg<16> { static constexpr int TE = 4, TPT = 2, BK = 128; };
+template <> struct WideCfg<32> { static constexpr int TE = 4, TPT = 4, BK = 64; };
+template <> struct WideCfg<64> { static constexpr int TE = 4, TPT = 4, BK = 64; };
 template <int EP>
-constexpr int wide_tb() { return kRouteThreads / (EP / WideCfg<EP>::TE) * WideCfg<EP>::TPT; }
+constexpr int wide_tb() { return kRouteThreads / (4 * EP / WideCfg<EP>::TE) * WideCfg<EP>::TPT; }
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
@@ -89,10 +93,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     int T, int d, int E, int K, int gate_mode,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
     int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum) {
-  constexpr int LE = EP / TE;             // lanes per token
-  constexpr int G = kRouteThreads / LE;   // token groups per block
+  constexpr int LE = EP / TE;             // expert lanes per chain
+  constexpr int LG = 4 * LE;              // lanes per token group: chain-major, then expert lane
+  constexpr int G = kRouteThreads / LG;   // token groups per block
   constexpr int TB = G * TPT;             // tokens per block
-  static_assert(LE >= 1 && LE <= 64 && (64 % LE) == 0, "token lanes must tile a wave");
+  static_assert(LE >= 1 && LG <= 64 && (64 % LG) == 0, "token-group lanes must tile a wave");
   constexpr int HP = BK + 4;              // h_s row stride (floats)
   constexpr int WP = EP + 4;              // w_s row stride (floats)
   constexpr int HN = TB * (BK / 8);                        // 8-value h vectors per stage
@@ -105,8 +110,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   __shared__ int hist_s[EP];
 
   const int tid = threadIdx.x;
-  const int tg = tid / LE;
+  const int tg = tid / LG;
+  const int cj = (tid % LG) / LE;  // chain of this lane
   const int el = tid % LE;
+  // Expert q of this lane. With TE a multiple of 4 the lane's experts are
+  // float4 runs at el*4, el*4 + 4*LE, ...: the LE lanes of one read then touch
+  // consecutive 16-byte slots of a w_s row (no bank conflicts).
+  auto expert_of = [&](int q) { return TE % 4 == 0 ? (q / 4) * (4 * LE) + el * 4 + q % 4 : el * TE + q; };
   const int t0 = blockIdx.x * TB;
   if (tid < EP) hist_s[tid] = 0;
   const int nc = (d + BK - 1) / BK;
@@ -169,17 +179,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     }
   };
 
-  float acc[TPT][TE][4];  // the four chains of each logit
+  float acc[TPT][TE];  // chain cj of each of the thread's logits
 #pragma unroll
   for (int i = 0; i < TPT; ++i)
 #pragma unroll
-    for (int q = 0; q < TE; ++q)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][q][j] = 0.0f;
+    for (int q = 0; q < TE; ++q) acc[i][q] = 0.0f;
 
-  // k = kk .. kk+3 of the stage: one group, chain j = (kk / 4) mod 4 (BK is a
-  // multiple of 16, so the stage offset does not move the round-robin)
-  auto compute4 = [&](int buf, int kk, int j) {
+  // One group of four k (kk .. kk+3 of the stage) for this lane's chain.
+  auto compute_group = [&](int buf, int kk) {
     float4 hv[TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) hv[i] = *reinterpret_cast<const float4*>(&h_s[buf][tg + i * G][kk]);
@@ -189,9 +196,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
       if constexpr (TE % 4 == 0) {
 #pragma unroll
         for (int q4 = 0; q4 < TE; q4 += 4) {
-          const float4 w4 = *reinterpret_cast<const float4*>(&w_s[buf][kk + s][el * TE + q4]);
+          const float4 w4 = *reinterpret_cast<const float4*>(&w_s[buf][kk + s][expert_of(q4)]);
           wv[s][q4] = w4.x; wv[s][q4 + 1] = w4.y; wv[s][q4 + 2] = w4.z; wv[s][q4 + 3] = w4.w;
         }
+      } else if constexpr (TE == 2) {
+        const float2 w2 = *reinterpret_cast<const float2*>(&w_s[buf][kk + s][el * TE]);
+        wv[s][0] = w2.x; wv[s][1] = w2.y;
       } else {
 #pragma unroll
         for (int q = 0; q < TE; ++q) wv[s][q] = w_s[buf][kk + s][el * TE + q];
@@ -203,25 +213,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int q = 0; q < TE; ++q) acc[i][q][j] = fmaf(hk[s], wv[s][q], acc[i][q][j]);
+        for (int q = 0; q < TE; ++q) acc[i][q] = fmaf(hk[s], wv[s][q], acc[i][q]);
     }
   };
+  // Chain cj takes the groups 4m + cj of the stage (BK is a multiple of 16, so
+  // the stage offset does not move the round-robin), in ascending k.
   static_assert(BK % 16 == 0, "a stage holds whole rounds of the four chains");
   auto compute_stage = [&](int c, int buf) {
-    const int kn = min(BK, d - c * BK);  // a multiple of 8
-    if (kn == BK) {
-      // fully unrolled so that LDS reads run ahead of the fma chains
+    const int ng = min(BK, d - c * BK) / 4;  // groups in the stage (kn is a multiple of 8)
+    if (ng == BK / 4) {
+      // fully unrolled so that LDS reads run ahead of the fmas
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += 4) compute4(buf, kk, (kk / 4) % 4);
+      for (int m = 0; m < BK / 16; ++m) compute_group(buf, 16 * m + 4 * cj);
     } else {
-      for (int kk = 0; kk < kn; kk += 16) {  // kn - kk >= 8: the first two groups always exist
-        compute4(buf, kk, 0);
-        compute4(buf, kk + 4, 1);
-        if (kk + 8 < kn) {
-          compute4(buf, kk + 8, 2);
-          compute4(buf, kk + 12, 3);
-        }
-      }
+      for (int m = 0; 4 * m + cj < ng; ++m) compute_group(buf, 16 * m + 4 * cj);
     }
   };
 
@@ -250,22 +255,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int t = t0 + tg + i * G;
-    const bool tok_ok = t < T;  // uniform across the LE lanes of this token
+    const bool tok_ok = t < T;  // uniform across the lanes of this token group
     float l[TE];
 #pragma unroll
     for (int q = 0; q < TE; ++q) {
-      const int e = el * TE + q;
+      const int e = expert_of(q);
+      // (c0 + c1) + (c2 + c3): every chain's lane ends with the same sums
+      const float c01 = acc[i][q] + __shfl_xor(acc[i][q], LE);
+      const float c0123 = c01 + __shfl_xor(c01, 2 * LE);
       if (e < E) {
-        l[q] = (acc[i][q][0] + acc[i][q][1]) + (acc[i][q][2] + acc[i][q][3]);
+        l[q] = c0123;
         if (br != nullptr) l[q] = l[q] + br[e];
       } else {
         l[q] = -INFINITY;
       }
     }
-    if (tok_ok && logits_out != nullptr) {
+    if (tok_ok && cj == 0 && logits_out != nullptr) {
 #pragma unroll
       for (int q = 0; q < TE; ++q) {
-        const int e = el * TE + q;
+        const int e = expert_of(q);
         if (e < E) logits_out[static_cast<size_t>(t) * E + e] = l[q];
       }
     }
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
         int bi = 0x7fffffff;
 #pragma unroll
         for (int q = 0; q < TE; ++q) {
-          const int e = el * TE + q;
+          const int e = expert_of(q);
           if (!taken[q] && e < E && better(l[q], e, bv, bi)) { bv = l[q]; bi = e; }
         }
 #pragma unroll
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
         cval[j] = bv;
 #pragma unroll
         for (int q = 0; q < TE; ++q)
-          if (el * TE + q == bi) taken[q] = true;
+          if (expert_of(q) == bi) taken[q] = true;
       }
     }
     // softmax over all E (the largest logit is the first choice)
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     float s = 0.0f;
 #pragma unroll
     for (int q = 0; q < TE; ++q) {
-      ex[q] = (el * TE + q < E) ? expf(l[q] - m) : 0.0f;
+      ex[q] = (expert_of(q) < E) ? expf(l[q] - m) : 0.0f;
       s += ex[q];
     }
 #pragma unroll
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
 #pragma unroll
       for (int q = 0; q < TE; ++q) psum_local[q] += ex[q] / s;
     }
-    if (tok_ok && el == 0) {
+    if (tok_ok && cj == 0 && el == 0) {
       float ec[8];
       float se = 0.0f;
 #pragma unroll
@@ -336,7 +344,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   }
 
 #pragma unroll
-  for (int q = 0; q < TE; ++q) psum_s[tg][el * TE + q] = psum_local[q];
+  for (int q = 0; q < TE; ++q)
+    if (cj == 0) psum_s[tg][expert_of(q)] = psum_local[q];
   __syncthreads();
   if (tid < E) {
     float s = 0.0f;
