@@ -148,7 +148,9 @@ int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float
 
 /* Grouping of the routing slots by expert (Lensa ML Step 5: experts take any
  * number of tokens). Stable: inside each expert's group tokens keep their order.
- * In:  topk_idx, h.
+ * In:  topk_idx, h. The K ids of a token must be distinct (as moe_route
+ *      writes them); an id outside [0, E) is skipped: it gets token_slot -1 and
+ *      no grouped row, and it is not counted in expert_offsets.
  * Out: expert_offsets, slot_token, token_slot, h_perm (gathered rows of h).
  * With desc->capacity = C > 0, token_slot is -1 for every slot at rank C or
  * more in its expert's group (dropped); the groups themselves keep every slot.

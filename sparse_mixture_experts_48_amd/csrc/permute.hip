@@ -7,11 +7,14 @@
 // per expert (Step 5), a slot whose rank in its group is C or more is dropped
 // (token_slot = -1): each expert keeps its first C tokens in token order.
 //
-// Block b owns the same token range as router block b. Its base row for
-// expert e is offsets[e] + (slots of e in blocks before b), computed by the
-// finalize kernel. Inside the block, wave w counts its 64 tokens per expert
-// with a ballot; a token's rank is the popcount of the lanes below it that
-// chose the same expert, plus the counts of earlier waves.
+// Block b owns the token ranges of M consecutive router blocks, starting at
+// router block b*M (M = 256 / tokens per router block, so a block holds up to
+// 256 tokens). Its base row for expert e is that of its first router block,
+// offsets[e] + (slots of e in router blocks before it), computed by the
+// finalize kernel. Inside the block, wave w takes one round per expert that
+// occurs among its 64 tokens: a ballot gives the wave's count, and a token's
+// rank is the popcount of the lanes below it that chose the same expert;
+// its slot adds the counts of earlier waves.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,10 +28,16 @@ constexpr int kMaxK = 8;
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_base,
     const int32_t* __restrict__ offsets, int T, int E, int K, int cap,
-    int TB, const char* __restrict__ h, size_t row_bytes, char* __restrict__ h_perm,
+    int TB, int M, const char* __restrict__ h, size_t row_bytes, char* __restrict__ h_perm,
     int32_t* __restrict__ slot_token, int32_t* __restrict__ token_slot) {
   __shared__ int cnt_s[kPermThreads / 64][64];
   __shared__ int slots_s[kPermThreads][kMaxK];
+  __shared__ int base_s[64];
+  __shared__ int off_s[64];
+  if (threadIdx.x < E) {  // one coalesced read instead of one read per expert below
+    base_s[threadIdx.x] = blk_base[static_cast<size_t>(blockIdx.x) * M * E + threadIdx.x];
+    off_s[threadIdx.x] = offsets[threadIdx.x];
+  }
   const int wave = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   const int t0 = blockIdx.x * TB;
@@ -40,32 +49,55 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   for (int j = 0; j < kMaxK; ++j) ids[j] = (ok && j < K) ? topk_idx[static_cast<size_t>(t) * K + j] : -1;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  for (int e = 0; e < E; ++e) {
-    bool has = false;
+  // Pass 1, one round per expert present in the wave (not per expert of the
+  // layer): the lanes holding it get their rank among the wave's tokens that
+  // chose it (popcount of those below), and the wave's count is recorded.
+  // Slot ids outside [0, E) are skipped.
+  cnt_s[wave][lane] = 0;
+  uint32_t rem = 0;  // bit j: slot j of this lane still to rank
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) has |= (ids[j] == e);
-    const uint64_t m = __ballot(has);
+  for (int j = 0; j < kMaxK; ++j)
+    if (static_cast<unsigned>(ids[j]) < static_cast<unsigned>(E)) rem |= 1u << j;
+  int rk[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) rk[j] = 0;
+  for (uint64_t active = __ballot(rem != 0); active != 0; active = __ballot(rem != 0)) {
+    const int leader = __builtin_ctzll(active);  // wave-uniform
+    int first = -1;
+#pragma unroll
+    for (int j = kMaxK - 1; j >= 0; --j)
+      if ((rem >> j) & 1u) first = ids[j];
+    const int e = __builtin_amdgcn_readlane(first, leader);
+    uint32_t hit = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (((rem >> j) & 1u) && ids[j] == e) hit |= 1u << j;
+    const uint64_t m = __ballot(hit != 0);
     if (lane == 0) cnt_s[wave][e] = __popcll(m);
+    const int r = __popcll(m & below);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if ((hit >> j) & 1u) rk[j] = r;
+    rem &= ~hit;
   }
   __syncthreads();
 
-  for (int e = 0; e < E; ++e) {
-    int base = blk_base[static_cast<size_t>(blockIdx.x) * E + e];
-    for (int w = 0; w < wave; ++w) base += cnt_s[w][e];
-    bool has = false;
+  // Pass 2: slot = block base + counts of earlier waves + rank in the wave.
+  // A slot id outside [0, E) gets token_slot -1 and no grouped row.
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) has |= (ids[j] == e);
-    const uint64_t m = __ballot(has);
-    if (has) {
-      const int slot = base + __popcll(m & below);
-      const bool kept = slot - offsets[e] < cap;  // rank in the expert's group, token order
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (ids[j] == e) {
-          token_slot[static_cast<size_t>(t) * K + j] = kept ? slot : -1;
-          slots_s[lt][j] = slot;
-        }
-      }
+  for (int j = 0; j < kMaxK; ++j) {
+    const int e = ids[j];
+    if (ok && j < K && static_cast<unsigned>(e) >= static_cast<unsigned>(E)) {
+      token_slot[static_cast<size_t>(t) * K + j] = -1;
+      slots_s[lt][j] = -1;
+    }
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
+      int base = base_s[e];
+      for (int w = 0; w < wave; ++w) base += cnt_s[w][e];
+      const int slot = base + rk[j];
+      const bool kept = slot - off_s[e] < cap;  // rank in the expert's group, token order
+      token_slot[static_cast<size_t>(t) * K + j] = kept ? slot : -1;
+      slots_s[lt][j] = slot;
       slot_token[slot] = t;
     }
   }
@@ -91,7 +123,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       }
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j) {
-        if (j < K) {
+        if (j < K && sl[j] >= 0) {
           uint4* dst = reinterpret_cast<uint4*>(h_perm + static_cast<size_t>(sl[j]) * row_bytes);
 #pragma unroll
           for (int u = 0; u < kU; ++u) {
@@ -109,9 +141,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, const int32_t* offsets, int T,
                           int E, int K, int cap, const RouteTiling& rt, const void* h, size_t row_bytes,
                           void* h_perm, int32_t* slot_token, int32_t* token_slot, hipStream_t st) {
-  if (rt.TB > kPermThreads) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(permute_kernel, dim3(rt.NB), dim3(kPermThreads), 0, st, topk_idx, blk_base, offsets, T,
-                     E, K, cap, rt.TB, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
+  if (rt.TB < 1 || rt.TB > kPermThreads) return hipErrorInvalidValue;
+  const int M = kPermThreads / rt.TB;  // router blocks per permute block
+  const int nb = (rt.NB + M - 1) / M;
+  hipLaunchKernelGGL(permute_kernel, dim3(nb), dim3(kPermThreads), 0, st, topk_idx, blk_base, offsets, T,
+                     E, K, cap, M * rt.TB, M, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
                      slot_token, token_slot);
   return hipGetLastError();
 }

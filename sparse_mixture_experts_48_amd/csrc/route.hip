@@ -599,12 +599,25 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const int per = (NB + kFinParts - 1) / kFinParts;
   const int b0 = min(NB, part * per);
   const int b1 = min(NB, b0 + per);
+  // Loads in batches of 8 (independent, in flight together), sums in block order.
+  constexpr int kU = 8;
   int c = 0;
   float ps = 0.0f;
   if (e < E) {
-    for (int b = b0; b < b1; ++b) {
-      c += blk_hist[static_cast<size_t>(b) * E + e];
-      if (blk_psum != nullptr) ps += blk_psum[static_cast<size_t>(b) * E + e];
+    for (int b = b0; b < b1; b += kU) {
+      int hv[kU];
+      float pv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const bool in = b + u < b1;
+        hv[u] = in ? blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
+        pv[u] = (in && blk_psum != nullptr) ? blk_psum[static_cast<size_t>(b + u) * E + e] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        c += hv[u];
+        if (b + u < b1) ps += pv[u];
+      }
     }
   }
   part_cnt[part][e] = c;
@@ -645,9 +658,15 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     // base[b][e] = offsets[e] + slots of e in blocks before b
     int pre = off_s[e];
     for (int p = 0; p < part; ++p) pre += part_cnt[p][e];
-    for (int b = b0; b < b1; ++b) {
-      blk_base[static_cast<size_t>(b) * E + e] = pre;
-      pre += blk_hist[static_cast<size_t>(b) * E + e];
+    for (int b = b0; b < b1; b += kU) {
+      int hv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) hv[u] = (b + u < b1) ? blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (b + u < b1) blk_base[static_cast<size_t>(b + u) * E + e] = pre;
+        pre += hv[u];
+      }
     }
   }
 }

@@ -210,6 +210,37 @@ def test_empty_batch():
     assert p["offsets"].tolist() == [0] * 9
 
 
+def test_permute_skips_out_of_range_ids():
+    """Slot ids outside [0, E) (only a caller of moe_permute can pass them):
+    token_slot -1, no grouped row, not counted; every other slot is grouped as
+    the stable sort by (expert, token) of the valid slots."""
+    cfg = SMALL["bf16_raw_k2_e40"]
+    H.say("[gpu] permute with out-of-range ids %s" % (cfg,))
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    r = H.run_oracle(cfg, inp)
+    idx = r["topk_idx"].copy()
+    rng = np.random.default_rng(5)
+    bad = rng.random(idx.shape) < 0.1
+    idx[bad] = rng.choice([-1, -7, cfg.E, cfg.E + 3], size=int(bad.sum()))
+    desc = moe.desc_of(cfg)
+    g = moe.permute(desc, torch.from_numpy(idx).cuda(), dev["h"])
+    torch.cuda.synchronize()
+    valid = ~bad
+    tt, jj = np.nonzero(valid)
+    ee = idx[tt, jj]
+    order = np.lexsort((tt, ee))  # by expert, then token
+    want_slot = np.full(idx.shape, -1, np.int64)
+    want_slot[tt[order], jj[order]] = np.arange(len(order))
+    counts = np.bincount(ee, minlength=cfg.E)
+    H.check_bits_equal("expert_offsets", H.to_np(g["offsets"]), np.concatenate([[0], np.cumsum(counts)]))
+    H.check_bits_equal("token_slot", H.to_np(g["token_slot"]), want_slot)
+    n = len(order)
+    H.check_bits_equal("slot_token", H.to_np(g["slot_token"])[:n], tt[order])
+    rows = torch.from_numpy(tt[order].astype(np.int64)).cuda()
+    assert torch.equal(g["h_perm"][:n].view(torch.int16), dev["h"][rows].view(torch.int16))
+
+
 FULL = ["micro", "skewed", "mixtral_prefill", "mixtral_decode", "switch_top1"]
 
 
