@@ -53,6 +53,18 @@ Function -> passage it follows -> what pins it (tests/test_oracle_pins.py):
                          a sort-based restatement of "first C in token order"
                          on small random routings; C >= T equals the dropless
                          layer; C = 0 gives y = 0.
+  moe_forward(bias_select_only=True)
+                      [LENSA] Step 4 (DeepSeek-V3 steers the load with a
+                      per-expert routing bias instead of the aux loss) and
+                      the summary (a routing bias keeps the load even): the
+                      bias enters the top-K choice only; softmax, gates and
+                      P use the unbiased logits (reading: the pages do not
+                      say what the gates see)
+                      -> zero bias equals the default path; the choice is the
+                         brute-force top-K of logits + bias; gates and P do
+                         not move with a bias that leaves the choice alone; a
+                         forcing bias picks its expert for every token with
+                         the unbiased gate ratio.
   param_counts        [CUR] "Parameters you hold..."; [LENSA] Steps 1 and 6
                       -> the printed 4.46M / 1.32M / 3.39x / 25.2x,
                          37.0B / 11.1B / 3.3x and 176M / 45.1B.
@@ -299,7 +311,7 @@ def drop_stats(counts: Sequence[int], C: int) -> Dict[str, float]:
 
 def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int,
                 act: int, gate: int, tokens: Optional[Sequence[int]] = None,
-                capacity: Optional[int] = None) -> Dict[str, np.ndarray]:
+                capacity: Optional[int] = None, bias_select_only: bool = False) -> Dict[str, np.ndarray]:
     """The whole layer. `inp` holds float32 arrays of the exact input values.
 
     Routing, grouping and the aux loss cover all T tokens. The expert FFNs and
@@ -310,12 +322,21 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
     slots contribute nothing; kept slots keep their gates; a token with every
     slot dropped has y = 0 (the layer adds nothing to its residual). Counts and
     the aux loss describe the router's choices, before any drop.
+
+    bias_select_only: the router bias b_r steers only which experts are chosen
+    ([LENSA] Step 4: a per-expert routing bias in place of the aux loss); the
+    probabilities, the gates and P come from the unbiased logits h W_r.
+    Otherwise b_r is part of the logits everywhere.
     """
     h32 = np.asarray(inp["h"], np.float32).reshape(T, d)
-    logits = router_logits_f32(h32, inp["W_r"], inp.get("b_r"))
+    logits = router_logits_f32(h32, inp["W_r"], inp.get("b_r"))  # the scores the choice is made on
+    if bias_select_only and inp.get("b_r") is not None:
+        gate_logits = router_logits_f32(h32, inp["W_r"], None)
+    else:
+        gate_logits = logits
     idx = select_topk(logits, K)
-    p = router_probs(logits)
-    g = gates(logits, idx, gate)
+    p = router_probs(gate_logits)
+    g = gates(gate_logits, idx, gate)
     counts = expert_counts(idx, E)
     offsets, slot_token, token_slot = stable_permutation(idx, E)
     aux = aux_loss(counts, p, K)
@@ -330,7 +351,8 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
         o = expert_ffn(h64[rows[sel_r]], e, inp, act)
         # y[t] += g[t,j] * E_e(h[t]); each token meets each expert at most once
         y[sel_r] += g[rows[sel_r], sel_j][:, None] * o
-    return {"logits": logits, "topk_idx": idx, "topk_gate": g, "probs": p, "counts": counts,
+    return {"logits": logits, "gate_logits": gate_logits, "topk_idx": idx, "topk_gate": g, "probs": p,
+            "counts": counts,
             "offsets": offsets, "slot_token": slot_token, "token_slot": token_slot,
             "token_slot_kept": np.where(keep, token_slot, -1).astype(np.int32), "keep": keep,
             "aux": aux, "y": y, "rows": rows}

@@ -452,10 +452,64 @@ def check_capacity_layer(seed=13):
     assert np.array_equal(cap["token_slot_kept"][keep], free["token_slot"][keep])
 
 
+def _bias_case(seed):
+    rng = np.random.default_rng(seed)
+    T, d, E, K, w = 40, 24, 6, 2, 8
+    inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+           "W_r": rng.standard_normal((d, E)).astype(np.float32), "b_r": None,
+           "W1": rng.standard_normal((E, w, d)) * 0.3, "W3": rng.standard_normal((E, w, d)) * 0.3,
+           "W2": rng.standard_normal((E, d, w)) * 0.3, "b1": None, "b2": None}
+    return rng, inp, (T, d, E, K)
+
+
+def check_bias_select_only(seed=21):
+    """Selection-only routing bias ([LENSA] Step 4, DeepSeek-V3's per-expert
+    routing bias): zero bias is the default path; the choice is the brute-force
+    top-K of logits + bias; gates and P are those of the unbiased logits, so a
+    bias that keeps the choice keeps them, and a forcing bias keeps the
+    unbiased gate ratio of the chosen pair."""
+    rng, inp, (T, d, E, K) = _bias_case(seed)
+    fwd = lambda b, sel: O.moe_forward({**inp, "b_r": b}, T, d, E, K, O.ACT_SWIGLU, O.GATE_RENORM,
+                                       bias_select_only=sel)
+    base = fwd(None, False)
+    r0 = fwd(np.zeros(E, np.float32), True)
+    for k in ("topk_idx", "topk_gate", "probs", "y", "counts"):
+        assert np.array_equal(r0[k], base[k]), k
+    assert r0["aux"] == base["aux"]
+    b = (rng.standard_normal(E) * 1.5).astype(np.float32)
+    r = fwd(b, True)
+    scores = base["logits"] + b[None, :]  # float32 addition, as the router does
+    for t in range(T):
+        best = max(itertools.combinations(range(E), K), key=lambda c: float(sum(scores[t, list(c)])))
+        assert sorted(best) == sorted(r["topk_idx"][t].tolist()), t
+        assert scores[t, r["topk_idx"][t, 0]] >= scores[t, r["topk_idx"][t, 1]]
+    # gates from the unbiased logits of the chosen pair; P unbiased
+    l = base["logits"].astype(np.float64)
+    i0, i1 = r["topk_idx"][:, 0], r["topk_idx"][:, 1]
+    ratio = r["topk_gate"][:, 0] / r["topk_gate"][:, 1]
+    assert np.allclose(ratio, np.exp(l[np.arange(T), i0] - l[np.arange(T), i1]), rtol=1e-12)
+    assert np.allclose(r["topk_gate"].sum(axis=1), 1.0, atol=1e-14)
+    assert np.array_equal(r["probs"], base["probs"])
+    f = r["counts"] / float(T * K)
+    assert abs(r["aux"] - E * float(np.sum(f * base["probs"].mean(axis=0)))) < 1e-12
+    # the same bias in the default mode moves the gates (the check above is not vacuous)
+    rd = fwd(b, False)
+    assert np.array_equal(rd["topk_idx"], r["topk_idx"])
+    assert not np.allclose(rd["topk_gate"], r["topk_gate"])
+    # a forcing bias: every token takes expert 3 first, gates still unbiased
+    bf = np.zeros(E, np.float32)
+    bf[3] = 1e4
+    rf = fwd(bf, True)
+    assert np.all(rf["topk_idx"][:, 0] == 3)
+    j1 = rf["topk_idx"][:, 1]
+    assert np.allclose(rf["topk_gate"][:, 0] / rf["topk_gate"][:, 1], np.exp(l[:, 3] - l[np.arange(T), j1]),
+                       rtol=1e-12)
+
+
 ALL_CHECKS = [check_router_logits_exact, check_router_logits_bound, check_topk_bruteforce,
               check_probs, check_gates_worked_example, check_gates_invariants,
               check_combine_worked_example, check_permutation_sorted, check_load_stats_page,
               check_aux_uniform_probs, check_aux_uniform_load, check_dense_reduction,
               check_soft_mixture_K_equals_E, check_forward_subset_consistency, check_param_counts,
               check_capacity_widget, check_capacity_order, check_capacity_slots_rounding,
-              check_capacity_layer]
+              check_capacity_layer, check_bias_select_only]

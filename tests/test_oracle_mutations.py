@@ -10,7 +10,7 @@ import oracle_pins
 from oracle import moe_oracle as O
 
 _orig = {name: getattr(O, name) for name in
-         ("router_logits_f32", "select_topk", "router_probs", "gates", "stable_permutation",
+         ("moe_forward", "router_logits_f32", "select_topk", "router_probs", "gates", "stable_permutation",
           "aux_loss", "gelu", "silu", "expert_ffn", "combine", "param_counts_micro",
           "param_counts_swiglu_model", "expert_counts", "capacity_keep", "capacity_slots", "drop_stats")}
 
@@ -57,6 +57,18 @@ def _logits_pairs_swapped(h, W, b):
     src = np.where(4 * partner < d, 4 * partner + k % 4, k)  # a group without partner stays
     return _orig["router_logits_f32"](np.ascontiguousarray(h[:, src]),
                                       np.ascontiguousarray(np.asarray(W, np.float32)[src, :]), b)
+
+
+def _forward_bias_everywhere(*a, bias_select_only=False, **kw):
+    # the selection-only flag ignored: gates and P see the bias too
+    return _orig["moe_forward"](*a, **kw)
+
+
+def _forward_bias_ignored(inp, *a, bias_select_only=False, **kw):
+    # the selection-only flag drops the bias altogether
+    if bias_select_only:
+        inp = {**inp, "b_r": None}
+    return _orig["moe_forward"](inp, *a, **kw)
 
 
 def _topk_high_index_wins(l, K):
@@ -170,6 +182,8 @@ MUTATIONS = {
     "router_drops_bias": ("router_logits_f32", _logits_no_bias),
     "router_reverse_k_order": ("router_logits_f32", _logits_reverse_k),
     "router_bias_first": ("router_logits_f32", _logits_bias_first),
+    "select_bias_reaches_gates": ("moe_forward", _forward_bias_everywhere),
+    "select_bias_ignored": ("moe_forward", _forward_bias_ignored),
     "router_single_chain": ("router_logits_f32", _logits_single_chain),
     "router_pairs_swapped": ("router_logits_f32", _logits_pairs_swapped),
     "topk_high_index_wins_ties": ("select_topk", _topk_high_index_wins),
