@@ -38,7 +38,7 @@
  * Tensor layouts (S = T*K routing slots, bpe = 4 for MOE_F32, 2 for MOE_BF16)
  *  h        [T][d]          dtype    token representations
  *  W_r      [d][E]          float32  router weight (always float32)
- *  b_r      [E]             float32  optional router bias, added to the logits
+ *  b_r      [E]             float32  optional router bias (see moe_bias_mode)
  *  W1, W3   [E][width][d]   dtype    row n of expert e = column n of the d x width
  *                                    matrix of the math (output-major: the reduction
  *                                    dimension d is contiguous)
@@ -88,7 +88,8 @@ typedef enum moe_status {
                                d or width above 2^20, T*K above 2^31 - 1, an operand
                                matrix (S x d, S x width or d x width) of more than
                                2^31 - 2^22 elements, an unknown act/gate/dtype, a
-                               misaligned pointer, or W3 missing for SwiGLU */
+                               misaligned pointer, an unknown bias_mode, or W3
+                               missing for SwiGLU */
   MOE_ERR_WORKSPACE = 4,    /* ws_bytes smaller than moe_workspace_size(), or ws misaligned */
   MOE_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
 } moe_status;
@@ -96,6 +97,12 @@ typedef enum moe_status {
 typedef enum moe_act { MOE_ACT_GELU = 0, MOE_ACT_SWIGLU = 1 } moe_act;
 typedef enum moe_gate { MOE_GATE_RENORM = 0, MOE_GATE_RAW = 1 } moe_gate;
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* What the router bias b_r acts on. MOE_BIAS_LOGITS: it is part of the logits
+ * (choice, softmax, gates, P). MOE_BIAS_SELECT: it steers only which experts
+ * are chosen (Lensa ML explainer, Step 4: DeepSeek-V3 keeps the load even with
+ * a per-expert routing bias instead of the aux loss); the softmax, the gates
+ * and P use the unbiased logits h . W_r. Without b_r both are the same. */
+typedef enum moe_bias_mode { MOE_BIAS_LOGITS = 0, MOE_BIAS_SELECT = 1 } moe_bias_mode;
 
 /* Shape of one layer, in the pages' terms: T tokens of width d, E experts of
  * width `width`, K chosen per token (Lensa ML Steps 1 and 3). */
@@ -118,6 +125,7 @@ typedef struct moe_desc {
                        the router's choices before any drop. Negative values
                        are MOE_ERR_SHAPE. moe_capacity_slots() gives C for a
                        capacity factor. */
+  int32_t bias_mode; /* moe_bias_mode; any other value is MOE_ERR_UNSUPPORTED */
 } moe_desc;
 
 /* Human-readable name of a moe_status value (static string, never NULL). */
@@ -139,7 +147,8 @@ int moe_workspace_size(const moe_desc* desc, size_t* bytes);
  * gates; Step 4: slot counts and the load-balance loss).
  * In:  h, W_r, b_r (nullable).
  * Out: topk_idx, topk_gate, expert_counts, prob_mean [E] (P_e, nullable),
- *      aux_loss [1] (nullable), logits [T][E] float32 (nullable).
+ *      aux_loss [1] (nullable), logits [T][E] float32 (nullable): the scores
+ *      the choice is made on, h . W_r + b_r (with either bias_mode).
  * Returns a moe_status. */
 int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
               int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,

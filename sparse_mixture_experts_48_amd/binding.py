@@ -29,7 +29,8 @@ KERNEL_IDS = {0: "route", 1: "finalize", 2: "hist", 3: "permute", 4: "gemm1", 5:
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int64), ("E", ctypes.c_int64),
                 ("K", ctypes.c_int64), ("width", ctypes.c_int64), ("act", ctypes.c_int32),
-                ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+                ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("bias_mode", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -82,10 +83,14 @@ def header_symbols() -> List[str]:
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
-def desc_of(cfg: W.LayerShape, T: Optional[int] = None, capacity: int = 0) -> MoeDesc:
-    """Descriptor of a layer shape; capacity = slots per expert (0: dropless)."""
+BIAS_LOGITS, BIAS_SELECT = 0, 1
+
+
+def desc_of(cfg: W.LayerShape, T: Optional[int] = None, capacity: int = 0, bias_mode: int = BIAS_LOGITS) -> MoeDesc:
+    """Descriptor of a layer shape; capacity = slots per expert (0: dropless);
+    bias_mode = what the router bias acts on (moe_bias_mode)."""
     return MoeDesc(cfg.T if T is None else T, cfg.d, cfg.E, cfg.K, cfg.width, cfg.act, cfg.gate, cfg.dtype,
-                   capacity)
+                   capacity, bias_mode)
 
 
 def capacity_slots(factor: float, T: int, K: int, E: int) -> int:

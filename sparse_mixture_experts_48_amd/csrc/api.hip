@@ -89,6 +89,7 @@ int check_desc(const moe_desc* d) {
   if (d->gate != MOE_GATE_RENORM && d->gate != MOE_GATE_RAW) return MOE_ERR_UNSUPPORTED;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->capacity < 0) return MOE_ERR_SHAPE;
+  if (d->bias_mode != MOE_BIAS_LOGITS && d->bias_mode != MOE_BIAS_SELECT) return MOE_ERR_UNSUPPORTED;
   if (d->T > kMaxInt / d->K || d->d > kMaxDim || d->width > kMaxDim) return MOE_ERR_UNSUPPORTED;
   const int64_t S = d->T * d->K;
   if (S > 0 && (S > kMaxElems / d->d || S > kMaxElems / d->width)) return MOE_ERR_UNSUPPORTED;
@@ -236,6 +237,7 @@ int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float
   moe::RouteArgs ra{h, W_r, b_r, static_cast<int>(d.T), static_cast<int>(d.d), static_cast<int>(d.E),
                     static_cast<int>(d.K), d.gate, topk_idx, topk_gate, logits,
                     at<int32_t>(ws, pl.blk_hist), at<float>(ws, pl.blk_psum)};
+  ra.bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, d.dtype == MOE_BF16, st));
   MOE_LAUNCH(MOE_K_FINALIZE, st,
              moe::launch_finalize(ra.blk_hist, ra.blk_psum, pl.rt.NB, ra.T, ra.E, ra.K, nullptr, expert_counts,
@@ -362,6 +364,7 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
 
   moe::RouteArgs ra{h, W_r, b_r, T, static_cast<int>(d.d), E, K, d.gate, topk_idx, topk_gate, nullptr,
                     blk_hist, blk_psum};
+  ra.bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
   MOE_LAUNCH(MOE_K_FINALIZE, st,
              moe::launch_finalize(blk_hist, blk_psum, pl.rt.NB, T, E, K, blk_base, counts, offsets, nullptr,

@@ -28,6 +28,7 @@ struct RouteArgs {
   float* logits;      // nullable
   int32_t* blk_hist;  // [NB][E]
   float* blk_psum;    // [NB][E]
+  int bias_select = 0;  // 1: br steers the choice only; softmax and gates use h . W_r
 };
 
 hipError_t launch_route(const RouteArgs& a, const RouteTiling& rt, bool bf16, hipStream_t st);

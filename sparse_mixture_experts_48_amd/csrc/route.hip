@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
     int T, int d, int E, int K, int gate_mode,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
-    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum) {
+    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, int bias_select) {
   constexpr int LE = EP / TE;             // expert lanes per chain
   constexpr int LG = 4 * LE;              // lanes per token group: chain-major, then expert lane
   constexpr int G = kRouteThreads / LG;   // token groups per block
@@ -256,7 +256,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   for (int i = 0; i < TPT; ++i) {
     const int t = t0 + tg + i * G;
     const bool tok_ok = t < T;  // uniform across the lanes of this token group
-    float l[TE];
+    // l: the score the choice is made on (logit + bias); lg: the logit of the
+    // softmax and the gates (l, or the unbiased logit when the bias only
+    // steers the choice)
+    float l[TE], lg[TE];
 #pragma unroll
     for (int q = 0; q < TE; ++q) {
       const int e = expert_of(q);
@@ -266,8 +269,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
       if (e < E) {
         l[q] = c0123;
         if (br != nullptr) l[q] = l[q] + br[e];
+        lg[q] = bias_select ? c0123 : l[q];
       } else {
         l[q] = -INFINITY;
+        lg[q] = -INFINITY;
       }
     }
     if (tok_ok && cj == 0 && logits_out != nullptr) {
@@ -282,37 +287,47 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
 #pragma unroll
     for (int q = 0; q < TE; ++q) taken[q] = false;
     int cidx[8];
-    float cval[8];
+    float cval[8], cg[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < K) {
-        float bv = -INFINITY;
+        float bv = -INFINITY, bg = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
         for (int q = 0; q < TE; ++q) {
           const int e = expert_of(q);
-          if (!taken[q] && e < E && better(l[q], e, bv, bi)) { bv = l[q]; bi = e; }
+          if (!taken[q] && e < E && better(l[q], e, bv, bi)) { bv = l[q]; bi = e; bg = lg[q]; }
         }
 #pragma unroll
         for (int off = 1; off < LE; off <<= 1) {
           const float ov = __shfl_xor(bv, off, LE);
           const int oi = __shfl_xor(bi, off, LE);
-          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+          const float og = __shfl_xor(bg, off, LE);
+          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; bg = og; }
         }
         cidx[j] = bi;
         cval[j] = bv;
+        cg[j] = bg;
 #pragma unroll
         for (int q = 0; q < TE; ++q)
           if (expert_of(q) == bi) taken[q] = true;
       }
     }
-    // softmax over all E (the largest logit is the first choice)
-    const float m = cval[0];
+    // softmax over all E (the largest lg is the first choice, unless the
+    // bias steers the choice)
+    float m = cval[0];
+    if (bias_select) {
+      m = lg[0];
+#pragma unroll
+      for (int q = 1; q < TE; ++q) m = fmaxf(m, lg[q]);
+#pragma unroll
+      for (int off = 1; off < LE; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, LE));
+    }
     float ex[TE];
     float s = 0.0f;
 #pragma unroll
     for (int q = 0; q < TE; ++q) {
-      ex[q] = (expert_of(q) < E) ? expf(l[q] - m) : 0.0f;
+      ex[q] = (expert_of(q) < E) ? expf(lg[q] - m) : 0.0f;
       s += ex[q];
     }
 #pragma unroll
@@ -327,7 +342,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < K) {
-          ec[j] = expf(cval[j] - m);
+          ec[j] = expf(cg[j] - m);
           se += ec[j];
         }
       }
@@ -364,7 +379,7 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
     const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
     int T, int d, int E, int K, int gate_mode,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
-    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum) {
+    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, int bias_select) {
   constexpr int KC = kNarrowKC;
   constexpr int NT = NW * 64;
   constexpr int WF4 = KC * EP / 4;         // float4 slots of a W_r chunk buffer
@@ -503,34 +518,46 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
   // lanes of inactive chains or experts hold +0 and are not used
   float part = acc + __shfl_xor(acc, EP);  // chains 0/1: c0 + c1; chains 2/3: c2 + c3
   part = part + __shfl_xor(part, 2 * EP);
-  // top-K by (logit descending, expert ascending), softmax, gates
+  // top-K by (score descending, expert ascending) on l = logit (+ bias);
+  // softmax and gates on lg, which is l, or the unbiased logit when the bias
+  // only steers the choice
   float l = -INFINITY;
+  float lg = -INFINITY;
   if (lane < E) {
     l = part;
     if (br != nullptr) l = l + br[lane];
+    lg = bias_select ? part : l;
   }
   if (tok_ok && logits_out != nullptr && lane < E) logits_out[static_cast<size_t>(t) * E + lane] = l;
   bool taken = false;
   int cidx[8];
-  float cval[8];
+  float cval[8], cg[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < K) {
       float bv = (!taken && lane < E) ? l : -INFINITY;
       int bi = (!taken && lane < E) ? lane : 0x7fffffff;
+      float bg = (!taken && lane < E) ? lg : -INFINITY;
 #pragma unroll
       for (int off = 1; off < EP; off <<= 1) {
         const float ov = __shfl_xor(bv, off, EP);
         const int oi = __shfl_xor(bi, off, EP);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        const float og = __shfl_xor(bg, off, EP);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; bg = og; }
       }
       cidx[j] = bi;
       cval[j] = bv;
+      cg[j] = bg;
       if (lane == bi) taken = true;
     }
   }
-  const float m = cval[0];
-  const float ex = (lane < E) ? expf(l - m) : 0.0f;
+  float m = cval[0];  // the largest lg: the first choice, unless the bias steers the choice
+  if (bias_select) {
+    m = lg;
+#pragma unroll
+    for (int off = 1; off < EP; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, EP));
+  }
+  const float ex = (lane < E) ? expf(lg - m) : 0.0f;
   float s = ex;
 #pragma unroll
   for (int off = 1; off < EP; off <<= 1) s += __shfl_xor(s, off, EP);
@@ -541,7 +568,7 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < K) {
-        ec[j] = expf(cval[j] - m);
+        ec[j] = expf(cg[j] - m);
         se += ec[j];
       }
     }
@@ -684,7 +711,7 @@ template <typename Tin, int EP, int TE, int TPT, int BK, int NS>
 hipError_t launch_route_wide(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
   hipLaunchKernelGGL((route_wide_kernel<Tin, EP, TE, TPT, BK, NS>), dim3(rt.NB), dim3(kRouteThreads), 0, st,
                      static_cast<const Tin*>(a.h), a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
-                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum);
+                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.bias_select);
   return hipGetLastError();
 }
 
@@ -692,7 +719,7 @@ template <typename Tin, int EP, int NW>
 hipError_t launch_route_narrow(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
   hipLaunchKernelGGL((route_narrow_kernel<Tin, EP, NW>), dim3(rt.NB), dim3(NW * 64), 0, st,
                      static_cast<const Tin*>(a.h), a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
-                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum);
+                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.bias_select);
   return hipGetLastError();
 }
 

@@ -44,9 +44,10 @@ def oracle_params(inp: Dict[str, Optional[torch.Tensor]]) -> Dict[str, object]:
     return p
 
 
-def run_oracle(cfg: W.LayerShape, inp, tokens: Optional[Sequence[int]] = None, capacity: Optional[int] = None):
+def run_oracle(cfg: W.LayerShape, inp, tokens: Optional[Sequence[int]] = None, capacity: Optional[int] = None,
+               bias_select_only: bool = False):
     return O.moe_forward(oracle_params(inp), cfg.T, cfg.d, cfg.E, cfg.K, cfg.act, cfg.gate, tokens=tokens,
-                         capacity=capacity)
+                         capacity=capacity, bias_select_only=bias_select_only)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -11,8 +11,8 @@ OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
 FAKE = 0x10000  # a 256-byte aligned, never dereferenced address
 
 
-def _d(T=64, d=128, E=8, K=2, w=512, act=1, gate=0, dtype=1, capacity=0):
-    return MoeDesc(T, d, E, K, w, act, gate, dtype, capacity)
+def _d(T=64, d=128, E=8, K=2, w=512, act=1, gate=0, dtype=1, capacity=0, bias_mode=0):
+    return MoeDesc(T, d, E, K, w, act, gate, dtype, capacity, bias_mode)
 
 
 def _ws(desc):
@@ -41,7 +41,8 @@ def test_status_strings():
     (dict(T=-1), SHAPE), (dict(d=0), SHAPE), (dict(w=0), SHAPE), (dict(E=0), SHAPE),
     (dict(K=0), SHAPE), (dict(K=9, E=8), SHAPE), (dict(E=65, K=2), UNSUP), (dict(E=64, K=9), UNSUP),
     (dict(d=100), UNSUP), (dict(w=1372), UNSUP), (dict(act=2), UNSUP), (dict(gate=5), UNSUP),
-    (dict(dtype=7), UNSUP), (dict(capacity=-1), SHAPE), (dict(capacity=5), OK), (dict(T=2 ** 30, K=2), UNSUP),
+    (dict(dtype=7), UNSUP), (dict(capacity=-1), SHAPE), (dict(capacity=5), OK),
+    (dict(bias_mode=1), OK), (dict(bias_mode=2), UNSUP), (dict(bias_mode=-1), UNSUP), (dict(T=2 ** 30, K=2), UNSUP),
     (dict(d=2 ** 20 + 8, w=8), UNSUP), (dict(w=2 ** 20 + 8, d=8), UNSUP), (dict(d=2 ** 20, w=8), OK),
     # operand matrices hold at most 2^31 - 2^22 elements: T*K*d = 2^31 - 2^22 exactly is the largest
     (dict(T=261632, d=4096, K=2, w=512), OK), (dict(T=261633, d=4096, K=2, w=512), UNSUP),

@@ -1,0 +1,98 @@
+"""Router bias that steers only the choice of experts (moe_bias_mode
+MOE_BIAS_SELECT; Lensa ML explainer "Mixture of Experts", Step 4: DeepSeek-V3
+keeps the load even with a per-expert routing bias instead of the aux loss).
+
+Against the CPU oracle on the same seeded inputs: the choice (top-K of logits +
+bias) and the scores it is made on bit for bit, counts exactly, gates from the
+unbiased logits within 1e-6, P and aux within 1e-5 relative, y within the layer
+tolerance. Both router layouts (one token per wave for small batches; token
+groups for large ones), renormalised and raw gates, K = 1..3, float32 and
+bfloat16; a forcing bias; and no bias at all, where both modes are the same.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import sparse_mixture_experts_48_amd as moe
+from sparse_mixture_experts_48_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - the CPU suite deselects these
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+L = W.LayerShape
+CASES = {
+    "narrow_e8_k2": L("sel_narrow", 16, 512, 8, 2, 1376, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 71),
+    "narrow_e16_k3": L("sel_narrow16", 200, 256, 16, 3, 264, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 72),
+    "wide_e8_k2": L("sel_wide8", 700, 256, 8, 2, 512, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 73),
+    "wide_e64_raw": L("sel_wide64", 300, 128, 64, 2, 256, W.ACT_GELU, W.GATE_RAW, W.DT_BF16, "zipf1.1", 74),
+    "wide_e40_k1": L("sel_k1", 517, 256, 40, 1, 344, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16, "zipf1.1", 75),
+    "f32_e12_k2": L("sel_f32", 97, 72, 12, 2, 136, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2", 76),
+}
+
+
+def _check(cfg, inp, dev):
+    r = H.run_oracle(cfg, inp, bias_select_only=True)
+    desc = moe.desc_of(cfg, bias_mode=moe.binding.BIAS_SELECT)
+    g = moe.route(desc, dev["h"], dev["W_r"], dev["b_r"], want_logits=True)
+    torch.cuda.synchronize()
+    H.check_logits_bits(H.to_np(g["logits"]), r["logits"])
+    H.check_bits_equal("topk_idx", H.to_np(g["topk_idx"]), r["topk_idx"])
+    H.check_bits_equal("expert_counts", H.to_np(g["counts"]), r["counts"])
+    gate_err = float(np.max(np.abs(H.to_np(g["topk_gate"]) - r["topk_gate"])))
+    assert gate_err <= H.GATE_ATOL, gate_err
+    P = r["probs"].mean(axis=0)
+    assert np.max(np.abs(H.to_np(g["prob_mean"]) - P)) <= H.PROB_RTOL * max(P.max(), 1e-30) + 1e-7
+    assert abs(float(H.to_np(g["aux"])[0]) - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0)
+    y, aux, counts = moe.forward(desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"],
+                                 dev["W2"], dev["b2"])
+    torch.cuda.synchronize()
+    H.check_bits_equal("expert_counts (forward)", H.to_np(counts), r["counts"])
+    assert abs(float(H.to_np(aux)[0]) - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0)
+    raw, net = H.layer_err(H.to_np(y), r["y"], cfg.dtype)
+    H.say("[gpu] %s y: max|d|/rms = %.4f (raw), %.4f (net of output rounding)" % (cfg.name, raw, net))
+    assert net <= H.Y_TOL[cfg.dtype], (raw, net)
+    return r
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_bias_select_only(name):
+    cfg = CASES[name]
+    H.say("[gpu] selection-only bias %s %s" % (name, cfg))
+    inp = W.make_inputs(cfg)
+    assert inp["b_r"] is not None
+    r = _check(cfg, inp, H.to_dev(inp))
+    # the same choice as with the bias in the logits, but other gates
+    r_logits = H.run_oracle(cfg, inp)
+    assert np.array_equal(r_logits["topk_idx"], r["topk_idx"])
+    assert not np.allclose(r_logits["topk_gate"], r["topk_gate"])
+
+
+@pytest.mark.parametrize("name", ["narrow_e8_k2", "wide_e64_raw"])
+def test_bias_select_forcing(name):
+    """A bias of 1e4 on one expert: every token chooses it first."""
+    cfg = CASES[name]
+    inp = W.make_inputs(cfg)
+    b = torch.zeros(cfg.E, dtype=torch.float32)
+    b[cfg.E // 2] = 1e4
+    inp["b_r"] = b
+    H.say("[gpu] forcing bias %s" % name)
+    r = _check(cfg, inp, H.to_dev(inp))
+    assert np.all(r["topk_idx"][:, 0] == cfg.E // 2)
+
+
+def test_bias_select_without_bias_is_default():
+    cfg = CASES["wide_e8_k2"]
+    inp = W.make_inputs(cfg)
+    inp["b_r"] = None
+    dev = H.to_dev(inp)
+    outs = []
+    for mode in (moe.binding.BIAS_LOGITS, moe.binding.BIAS_SELECT):
+        desc = moe.desc_of(cfg, bias_mode=mode)
+        y, aux, counts = moe.forward(desc, dev["h"], dev["W_r"], None, dev["W1"], dev["b1"], dev["W3"],
+                                     dev["W2"], dev["b2"])
+        torch.cuda.synchronize()
+        outs.append((y.view(torch.int16).clone(), aux.clone(), counts.clone()))
+    assert all(torch.equal(a, b) for a, b in zip(*outs))
