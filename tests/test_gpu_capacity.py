@@ -31,6 +31,11 @@ CASES = {
     "f32_k2": (L("cap_f32", 300, 128, 8, 2, 512, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2", 45), 0.6),
     "stream_k2": (L("cap_stream", 24, 264, 8, 2, 520, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 46), 0.5),
     "stream_k1": (L("cap_stream_k1", 31, 256, 8, 1, 128, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16, "zipf1.1", 47), 1.0),
+    # decode-sized batches with drops
+    "one_block_k2": (L("cap_one_block", 16, 256, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 48),
+                     0.5),
+    "one_block_f32_k3": (L("cap_one_block_f32", 12, 64, 6, 3, 64, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2",
+                           49), 0.75),
 }
 
 
