@@ -311,7 +311,8 @@ def drop_stats(counts: Sequence[int], C: int) -> Dict[str, float]:
 
 def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int,
                 act: int, gate: int, tokens: Optional[Sequence[int]] = None,
-                capacity: Optional[int] = None, bias_select_only: bool = False) -> Dict[str, np.ndarray]:
+                capacity: Optional[int] = None, bias_select_only: bool = False,
+                logits_f64: bool = False) -> Dict[str, np.ndarray]:
     """The whole layer. `inp` holds float32 arrays of the exact input values.
 
     Routing, grouping and the aux loss cover all T tokens. The expert FFNs and
@@ -327,11 +328,17 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
     ([LENSA] Step 4: a per-expert routing bias in place of the aux loss); the
     probabilities, the gates and P come from the unbiased logits h W_r.
     Otherwise b_r is part of the logits everywhere.
+
+    logits_f64: router logits in float64 instead of the float32 contract (a
+    smooth function of the inputs, for finite-difference checks of the
+    backward pass).
     """
     h32 = np.asarray(inp["h"], np.float32).reshape(T, d)
-    logits = router_logits_f32(h32, inp["W_r"], inp.get("b_r"))  # the scores the choice is made on
+    router = router_logits_f64 if logits_f64 else router_logits_f32
+    hin = np.asarray(inp["h"], np.float64).reshape(T, d) if logits_f64 else h32
+    logits = router(hin, inp["W_r"], inp.get("b_r"))  # the scores the choice is made on
     if bias_select_only and inp.get("b_r") is not None:
-        gate_logits = router_logits_f32(h32, inp["W_r"], None)
+        gate_logits = router(hin, inp["W_r"], None)
     else:
         gate_logits = logits
     idx = select_topk(logits, K)
@@ -343,7 +350,7 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
     keep = np.ones((T, K), dtype=bool) if capacity is None else capacity_keep(idx, E, capacity)
     rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     y = np.zeros((len(rows), d), dtype=np.float64)
-    h64 = h32.astype(np.float64)
+    h64 = np.asarray(inp["h"], np.float64).reshape(T, d) if logits_f64 else h32.astype(np.float64)
     for e in range(E):
         sel_r, sel_j = np.nonzero((idx[rows] == e) & keep[rows])
         if len(sel_r) == 0:
@@ -356,6 +363,122 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
             "offsets": offsets, "slot_token": slot_token, "token_slot": token_slot,
             "token_slot_kept": np.where(keep, token_slot, -1).astype(np.int32), "keep": keep,
             "aux": aux, "y": y, "rows": rows}
+
+
+# ----------------------------------------------------------------------------- backward
+
+def gelu_grad(z: np.ndarray) -> np.ndarray:
+    """d GELU / dz = Phi(z) + z phi(z) (exact GELU; Phi, phi: normal cdf and density)."""
+    return 0.5 * (1.0 + _erf(z / np.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d SiLU / dz = s (1 + z (1 - s)), s = sigmoid(z)."""
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def gate_logit_grad(gl: np.ndarray, idx: np.ndarray, g: np.ndarray, p: np.ndarray, dg: np.ndarray,
+                    gate: int, daux: float, f: np.ndarray) -> np.ndarray:
+    """d loss / d gate logits, given d loss / d gates (dg) and the aux weight.
+
+    The choice itself passes no gradient ([MTA] "The difficulties": top-k is
+    not differentiable, the router learns through the weights of the chosen
+    experts). RENORM: g = softmax over the chosen logits, so
+    dl[c_j] = g_j (dg_j - sum_i g_i dg_i). RAW: g_j = p[c_j] of the full
+    softmax ([LENSA] Step 3: the gradient reaches the router through p_i).
+    aux = E sum_e f_e P_e with P_e = mean_t p[t, e]; only P is differentiable
+    ([LENSA] Step 4), d aux / d p[t, e] = E f_e / T.
+    """
+    T, E = gl.shape
+    dl = np.zeros((T, E))
+    dp = np.zeros((T, E))
+    rows = np.arange(T)[:, None]
+    if gate == GATE_RENORM:
+        sdot = np.sum(g * dg, axis=1, keepdims=True)
+        np.add.at(dl, (np.broadcast_to(rows, idx.shape), idx), g * (dg - sdot))
+    elif gate == GATE_RAW:
+        np.add.at(dp, (np.broadcast_to(rows, idx.shape), idx), dg)
+    else:
+        raise ValueError(gate)
+    if daux != 0.0 and T > 0:
+        dp = dp + daux * E * np.asarray(f, np.float64)[None, :] / T
+    return dl + p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+
+
+def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int, act: int, gate: int,
+                 dy: np.ndarray, daux: float = 0.0, capacity: Optional[int] = None,
+                 bias_select_only: bool = False, logits_f64: bool = False) -> Dict[str, Optional[np.ndarray]]:
+    """Gradients of loss = sum(dy * y) + daux * aux with respect to every input
+    of the layer, float64 (reading: the expert choice and the capacity drops
+    are held fixed; see gate_logit_grad for the router).
+
+    Returns dh [T][d], dW_r [d][E], db_r [E] (zero when the bias only steers
+    the choice; None without a bias), and per expert dW1, dW3 (SwiGLU), dW2 in
+    the stored layouts and db1, db2 (GELU with biases; else None).
+    """
+    fwd = moe_forward(inp, T, d, E, K, act, gate, capacity=capacity, bias_select_only=bias_select_only,
+                      logits_f64=logits_f64)
+    idx, g, p, keep = fwd["topk_idx"], fwd["topk_gate"], fwd["probs"], fwd["keep"]
+    h = np.asarray(inp["h"], np.float64).reshape(T, d)
+    dy = np.asarray(dy, np.float64).reshape(T, d)
+    W1 = [np.asarray(inp["W1"][e], np.float64) for e in range(E)]
+    W2 = [np.asarray(inp["W2"][e], np.float64) for e in range(E)]
+    W3 = [np.asarray(inp["W3"][e], np.float64) for e in range(E)] if act == ACT_SWIGLU else None
+    b1 = inp.get("b1") if act == ACT_GELU else None
+    b2 = inp.get("b2") if act == ACT_GELU else None
+    out = {"dh": np.zeros((T, d)), "dW1": np.zeros((E,) + W1[0].shape), "dW2": np.zeros((E,) + W2[0].shape),
+           "dW3": None if W3 is None else np.zeros((E,) + W3[0].shape),
+           "db1": None if b1 is None else np.zeros((E, W1[0].shape[0])),
+           "db2": None if b2 is None else np.zeros((E, d))}
+    dg = np.zeros((T, K))
+    for e in range(E):
+        st, sj = np.nonzero((idx == e) & keep)
+        if len(st) == 0:
+            continue
+        x = h[st]
+        if act == ACT_GELU:
+            z = x @ W1[e].T
+            if b1 is not None:
+                z = z + np.asarray(b1[e], np.float64)
+            a = gelu(z)
+        else:
+            z1, z3 = x @ W1[e].T, x @ W3[e].T
+            a = silu(z1) * z3
+        o = a @ W2[e].T
+        if b2 is not None:
+            o = o + np.asarray(b2[e], np.float64)
+        do = g[st, sj][:, None] * dy[st]           # y[t] = sum_j g[t, j] o_j
+        dg[st, sj] = np.sum(dy[st] * o, axis=1)
+        out["dW2"][e] = do.T @ a
+        if b2 is not None:
+            out["db2"][e] = do.sum(axis=0)
+        da = do @ W2[e]
+        if act == ACT_GELU:
+            dz = da * gelu_grad(z)
+            out["dW1"][e] = dz.T @ x
+            if b1 is not None:
+                out["db1"][e] = dz.sum(axis=0)
+            dx = dz @ W1[e]
+        else:
+            dz1 = da * z3 * silu_grad(z1)
+            dz3 = da * silu(z1)
+            out["dW1"][e] = dz1.T @ x
+            out["dW3"][e] = dz3.T @ x
+            dx = dz1 @ W1[e] + dz3 @ W3[e]
+        out["dh"][st] += dx                          # a token meets an expert at most once
+    f = fwd["counts"] / float(max(T * K, 1))
+    dl = gate_logit_grad(fwd["gate_logits"].astype(np.float64), idx, g, p, dg, gate, daux, f)
+    W_r = np.asarray(inp["W_r"], np.float64)
+    out["dh"] += dl @ W_r.T                          # gate logits = h W_r (+ b_r)
+    out["dW_r"] = h.T @ dl
+    if inp.get("b_r") is None:
+        out["db_r"] = None
+    else:
+        out["db_r"] = np.zeros(E) if bias_select_only else dl.sum(axis=0)
+    out["dgates"] = dg
+    out["dlogits"] = dl
+    return out
 
 
 # ----------------------------------------------------------------------------- closed forms

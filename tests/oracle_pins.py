@@ -506,10 +506,100 @@ def check_bias_select_only(seed=21):
                        rtol=1e-12)
 
 
+def _bw_case(seed, T, d, E, K, w, act, bias=True, ffn_bias=False):
+    rng = np.random.default_rng(seed)
+    inp = {"h": rng.standard_normal((T, d)), "W_r": rng.standard_normal((d, E)),
+           "b_r": rng.standard_normal(E) if bias else None,
+           "W1": rng.standard_normal((E, w, d)) * 0.4, "W2": rng.standard_normal((E, d, w)) * 0.4,
+           "W3": rng.standard_normal((E, w, d)) * 0.4 if act == O.ACT_SWIGLU else None,
+           "b1": rng.standard_normal((E, w)) * 0.3 if ffn_bias else None,
+           "b2": rng.standard_normal((E, d)) * 0.3 if ffn_bias else None}
+    return rng, inp
+
+
+def _fd_backward(seed, T, d, E, K, w, act, gate, daux, n_probe=5, eps=1e-6, bias=True, ffn_bias=False, **kw):
+    rng, inp = _bw_case(seed, T, d, E, K, w, act, bias, ffn_bias)
+    dy = rng.standard_normal((T, d))
+
+    def loss(x):
+        r = O.moe_forward(x, T, d, E, K, act, gate, logits_f64=True, **kw)
+        return float(np.sum(dy * r["y"]) + daux * r["aux"])
+
+    # the expert choice must not flip inside +-eps: keep clear top-K margins
+    l = O.router_logits_f64(inp["h"], inp["W_r"], inp["b_r"])
+    srt = np.sort(l, axis=1)[:, ::-1]
+    assert K == E or np.min(srt[:, K - 1] - srt[:, K]) > 1e-3
+    g = O.moe_backward(inp, T, d, E, K, act, gate, dy, daux=daux, logits_f64=True, **kw)
+    for pname, gname in (("h", "dh"), ("W_r", "dW_r"), ("b_r", "db_r"), ("W1", "dW1"), ("W3", "dW3"),
+                         ("W2", "dW2"), ("b1", "db1"), ("b2", "db2")):
+        if inp[pname] is None:
+            assert g[gname] is None, gname
+            continue
+        base = np.asarray(inp[pname], np.float64)
+        for _ in range(n_probe):
+            i = tuple(int(rng.integers(0, n)) for n in base.shape)
+            up, dn = base.copy(), base.copy()
+            up[i] += eps
+            dn[i] -= eps
+            fd = (loss({**inp, pname: up}) - loss({**inp, pname: dn})) / (2 * eps)
+            an = float(g[gname][i])
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gname, i, fd, an)
+    return g
+
+
+def check_backward_fd_swiglu_renorm(seed=31):
+    """Backward (reading: choice held fixed; gradient through the gates and
+    through P of the aux loss) against central differences of the float64
+    layer: SwiGLU, renormalised top-2, router bias, aux weight 0.7."""
+    _fd_backward(seed, T=12, d=10, E=4, K=2, w=6, act=O.ACT_SWIGLU, gate=O.GATE_RENORM, daux=0.7)
+
+
+def check_backward_fd_gelu_raw_capacity(seed=32):
+    """GELU with biases, raw top-2 gates, a capacity that drops slots and a
+    selection-only bias (whose gradient is 0)."""
+    g = _fd_backward(seed, T=14, d=8, E=5, K=2, w=7, act=O.ACT_GELU, gate=O.GATE_RAW, daux=0.3, ffn_bias=True,
+                     capacity=3, bias_select_only=True)
+    assert not g["db_r"].any()
+
+
+def check_backward_fd_switch_top1(seed=33):
+    """Switch top-1 (raw p_i gate) with the aux loss, no router bias."""
+    _fd_backward(seed, T=16, d=8, E=3, K=1, w=6, act=O.ACT_SWIGLU, gate=O.GATE_RAW, daux=1.0, bias=False)
+
+
+def check_backward_dense_reduction(seed=34):
+    """E = K = 1: the gate is 1 and aux is constant, so the layer is one dense
+    FFN; its gradients equal torch autograd of that FFN in float64, and the
+    router gets none."""
+    T, d, w = 9, 6, 5
+    for act in (O.ACT_SWIGLU, O.ACT_GELU):
+        rng, inp = _bw_case(seed, T, d, 1, 1, w, act, bias=True, ffn_bias=(act == O.ACT_GELU))
+        dy = rng.standard_normal((T, d))
+        g = O.moe_backward(inp, T, d, 1, 1, act, O.GATE_RENORM, dy, daux=0.5)
+        x = torch.tensor(inp["h"], requires_grad=True)
+        W1 = torch.tensor(inp["W1"][0], requires_grad=True)
+        W2 = torch.tensor(inp["W2"][0], requires_grad=True)
+        if act == O.ACT_SWIGLU:
+            W3 = torch.tensor(inp["W3"][0], requires_grad=True)
+            y = (torch.nn.functional.silu(x @ W1.T) * (x @ W3.T)) @ W2.T
+            ref_params = {"dW1": W1, "dW2": W2, "dW3": W3}
+        else:
+            b1 = torch.tensor(inp["b1"][0], requires_grad=True)
+            b2 = torch.tensor(inp["b2"][0], requires_grad=True)
+            y = torch.nn.functional.gelu(x @ W1.T + b1) @ W2.T + b2
+            ref_params = {"dW1": W1, "dW2": W2, "db1": b1, "db2": b2}
+        (y * torch.tensor(dy)).sum().backward()
+        assert np.allclose(g["dh"], x.grad.numpy(), rtol=1e-12, atol=1e-12)
+        for k, t in ref_params.items():
+            assert np.allclose(g[k][0], t.grad.numpy(), rtol=1e-12, atol=1e-12), k
+        assert not g["dW_r"].any() and not g["db_r"].any()
+
+
 ALL_CHECKS = [check_router_logits_exact, check_router_logits_bound, check_topk_bruteforce,
               check_probs, check_gates_worked_example, check_gates_invariants,
               check_combine_worked_example, check_permutation_sorted, check_load_stats_page,
               check_aux_uniform_probs, check_aux_uniform_load, check_dense_reduction,
               check_soft_mixture_K_equals_E, check_forward_subset_consistency, check_param_counts,
               check_capacity_widget, check_capacity_order, check_capacity_slots_rounding,
-              check_capacity_layer, check_bias_select_only]
+              check_capacity_layer, check_bias_select_only, check_backward_fd_swiglu_renorm,
+              check_backward_fd_gelu_raw_capacity, check_backward_fd_switch_top1, check_backward_dense_reduction]

@@ -10,7 +10,7 @@ import oracle_pins
 from oracle import moe_oracle as O
 
 _orig = {name: getattr(O, name) for name in
-         ("moe_forward", "router_logits_f32", "select_topk", "router_probs", "gates", "stable_permutation",
+         ("moe_forward", "gelu_grad", "silu_grad", "gate_logit_grad", "router_logits_f32", "select_topk", "router_probs", "gates", "stable_permutation",
           "aux_loss", "gelu", "silu", "expert_ffn", "combine", "param_counts_micro",
           "param_counts_swiglu_model", "expert_counts", "capacity_keep", "capacity_slots", "drop_stats")}
 
@@ -69,6 +69,30 @@ def _forward_bias_ignored(inp, *a, bias_select_only=False, **kw):
     if bias_select_only:
         inp = {**inp, "b_r": None}
     return _orig["moe_forward"](inp, *a, **kw)
+
+
+def _silu_grad_sigmoid_only(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _gelu_grad_cdf_only(z):
+    return 0.5 * (1.0 + O._erf(z / np.sqrt(2.0)))
+
+
+def _gate_grad_no_centering(gl, idx, g, p, dg, gate, daux, f):
+    # renormalised gates: g * dg instead of g * (dg - sum g dg)
+    out = _orig["gate_logit_grad"](gl, idx, g, p, dg, gate, daux, f)
+    if gate == O.GATE_RENORM:
+        T = gl.shape[0]
+        fix = np.zeros_like(out)
+        sdot = np.sum(g * dg, axis=1, keepdims=True)
+        np.add.at(fix, (np.broadcast_to(np.arange(T)[:, None], idx.shape), idx), g * sdot)
+        out = out + fix
+    return out
+
+
+def _gate_grad_aux_without_E(gl, idx, g, p, dg, gate, daux, f):
+    return _orig["gate_logit_grad"](gl, idx, g, p, dg, gate, daux / gl.shape[1], f)
 
 
 def _topk_high_index_wins(l, K):
@@ -184,6 +208,10 @@ MUTATIONS = {
     "router_bias_first": ("router_logits_f32", _logits_bias_first),
     "select_bias_reaches_gates": ("moe_forward", _forward_bias_everywhere),
     "select_bias_ignored": ("moe_forward", _forward_bias_ignored),
+    "backward_silu_grad_sigmoid_only": ("silu_grad", _silu_grad_sigmoid_only),
+    "backward_gelu_grad_cdf_only": ("gelu_grad", _gelu_grad_cdf_only),
+    "backward_renorm_not_centred": ("gate_logit_grad", _gate_grad_no_centering),
+    "backward_aux_without_E": ("gate_logit_grad", _gate_grad_aux_without_E),
     "router_single_chain": ("router_logits_f32", _logits_single_chain),
     "router_pairs_swapped": ("router_logits_f32", _logits_pairs_swapped),
     "topk_high_index_wins_ties": ("select_topk", _topk_high_index_wins),
