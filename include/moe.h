@@ -198,6 +198,35 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
                 const void* b2, void* y, float* aux_loss, int32_t* expert_counts,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of workspace moe_backward needs for this layer shape (bfloat16 layers
+ * only: MOE_ERR_UNSUPPORTED otherwise). Host-only; enqueues nothing. */
+int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes);
+
+/* Backward pass of the layer: gradients of loss = sum(dy * y) + daux * aux
+ * with respect to every input, for bfloat16 layers. The gradient reaches the
+ * router only through the gate weights of the chosen experts (maptheai.com
+ * "Mixture of Experts", "The difficulties": the top-k choice is not
+ * differentiable), through p_i for raw gates (Lensa ML Step 3), and through
+ * P of the aux loss, whose f is a count (Step 4: only P_i is
+ * differentiable); the choice and the capacity drops are held fixed, and a
+ * selection-only bias gets a zero gradient. The forward pass is recomputed
+ * from the inputs (same routing, bit for bit).
+ * In:  the forward's inputs (h, W_r, b_r, W1, b1, W3, W2, b2), dy [T][d]
+ *      dtype, daux (finite; the weight of aux in the loss).
+ * Out: dh [T][d] dtype; dW_r [d][E], db_r [E] (nullable), dW1 [E][width][d],
+ *      db1 [E][width] (nullable, GELU only), dW3 [E][width][d] (SwiGLU),
+ *      dW2 [E][d][width], db2 [E][d] (nullable, GELU only), all float32.
+ *      With T = 0 every gradient is zero.
+ * Sums over tokens and slots run in a fixed order: results are bitwise
+ * reproducible. Returns a moe_status (MOE_ERR_UNSUPPORTED for float32 layers,
+ * bias gradients of SwiGLU layers, or transposed operands past the 32-bit
+ * offset range; MOE_ERR_SHAPE for a non-finite daux). */
+int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
+                 const void* W1, const void* b1, const void* W3, const void* W2, const void* b2,
+                 const void* dy, float daux, void* dh, float* dW_r, float* db_r, float* dW1,
+                 float* db1, float* dW3, float* dW2, float* db2, void* ws, size_t ws_bytes,
+                 void* stream);
+
 /* Instrumentation (not part of the layer). While enabled, every kernel the
  * library launches is bracketed by two hipEvents recorded on its launch
  * stream, for up to `capacity` launches (later launches are not traced).
@@ -207,7 +236,9 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
  * buffer; moe_trace_disable frees the events. Not thread-safe. */
 typedef enum moe_kernel_id {
   MOE_K_ROUTE = 0, MOE_K_FINALIZE = 1, MOE_K_HIST = 2, MOE_K_PERMUTE = 3,
-  MOE_K_GEMM1 = 4, MOE_K_GEMM2 = 5, MOE_K_COMBINE = 6, MOE_K_ZERO = 7
+  MOE_K_GEMM1 = 4, MOE_K_GEMM2 = 5, MOE_K_COMBINE = 6, MOE_K_ZERO = 7,
+  MOE_K_BWD = 8,   /* backward pass: elementwise, transpose and reduction kernels */
+  MOE_K_WGRAD = 9  /* backward pass: weight-gradient GEMMs */
 } moe_kernel_id;
 int moe_trace_enable(int capacity);
 int moe_trace_read(int32_t* kernel_id, float* ms, int max, int* n);

@@ -408,7 +408,8 @@ def gate_logit_grad(gl: np.ndarray, idx: np.ndarray, g: np.ndarray, p: np.ndarra
 
 def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int, act: int, gate: int,
                  dy: np.ndarray, daux: float = 0.0, capacity: Optional[int] = None,
-                 bias_select_only: bool = False, logits_f64: bool = False) -> Dict[str, Optional[np.ndarray]]:
+                 bias_select_only: bool = False, logits_f64: bool = False,
+                 with_scales: bool = False) -> Dict[str, Optional[np.ndarray]]:
     """Gradients of loss = sum(dy * y) + daux * aux with respect to every input
     of the layer, float64 (reading: the expert choice and the capacity drops
     are held fixed; see gate_logit_grad for the router).
@@ -416,6 +417,10 @@ def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K
     Returns dh [T][d], dW_r [d][E], db_r [E] (zero when the bias only steers
     the choice; None without a bias), and per expert dW1, dW3 (SwiGLU), dW2 in
     the stored layouts and db1, db2 (GELU with biases; else None).
+
+    with_scales: also "scale", the same sums taken over the absolute values of
+    their terms (|do|^T |a| for dW2, and so on): the size against which the
+    rounding error of an implementation's sum is judged.
     """
     fwd = moe_forward(inp, T, d, E, K, act, gate, capacity=capacity, bias_select_only=bias_select_only,
                       logits_f64=logits_f64)
@@ -432,6 +437,7 @@ def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K
            "db1": None if b1 is None else np.zeros((E, W1[0].shape[0])),
            "db2": None if b2 is None else np.zeros((E, d))}
     dg = np.zeros((T, K))
+    sc = {k: (None if v is None else np.zeros_like(v)) for k, v in out.items()}
     for e in range(E):
         st, sj = np.nonzero((idx == e) & keep)
         if len(st) == 0:
@@ -467,6 +473,19 @@ def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K
             out["dW3"][e] = dz3.T @ x
             dx = dz1 @ W1[e] + dz3 @ W3[e]
         out["dh"][st] += dx                          # a token meets an expert at most once
+        if with_scales:
+            sc["dW2"][e] = np.abs(do).T @ np.abs(a)
+            if b2 is not None:
+                sc["db2"][e] = np.abs(do).sum(axis=0)
+            if act == ACT_GELU:
+                sc["dW1"][e] = np.abs(dz).T @ np.abs(x)
+                if b1 is not None:
+                    sc["db1"][e] = np.abs(dz).sum(axis=0)
+                sc["dh"][st] += np.abs(dz) @ np.abs(W1[e])
+            else:
+                sc["dW1"][e] = np.abs(dz1).T @ np.abs(x)
+                sc["dW3"][e] = np.abs(dz3).T @ np.abs(x)
+                sc["dh"][st] += np.abs(dz1) @ np.abs(W1[e]) + np.abs(dz3) @ np.abs(W3[e])
     f = fwd["counts"] / float(max(T * K, 1))
     dl = gate_logit_grad(fwd["gate_logits"].astype(np.float64), idx, g, p, dg, gate, daux, f)
     W_r = np.asarray(inp["W_r"], np.float64)
@@ -478,6 +497,11 @@ def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K
         out["db_r"] = np.zeros(E) if bias_select_only else dl.sum(axis=0)
     out["dgates"] = dg
     out["dlogits"] = dl
+    if with_scales:
+        sc["dh"] += np.abs(dl) @ np.abs(W_r).T
+        sc["dW_r"] = np.abs(h).T @ np.abs(dl)
+        sc["db_r"] = None if out["db_r"] is None else np.abs(dl).sum(axis=0)
+        out["scale"] = sc
     return out
 
 

@@ -5,5 +5,6 @@ include/moe.h); this package holds its ctypes binding, the build script and the
 seeded synthetic workloads.
 """
 from . import workloads  # noqa: F401
-from .binding import (MoeDesc, MoeError, MoELayer, Trace, capacity_slots, combine, desc_of, expert_ffn,  # noqa: F401
-                      forward, header_symbols, lib, permute, route, workspace, workspace_size)
+from .binding import (MoeDesc, MoeError, MoELayer, Trace, backward, backward_workspace, capacity_slots,  # noqa: F401
+                      combine, desc_of, expert_ffn, forward, header_symbols, lib, permute, route, workspace,
+                      workspace_size)

@@ -23,7 +23,7 @@ MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
                 4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
 KERNEL_IDS = {0: "route", 1: "finalize", 2: "hist", 3: "permute", 4: "gemm1", 5: "gemm2",
-              6: "combine", 7: "zero"}
+              6: "combine", 7: "zero", 8: "backward", 9: "wgrad"}
 
 
 class MoeDesc(ctypes.Structure):
@@ -51,6 +51,9 @@ _SIGS = {
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]),
     "moe_capacity_slots": (ctypes.c_int, [ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.POINTER(ctypes.c_int32)]),
+    "moe_backward_workspace_size": (ctypes.c_int, [ctypes.POINTER(MoeDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_backward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 9 + [ctypes.c_float] + [_vp] * 8
+                     + [_vp, ctypes.c_size_t, _vp]),
     "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_trace_read": (ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
     "moe_trace_disable": (ctypes.c_int, []),
@@ -189,6 +192,35 @@ def forward(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, ws=None, y=None, aux
         ctypes.byref(desc), _ptr(h), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2), _ptr(b2),
         _ptr(y), _ptr(aux), _ptr(counts), _ptr(ws), ws.numel(), _stream()))
     return y, aux, counts
+
+
+def backward_workspace(desc: MoeDesc, device="cuda") -> torch.Tensor:
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size", lib().moe_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return torch.empty(max(n.value, 256), dtype=torch.uint8, device=device)
+
+
+def backward(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, dy, daux: float = 0.0, ws=None,
+             bias_grads: bool = True) -> Dict[str, Optional[torch.Tensor]]:
+    """Gradients of sum(dy * y) + daux * aux (moe_backward); float32 except dh."""
+    dev = h.device
+    E, d, w = desc.E, desc.d, desc.width
+    f32 = dict(dtype=torch.float32, device=dev)
+    swiglu = desc.act == W.ACT_SWIGLU
+    out = {"dh": torch.empty((desc.T, d), dtype=h.dtype, device=dev),
+           "dW_r": torch.empty((d, E), **f32),
+           "db_r": torch.empty(E, **f32) if bias_grads and b_r is not None else None,
+           "dW1": torch.empty((E, w, d), **f32),
+           "db1": torch.empty((E, w), **f32) if bias_grads and not swiglu and b1 is not None else None,
+           "dW3": torch.empty((E, w, d), **f32) if swiglu else None,
+           "dW2": torch.empty((E, d, w), **f32),
+           "db2": torch.empty((E, d), **f32) if bias_grads and not swiglu and b2 is not None else None}
+    ws = backward_workspace(desc, dev) if ws is None else ws
+    _check("moe_backward", lib().moe_backward(
+        ctypes.byref(desc), _ptr(h), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2), _ptr(b2),
+        _ptr(dy), float(daux), _ptr(out["dh"]), _ptr(out["dW_r"]), _ptr(out["db_r"]), _ptr(out["dW1"]),
+        _ptr(out["db1"]), _ptr(out["dW3"]), _ptr(out["dW2"]), _ptr(out["db2"]), _ptr(ws), ws.numel(), _stream()))
+    return out
 
 
 class MoELayer:

@@ -78,6 +78,77 @@ Plan make_plan(const moe_desc& d) {
   return p;
 }
 
+// Workspace of moe_backward (bfloat16 layers). Zw = width of the first GEMM's
+// pre-activations (2 width for SwiGLU); ldk = row length of the transposed
+// per-slot operands: every expert's slots padded to a multiple of 64.
+struct BwdPlan {
+  RouteTiling rt;
+  int64_t S, Zw, ldk;
+  int nwr;
+  size_t blk_hist, blk_psum, blk_base, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux, logits;
+  size_t z, a, o, dgate, dO, dA, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
+  size_t total;
+};
+
+BwdPlan make_bwd_plan(const moe_desc& d) {
+  BwdPlan p{};
+  p.rt = moe::route_tiling(d.T, d.E);
+  p.S = d.T * d.K;
+  p.Zw = d.act == MOE_ACT_SWIGLU ? 2 * d.width : d.width;
+  p.ldk = 64 * ((p.S + 63) / 64 + d.E);
+  p.nwr = moe::dwr_chunks(static_cast<int>(d.T));
+  const size_t S = static_cast<size_t>(p.S), nbe = static_cast<size_t>(p.rt.NB) * d.E;
+  const size_t dd = static_cast<size_t>(d.d), w = static_cast<size_t>(d.width), Zw = static_cast<size_t>(p.Zw);
+  const size_t E = static_cast<size_t>(d.E), ldk = static_cast<size_t>(p.ldk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  p.blk_hist = take(nbe * 4);
+  p.blk_psum = take(nbe * 4);
+  p.blk_base = take(nbe * 4);
+  p.topk_idx = take(S * 4);
+  p.topk_gate = take(S * 4);
+  p.token_slot = take(S * 4);
+  p.slot_token = take(S * 4);
+  p.counts = take(E * 4);
+  p.offsets = take((E + 1) * 4);
+  p.aux = take(4);
+  p.logits = take(static_cast<size_t>(d.T) * E * 4);
+  p.z = take(S * Zw * 2);
+  p.a = take(S * w * 2);
+  p.o = take(S * dd * 4);
+  p.dgate = take(S * 4);
+  p.dO = take(S * dd * 2);
+  p.dA = take(S * w * 4);
+  p.dZ = take(S * Zw * 2);
+  p.dX = take(S * dd * 4);
+  p.kofs = take((E + 1) * 4);
+  p.xT = take(dd * ldk * 2);
+  p.aT = take(w * ldk * 2);
+  p.dOT = take(dd * ldk * 2);
+  p.dZT = take(Zw * ldk * 2);
+  p.W2T = take(E * w * dd * 2);
+  p.W13T = take(E * dd * Zw * 2);
+  p.dl = take(static_cast<size_t>(d.T) * E * 4);
+  p.wr_part = take(static_cast<size_t>(p.nwr) * dd * E * 4);
+  p.total = off;
+  return p;
+}
+
+// Shapes moe_backward supports beyond check_desc: bfloat16, and every
+// transposed or widened operand within the 32-bit offset range of the GEMMs.
+int check_bwd_desc(const moe_desc& d) {
+  if (d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int64_t S = d.T * d.K, Zw = d.act == MOE_ACT_SWIGLU ? 2 * d.width : d.width;
+  const int64_t ldk = 64 * ((S + 63) / 64 + d.E);
+  if (S > 0 && S > kMaxElems / Zw) return MOE_ERR_UNSUPPORTED;
+  if (ldk > kMaxElems / Zw || ldk > kMaxElems / d.d || d.d > kMaxElems / Zw) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 // Rows an expert processes at most: its capacity, or every row when dropless.
 int cap_of(const moe_desc& d) { return d.capacity > 0 ? d.capacity : INT_MAX; }
 
@@ -190,6 +261,8 @@ const char* moe_kernel_name(int kernel_id) {
     case MOE_K_GEMM2: return "gemm2";
     case MOE_K_COMBINE: return "combine";
     case MOE_K_ZERO: return "zero";
+    case MOE_K_BWD: return "backward";
+    case MOE_K_WGRAD: return "wgrad";
     default: return "unknown";
   }
 }
@@ -400,6 +473,144 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
   if (!f.fused_y) {
     MOE_LAUNCH(MOE_K_COMBINE, st, moe::launch_combine(f.o_perm, token_slot, topk_gate, T, f.d, K, bf16, y, st));
   }
+  return MOE_OK;
+}
+
+int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes) {
+  MOE_CHECK(check_desc(desc));
+  MOE_CHECK(check_bwd_desc(*desc));
+  if (bytes == nullptr) return MOE_ERR_NULL;
+  *bytes = make_bwd_plan(*desc).total;
+  return MOE_OK;
+}
+
+int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, const void* W1,
+                 const void* b1, const void* W3, const void* W2, const void* b2, const void* dy, float daux,
+                 void* dh, float* dW_r, float* db_r, float* dW1, float* db1, float* dW3, float* dW2, float* db2,
+                 void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_desc(desc));
+  const moe_desc& d = *desc;
+  MOE_CHECK(check_bwd_desc(d));
+  const bool any = d.T > 0;
+  const bool swiglu = d.act == MOE_ACT_SWIGLU;
+  MOE_CHECK(check_ptr(h, any));
+  MOE_CHECK(check_ptr(W_r, true));
+  MOE_CHECK(check_ptr(b_r, false));
+  MOE_CHECK(check_experts(d, W1, b1, W3, W2, b2));
+  MOE_CHECK(check_ptr(dy, any));
+  MOE_CHECK(check_ptr(dh, any));
+  MOE_CHECK(check_ptr(dW_r, true));
+  MOE_CHECK(check_ptr(db_r, false));
+  MOE_CHECK(check_ptr(dW1, true));
+  MOE_CHECK(check_ptr(dW2, true));
+  MOE_CHECK(check_ptr(db1, false));
+  MOE_CHECK(check_ptr(db2, false));
+  if (swiglu) MOE_CHECK(check_ptr(dW3, true));
+  if (swiglu && (db1 != nullptr || db2 != nullptr || b1 != nullptr || b2 != nullptr)) return MOE_ERR_UNSUPPORTED;
+  if (!std::isfinite(daux)) return MOE_ERR_SHAPE;
+  const BwdPlan pl = make_bwd_plan(d);
+  if (ws_bytes < pl.total || ws == nullptr || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t E = static_cast<size_t>(d.E), dd = static_cast<size_t>(d.d), w = static_cast<size_t>(d.width);
+  if (!any) {  // no tokens: every gradient is zero
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(dW_r, dd * E * 4, st));
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(db_r, E * 4, st));
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(dW1, E * w * dd * 4, st));
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(dW2, E * w * dd * 4, st));
+    if (swiglu) MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(dW3, E * w * dd * 4, st));
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(db1, E * w * 4, st));
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(db2, E * dd * 4, st));
+    return MOE_OK;
+  }
+  const int T = static_cast<int>(d.T), E_ = static_cast<int>(d.E), K = static_cast<int>(d.K);
+  const int D = static_cast<int>(d.d), Wd = static_cast<int>(d.width), S = static_cast<int>(pl.S);
+  const int Zw = static_cast<int>(pl.Zw), ldk = static_cast<int>(pl.ldk);
+  const int cap = cap_of(d);
+  const int act = swiglu ? 1 : 0;
+  int32_t* topk_idx = at<int32_t>(ws, pl.topk_idx);
+  float* topk_gate = at<float>(ws, pl.topk_gate);
+  int32_t* blk_hist = at<int32_t>(ws, pl.blk_hist);
+  float* blk_psum = at<float>(ws, pl.blk_psum);
+  int32_t* blk_base = at<int32_t>(ws, pl.blk_base);
+  int32_t* offsets = at<int32_t>(ws, pl.offsets);
+  int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
+  int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
+  int32_t* counts = at<int32_t>(ws, pl.counts);
+  float* logits = at<float>(ws, pl.logits);
+  const int bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
+
+  // forward: routing (with the logits), grouping, the expert GEMMs
+  moe::RouteArgs ra{h, W_r, b_r, T, D, E_, K, d.gate, topk_idx, topk_gate, logits, blk_hist, blk_psum};
+  ra.bias_select = bias_select;
+  MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, true, st));
+  MOE_LAUNCH(MOE_K_FINALIZE, st,
+             moe::launch_finalize(blk_hist, blk_psum, pl.rt.NB, T, E_, K, blk_base, counts, offsets, nullptr,
+                                  at<float>(ws, pl.aux), st));
+  MOE_LAUNCH(MOE_K_PERMUTE, st,
+             moe::launch_permute(topk_idx, blk_base, offsets, T, E_, K, cap, pl.rt, h, dd * 2, nullptr, slot_token,
+                                 token_slot, st));
+  int32_t* kofs = at<int32_t>(ws, pl.kofs);
+  MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_pad_offsets(offsets, E_, S, cap, kofs, st));
+  moe::FfnArgs f{};
+  f.S = S;
+  f.d = D;
+  f.E = E_;
+  f.K = K;
+  f.width = Wd;
+  f.act = d.act;
+  f.bf16 = true;
+  f.x = h;
+  f.x_rows = slot_token;
+  f.offsets = offsets;
+  f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
+  f.cap = cap;
+  f.max_rows_per_expert = std::min(T, cap);
+  void* z = at<char>(ws, pl.z);
+  void* a = at<char>(ws, pl.a);
+  float* o = at<float>(ws, pl.o);
+  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_z_bf16(f, z, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_act_forward(z, S, Wd, act, a, st));
+  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_bwd_grouped_bf16(a, S, offsets, cap, E_, W2, b2, D, Wd, o, st));
+
+  // backward through the combine, the second GEMM, the activation, the first GEMM
+  float* dgate = at<float>(ws, pl.dgate);
+  void* dO = at<char>(ws, pl.dO);
+  float* dA = at<float>(ws, pl.dA);
+  void* dZ = at<char>(ws, pl.dZ);
+  float* dX = at<float>(ws, pl.dX);
+  void* W2T = at<char>(ws, pl.W2T);
+  void* W13T = at<char>(ws, pl.W13T);
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dout(dy, o, token_slot, topk_gate, T, D, K, dO, dgate, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W2, E_, D, Wd, W2T, D, 0, st));
+  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_bwd_grouped_bf16(dO, S, offsets, cap, E_, W2T, nullptr, Wd, D, dA, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_act_backward(dA, z, S, Wd, act, dZ, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W1, E_, Wd, D, W13T, Zw, 0, st));
+  if (swiglu) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W3, E_, Wd, D, W13T, Zw, Wd, st));
+  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_grouped_bf16(dZ, S, offsets, cap, E_, W13T, nullptr, D, Zw, dX, st));
+
+  // router, dh, dW_r, db_r
+  float* dl = at<float>(ws, pl.dl);
+  MOE_LAUNCH(MOE_K_BWD, st,
+             moe::launch_router_backward(logits, b_r, bias_select, topk_idx, topk_gate, dgate, counts, T, E_, K,
+                                         d.gate, daux, dl, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dh(dX, token_slot, dl, W_r, T, D, E_, K, dh, st));
+  MOE_LAUNCH(MOE_K_BWD, st,
+             moe::launch_dwr(h, dl, T, D, E_, at<float>(ws, pl.wr_part), dW_r, bias_select ? nullptr : db_r, st));
+  if (bias_select) MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(db_r, E * 4, st));
+
+  // weight gradients: sums over each expert's kept rows of transposed operands
+  void* xT = at<char>(ws, pl.xT);
+  void* aT = at<char>(ws, pl.aT);
+  void* dOT = at<char>(ws, pl.dOT);
+  void* dZT = at<char>(ws, pl.dZT);
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(h, slot_token, D, offsets, kofs, E_, S, cap, xT, ldk, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(a, nullptr, Wd, offsets, kofs, E_, S, cap, aT, ldk, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(dO, nullptr, D, offsets, kofs, E_, S, cap, dOT, ldk, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(dZ, nullptr, Zw, offsets, kofs, E_, S, cap, dZT, ldk, st));
+  MOE_LAUNCH(MOE_K_WGRAD, st, moe::launch_bwd_wgrad_bf16(dOT, D, aT, Wd, ldk, kofs, E_, dW2, nullptr, D, st));
+  MOE_LAUNCH(MOE_K_WGRAD, st, moe::launch_bwd_wgrad_bf16(dZT, Zw, xT, D, ldk, kofs, E_, dW1, dW3, Wd, st));
+  if (db1 != nullptr) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dZ, Wd, offsets, E_, S, cap, db1, st));
+  if (db2 != nullptr) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dO, D, offsets, E_, S, cap, db2, st));
   return MOE_OK;
 }
 

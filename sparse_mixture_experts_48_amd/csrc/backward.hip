@@ -1,0 +1,419 @@
+// Backward pass of the MoE layer (bfloat16 layers): the elementwise, gather,
+// transpose and reduction kernels around the expert GEMMs.
+//
+// The gradient reaches the router only through the gate weights of the chosen
+// experts (maptheai.com "Mixture of Experts", section "The difficulties": the
+// top-k choice is not differentiable) — through p_i for Switch-style gates
+// (Lensa ML explainer "Mixture of Experts", Step 3) — and through P of the
+// load-balancing loss, whose f is a count (Step 4: only P_i is
+// differentiable). The choice and the capacity drops are held fixed.
+//
+// Loss = sum(dy * y) + daux * aux. With y[t] = sum_j g[t][j] o[slot(t, j)]:
+//   dO[s] = g dy[t],  dgate[t][j] = dy[t] . o[s]
+//   dA = dO W2 (rows of W2^T),  dZ = dA * act'(Z),  dX = dZ [W1; W3]
+//   dh[t] = sum_j dX[slot(t, j)] + dlogits[t] W_r^T
+//   dW2_e = dO_e^T A_e,  dW1_e = dZ1_e^T X_e,  dW3_e = dZ3_e^T X_e
+//   dW_r = h^T dlogits,  db_r = sum_t dlogits   (not when the bias only steers the choice)
+// Weight gradients need sums over each expert's grouped rows; the rows of
+// the operands are transposed into [feature][slot] matrices in which every
+// expert's slots start at a multiple of 64 and are padded with zeros to a
+// whole number of GEMM stages.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTile = 64;
+
+// Rows each expert keeps, and its padded column range kofs[e] .. kofs[e+1].
+__global__ void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int S, int cap,
+                                   int32_t* __restrict__ kofs) {
+  if (threadIdx.x != 0) return;
+  int run = 0;
+  for (int e = 0; e < E; ++e) {
+    int beg, end;
+    expert_rows(offsets, e, S, cap, &beg, &end);
+    kofs[e] = run;
+    run += (end - beg + kTile - 1) / kTile * kTile;
+  }
+  kofs[E] = run;
+}
+
+// dst[r][kofs[e] + i] = src[row(offsets[e] + i)][r] for the kept rows i of
+// expert e, 0 in the padding; row(s) = src_rows[s] or s. 64 x 64 tiles.
+__global__ __launch_bounds__(256) void transpose_groups_kernel(
+    const bf16_t* __restrict__ src, const int32_t* __restrict__ src_rows, int R,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ kofs, int E, int S, int cap,
+    bf16_t* __restrict__ dst, int ldk) {
+  __shared__ uint16_t tile[kTile][kTile + 2];
+  __shared__ int e_s, beg_s, n_s;
+  const int c0 = blockIdx.x * kTile;  // first padded column of the tile
+  const int r0 = blockIdx.y * kTile;
+  if (threadIdx.x == 0) {
+    int e = -1;
+    for (int x = 0; x < E; ++x)
+      if (kofs[x] <= c0 && c0 < kofs[x + 1]) e = x;
+    e_s = e;
+    if (e >= 0) {
+      int beg, end;
+      expert_rows(offsets, e, S, cap, &beg, &end);
+      beg_s = beg + (c0 - kofs[e]);  // grouped row of the tile's first column
+      n_s = end - beg_s;             // kept rows from there on
+    }
+  }
+  __syncthreads();
+  if (e_s < 0) return;  // past the last expert's range
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;  // 64 x 4
+  for (int i = ty; i < kTile; i += 4) {  // column i of the tile = grouped row beg_s + i
+    uint16_t v = 0;
+    if (i < n_s && r0 + tx < R) {
+      const int s = beg_s + i;
+      const int row = src_rows != nullptr ? src_rows[s] : s;
+      v = reinterpret_cast<const uint16_t*>(src)[static_cast<size_t>(row) * R + r0 + tx];
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  for (int r = ty; r < kTile; r += 4) {
+    if (r0 + r < R)
+      reinterpret_cast<uint16_t*>(dst)[static_cast<size_t>(r0 + r) * ldk + c0 + tx] = tile[tx][r];
+  }
+}
+
+// dst[e][c][coff + r] = src[e][r][c]: src [E][R][C], dst rows of length ldd.
+__global__ __launch_bounds__(256) void transpose_weights_kernel(const bf16_t* __restrict__ src, int R, int C,
+                                                                bf16_t* __restrict__ dst, int ldd, int coff) {
+  __shared__ uint16_t tile[kTile][kTile + 2];
+  const int e = blockIdx.z;
+  const int c0 = blockIdx.x * kTile, r0 = blockIdx.y * kTile;
+  const uint16_t* s = reinterpret_cast<const uint16_t*>(src) + static_cast<size_t>(e) * R * C;
+  uint16_t* d = reinterpret_cast<uint16_t*>(dst) + static_cast<size_t>(e) * C * ldd;
+  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
+  for (int r = ty; r < kTile; r += 4)
+    tile[r][tx] = (r0 + r < R && c0 + tx < C) ? s[static_cast<size_t>(r0 + r) * C + c0 + tx] : 0;
+  __syncthreads();
+  for (int c = ty; c < kTile; c += 4)
+    if (c0 + c < C && r0 + tx < R) d[static_cast<size_t>(c0 + c) * ldd + coff + r0 + tx] = tile[tx][c];
+}
+
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+// a = act(z) for every grouped row (rows past a group's capacity are never read).
+__global__ __launch_bounds__(256) void act_forward_kernel(const bf16_t* __restrict__ z, int S, int w, int act,
+                                                          bf16_t* __restrict__ a) {
+  const size_t n = static_cast<size_t>(S) * w;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const size_t s = i / w, c = i % w;
+    float v;
+    if (act == 1) {
+      const float z1 = bf16_to_f32(z[s * 2 * w + c]), z3 = bf16_to_f32(z[s * 2 * w + w + c]);
+      v = silu(z1) * z3;
+    } else {
+      v = gelu_exact(bf16_to_f32(z[i]));
+    }
+    a[i] = f32_to_bf16(v);
+  }
+}
+
+// One block per (token, slot j): dO[s] = g dy[t] and dgate[t][j] = dy[t] . o[s]
+// (fixed-order sum: per-thread strided partials, then a tree). Dropped slots:
+// dgate 0 and no row.
+__global__ __launch_bounds__(256) void dout_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ o_perm,
+                                                   const int32_t* __restrict__ token_slot,
+                                                   const float* __restrict__ gate, int d, int K,
+                                                   bf16_t* __restrict__ dO, float* __restrict__ dgate) {
+  __shared__ float red[256];
+  const int tj = blockIdx.x;
+  const int t = tj / K;
+  const int s = token_slot[tj];
+  if (s < 0) {
+    if (threadIdx.x == 0) dgate[tj] = 0.0f;
+    return;
+  }
+  const float g = gate[tj];
+  const bf16_t* dyr = dy + static_cast<size_t>(t) * d;
+  const float* orow = o_perm + static_cast<size_t>(s) * d;
+  bf16_t* dor = dO + static_cast<size_t>(s) * d;
+  float acc = 0.0f;
+  for (int n = threadIdx.x; n < d; n += 256) {
+    const float v = bf16_to_f32(dyr[n]);
+    dor[n] = f32_to_bf16(g * v);
+    acc = fmaf(v, orow[n], acc);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dgate[tj] = red[0];
+}
+
+// dZ from dA (float32) and Z: SwiGLU dz1 = dA z3 silu'(z1), dz3 = dA silu(z1)
+// (rows of 2w); GELU dz = dA gelu'(z).
+__global__ __launch_bounds__(256) void act_backward_kernel(const float* __restrict__ dA, const bf16_t* __restrict__ z,
+                                                           int S, int w, int act, bf16_t* __restrict__ dZ) {
+  const size_t n = static_cast<size_t>(S) * w;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const size_t s = i / w, c = i % w;
+    const float da = dA[i];
+    if (act == 1) {
+      const float z1 = bf16_to_f32(z[s * 2 * w + c]), z3 = bf16_to_f32(z[s * 2 * w + w + c]);
+      const float sg = sigmoid_fast(z1);
+      dZ[s * 2 * w + c] = f32_to_bf16(da * z3 * (sg * (1.0f + z1 * (1.0f - sg))));
+      dZ[s * 2 * w + w + c] = f32_to_bf16(da * (z1 * sg));
+    } else {
+      const float x = bf16_to_f32(z[i]);
+      const float gp = 0.5f * (1.0f + erff(x * 0.70710678118654752440f)) +
+                       x * expf(-0.5f * x * x) * 0.39894228040143267794f;
+      dZ[i] = f32_to_bf16(da * gp);
+    }
+  }
+}
+
+// One wave per token, lane = expert: d loss / d gate logits.
+__global__ __launch_bounds__(256) void router_backward_kernel(
+    const float* __restrict__ logits, const float* __restrict__ br, int bias_select,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ gate, const float* __restrict__ dgate,
+    const int32_t* __restrict__ counts, int T, int E, int K, int gate_mode, float daux,
+    float* __restrict__ dl) {
+  const int t = blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (t >= T) return;
+  const bool on = lane < E;
+  float gl = -INFINITY;
+  if (on) {
+    gl = logits[static_cast<size_t>(t) * E + lane];
+    if (bias_select && br != nullptr) gl -= br[lane];
+  }
+  float m = gl;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float ex = on ? expf(gl - m) : 0.0f;
+  float sum = ex;
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  const float p = ex / sum;
+  float dlv = 0.0f, dp = 0.0f;
+  if (gate_mode == 0) {  // renormalised: dl[c_j] = g_j (dg_j - sum_i g_i dg_i)
+    float sdot = 0.0f;
+    for (int j = 0; j < K; ++j) sdot += gate[t * K + j] * dgate[t * K + j];
+    for (int j = 0; j < K; ++j)
+      if (topk_idx[t * K + j] == lane) dlv += gate[t * K + j] * (dgate[t * K + j] - sdot);
+  } else {  // raw: g_j = p[c_j]
+    for (int j = 0; j < K; ++j)
+      if (topk_idx[t * K + j] == lane) dp += dgate[t * K + j];
+  }
+  if (on && daux != 0.0f) {
+    const float f = static_cast<float>(counts[lane]) / (static_cast<float>(T) * static_cast<float>(K));
+    dp += daux * static_cast<float>(E) * f / static_cast<float>(T);
+  }
+  float pdp = on ? p * dp : 0.0f;
+  for (int off = 32; off > 0; off >>= 1) pdp += __shfl_xor(pdp, off);
+  if (on) dl[static_cast<size_t>(t) * E + lane] = dlv + p * (dp - pdp);
+}
+
+// dh[t] = sum_j dX[slot(t, j)] (ascending j, kept slots) + sum_e dl[t][e] W_r[k][e].
+// Block: 16 tokens; a thread keeps one row of W_r in registers across them.
+constexpr int kDhTokens = 16;
+__global__ __launch_bounds__(256) void dh_kernel(const float* __restrict__ dX, const int32_t* __restrict__ token_slot,
+                                                 const float* __restrict__ dl, const float* __restrict__ Wr, int T,
+                                                 int d, int E, int K, bf16_t* __restrict__ dh) {
+  __shared__ float dl_s[kDhTokens][64];
+  const int t0 = blockIdx.x * kDhTokens;
+  for (int i = threadIdx.x; i < kDhTokens * 64; i += 256) {
+    const int tt = t0 + i / 64, e = i % 64;
+    dl_s[i / 64][e] = (tt < T && e < E) ? dl[static_cast<size_t>(tt) * E + e] : 0.0f;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < d; k += 256) {
+    float wr[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) wr[e] = e < E ? Wr[static_cast<size_t>(k) * E + e] : 0.0f;
+    for (int i = 0; i < kDhTokens; ++i) {
+      const int t = t0 + i;
+      if (t >= T) break;
+      float acc = 0.0f;
+      for (int j = 0; j < K; ++j) {
+        const int s = token_slot[t * K + j];
+        if (s >= 0) acc += dX[static_cast<size_t>(s) * d + k];
+      }
+      float r = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 64; ++e) r = fmaf(dl_s[i][e], wr[e], r);
+      dh[static_cast<size_t>(t) * d + k] = f32_to_bf16(acc + r);
+    }
+  }
+}
+
+// Partial sums over chunks of kWrChunk tokens: part[c][k][e] = sum_t h[t][k] dl[t][e];
+// column e of chunk c, row k: one thread, tokens in order.
+constexpr int kWrChunk = 256;
+__global__ __launch_bounds__(256) void dwr_partial_kernel(const bf16_t* __restrict__ h, const float* __restrict__ dl,
+                                                          int T, int d, int E, float* __restrict__ part) {
+  __shared__ float dl_s[kWrChunk][65];
+  const int c = blockIdx.y;
+  const int t0 = c * kWrChunk;
+  const int nt = min(kWrChunk, T - t0);
+  for (int i = threadIdx.x; i < kWrChunk * E; i += 256) {
+    const int tt = i / E, e = i % E;
+    dl_s[tt][e] = tt < nt ? dl[static_cast<size_t>(t0 + tt) * E + e] : 0.0f;
+  }
+  __syncthreads();
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= d) return;
+  float acc[64];
+#pragma unroll
+  for (int e = 0; e < 64; ++e) acc[e] = 0.0f;
+  for (int tt = 0; tt < nt; ++tt) {
+    const float hv = bf16_to_f32(h[static_cast<size_t>(t0 + tt) * d + k]);
+#pragma unroll
+    for (int e = 0; e < 64; ++e)
+      if (e < E) acc[e] = fmaf(hv, dl_s[tt][e], acc[e]);
+  }
+  float* dst = part + (static_cast<size_t>(c) * d + k) * E;
+#pragma unroll
+  for (int e = 0; e < 64; ++e)
+    if (e < E) dst[e] = acc[e];
+}
+
+// dW_r[k][e] = sum over chunks in order; db_r[e] = sum_t dl[t][e] in order.
+__global__ __launch_bounds__(256) void dwr_final_kernel(const float* __restrict__ part, int nchunk,
+                                                        const float* __restrict__ dl, int T, int d, int E,
+                                                        float* __restrict__ dWr, float* __restrict__ dbr) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t n = static_cast<size_t>(d) * E;
+  if (i < n) {
+    float s = 0.0f;
+    for (int c = 0; c < nchunk; ++c) s += part[static_cast<size_t>(c) * n + i];
+    dWr[i] = s;
+  }
+  if (dbr != nullptr && blockIdx.x == 0 && threadIdx.x < E) {
+    float s = 0.0f;
+    for (int t = 0; t < T; ++t) s += dl[static_cast<size_t>(t) * E + threadIdx.x];
+    dbr[threadIdx.x] = s;
+  }
+}
+
+// out[e][c] = sum over the kept grouped rows of expert e of src[row][c] (in order).
+__global__ __launch_bounds__(256) void group_colsum_kernel(const bf16_t* __restrict__ src, int C,
+                                                           const int32_t* __restrict__ offsets, int S, int cap,
+                                                           float* __restrict__ out) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  int beg, end;
+  expert_rows(offsets, e, S, cap, &beg, &end);
+  float s = 0.0f;
+  for (int r = beg; r < end; ++r) s += bf16_to_f32(src[static_cast<size_t>(r) * C + c]);
+  out[static_cast<size_t>(e) * C + c] = s;
+}
+
+unsigned grid1d(size_t n) {
+  const size_t b = (n + 255) / 256;
+  return static_cast<unsigned>(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
+}  // namespace
+
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int S, int cap, int32_t* kofs, hipStream_t st) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, st, offsets, E, S, cap, kofs);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_groups(const void* src, const int32_t* src_rows, int R, const int32_t* offsets,
+                                   const int32_t* kofs, int E, int S, int cap, void* dst, int ldk,
+                                   hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(ldk / kTile), static_cast<unsigned>((R + kTile - 1) / kTile));
+  hipLaunchKernelGGL(transpose_groups_kernel, grid, dim3(256), 0, st, static_cast<const bf16_t*>(src), src_rows,
+                     R, offsets, kofs, E, S, cap, static_cast<bf16_t*>(dst), ldk);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* dst, int ldd, int coff,
+                                   hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((C + kTile - 1) / kTile), static_cast<unsigned>((R + kTile - 1) / kTile),
+                  static_cast<unsigned>(E));
+  hipLaunchKernelGGL(transpose_weights_kernel, grid, dim3(256), 0, st, static_cast<const bf16_t*>(src), R, C,
+                     static_cast<bf16_t*>(dst), ldd, coff);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_forward(const void* z, int S, int w, int act, void* a, hipStream_t st) {
+  hipLaunchKernelGGL(act_forward_kernel, dim3(grid1d(static_cast<size_t>(S) * w)), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(z), S, w, act, static_cast<bf16_t*>(a));
+  return hipGetLastError();
+}
+
+hipError_t launch_dout(const void* dy, const float* o_perm, const int32_t* token_slot, const float* gate, int T,
+                       int d, int K, void* dO, float* dgate, hipStream_t st) {
+  hipLaunchKernelGGL(dout_kernel, dim3(static_cast<unsigned>(T * K)), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(dy), o_perm, token_slot, gate, d, K, static_cast<bf16_t*>(dO),
+                     dgate);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_backward(const float* dA, const void* z, int S, int w, int act, void* dZ, hipStream_t st) {
+  hipLaunchKernelGGL(act_backward_kernel, dim3(grid1d(static_cast<size_t>(S) * w)), dim3(256), 0, st, dA,
+                     static_cast<const bf16_t*>(z), S, w, act, static_cast<bf16_t*>(dZ));
+  return hipGetLastError();
+}
+
+hipError_t launch_router_backward(const float* logits, const float* br, int bias_select, const int32_t* topk_idx,
+                                  const float* gate, const float* dgate, const int32_t* counts, int T, int E,
+                                  int K, int gate_mode, float daux, float* dl, hipStream_t st) {
+  hipLaunchKernelGGL(router_backward_kernel, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(256), 0, st, logits,
+                     br, bias_select, topk_idx, gate, dgate, counts, T, E, K, gate_mode, daux, dl);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
+                     int E, int K, void* dh, hipStream_t st) {
+  hipLaunchKernelGGL(dh_kernel, dim3(static_cast<unsigned>((T + kDhTokens - 1) / kDhTokens)), dim3(256), 0, st,
+                     dX, token_slot, dl, Wr, T, d, E, K, static_cast<bf16_t*>(dh));
+  return hipGetLastError();
+}
+
+int dwr_chunks(int T) { return (T + kWrChunk - 1) / kWrChunk; }
+
+hipError_t launch_dwr(const void* h, const float* dl, int T, int d, int E, float* part, float* dWr, float* dbr,
+                      hipStream_t st) {
+  const int nc = dwr_chunks(T);
+  hipLaunchKernelGGL(dwr_partial_kernel, dim3(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(nc)),
+                     dim3(256), 0, st, static_cast<const bf16_t*>(h), dl, T, d, E, part);
+  hipLaunchKernelGGL(dwr_final_kernel, dim3(static_cast<unsigned>((static_cast<size_t>(d) * E + 255) / 256)),
+                     dim3(256), 0, st, part, nc, dl, T, d, E, dWr, dbr);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_colsum(const void* src, int C, const int32_t* offsets, int E, int S, int cap, float* out,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(group_colsum_kernel, dim3(static_cast<unsigned>((C + 255) / 256), static_cast<unsigned>(E)),
+                     dim3(256), 0, st, static_cast<const bf16_t*>(src), C, offsets, S, cap, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+namespace {
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<size_t>(gridDim.x) * 256)
+    p[i] = 0u;
+}
+}  // namespace
+
+// Zero `bytes` bytes (a multiple of 4) with a kernel, so that the call can be
+// captured in a graph.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  if (p == nullptr || bytes == 0) return hipSuccess;
+  const size_t n = bytes / 4;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid1d(n)), dim3(256), 0, st, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -32,7 +32,12 @@ namespace moe {
 
 namespace {
 
-enum { G1_SWIGLU = 0, G1_GELU = 1, G2_OPERM = 2, G2_FUSED_Y = 3 };
+enum {
+  G1_SWIGLU = 0, G1_GELU = 1, G2_OPERM = 2, G2_FUSED_Y = 3,
+  // backward pass: the first GEMM's pre-activations (SwiGLU: x W1 and x W3,
+  // side by side in rows of 2N; GELU: x W1 + b1), and the weight gradients
+  G1_SWIGLU_Z = 4, G1_GELU_Z = 5, G_WGRAD = 6
+};
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -52,6 +57,13 @@ struct GemmParams {
   int cap;                  // rows each expert processes at most
   int x_nrows;              // rows of x
   int n_mt;                 // m-tile slots in the grid (upper bound)
+  // G_WGRAD: for every expert e, C_e[M][N] = sum over k in [kofs[e], kofs[e+1])
+  // of x[m][k] B[n][k] (both row-major with row stride ldk; every expert's
+  // range is whole 64-k stages, zero-padded); rows m < split go to out
+  // ([E][split][N], float32), the rest to out2 ([E][M - split][N]).
+  const int32_t* kofs;
+  int M, ldk, split;
+  float* out2;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -135,7 +147,9 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 template <int BM, int BN, int WM, int WN, int MODE>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
-  constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
+  constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
+  constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_SWIGLU_Z || MODE == G1_GELU_Z);
+  constexpr bool WGRAD = (MODE == G_WGRAD);
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int A_IN = BM / (NW * kRPI);  // token-row loads per wave per stage
@@ -168,7 +182,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const int mt = (t / kNG) % p.n_mt;
   if (nt >= n_nt) return;
   int e, row0, rows;
-  if (!find_m_tile(p.offsets, p.E, p.S, p.cap, BM, mt, &e, &row0, &rows)) return;
+  if constexpr (WGRAD) {  // fixed M rows for every expert: m-tile mt = (expert, tile)
+    const int n_mte = (p.M + BM - 1) / BM;
+    e = mt / n_mte;
+    row0 = (mt % n_mte) * BM;
+    rows = min(BM, p.M - row0);
+    if (e >= p.E) return;
+  } else {
+    if (!find_m_tile(p.offsets, p.E, p.S, p.cap, BM, mt, &e, &row0, &rows)) return;
+  }
   const int n0 = nt * NCOLS;
 
   const int tid = threadIdx.x;
@@ -194,12 +216,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // lane%8, i.e. logical chunk (lane%8) ^ swz_key(row). Byte offsets are
   // 32-bit: the host keeps every operand matrix at or below 2^32 - 2^23 bytes
   // and d, width at or below 2^20, so row offset + k offset never wraps.
-  const int nk = (Kd + kBK - 1) / kBK;
-  const int k_last = (nk - 1) * kBK;  // first k of the last stage
-  const uint32_t a_bytes = static_cast<uint32_t>(p.x_nrows) * static_cast<uint32_t>(Kd) * 2u;
-  const uint32_t b_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(Kd) * 2u;
+  // Forward GEMMs reduce over k = 0 .. Kd-1 of rows of length Kd; G_WGRAD
+  // over expert e's padded range of rows of length ldk, a whole number of
+  // stages (so its last stage needs no zero fill).
+  const int stride = WGRAD ? p.ldk : Kd;
+  const int kb = WGRAD ? p.kofs[e] : 0;
+  const int nk = WGRAD ? (p.kofs[e + 1] - kb) / kBK : (Kd + kBK - 1) / kBK;
+  const int k_last = WGRAD ? (1 << 30) : (nk - 1) * kBK;  // first k of the last stage
+  const uint32_t a_bytes = static_cast<uint32_t>(WGRAD ? p.M : p.x_nrows) * static_cast<uint32_t>(stride) * 2u;
+  const uint32_t b_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(stride) * 2u;
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.x, a_bytes);
-  const __amdgpu_buffer_rsrc_t rb1 = buffer_rsrc(p.B + static_cast<size_t>(e) * N * Kd, b_bytes);
+  const __amdgpu_buffer_rsrc_t rb1 = buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * N * Kd), b_bytes);
   const __amdgpu_buffer_rsrc_t rb3 =
       (NMAT == 2) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * N * Kd, b_bytes) : rb1;
   // per lane: offset for every stage, and for the last one (out of range past the end of k)
@@ -210,8 +237,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
     const int s = row0 + min(r, rows - 1);
     const int src_row = (p.x_rows != nullptr) ? p.x_rows[s] : s;
-    a_vo[u] = (static_cast<uint32_t>(src_row) * static_cast<uint32_t>(Kd) + static_cast<uint32_t>(kc)) * 2u;
-    a_vl[u] = (k_last + kc < Kd) ? a_vo[u] : a_bytes;
+    a_vo[u] = (static_cast<uint32_t>(src_row) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
+    a_vl[u] = (WGRAD || k_last + kc < Kd) ? a_vo[u] : a_bytes;
   }
 #pragma unroll
   for (int u = 0; u < B_IN; ++u) {
@@ -219,17 +246,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     const int r = (wid * B_IN + u) * kRPI + lane / kCH;
     const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
     const int n = min(brow_col(r, &mat), N - 1);
-    b_vo[u] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(Kd) + static_cast<uint32_t>(kc)) * 2u;
-    b_vl[u] = (k_last + kc < Kd) ? b_vo[u] : b_bytes;
+    b_vo[u] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
+    b_vl[u] = (WGRAD || k_last + kc < Kd) ? b_vo[u] : b_bytes;
   }
   // Load u of the token rows of the stage starting at k0.
   auto load_a = [&](int u, int k0, u32x4_t* As) {
-    lds_load16(ra, k0 >= k_last ? a_vl[u] : a_vo[u], min(k0, k_last) * 2, As + (wid * A_IN + u) * 64);
+    lds_load16(ra, k0 >= k_last ? a_vl[u] : a_vo[u], (kb + min(k0, k_last)) * 2, As + (wid * A_IN + u) * 64);
   };
   auto load_b = [&](int u, int k0, u32x4_t* Bs) {
     int mat;
     (void)brow_col((wid * B_IN + u) * kRPI, &mat);  // the 8 rows of one instruction share a matrix
-    lds_load16((NMAT == 2 && mat) ? rb3 : rb1, k0 >= k_last ? b_vl[u] : b_vo[u], min(k0, k_last) * 2,
+    lds_load16((NMAT == 2 && mat) ? rb3 : rb1, k0 >= k_last ? b_vl[u] : b_vo[u], (kb + min(k0, k_last)) * 2,
                Bs + (wid * B_IN + u) * 64);
   };
 
@@ -318,6 +345,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * (WTN / NMAT) + j * 32 + g * 8 + (lane / 32) * 4;
         if (n >= N) continue;  // N % 8 == 0: four columns are all in or all out
+        if constexpr (MODE == G1_SWIGLU_Z) {  // x W1 | x W3 side by side, rows of 2N
+          float z1[4], z3[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            z1[q] = acc[j][i][g * 4 + q];
+            z3[q] = acc[j + TNO][i][g * 4 + q];
+          }
+          bf16_t* row = static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * 2 * N;
+          *reinterpret_cast<u32x2_t*>(row + n) = u32x2_t{pack_bf16x2(z1[0], z1[1]), pack_bf16x2(z1[2], z1[3])};
+          *reinterpret_cast<u32x2_t*>(row + N + n) =
+              u32x2_t{pack_bf16x2(z3[0], z3[1]), pack_bf16x2(z3[2], z3[3])};
+          continue;
+        }
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -329,9 +369,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
             if (p.bias != nullptr) v[q] += bf16_to_f32(p.bias[static_cast<size_t>(e) * N + n + q]);
           }
         }
-        if (MODE == G1_SWIGLU || MODE == G1_GELU) {
+        if (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_GELU_Z) {
           *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        } else if (MODE == G_WGRAD) {
+          float* dst = s < p.split
+                           ? static_cast<float*>(p.out) + (static_cast<size_t>(e) * p.split + s) * N + n
+                           : p.out2 + (static_cast<size_t>(e) * (p.M - p.split) + (s - p.split)) * N + n;
+          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
         } else if (MODE == G2_OPERM) {
           *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + static_cast<size_t>(s) * N + n) =
               f32x4_t{v[0], v[1], v[2], v[3]};
@@ -484,8 +529,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmPara
 
 template <int BM, int BN, int WM, int WN, int MODE>
 hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
-  constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
-  p.n_mt = (S + BM - 1) / BM + min(p.E, S);
+  constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
+  p.n_mt = MODE == G_WGRAD ? p.E * ((p.M + BM - 1) / BM) : (S + BM - 1) / BM + min(p.E, S);
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
   const size_t total = static_cast<size_t>((n_nt + kTileGroupN - 1) / kTileGroupN) * p.n_mt * kTileGroupN;
   const size_t grid = (total + 7) / 8 * 8;
@@ -505,8 +550,8 @@ hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
 // 128 x 128 so that the chip is still covered.
 template <int MODE>
 hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
-  constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU);
-  constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
+  constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_SWIGLU_Z || MODE == G1_GELU_Z);
+  constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   const int mean_rows = S / max(p.E, 1);
   auto blocks = [&](int bm, int bn) {
     return static_cast<long>((S + bm - 1) / bm + min(p.E, S)) * ((p.N + bn / NMAT - 1) / (bn / NMAT));
@@ -587,6 +632,64 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
                      : launch_stream<G2_OPERM, kStreamNR2, kStreamBuf2>(p, f.max_rows_per_expert, st);
   }
   return f.fused_y ? launch_tile_auto<G2_FUSED_Y>(p, f.S, st) : launch_tile_auto<G2_OPERM>(p, f.S, st);
+}
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------- backward pass GEMMs
+
+namespace moe {
+
+hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, hipStream_t st) {
+  GemmParams p{};
+  p.x = static_cast<const bf16_t*>(f.x);
+  p.x_rows = f.x_rows;
+  p.x_nrows = f.x_rows != nullptr ? f.S / f.K : f.S;
+  p.cap = f.cap;
+  p.offsets = f.offsets;
+  p.B = static_cast<const bf16_t*>(f.W1);
+  p.B3 = static_cast<const bf16_t*>(f.W3);
+  p.bias = static_cast<const bf16_t*>(f.b1);
+  p.out = z;
+  p.E = f.E;
+  p.N = f.width;
+  p.Kd = f.d;
+  p.S = f.S;
+  return f.act == 1 ? launch_tile_auto<G1_SWIGLU_Z>(p, f.S, st) : launch_tile_auto<G1_GELU_Z>(p, f.S, st);
+}
+
+hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets, int cap, int E, const void* B,
+                                   const void* bias, int N, int Kd, float* out, hipStream_t st) {
+  GemmParams p{};
+  p.x = static_cast<const bf16_t*>(x);
+  p.bias = static_cast<const bf16_t*>(bias);
+  p.x_nrows = S;
+  p.cap = cap;
+  p.offsets = offsets;
+  p.B = static_cast<const bf16_t*>(B);
+  p.out = out;
+  p.E = E;
+  p.N = N;
+  p.Kd = Kd;
+  p.S = S;
+  return launch_tile_auto<G2_OPERM>(p, S, st);
+}
+
+hipError_t launch_bwd_wgrad_bf16(const void* A, int M, const void* B, int N, int ldk, const int32_t* kofs, int E,
+                                 float* out, float* out2, int split, hipStream_t st) {
+  GemmParams p{};
+  p.x = static_cast<const bf16_t*>(A);
+  p.B = static_cast<const bf16_t*>(B);
+  p.kofs = kofs;
+  p.M = M;
+  p.ldk = ldk;
+  p.split = split;
+  p.out = out;
+  p.out2 = out2;
+  p.E = E;
+  p.N = N;
+  p.Kd = ldk;
+  return launch_tile<256, 256, 4, 2, G_WGRAD>(p, 0, st);
 }
 
 }  // namespace moe

@@ -71,4 +71,40 @@ hipError_t launch_gemm2(const FfnArgs& f, hipStream_t st);
 hipError_t launch_combine(const float* o_perm, const int32_t* token_slot, const float* topk_gate,
                           int T, int d, int K, bool bf16, void* y, hipStream_t st);
 
+// ---- backward pass (bfloat16 layers)
+// First GEMM without its activation: SwiGLU z = [x W1 | x W3] as rows of 2*width,
+// GELU z = x W1 + b1; grouped rows as in launch_gemm1.
+hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, hipStream_t st);
+// out[s] = x[s] . B_e^T (+ bias_e) (float32) for the grouped rows s of every
+// expert e (the first cap of each group); B stored [E][N][Kd], bias [E][N] or null.
+hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets, int cap, int E, const void* B,
+                                   const void* bias, int N, int Kd, float* out, hipStream_t st);
+// Weight gradients: C_e[m][n] = sum over k in [kofs[e], kofs[e+1]) of A[m][k] B[n][k];
+// A [M][ldk], B [N][ldk] bfloat16, every range whole 64-k stages (zero padded);
+// rows m < split to out [E][split][N], the rest to out2 [E][M - split][N] (float32).
+hipError_t launch_bwd_wgrad_bf16(const void* A, int M, const void* B, int N, int ldk, const int32_t* kofs, int E,
+                                 float* out, float* out2, int split, hipStream_t st);
+// Elementwise, transpose and reduction kernels of the backward pass (csrc/backward.hip).
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int S, int cap, int32_t* kofs, hipStream_t st);
+hipError_t launch_transpose_groups(const void* src, const int32_t* src_rows, int R, const int32_t* offsets,
+                                   const int32_t* kofs, int E, int S, int cap, void* dst, int ldk,
+                                   hipStream_t st);
+hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* dst, int ldd, int coff,
+                                    hipStream_t st);
+hipError_t launch_act_forward(const void* z, int S, int w, int act, void* a, hipStream_t st);
+hipError_t launch_dout(const void* dy, const float* o_perm, const int32_t* token_slot, const float* gate, int T,
+                       int d, int K, void* dO, float* dgate, hipStream_t st);
+hipError_t launch_act_backward(const float* dA, const void* z, int S, int w, int act, void* dZ, hipStream_t st);
+hipError_t launch_router_backward(const float* logits, const float* br, int bias_select, const int32_t* topk_idx,
+                                  const float* gate, const float* dgate, const int32_t* counts, int T, int E,
+                                  int K, int gate_mode, float daux, float* dl, hipStream_t st);
+hipError_t launch_dh(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
+                     int E, int K, void* dh, hipStream_t st);
+int dwr_chunks(int T);
+hipError_t launch_dwr(const void* h, const float* dl, int T, int d, int E, float* part, float* dWr, float* dbr,
+                      hipStream_t st);
+hipError_t launch_group_colsum(const void* src, int C, const int32_t* offsets, int E, int S, int cap, float* out,
+                               hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
 }  // namespace moe

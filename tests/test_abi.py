@@ -129,3 +129,38 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         moe.binding._ptr(torch.zeros(4))
+
+
+def _bws(desc):
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)) == OK
+    return n.value
+
+
+def _backward(desc, h=FAKE, Wr=FAKE, br=None, W1=FAKE, b1=None, W3=FAKE, W2=FAKE, b2=None, dy=FAKE, daux=0.0,
+              dh=FAKE, dWr=FAKE, dbr=None, dW1=FAKE, db1=None, dW3=FAKE, dW2=FAKE, db2=None, ws=FAKE, ws_bytes=None):
+    wsb = _bws(desc) if ws_bytes is None else ws_bytes
+    return moe.lib().moe_backward(ctypes.byref(desc), h, Wr, br, W1, b1, W3, W2, b2, dy, daux, dh, dWr, dbr, dW1,
+                                  db1, dW3, dW2, db2, ws, wsb, None)
+
+
+def test_backward_error_paths():
+    """Validation happens before any HIP call (no GPU needed for these)."""
+    L = moe.lib()
+    d = _d()
+    n = ctypes.c_size_t(0)
+    assert L.moe_backward_workspace_size(ctypes.byref(_d(dtype=0)), ctypes.byref(n)) == UNSUP  # bfloat16 only
+    assert L.moe_backward_workspace_size(ctypes.byref(d), None) == NULL
+    assert _bws(d) > _ws(d)
+    assert _backward(d, dy=None) == NULL
+    assert _backward(d, dh=None) == NULL
+    assert _backward(d, dWr=None) == NULL
+    assert _backward(d, dW1=None) == NULL
+    assert _backward(d, dW2=None) == NULL
+    assert _backward(d, dW3=None) == NULL                     # SwiGLU needs dW3
+    assert _backward(d, db1=FAKE) == UNSUP                    # SwiGLU layers have no biases
+    assert _backward(d, daux=float("inf")) == SHAPE
+    assert _backward(d, dh=FAKE + 8) == UNSUP                 # misaligned
+    assert _backward(d, ws_bytes=_bws(d) - 1) == WS
+    assert _backward(_d(dtype=0), ws_bytes=1 << 30) == UNSUP
+    assert _backward(_d(K=0), ws_bytes=1 << 30) == SHAPE
