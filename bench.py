@@ -4,9 +4,9 @@ One step = one moe_forward call (route, group, expert GEMMs, combine, aux) over
 one batch of seeded synthetic input already resident in HBM.
 
 Headline (`value`): tokens/s on the Mixtral-shaped prefill layer (T=4096,
-d=4096, E=8, top-2, SwiGLU width 14336, bf16). The decode-shaped layer (T=16)
-and the Switch-style top-1 layer (T=8192, E=64, width 1376) are reported in
-extra objects of the same JSON line. Each carries a roofline for its dominant
+d=4096, E=8, top-2, SwiGLU width 14336, bf16). The decode-shaped layer (T=16),
+the Switch-style top-1 layer (T=8192, E=64, width 1376) and the backward pass
+of the prefill layer are reported in extra objects of the same JSON line. Each carries a roofline for its dominant
 kernel: algorithmic flops or bytes per launch divided by that kernel's mean
 duration, measured with HIP events that the library records on the launch
 stream during the timed region.
@@ -107,6 +107,55 @@ def time_workload(cfg, steps, warmup, label):
     return ms, kernels, alg, counts, aux, ms_graph
 
 
+def time_backward(cfg, steps, warmup):
+    """moe_backward on one layer (forward recompute + gradients of every input)."""
+    sys.stderr.write("[bench] backward %s: generating inputs\n" % cfg.name)
+    sys.stderr.flush()
+    inp = W.make_inputs(cfg)
+    dev = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    del inp
+    g = torch.Generator().manual_seed(cfg.seed + 1000)
+    dy = torch.randn((cfg.T, cfg.d), generator=g).to(torch.bfloat16).cuda()
+    desc = moe.desc_of(cfg)
+    ws = moe.backward_workspace(desc)
+
+    def step():
+        return moe.backward(desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"], dev["W2"],
+                            dev["b2"], dy, 0.01, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    sys.stderr.write("[bench] backward: timing %d steps\n" % steps)
+    sys.stderr.flush()
+    with moe.Trace(capacity=64 * steps + 64) as tr:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        events = tr.read()
+    per_call = len(events) // steps
+    calls = [events[i * per_call:(i + 1) * per_call] for i in range(steps)]
+
+    def launches(name):  # durations of the launches of `name`, in call order
+        return [[ms_ for n, ms_ in c if n == name] for c in calls]
+
+    wg = launches("wgrad")
+    g1 = launches("gemm1")
+    per_kernel = {}
+    for name, dur in events:
+        per_kernel.setdefault(name, []).append(dur)
+    del ws, dev
+    torch.cuda.empty_cache()
+    return ms, {"dW13_ms": float(np.mean([c[-1] for c in wg])), "dW2_ms": float(np.mean([c[0] for c in wg])),
+                "dX_ms": float(np.mean([c[-1] for c in g1])),
+                "kernels_ms": {k: round(float(np.sum(v)) / steps, 4) for k, v in per_kernel.items()},
+                "launches_ms": [[calls[0][i][0], round(float(np.mean([c[i][1] for c in calls])), 4)]
+                                for i in range(per_call)]}
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary of `workload` (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy);
@@ -163,7 +212,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="time only the prefill workload")
-    ap.add_argument("--only", choices=["prefill", "decode", "switch"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "switch", "backward"], default=None,
                     help="time one workload only (for per-workload profiles); prints its own JSON object")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=1024)
@@ -185,6 +234,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only == "backward":
+        c = W.WORKLOADS["mixtral_prefill"]
+        bms, bk = time_backward(c, args.steps, args.warmup)
+        print(json.dumps({"workload": c.name, "backward_ms_per_step": round(bms, 4), **bk}))
+        return
     if args.only is not None:
         name = {"prefill": "mixtral_prefill", "decode": "mixtral_decode", "switch": "switch_top1"}[args.only]
         c = W.WORKLOADS[name]
@@ -253,6 +307,22 @@ def main():
             "aux_loss": round(saux, 6), "experts_hit": salg["experts_hit"],
             "max_expert_rows": int(scounts.max()),
             "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in sk.items()},
+        }
+    if not args.no_extra:
+        bcfg = W.WORKLOADS["mixtral_prefill"]
+        bms, bk = time_backward(bcfg, max(args.steps // 4, 3), 2)
+        F = 2.0 * bcfg.S * bcfg.d * bcfg.width * 3  # forward expert flops (SwiGLU: 3 matrices)
+        f13 = 2.0 * bcfg.S * (2 * bcfg.width) * bcfg.d  # dW1 and dW3 together
+        out["backward"] = {
+            "workload": bcfg.name, "ms_per_step": round(bms, 4),
+            "tokens_per_s": round(bcfg.T / (bms * 1e-3), 1),
+            "expert_tflops": round(3 * F / (bms * 1e-3) / 1e12, 2),
+            "note": "moe_backward: forward recompute (F) + input and weight gradients (2F) of the expert FFNs, "
+                    "router gradient, dh",
+            "roofline": dict(roofline_mfma(f13, bk["dW13_ms"], PEAK_BF16_TFLOPS), kernel="wgrad dW1+dW3"),
+            "dX_tflops": round(f13 / (bk["dX_ms"] * 1e-3) / 1e12, 2),
+            "dW2_tflops": round(F / 3 / (bk["dW2_ms"] * 1e-3) / 1e12, 2),
+            "kernels_ms": bk["kernels_ms"], "launches_ms": bk["launches_ms"],
         }
     if not args.no_cpu:
         sys.stderr.write("[bench] cpu baseline: oracle on %d tokens\n" % args.cpu_tokens)

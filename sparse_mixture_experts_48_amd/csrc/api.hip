@@ -86,7 +86,7 @@ struct BwdPlan {
   int64_t S, Zw, ldk;
   int nwr;
   size_t blk_hist, blk_psum, blk_base, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux, logits;
-  size_t z, a, o, dgate, dO, dA, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
+  size_t z, a, o, dgate, dO, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
   size_t total;
 };
 
@@ -122,7 +122,6 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   p.o = take(S * dd * 4);
   p.dgate = take(S * 4);
   p.dO = take(S * dd * 2);
-  p.dA = take(S * w * 4);
   p.dZ = take(S * Zw * 2);
   p.dX = take(S * dd * 4);
   p.kofs = take((E + 1) * 4);
@@ -568,22 +567,19 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   void* z = at<char>(ws, pl.z);
   void* a = at<char>(ws, pl.a);
   float* o = at<float>(ws, pl.o);
-  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_z_bf16(f, z, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_act_forward(z, S, Wd, act, a, st));
+  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_z_bf16(f, z, a, st));
   MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_bwd_grouped_bf16(a, S, offsets, cap, E_, W2, b2, D, Wd, o, st));
 
   // backward through the combine, the second GEMM, the activation, the first GEMM
   float* dgate = at<float>(ws, pl.dgate);
   void* dO = at<char>(ws, pl.dO);
-  float* dA = at<float>(ws, pl.dA);
   void* dZ = at<char>(ws, pl.dZ);
   float* dX = at<float>(ws, pl.dX);
   void* W2T = at<char>(ws, pl.W2T);
   void* W13T = at<char>(ws, pl.W13T);
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dout(dy, o, token_slot, topk_gate, T, D, K, dO, dgate, st));
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W2, E_, D, Wd, W2T, D, 0, st));
-  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_bwd_grouped_bf16(dO, S, offsets, cap, E_, W2T, nullptr, Wd, D, dA, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_act_backward(dA, z, S, Wd, act, dZ, st));
+  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_bwd_dz_bf16(dO, S, offsets, cap, E_, W2T, Wd, D, z, act, dZ, st));
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W1, E_, Wd, D, W13T, Zw, 0, st));
   if (swiglu) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W3, E_, Wd, D, W13T, Zw, Wd, st));
   MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_grouped_bf16(dZ, S, offsets, cap, E_, W13T, nullptr, D, Zw, dX, st));

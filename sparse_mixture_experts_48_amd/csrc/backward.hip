@@ -11,6 +11,8 @@
 // Loss = sum(dy * y) + daux * aux. With y[t] = sum_j g[t][j] o[slot(t, j)]:
 //   dO[s] = g dy[t],  dgate[t][j] = dy[t] . o[s]
 //   dA = dO W2 (rows of W2^T),  dZ = dA * act'(Z),  dX = dZ [W1; W3]
+//   (the pre-activation GEMM also writes A = act(Z); the dA GEMM applies
+//   act' in its epilogue and writes dZ)
 //   dh[t] = sum_j dX[slot(t, j)] + dlogits[t] W_r^T
 //   dW2_e = dO_e^T A_e,  dW1_e = dZ1_e^T X_e,  dW3_e = dZ3_e^T X_e
 //   dW_r = h^T dlogits,  db_r = sum_t dlogits   (not when the bias only steers the choice)
@@ -41,13 +43,37 @@ __global__ void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, i
   kofs[E] = run;
 }
 
+// Both transposes move 64 x 64 tiles through LDS in 16-byte pieces: a thread
+// loads two runs of 8 elements along a source row and stores two runs of 8
+// along a destination row (every row length and offset is a multiple of 8).
+constexpr int kTP = kTile + 8;  // LDS row stride of a tile (elements)
+
+// Tile column j <- source row r (8 elements at column f8 of the tile row).
+__device__ __forceinline__ void tile_put8(uint16_t (*tile)[kTP], int row, int f8, uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    tile[row][f8 + 2 * u] = static_cast<uint16_t>(w[u] & 0xFFFFu);
+    tile[row][f8 + 2 * u + 1] = static_cast<uint16_t>(w[u] >> 16);
+  }
+}
+
+// 8 elements tile[r8 .. r8+7][col] packed into 16 bytes.
+__device__ __forceinline__ uint4 tile_get8_column(const uint16_t (*tile)[kTP], int r8, int col) {
+  uint32_t w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    w[u] = static_cast<uint32_t>(tile[r8 + 2 * u][col]) | (static_cast<uint32_t>(tile[r8 + 2 * u + 1][col]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // dst[r][kofs[e] + i] = src[row(offsets[e] + i)][r] for the kept rows i of
-// expert e, 0 in the padding; row(s) = src_rows[s] or s. 64 x 64 tiles.
+// expert e, 0 in the padding; row(s) = src_rows[s] or s.
 __global__ __launch_bounds__(256) void transpose_groups_kernel(
     const bf16_t* __restrict__ src, const int32_t* __restrict__ src_rows, int R,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ kofs, int E, int S, int cap,
     bf16_t* __restrict__ dst, int ldk) {
-  __shared__ uint16_t tile[kTile][kTile + 2];
+  __shared__ uint16_t tile[kTile][kTP];  // [slot i][feature]
   __shared__ int e_s, beg_s, n_s;
   const int c0 = blockIdx.x * kTile;  // first padded column of the tile
   const int r0 = blockIdx.y * kTile;
@@ -65,58 +91,51 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(
   }
   __syncthreads();
   if (e_s < 0) return;  // past the last expert's range
-  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;  // 64 x 4
-  for (int i = ty; i < kTile; i += 4) {  // column i of the tile = grouped row beg_s + i
-    uint16_t v = 0;
-    if (i < n_s && r0 + tx < R) {
-      const int s = beg_s + i;
-      const int row = src_rows != nullptr ? src_rows[s] : s;
-      v = reinterpret_cast<const uint16_t*>(src)[static_cast<size_t>(row) * R + r0 + tx];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int q = threadIdx.x + 256 * h2;
+    const int i = q / 8, f8 = (q % 8) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (i < n_s && r0 + f8 < R) {
+      const int sl = beg_s + i;
+      const int row = src_rows != nullptr ? src_rows[sl] : sl;
+      v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * R + r0 + f8);
     }
-    tile[i][tx] = v;
+    tile_put8(tile, i, f8, v);
   }
   __syncthreads();
-  for (int r = ty; r < kTile; r += 4) {
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int q = threadIdx.x + 256 * h2;
+    const int r = q / 8, c8 = (q % 8) * 8;
     if (r0 + r < R)
-      reinterpret_cast<uint16_t*>(dst)[static_cast<size_t>(r0 + r) * ldk + c0 + tx] = tile[tx][r];
+      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r0 + r) * ldk + c0 + c8) = tile_get8_column(tile, c8, r);
   }
 }
 
 // dst[e][c][coff + r] = src[e][r][c]: src [E][R][C], dst rows of length ldd.
 __global__ __launch_bounds__(256) void transpose_weights_kernel(const bf16_t* __restrict__ src, int R, int C,
                                                                 bf16_t* __restrict__ dst, int ldd, int coff) {
-  __shared__ uint16_t tile[kTile][kTile + 2];
+  __shared__ uint16_t tile[kTile][kTP];  // [r][c]
   const int e = blockIdx.z;
   const int c0 = blockIdx.x * kTile, r0 = blockIdx.y * kTile;
-  const uint16_t* s = reinterpret_cast<const uint16_t*>(src) + static_cast<size_t>(e) * R * C;
-  uint16_t* d = reinterpret_cast<uint16_t*>(dst) + static_cast<size_t>(e) * C * ldd;
-  const int tx = threadIdx.x % kTile, ty = threadIdx.x / kTile;
-  for (int r = ty; r < kTile; r += 4)
-    tile[r][tx] = (r0 + r < R && c0 + tx < C) ? s[static_cast<size_t>(r0 + r) * C + c0 + tx] : 0;
+  const bf16_t* sp = src + static_cast<size_t>(e) * R * C;
+  bf16_t* dp = dst + static_cast<size_t>(e) * C * ldd;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int q = threadIdx.x + 256 * h2;
+    const int r = q / 8, c8 = (q % 8) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r0 + r < R && c0 + c8 < C) v = *reinterpret_cast<const uint4*>(sp + static_cast<size_t>(r0 + r) * C + c0 + c8);
+    tile_put8(tile, r, c8, v);
+  }
   __syncthreads();
-  for (int c = ty; c < kTile; c += 4)
-    if (c0 + c < C && r0 + tx < R) d[static_cast<size_t>(c0 + c) * ldd + coff + r0 + tx] = tile[tx][c];
-}
-
-__device__ __forceinline__ float sigmoid_fast(float z) {
-  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-}
-
-// a = act(z) for every grouped row (rows past a group's capacity are never read).
-__global__ __launch_bounds__(256) void act_forward_kernel(const bf16_t* __restrict__ z, int S, int w, int act,
-                                                          bf16_t* __restrict__ a) {
-  const size_t n = static_cast<size_t>(S) * w;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t s = i / w, c = i % w;
-    float v;
-    if (act == 1) {
-      const float z1 = bf16_to_f32(z[s * 2 * w + c]), z3 = bf16_to_f32(z[s * 2 * w + w + c]);
-      v = silu(z1) * z3;
-    } else {
-      v = gelu_exact(bf16_to_f32(z[i]));
-    }
-    a[i] = f32_to_bf16(v);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int q = threadIdx.x + 256 * h2;
+    const int c = q / 8, r8 = (q % 8) * 8;
+    if (c0 + c < C && r0 + r8 < R)
+      *reinterpret_cast<uint4*>(dp + static_cast<size_t>(c0 + c) * ldd + coff + r0 + r8) = tile_get8_column(tile, r8, c);
   }
 }
 
@@ -152,29 +171,6 @@ __global__ __launch_bounds__(256) void dout_kernel(const bf16_t* __restrict__ dy
     __syncthreads();
   }
   if (threadIdx.x == 0) dgate[tj] = red[0];
-}
-
-// dZ from dA (float32) and Z: SwiGLU dz1 = dA z3 silu'(z1), dz3 = dA silu(z1)
-// (rows of 2w); GELU dz = dA gelu'(z).
-__global__ __launch_bounds__(256) void act_backward_kernel(const float* __restrict__ dA, const bf16_t* __restrict__ z,
-                                                           int S, int w, int act, bf16_t* __restrict__ dZ) {
-  const size_t n = static_cast<size_t>(S) * w;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t s = i / w, c = i % w;
-    const float da = dA[i];
-    if (act == 1) {
-      const float z1 = bf16_to_f32(z[s * 2 * w + c]), z3 = bf16_to_f32(z[s * 2 * w + w + c]);
-      const float sg = sigmoid_fast(z1);
-      dZ[s * 2 * w + c] = f32_to_bf16(da * z3 * (sg * (1.0f + z1 * (1.0f - sg))));
-      dZ[s * 2 * w + w + c] = f32_to_bf16(da * (z1 * sg));
-    } else {
-      const float x = bf16_to_f32(z[i]);
-      const float gp = 0.5f * (1.0f + erff(x * 0.70710678118654752440f)) +
-                       x * expf(-0.5f * x * x) * 0.39894228040143267794f;
-      dZ[i] = f32_to_bf16(da * gp);
-    }
-  }
 }
 
 // One wave per token, lane = expert: d loss / d gate logits.
@@ -219,33 +215,57 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
 
 // dh[t] = sum_j dX[slot(t, j)] (ascending j, kept slots) + sum_e dl[t][e] W_r[k][e].
 // Block: 16 tokens; a thread keeps one row of W_r in registers across them.
+// EP = E padded to 8, 16, 32 or 64 (padding entries are 0). A thread covers KV
+// consecutive features (16-byte loads of dX when KV = 4) and keeps their W_r
+// rows in registers across the block's tokens.
 constexpr int kDhTokens = 16;
+template <int EP, int KV>
 __global__ __launch_bounds__(256) void dh_kernel(const float* __restrict__ dX, const int32_t* __restrict__ token_slot,
                                                  const float* __restrict__ dl, const float* __restrict__ Wr, int T,
                                                  int d, int E, int K, bf16_t* __restrict__ dh) {
-  __shared__ float dl_s[kDhTokens][64];
+  __shared__ float dl_s[kDhTokens][EP];
+  __shared__ int slot_s[kDhTokens][8];
   const int t0 = blockIdx.x * kDhTokens;
-  for (int i = threadIdx.x; i < kDhTokens * 64; i += 256) {
-    const int tt = t0 + i / 64, e = i % 64;
-    dl_s[i / 64][e] = (tt < T && e < E) ? dl[static_cast<size_t>(tt) * E + e] : 0.0f;
+  for (int i = threadIdx.x; i < kDhTokens * EP; i += 256) {
+    const int tt = t0 + i / EP, e = i % EP;
+    dl_s[i / EP][e] = (tt < T && e < E) ? dl[static_cast<size_t>(tt) * E + e] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < kDhTokens * 8; i += 256) {
+    const int tt = t0 + i / 8, j = i % 8;
+    slot_s[i / 8][j] = (tt < T && j < K) ? token_slot[tt * K + j] : -1;
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < d; k += 256) {
-    float wr[64];
+  for (int k0 = threadIdx.x * KV; k0 < d; k0 += 256 * KV) {  // d is a multiple of 8
+    float wr[KV][EP];
 #pragma unroll
-    for (int e = 0; e < 64; ++e) wr[e] = e < E ? Wr[static_cast<size_t>(k) * E + e] : 0.0f;
+    for (int v = 0; v < KV; ++v)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) wr[v][e] = e < E ? Wr[static_cast<size_t>(k0 + v) * E + e] : 0.0f;
     for (int i = 0; i < kDhTokens; ++i) {
       const int t = t0 + i;
       if (t >= T) break;
-      float acc = 0.0f;
-      for (int j = 0; j < K; ++j) {
-        const int s = token_slot[t * K + j];
-        if (s >= 0) acc += dX[static_cast<size_t>(s) * d + k];
-      }
-      float r = 0.0f;
+      float acc[KV];
 #pragma unroll
-      for (int e = 0; e < 64; ++e) r = fmaf(dl_s[i][e], wr[e], r);
-      dh[static_cast<size_t>(t) * d + k] = f32_to_bf16(acc + r);
+      for (int v = 0; v < KV; ++v) acc[v] = 0.0f;
+      for (int j = 0; j < K; ++j) {
+        const int s = slot_s[i][j];
+        if (s < 0) continue;
+        const float* src = dX + static_cast<size_t>(s) * d + k0;
+        if constexpr (KV == 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src);
+          acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
+        } else {
+#pragma unroll
+          for (int v = 0; v < KV; ++v) acc[v] += src[v];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < KV; ++v) {
+        float r = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) r = fmaf(dl_s[i][e], wr[v][e], r);
+        dh[static_cast<size_t>(t) * d + k0 + v] = f32_to_bf16(acc[v] + r);
+      }
     }
   }
 }
@@ -253,31 +273,31 @@ __global__ __launch_bounds__(256) void dh_kernel(const float* __restrict__ dX, c
 // Partial sums over chunks of kWrChunk tokens: part[c][k][e] = sum_t h[t][k] dl[t][e];
 // column e of chunk c, row k: one thread, tokens in order.
 constexpr int kWrChunk = 256;
+template <int EP>
 __global__ __launch_bounds__(256) void dwr_partial_kernel(const bf16_t* __restrict__ h, const float* __restrict__ dl,
                                                           int T, int d, int E, float* __restrict__ part) {
-  __shared__ float dl_s[kWrChunk][65];
+  __shared__ float dl_s[kWrChunk][EP + 1];
   const int c = blockIdx.y;
   const int t0 = c * kWrChunk;
   const int nt = min(kWrChunk, T - t0);
-  for (int i = threadIdx.x; i < kWrChunk * E; i += 256) {
-    const int tt = i / E, e = i % E;
-    dl_s[tt][e] = tt < nt ? dl[static_cast<size_t>(t0 + tt) * E + e] : 0.0f;
+  for (int i = threadIdx.x; i < kWrChunk * EP; i += 256) {
+    const int tt = i / EP, e = i % EP;
+    dl_s[tt][e] = (tt < nt && e < E) ? dl[static_cast<size_t>(t0 + tt) * E + e] : 0.0f;
   }
   __syncthreads();
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (k >= d) return;
-  float acc[64];
+  float acc[EP];
 #pragma unroll
-  for (int e = 0; e < 64; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < EP; ++e) acc[e] = 0.0f;
   for (int tt = 0; tt < nt; ++tt) {
     const float hv = bf16_to_f32(h[static_cast<size_t>(t0 + tt) * d + k]);
 #pragma unroll
-    for (int e = 0; e < 64; ++e)
-      if (e < E) acc[e] = fmaf(hv, dl_s[tt][e], acc[e]);
+    for (int e = 0; e < EP; ++e) acc[e] = fmaf(hv, dl_s[tt][e], acc[e]);  // padding columns are 0
   }
   float* dst = part + (static_cast<size_t>(c) * d + k) * E;
 #pragma unroll
-  for (int e = 0; e < 64; ++e)
+  for (int e = 0; e < EP; ++e)
     if (e < E) dst[e] = acc[e];
 }
 
@@ -343,23 +363,11 @@ hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_act_forward(const void* z, int S, int w, int act, void* a, hipStream_t st) {
-  hipLaunchKernelGGL(act_forward_kernel, dim3(grid1d(static_cast<size_t>(S) * w)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(z), S, w, act, static_cast<bf16_t*>(a));
-  return hipGetLastError();
-}
-
 hipError_t launch_dout(const void* dy, const float* o_perm, const int32_t* token_slot, const float* gate, int T,
                        int d, int K, void* dO, float* dgate, hipStream_t st) {
   hipLaunchKernelGGL(dout_kernel, dim3(static_cast<unsigned>(T * K)), dim3(256), 0, st,
                      static_cast<const bf16_t*>(dy), o_perm, token_slot, gate, d, K, static_cast<bf16_t*>(dO),
                      dgate);
-  return hipGetLastError();
-}
-
-hipError_t launch_act_backward(const float* dA, const void* z, int S, int w, int act, void* dZ, hipStream_t st) {
-  hipLaunchKernelGGL(act_backward_kernel, dim3(grid1d(static_cast<size_t>(S) * w)), dim3(256), 0, st, dA,
-                     static_cast<const bf16_t*>(z), S, w, act, static_cast<bf16_t*>(dZ));
   return hipGetLastError();
 }
 
@@ -371,11 +379,21 @@ hipError_t launch_router_backward(const float* logits, const float* br, int bias
   return hipGetLastError();
 }
 
+template <int EP>
+hipError_t launch_dh_ep(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
+                        int E, int K, void* dh, hipStream_t st) {
+  constexpr int KV = EP <= 16 ? 4 : 1;
+  hipLaunchKernelGGL((dh_kernel<EP, KV>), dim3(static_cast<unsigned>((T + kDhTokens - 1) / kDhTokens)), dim3(256), 0,
+                     st, dX, token_slot, dl, Wr, T, d, E, K, static_cast<bf16_t*>(dh));
+  return hipGetLastError();
+}
+
 hipError_t launch_dh(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
                      int E, int K, void* dh, hipStream_t st) {
-  hipLaunchKernelGGL(dh_kernel, dim3(static_cast<unsigned>((T + kDhTokens - 1) / kDhTokens)), dim3(256), 0, st,
-                     dX, token_slot, dl, Wr, T, d, E, K, static_cast<bf16_t*>(dh));
-  return hipGetLastError();
+  if (E <= 8) return launch_dh_ep<8>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+  if (E <= 16) return launch_dh_ep<16>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+  if (E <= 32) return launch_dh_ep<32>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+  return launch_dh_ep<64>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
 }
 
 int dwr_chunks(int T) { return (T + kWrChunk - 1) / kWrChunk; }
@@ -383,8 +401,12 @@ int dwr_chunks(int T) { return (T + kWrChunk - 1) / kWrChunk; }
 hipError_t launch_dwr(const void* h, const float* dl, int T, int d, int E, float* part, float* dWr, float* dbr,
                       hipStream_t st) {
   const int nc = dwr_chunks(T);
-  hipLaunchKernelGGL(dwr_partial_kernel, dim3(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(nc)),
-                     dim3(256), 0, st, static_cast<const bf16_t*>(h), dl, T, d, E, part);
+  const dim3 grid(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(nc));
+  const bf16_t* hb = static_cast<const bf16_t*>(h);
+  if (E <= 8) hipLaunchKernelGGL(dwr_partial_kernel<8>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+  else if (E <= 16) hipLaunchKernelGGL(dwr_partial_kernel<16>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+  else if (E <= 32) hipLaunchKernelGGL(dwr_partial_kernel<32>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+  else hipLaunchKernelGGL(dwr_partial_kernel<64>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
   hipLaunchKernelGGL(dwr_final_kernel, dim3(static_cast<unsigned>((static_cast<size_t>(d) * E + 255) / 256)),
                      dim3(256), 0, st, part, nc, dl, T, d, E, dWr, dbr);
   return hipGetLastError();

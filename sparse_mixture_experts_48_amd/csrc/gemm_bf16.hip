@@ -36,7 +36,10 @@ enum {
   G1_SWIGLU = 0, G1_GELU = 1, G2_OPERM = 2, G2_FUSED_Y = 3,
   // backward pass: the first GEMM's pre-activations (SwiGLU: x W1 and x W3,
   // side by side in rows of 2N; GELU: x W1 + b1), and the weight gradients
-  G1_SWIGLU_Z = 4, G1_GELU_Z = 5, G_WGRAD = 6
+  G1_SWIGLU_Z = 4, G1_GELU_Z = 5, G_WGRAD = 6,
+  // backward pass: dA = dO W2 with the activation's gradient applied in the
+  // epilogue, writing dZ (SwiGLU: [dz1 | dz3] in rows of 2N; GELU: dz)
+  G2_DZ_SWIGLU = 7, G2_DZ_GELU = 8
 };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -64,6 +67,8 @@ struct GemmParams {
   const int32_t* kofs;
   int M, ldk, split;
   float* out2;
+  void* out_act;       // G1_*_Z: also the activation a = act(z), bfloat16 [S][N]
+  const bf16_t* zin;   // G2_DZ_*: the pre-activations written by G1_*_Z
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -345,17 +350,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * (WTN / NMAT) + j * 32 + g * 8 + (lane / 32) * 4;
         if (n >= N) continue;  // N % 8 == 0: four columns are all in or all out
-        if constexpr (MODE == G1_SWIGLU_Z) {  // x W1 | x W3 side by side, rows of 2N
-          float z1[4], z3[4];
+        if constexpr (MODE == G1_SWIGLU_Z) {  // x W1 | x W3 side by side, rows of 2N; and a
+          float z1[4], z3[4], av[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             z1[q] = acc[j][i][g * 4 + q];
             z3[q] = acc[j + TNO][i][g * 4 + q];
+            av[q] = silu(z1[q]) * z3[q];
           }
           bf16_t* row = static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * 2 * N;
           *reinterpret_cast<u32x2_t*>(row + n) = u32x2_t{pack_bf16x2(z1[0], z1[1]), pack_bf16x2(z1[2], z1[3])};
           *reinterpret_cast<u32x2_t*>(row + N + n) =
               u32x2_t{pack_bf16x2(z3[0], z3[1]), pack_bf16x2(z3[2], z3[3])};
+          *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out_act) + static_cast<size_t>(s) * N + n) =
+              u32x2_t{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
           continue;
         }
         float v[4];
@@ -372,6 +380,43 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
         if (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_GELU_Z) {
           *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          if (MODE == G1_GELU_Z) {
+            *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out_act) + static_cast<size_t>(s) * N + n) =
+                u32x2_t{pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
+                        pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
+          }
+        } else if (MODE == G2_DZ_SWIGLU) {  // v = dA; dz1 = dA z3 silu'(z1), dz3 = dA silu(z1)
+          const bf16_t* zr = p.zin + static_cast<size_t>(s) * 2 * N;
+          const u32x2_t z1p = *reinterpret_cast<const u32x2_t*>(zr + n);
+          const u32x2_t z3p = *reinterpret_cast<const u32x2_t*>(zr + N + n);
+          const uint32_t z1w[2] = {z1p[0], z1p[1]}, z3w[2] = {z3p[0], z3p[1]};
+          float d1[4], d3[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t a1 = z1w[q / 2], a3 = z3w[q / 2];
+            const float z1 = __uint_as_float(q % 2 ? (a1 & 0xFFFF0000u) : (a1 << 16));
+            const float z3 = __uint_as_float(q % 2 ? (a3 & 0xFFFF0000u) : (a3 << 16));
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1 * -1.4426950408889634f));
+            d1[q] = v[q] * z3 * (sg * (1.0f + z1 * (1.0f - sg)));
+            d3[q] = v[q] * (z1 * sg);
+          }
+          bf16_t* orow = static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * 2 * N;
+          *reinterpret_cast<u32x2_t*>(orow + n) = u32x2_t{pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3])};
+          *reinterpret_cast<u32x2_t*>(orow + N + n) = u32x2_t{pack_bf16x2(d3[0], d3[1]), pack_bf16x2(d3[2], d3[3])};
+        } else if (MODE == G2_DZ_GELU) {  // dz = dA gelu'(z)
+          const u32x2_t zp = *reinterpret_cast<const u32x2_t*>(p.zin + static_cast<size_t>(s) * N + n);
+          const uint32_t zw[2] = {zp[0], zp[1]};
+          float dz[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t a = zw[q / 2];
+            const float x = __uint_as_float(q % 2 ? (a & 0xFFFF0000u) : (a << 16));
+            const float gp = 0.5f * (1.0f + erff(x * 0.70710678118654752440f)) +
+                             x * expf(-0.5f * x * x) * 0.39894228040143267794f;
+            dz[q] = v[q] * gp;
+          }
+          *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n) =
+              u32x2_t{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
         } else if (MODE == G_WGRAD) {
           float* dst = s < p.split
                            ? static_cast<float*>(p.out) + (static_cast<size_t>(e) * p.split + s) * N + n
@@ -640,8 +685,9 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
 
 namespace moe {
 
-hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, hipStream_t st) {
+hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, void* a, hipStream_t st) {
   GemmParams p{};
+  p.out_act = a;
   p.x = static_cast<const bf16_t*>(f.x);
   p.x_rows = f.x_rows;
   p.x_nrows = f.x_rows != nullptr ? f.S / f.K : f.S;
@@ -673,6 +719,23 @@ hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets,
   p.Kd = Kd;
   p.S = S;
   return launch_tile_auto<G2_OPERM>(p, S, st);
+}
+
+hipError_t launch_bwd_dz_bf16(const void* dO, int S, const int32_t* offsets, int cap, int E, const void* W2T, int N,
+                              int Kd, const void* z, int act, void* dZ, hipStream_t st) {
+  GemmParams p{};
+  p.x = static_cast<const bf16_t*>(dO);
+  p.x_nrows = S;
+  p.cap = cap;
+  p.offsets = offsets;
+  p.B = static_cast<const bf16_t*>(W2T);
+  p.zin = static_cast<const bf16_t*>(z);
+  p.out = dZ;
+  p.E = E;
+  p.N = N;
+  p.Kd = Kd;
+  p.S = S;
+  return act == 1 ? launch_tile_auto<G2_DZ_SWIGLU>(p, S, st) : launch_tile_auto<G2_DZ_GELU>(p, S, st);
 }
 
 hipError_t launch_bwd_wgrad_bf16(const void* A, int M, const void* B, int N, int ldk, const int32_t* kofs, int E,

@@ -73,8 +73,12 @@ hipError_t launch_combine(const float* o_perm, const int32_t* token_slot, const 
 
 // ---- backward pass (bfloat16 layers)
 // First GEMM without its activation: SwiGLU z = [x W1 | x W3] as rows of 2*width,
-// GELU z = x W1 + b1; grouped rows as in launch_gemm1.
-hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, hipStream_t st);
+// GELU z = x W1 + b1; grouped rows as in launch_gemm1; also a = act(z) [S][width].
+hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, void* a, hipStream_t st);
+// dZ = (dO W2) * act'(z) for the grouped rows: W2T stored [E][N = width][Kd = d];
+// z as written by launch_bwd_z_bf16; dZ like z (bfloat16).
+hipError_t launch_bwd_dz_bf16(const void* dO, int S, const int32_t* offsets, int cap, int E, const void* W2T, int N,
+                              int Kd, const void* z, int act, void* dZ, hipStream_t st);
 // out[s] = x[s] . B_e^T (+ bias_e) (float32) for the grouped rows s of every
 // expert e (the first cap of each group); B stored [E][N][Kd], bias [E][N] or null.
 hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets, int cap, int E, const void* B,
@@ -91,10 +95,8 @@ hipError_t launch_transpose_groups(const void* src, const int32_t* src_rows, int
                                    hipStream_t st);
 hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* dst, int ldd, int coff,
                                     hipStream_t st);
-hipError_t launch_act_forward(const void* z, int S, int w, int act, void* a, hipStream_t st);
 hipError_t launch_dout(const void* dy, const float* o_perm, const int32_t* token_slot, const float* gate, int T,
                        int d, int K, void* dO, float* dgate, hipStream_t st);
-hipError_t launch_act_backward(const float* dA, const void* z, int S, int w, int act, void* dZ, hipStream_t st);
 hipError_t launch_router_backward(const float* logits, const float* br, int bias_select, const int32_t* topk_idx,
                                   const float* gate, const float* dgate, const int32_t* counts, int T, int E,
                                   int K, int gate_mode, float daux, float* dl, hipStream_t st);
