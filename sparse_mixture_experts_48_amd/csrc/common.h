@@ -64,28 +64,51 @@ __device__ __forceinline__ void expert_rows(const int32_t* __restrict__ offsets,
   *end = b + min(n, cap);  // cap may be INT_MAX: never form b + cap
 }
 
-// Which expert owns global m-tile `mt` when every expert's rows are cut into
-// tiles of `bm` rows. Returns false if `mt` is past the last tile.
-// offsets: [E+1] exclusive prefix of the per-expert row counts (clamped to [0, S));
-// each expert contributes at most cap rows.
-__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ offsets, int E, int S, int cap,
-                                            int bm, int mt, int* expert, int* row0, int* rows) {
-  int acc = 0;
-  for (int e = 0; e < E; ++e) {
-    int beg, end;
-    expert_rows(offsets, e, S, cap, &beg, &end);
-    const int cnt = end - beg;
-    const int nt = (cnt + bm - 1) / bm;
-    if (mt < acc + nt) {
-      const int local = mt - acc;
-      *expert = e;
-      *row0 = beg + local * bm;
-      *rows = min(bm, cnt - local * bm);
-      return true;
-    }
-    acc += nt;
+// Ragged m-tiles: every expert's rows (at most cap of them) are cut into tiles
+// of `bm` rows, experts in index order.
+// The enumeration is done by one wave at once (E <= 64; every lane of the
+// wave must be active): lane e holds expert e's row range and tile count, a
+// prefix sum over the lanes gives every expert's first tile, and a ballot finds
+// the owner of a tile. One round of loads instead of a serial scan over E.
+struct WaveTiles {
+  int beg, cnt, incl;  // this lane's expert: first row, rows, tiles up to and including it
+  int total;           // m-tiles over all experts (wave-uniform)
+};
+
+__device__ __forceinline__ WaveTiles wave_tiles(const int32_t* __restrict__ offsets, int E, int S, int cap,
+                                                int bm) {
+  const int lane = static_cast<int>(threadIdx.x % 64);
+  WaveTiles w{0, 0, 0, 0};
+  int nt = 0;
+  if (lane < E) {
+    int b, e;
+    expert_rows(offsets, lane, S, cap, &b, &e);
+    w.beg = b;
+    w.cnt = e - b;
+    nt = (w.cnt + bm - 1) / bm;
   }
-  return false;
+  int incl = nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  w.incl = incl;
+  w.total = __shfl(incl, 63);
+  return w;
+}
+
+// Owner of m-tile mt (wave-uniform, 0 <= mt < w.total).
+__device__ __forceinline__ void wave_tile_owner(const WaveTiles& w, int bm, int mt, int* expert, int* row0,
+                                                int* rows) {
+  // tile counts are non-negative, so the lanes whose tiles all lie at or
+  // before mt form a prefix of the wave
+  const int e = __popcll(__ballot(w.incl <= mt));
+  const int first = __shfl(w.incl, e) - (__shfl(w.cnt, e) + bm - 1) / bm;
+  const int local = mt - first;
+  *expert = e;
+  *row0 = __shfl(w.beg, e) + local * bm;
+  *rows = min(bm, __shfl(w.cnt, e) - local * bm);
 }
 
 }  // namespace moe

@@ -164,27 +164,47 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int NCOLS = BN / NMAT;        // output columns per block
   static_assert(TM >= 1 && TN >= NMAT && A_IN >= 1 && B_IN >= 1, "tile too small");
   static_assert(WTM % 32 == 0 && WTN % (32 * NMAT) == 0, "wave tile");
-  static_assert(2 * A_IN + B_IN <= 63, "vmcnt range");
-  static_assert((3 * BM + 2 * BN) * kCH * 16 <= 160 * 1024, "LDS");
+  // Weight ring: two slots (weights one stage ahead) when that lets two blocks
+  // share a CU or a third slot does not fit; else three (two stages ahead,
+  // like the tokens), for tiles whose stage is too short to cover a trip to HBM.
+  constexpr int kLds2 = (3 * BM + 2 * BN) * kCH * 16, kLds3 = (3 * BM + 3 * BN) * kCH * 16;
+  constexpr int NBS = (kLds2 > 80 * 1024 && kLds3 <= 160 * 1024) ? 3 : 2;
+  constexpr int DB = NBS - 1;                       // weight prefetch distance in stages
+  constexpr int WAITN = NBS == 3 ? A_IN + B_IN : A_IN;  // loads that may stay in flight at a stage start
+  static_assert(WAITN + A_IN + B_IN <= 63, "vmcnt range");
+  static_assert((3 * BM + NBS * BN) * kCH * 16 <= 160 * 1024, "LDS");
 
   // One array per ring slot, so that reads of one slot are known not to alias
   // the direct loads that fill another.
   __shared__ u32x4_t A0[BM * kCH], A1[BM * kCH], A2[BM * kCH];
   __shared__ u32x4_t B0[BN * kCH], B1[BN * kCH];
+  u32x4_t* B2 = B0;  // third weight slot, declared only where it fits
+  if constexpr (NBS == 3) {
+    __shared__ u32x4_t B2s[BN * kCH];
+    B2 = B2s;
+  }
 
   // XCD-aware order. Hardware sends block b to XCD b % 8; give each XCD a
   // contiguous run of logical tiles, ordered (n-tile group of kNG) x (m-tile)
   // x (n-tile in group), so the blocks that run together on one XCD share
-  // their token and weight slices in that XCD's L2.
+  // their token and weight slices in that XCD's L2. The grid is sized for the
+  // most m-tiles any grouping can have; the runs are cut from the m-tiles this
+  // grouping has (counted from the offsets), so every XCD gets an equal share
+  // and the surplus blocks exit at once.
   constexpr int kNG = kTileGroupN;
   const int n_nt = (p.N + NCOLS - 1) / NCOLS;
   const int n_ntg = (n_nt + kNG - 1) / kNG;
-  const int total = n_ntg * p.n_mt * kNG;
+  WaveTiles wt{};
+  if constexpr (!WGRAD) wt = wave_tiles(p.offsets, p.E, p.S, p.cap, BM);
+  const int n_mt = WGRAD ? p.n_mt : min(p.n_mt, wt.total);
+  const int total = n_ntg * n_mt * kNG;
   const int per_xcd = (total + 7) / 8;
-  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int xi = static_cast<int>(blockIdx.x / 8);
+  if (xi >= per_xcd) return;
+  const int t = static_cast<int>(blockIdx.x % 8) * per_xcd + xi;
   if (t >= total) return;
-  const int nt = (t / (kNG * p.n_mt)) * kNG + t % kNG;
-  const int mt = (t / kNG) % p.n_mt;
+  const int nt = (t / (kNG * n_mt)) * kNG + t % kNG;
+  const int mt = (t / kNG) % n_mt;
   if (nt >= n_nt) return;
   int e, row0, rows;
   if constexpr (WGRAD) {  // fixed M rows for every expert: m-tile mt = (expert, tile)
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     rows = min(BM, p.M - row0);
     if (e >= p.E) return;
   } else {
-    if (!find_m_tile(p.offsets, p.E, p.S, p.cap, BM, mt, &e, &row0, &rows)) return;
+    wave_tile_owner(wt, BM, mt, &e, &row0, &rows);
   }
   const int n0 = nt * NCOLS;
 
@@ -276,10 +296,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const int frow = lane % 32;
   const int fsub = lane / 32;  // which of the two 8-wide k chunks of a 16-k step
 
-  // Stage kt: MFMAs on slots (As, Bs); loads of weights (kt+1) into Bn and of
+  // Stage kt: MFMAs on slots (As, Bs); loads of weights (kt+DB) into Bn and of
   // tokens (kt+2) into An2, weights first.
   auto run_stage = [&](int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* Bn, u32x4_t* An2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(A_IN));  // all but this wave's newest token batch landed
+    // all of this wave's loads for stage kt landed: with DB = 1 the newest
+    // token batch may still be in flight, with DB = 2 the newest stage's batch
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAITN));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();                 // ... for every wave
     asm volatile("" ::: "memory");
@@ -297,7 +319,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const int idx = ks * PER + q;
-        if (idx < B_IN) load_b(idx, (kt + 1) * kBK, Bn);
+        if (idx < B_IN) load_b(idx, (kt + DB) * kBK, Bn);
         else if (idx < A_IN + B_IN) load_a(idx - B_IN, (kt + 2) * kBK, An2);
       }
       asm volatile("" ::: "memory");  // keep the loads ahead of the later fragment reads
@@ -310,29 +332,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     }
   };
 
-  // Prologue: tokens of stages 0 and 1, weights of stage 0 (in the order the
-  // stage waits expect: the newest token batch may stay in flight).
+  // Prologue, in the order the stage waits expect. DB = 1: tokens of stage 0,
+  // weights of stage 0, tokens of stage 1 (the newest token batch may stay in
+  // flight). DB = 2: weights and tokens of stage 0, then of stage 1.
+  if constexpr (NBS == 3) {
 #pragma unroll
-  for (int u = 0; u < A_IN; ++u) load_a(u, 0, A0);
+    for (int u = 0; u < B_IN; ++u) load_b(u, 0, B0);
 #pragma unroll
-  for (int u = 0; u < B_IN; ++u) load_b(u, 0, B0);
+    for (int u = 0; u < A_IN; ++u) load_a(u, 0, A0);
 #pragma unroll
-  for (int u = 0; u < A_IN; ++u) load_a(u, kBK, A1);
-  // Straight-line ring over lcm(3, 2) = 6 stages: no merge point for acc inside the loop.
-  int kt = 0;
-  for (; kt + 6 <= nk; kt += 6) {
-    run_stage(kt, A0, B0, B1, A2);
-    run_stage(kt + 1, A1, B1, B0, A0);
-    run_stage(kt + 2, A2, B0, B1, A1);
-    run_stage(kt + 3, A0, B1, B0, A2);
-    run_stage(kt + 4, A1, B0, B1, A0);
-    run_stage(kt + 5, A2, B1, B0, A1);
+    for (int u = 0; u < B_IN; ++u) load_b(u, kBK, B1);
+#pragma unroll
+    for (int u = 0; u < A_IN; ++u) load_a(u, kBK, A1);
+  } else {
+#pragma unroll
+    for (int u = 0; u < A_IN; ++u) load_a(u, 0, A0);
+#pragma unroll
+    for (int u = 0; u < B_IN; ++u) load_b(u, 0, B0);
+#pragma unroll
+    for (int u = 0; u < A_IN; ++u) load_a(u, kBK, A1);
   }
-  if (kt < nk) run_stage(kt, A0, B0, B1, A2);
-  if (kt + 1 < nk) run_stage(kt + 1, A1, B1, B0, A0);
-  if (kt + 2 < nk) run_stage(kt + 2, A2, B0, B1, A1);
-  if (kt + 3 < nk) run_stage(kt + 3, A0, B1, B0, A2);
-  if (kt + 4 < nk) run_stage(kt + 4, A1, B0, B1, A0);
+  // Straight-line ring over lcm(3, NBS) stages: no merge point for acc inside
+  // the loop. Stage i uses token slot i % 3 and weight slot i % NBS and fills
+  // token slot (i + 2) % 3 and weight slot (i + DB) % NBS.
+  u32x4_t* const as[3] = {A0, A1, A2};
+  u32x4_t* const bs[3] = {B0, B1, B2};
+  constexpr int RING = NBS == 3 ? 3 : 6;
+  int kt = 0;
+  for (; kt + RING <= nk; kt += RING) {
+#pragma unroll
+    for (int i = 0; i < RING; ++i) run_stage(kt + i, as[i % 3], bs[i % NBS], bs[(i + DB) % NBS], as[(i + 2) % 3]);
+  }
+#pragma unroll
+  for (int i = 0; i + 1 < RING; ++i)
+    if (kt + i < nk) run_stage(kt + i, as[i % 3], bs[i % NBS], bs[(i + DB) % NBS], as[(i + 2) % 3]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
   asm volatile("" ::: "memory");
 

@@ -39,7 +39,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
   const int mt = blockIdx.x % p.n_mt;
   const int nt = blockIdx.x / p.n_mt;
   int e, row0, rows;
-  if (!find_m_tile(p.offsets, p.E, p.S, p.cap, kFBM, mt, &e, &row0, &rows)) return;
+  const WaveTiles wt = wave_tiles(p.offsets, p.E, p.S, p.cap, kFBM);
+  if (mt >= wt.total) return;
+  wave_tile_owner(wt, kFBM, mt, &e, &row0, &rows);
   const int n0 = nt * kFBN;
   const int tid = threadIdx.x;
   const int tx = tid % 16, ty = tid / 16;

@@ -58,6 +58,12 @@ SMALL = {
     "bf16_short_k": L("bf16_short_k", 300, 40, 4, 2, 48, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 28),
     "T1": L("T1", 1, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 26),
     "f32_T1": L("f32_T1", 1, 64, 8, 2, 64, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2", 27),
+    # ragged groups of small mean size with long reductions: many one-tile
+    # experts beside a few many-tile ones
+    "ragged_switch_k1": L("ragged_switch_k1", 600, 1024, 16, 1, 1024, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
+                         "zipf1.1", 41),
+    "ragged_gelu_k2": L("ragged_gelu_k2", 300, 1024, 32, 2, 1032, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16,
+                       "zipf1.1", 42),
 }
 
 
@@ -239,6 +245,34 @@ def test_permute_skips_out_of_range_ids():
     H.check_bits_equal("slot_token", H.to_np(g["slot_token"])[:n], tt[order])
     rows = torch.from_numpy(tt[order].astype(np.int64)).cuda()
     assert torch.equal(g["h_perm"][:n].view(torch.int16), dev["h"][rows].view(torch.int16))
+
+
+@pytest.mark.parametrize("act", [W.ACT_SWIGLU, W.ACT_GELU])
+def test_group_size_boundaries(act):
+    """Group sizes on both sides of the 16-, 32-, 64- and 128-row tile and
+    fragment edges, with empty groups between, given to moe_expert_ffn
+    directly as offsets over rows in token order (the tiled kernels enumerate
+    their tiles from these offsets on the device)."""
+    sizes = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 128, 129, 200, 0, 5]
+    T = int(sum(sizes))
+    cfg = L("group_bounds", T, 1024, len(sizes), 1, 1032, act, W.GATE_RAW, W.DT_BF16, "none", 43)
+    H.say("[gpu] group size boundaries %s" % (cfg,))
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    o = moe.expert_ffn(moe.desc_of(cfg), dev["h"], torch.from_numpy(offs).cuda(), dev["W1"], dev["b1"],
+                       dev["W3"], dev["W2"], dev["b2"])
+    torch.cuda.synchronize()
+    o = H.to_np(o)
+    p = H.oracle_params(inp)
+    ref = np.zeros((T, cfg.d))
+    for e, n in enumerate(sizes):
+        if n:
+            ref[offs[e]:offs[e + 1]] = O.expert_ffn(p["h"][offs[e]:offs[e + 1]], e, p, act)
+    for e, n in enumerate(sizes):
+        if n:
+            err = H.rel_err(o[offs[e]:offs[e + 1]], ref[offs[e]:offs[e + 1]])
+            assert err <= H.Y_TOL[cfg.dtype], (e, n, err)
 
 
 FULL = ["micro", "skewed", "mixtral_prefill", "mixtral_decode", "switch_top1"]
