@@ -202,24 +202,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // contiguous run of logical tiles, ordered (n-tile group of kNG) x (m-tile)
   // x (n-tile in group), so the blocks that run together on one XCD share
   // their token and weight slices in that XCD's L2. The grid is sized for the
-  // most m-tiles any grouping can have; the runs are cut from the m-tiles this
-  // grouping has (counted from the offsets), so every XCD gets an equal share
-  // and the surplus blocks exit at once.
+  // most m-tiles any grouping can have; the runs are cut from the tiles this
+  // grouping has (m-tiles counted from the offsets, and the last group of
+  // n-tiles may hold fewer than kNG), so every XCD gets an equal share and the
+  // surplus blocks exit at once.
   constexpr int kNG = kTileGroupN;
   const int n_nt = (p.N + NCOLS - 1) / NCOLS;
-  const int n_ntg = (n_nt + kNG - 1) / kNG;
   WaveTiles wt{};
   if constexpr (!WGRAD) wt = wave_tiles(p.offsets, p.E, p.S, p.cap, BM);
   const int n_mt = WGRAD ? p.n_mt : min(p.n_mt, wt.total);
-  const int total = n_ntg * n_mt * kNG;
-  const int per_xcd = (total + 7) / 8;
+  const int n_t = n_nt * n_mt;
+  const int per_xcd = (n_t + 7) / 8;
   const int xi = static_cast<int>(blockIdx.x / 8);
   if (xi >= per_xcd) return;
   const int t = static_cast<int>(blockIdx.x % 8) * per_xcd + xi;
-  if (t >= total) return;
-  const int nt = (t / (kNG * n_mt)) * kNG + t % kNG;
-  const int mt = (t / kNG) % n_mt;
-  if (nt >= n_nt) return;
+  if (t >= n_t) return;
+  // logical tile t -> (n-tile group g of up to kNG n-tiles, m-tile, n-tile in group)
+  const int g = t / (kNG * n_mt);
+  const int gs = min(kNG, n_nt - g * kNG);
+  const int rem = t - g * kNG * n_mt;
+  const int mt = rem / gs;
+  const int nt = g * kNG + rem % gs;
   int e, row0, rows;
   if constexpr (WGRAD) {  // fixed M rows for every expert: m-tile mt = (expert, tile)
     const int n_mte = (p.M + BM - 1) / BM;
@@ -625,7 +628,7 @@ hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   p.n_mt = MODE == G_WGRAD ? p.E * ((p.M + BM - 1) / BM) : (S + BM - 1) / BM + min(p.E, S);
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
-  const size_t total = static_cast<size_t>((n_nt + kTileGroupN - 1) / kTileGroupN) * p.n_mt * kTileGroupN;
+  const size_t total = static_cast<size_t>(n_nt) * p.n_mt;
   const size_t grid = (total + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * 64), 0, st, p);

@@ -64,6 +64,10 @@ SMALL = {
                          "zipf1.1", 41),
     "ragged_gelu_k2": L("ragged_gelu_k2", 300, 1024, 32, 2, 1032, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16,
                        "zipf1.1", 42),
+    # K = 1 over 64 experts, 13 of them hit, on 128 x 256 tiles: the gated
+    # scatter into y from a grid far smaller than the chip
+    "ragged_fused_k1": L("ragged_fused_k1", 400, 2048, 64, 1, 520, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
+                         "zipf1.1", 60),
 }
 
 
