@@ -39,16 +39,40 @@ def short_name(kernel: str) -> str:
     return k.strip()
 
 
-def summarize_trace(stats_csv: str, command: str, title: str) -> str:
+def dispatch_medians(trace_csv: str) -> dict:
+    """{kernel name: median duration in ns} over the dispatches of a
+    ``--kernel-trace`` CSV (the mean of a short profiled run is pulled up by
+    its first, cold launches)."""
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        per.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for name, d in per.items():
+        d.sort()
+        n = len(d)
+        out[name] = d[n // 2] if n % 2 else 0.5 * (d[n // 2 - 1] + d[n // 2])
+    return out
+
+
+def summarize_trace(stats_csv: str, command: str, title: str, trace_csv: str = None) -> str:
     rows = list(csv.DictReader(open(stats_csv)))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
-    out = ["# %s" % title, "", "Command:", "", "```", command, "```", "",
-           "| kernel | calls | mean (us) | min (us) | max (us) | share of GPU time |",
-           "|---|---:|---:|---:|---:|---:|"]
+    med = dispatch_medians(trace_csv) if trace_csv else None
+    out = ["# %s" % title, "", "Command:", "", "```", command, "```", ""]
+    if med is None:
+        out += ["| kernel | calls | mean (us) | min (us) | max (us) | share of GPU time |",
+                "|---|---:|---:|---:|---:|---:|"]
+    else:
+        out += ["| kernel | calls | mean (us) | median (us) | min (us) | max (us) | share of GPU time |",
+                "|---|---:|---:|---:|---:|---:|---:|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f %% |" % (
-            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-            float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
+        cells = [float(r["AverageNs"]) / 1e3]
+        if med is not None:
+            cells.append(med.get(r["Name"], float("nan")) / 1e3)
+        cells += [float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3]
+        out.append("| `%s` | %s | %s | %.1f %% |" % (
+            short_name(r["Name"]), r["Calls"], " | ".join("%.1f" % c for c in cells),
+            100.0 * float(r["TotalDurationNs"]) / total))
     return "\n".join(out) + "\n"
 
 
@@ -134,6 +158,7 @@ def main():
     t.add_argument("stats_csv")
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="Kernel trace")
+    t.add_argument("--trace-csv", default=None, help="per-dispatch kernel trace CSV: adds a median column")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_csv")
     f.add_argument("write_csv")
@@ -145,7 +170,7 @@ def main():
     a = ap.parse_args()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     if a.what == "trace":
-        print(summarize_trace(a.stats_csv, a.command, a.title), end="")
+        print(summarize_trace(a.stats_csv, a.command, a.title, a.trace_csv), end="")
     else:
         kernels = OrderedDict(kv.split("=", 1) for kv in a.kernel)
         print(summarize_traffic(a.fetch_csv, a.write_csv, a.copy_mib, kernels, a.source, a.workload, a.command,

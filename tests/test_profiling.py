@@ -41,3 +41,26 @@ def test_short_kernel_names():
         "void moe::(anonymous namespace)::gemm_tile_kernel<256, 256, 4, 2, 0>(moe::(anonymous namespace)::GemmParams)"
     ) == "gemm_tile_kernel<256, 256, 4, 2, 0>"
     assert profiling.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_trace_medians(tmp_path):
+    """The median column comes from the per-dispatch trace (odd and even
+    counts), beside the stats file's mean."""
+    import csv as _csv
+    stats = tmp_path / "s.csv"
+    trace = tmp_path / "t.csv"
+    with open(stats, "w", newline="") as f:
+        w = _csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"])
+        w.writerow(["void k_a(int)", 3, 700, 233.3, 100, 500])
+        w.writerow(["void k_b(int)", 2, 300, 150, 100, 200])
+    with open(trace, "w", newline="") as f:
+        w = _csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for name, dur in (("void k_a(int)", 500), ("void k_a(int)", 100), ("void k_a(int)", 100),
+                          ("void k_b(int)", 100), ("void k_b(int)", 200)):
+            w.writerow([name, 1000, 1000 + dur])
+    med = profiling.dispatch_medians(str(trace))
+    assert med == {"void k_a(int)": 100, "void k_b(int)": 150.0}
+    md = profiling.summarize_trace(str(stats), "cmd", "T", str(trace))
+    assert "| `k_a` | 3 | 0.2 | 0.1 | 0.1 | 0.5 | 70.0 % |" in md
