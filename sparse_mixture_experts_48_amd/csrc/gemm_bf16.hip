@@ -499,11 +499,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------- streaming kernel
 
 constexpr int kStreamWaves = 4;
-constexpr int kKS = 128;  // k per step: 4 loads of 32 contiguous k (8 per lane group) per row
 
-template <int MODE, int NR, int MC, int NBUF>
+// KU: k per step = KU runs of 32 contiguous k (8 per lane group) per row.
+template <int MODE, int NR, int MC, int NBUF, int KU>
 __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmParams p, int n_groups) {
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
+  constexpr int kKS = KU * 32;
   const int e = blockIdx.x / n_groups;
   const int grp = blockIdx.x % n_groups;
   int beg, end_row;
@@ -543,11 +544,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmPara
 #pragma unroll
       for (int c = 0; c < MC; ++c) acc[m][q][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t wreg[NBUF][NMAT][NR][4];
-  u32x4_t xreg[NBUF][MC][4];
+  u32x4_t wreg[NBUF][NMAT][NR][KU];
+  u32x4_t xreg[NBUF][MC][KU];
   auto load = [&](int slot, int k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < KU; ++u) {
       const bool kin = k0 + u * 32 + lg * 8 < Kd;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmPara
   };
   auto compute = [&](int slot) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < KU; ++u)
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -674,24 +675,28 @@ hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
   return launch_tile<128, 128, 2, 2, MODE>(p, S, st);
 }
 
-template <int MODE, int NR, int NBUF>
+template <int MODE, int NR, int NBUF, int KU>
 hipError_t launch_stream(GemmParams p, int max_rows, hipStream_t st) {
   const int n_groups = (p.N + kStreamWaves * NR * 16 - 1) / (kStreamWaves * NR * 16);
   const dim3 grid(static_cast<unsigned>(p.E * n_groups));
   if (max_rows <= 16) {
-    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 1, NBUF>), grid, dim3(kStreamWaves * 64), 0, st, p, n_groups);
+    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 1, NBUF, KU>), grid, dim3(kStreamWaves * 64), 0, st, p,
+                       n_groups);
   } else {
-    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 2, NBUF>), grid, dim3(kStreamWaves * 64), 0, st, p, n_groups);
+    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 2, NBUF, KU>), grid, dim3(kStreamWaves * 64), 0, st, p,
+                       n_groups);
   }
   return hipGetLastError();
 }
 
 constexpr int kStreamMaxRows = 32;
 // Measured on the Mixtral-shaped decode layer: one 16-row weight fragment per
-// wave (many waves, no second round) with a register double buffer for GEMM1
-// and a single buffer (more waves per SIMD) for GEMM2.
-constexpr int kStreamNR1 = 1, kStreamBuf1 = 2;  // weight fragments per wave, register buffers
-constexpr int kStreamNR2 = 1, kStreamBuf2 = 1;
+// wave, with a register double buffer of 64-k steps for GEMM1 (96 registers:
+// five waves per SIMD, so its 7168 waves run in 1.4 rounds; 128-k steps took 144
+// registers and 2.3 rounds and were 1.5 % slower, 32-k steps no faster) and a
+// single buffer of 128-k steps (more waves per SIMD) for GEMM2.
+constexpr int kStreamNR1 = 1, kStreamBuf1 = 2, kStreamKU1 = 2;  // fragments per wave, buffers, 32-k runs per step
+constexpr int kStreamNR2 = 1, kStreamBuf2 = 1, kStreamKU2 = 4;
 
 }  // namespace
 
@@ -712,8 +717,8 @@ hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st) {
   p.S = f.S;
   const bool swiglu = f.act == 1;
   if (f.max_rows_per_expert <= kStreamMaxRows) {
-    return swiglu ? launch_stream<G1_SWIGLU, kStreamNR1, kStreamBuf1>(p, f.max_rows_per_expert, st)
-                  : launch_stream<G1_GELU, kStreamNR1, kStreamBuf1>(p, f.max_rows_per_expert, st);
+    return swiglu ? launch_stream<G1_SWIGLU, kStreamNR1, kStreamBuf1, kStreamKU1>(p, f.max_rows_per_expert, st)
+                  : launch_stream<G1_GELU, kStreamNR1, kStreamBuf1, kStreamKU1>(p, f.max_rows_per_expert, st);
   }
   return swiglu ? launch_tile_auto<G1_SWIGLU>(p, f.S, st) : launch_tile_auto<G1_GELU>(p, f.S, st);
 }
@@ -739,8 +744,8 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
     p.out = f.o_perm;
   }
   if (f.max_rows_per_expert <= kStreamMaxRows) {
-    return f.fused_y ? launch_stream<G2_FUSED_Y, kStreamNR2, kStreamBuf2>(p, f.max_rows_per_expert, st)
-                     : launch_stream<G2_OPERM, kStreamNR2, kStreamBuf2>(p, f.max_rows_per_expert, st);
+    return f.fused_y ? launch_stream<G2_FUSED_Y, kStreamNR2, kStreamBuf2, kStreamKU2>(p, f.max_rows_per_expert, st)
+                     : launch_stream<G2_OPERM, kStreamNR2, kStreamBuf2, kStreamKU2>(p, f.max_rows_per_expert, st);
   }
   return f.fused_y ? launch_tile_auto<G2_FUSED_Y>(p, f.S, st) : launch_tile_auto<G2_OPERM>(p, f.S, st);
 }
