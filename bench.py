@@ -108,7 +108,7 @@ def time_workload(cfg, steps, warmup, label):
 
 
 def time_backward(cfg, steps, warmup):
-    """moe_backward on one layer (forward recompute + gradients of every input)."""
+    """moe_backward on one layer (first-GEMM recompute + gradients of every input)."""
     sys.stderr.write("[bench] backward %s: generating inputs\n" % cfg.name)
     sys.stderr.flush()
     inp = W.make_inputs(cfg)
@@ -316,9 +316,9 @@ def main():
         out["backward"] = {
             "workload": bcfg.name, "ms_per_step": round(bms, 4),
             "tokens_per_s": round(bcfg.T / (bms * 1e-3), 1),
-            "expert_tflops": round(3 * F / (bms * 1e-3) / 1e12, 2),
-            "note": "moe_backward: forward recompute (F) + input and weight gradients (2F) of the expert FFNs, "
-                    "router gradient, dh",
+            "gradient_tflops": round(2 * F / (bms * 1e-3) / 1e12, 2),
+            "note": "moe_backward: input and weight gradients of the expert FFNs (2F, the flops counted) plus a "
+                    "recompute of the first expert GEMM (2F/3), router gradient, dh",
             "roofline": dict(roofline_mfma(f13, bk["dW13_ms"], PEAK_BF16_TFLOPS), kernel="wgrad dW1+dW3"),
             "dX_tflops": round(f13 / (bk["dX_ms"] * 1e-3) / 1e12, 2),
             "dW2_tflops": round(F / 3 / (bk["dW2_ms"] * 1e-3) / 1e12, 2),

@@ -86,7 +86,7 @@ struct BwdPlan {
   int64_t S, Zw, ldk;
   int nwr;
   size_t blk_hist, blk_psum, blk_base, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux, logits;
-  size_t z, a, o, dgate, dO, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
+  size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
   size_t total;
 };
 
@@ -119,8 +119,10 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   p.logits = take(static_cast<size_t>(d.T) * E * 4);
   p.z = take(S * Zw * 2);
   p.a = take(S * w * 2);
-  p.o = take(S * dd * 4);
-  p.dgate = take(S * 4);
+  p.rgate = take(S * 4);
+  p.dyb = take(S * 4);
+  p.dgp = take(static_cast<size_t>((w + moe::kDgpColsHost - 1) / moe::kDgpColsHost) * S * 4);
+  p.dgs = take(S * 4);
   p.dO = take(S * dd * 2);
   p.dZ = take(S * Zw * 2);
   p.dX = take(S * dd * 4);
@@ -566,20 +568,29 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   f.max_rows_per_expert = std::min(T, cap);
   void* z = at<char>(ws, pl.z);
   void* a = at<char>(ws, pl.a);
-  float* o = at<float>(ws, pl.o);
   MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_z_bf16(f, z, a, st));
-  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_bwd_grouped_bf16(a, S, offsets, cap, E_, W2, b2, D, Wd, o, st));
 
-  // backward through the combine, the second GEMM, the activation, the first GEMM
-  float* dgate = at<float>(ws, pl.dgate);
+  // backward through the combine, the second GEMM, the activation, the first
+  // GEMM. The gate gradient dy . o = dy . (a W2^T + b2) is taken as
+  // a . (dy W2) inside the dZ GEMM (which reduces dy W2 anyway) plus dy . b2,
+  // so the expert outputs o are never recomputed.
+  float* rgate = at<float>(ws, pl.rgate);
+  float* dyb = at<float>(ws, pl.dyb);
+  float* dgp = at<float>(ws, pl.dgp);
+  float* dgs = at<float>(ws, pl.dgs);
   void* dO = at<char>(ws, pl.dO);
   void* dZ = at<char>(ws, pl.dZ);
   float* dX = at<float>(ws, pl.dX);
   void* W2T = at<char>(ws, pl.W2T);
   void* W13T = at<char>(ws, pl.W13T);
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dout(dy, o, token_slot, topk_gate, T, D, K, dO, dgate, st));
+  MOE_LAUNCH(MOE_K_BWD, st,
+             moe::launch_dout(dy, token_slot, topk_idx, topk_gate, b2, T, D, K, dO, rgate, dyb, st));
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W2, E_, D, Wd, W2T, D, 0, st));
-  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_bwd_dz_bf16(dO, S, offsets, cap, E_, W2T, Wd, D, z, act, dZ, st));
+  MOE_LAUNCH(MOE_K_GEMM2, st,
+             moe::launch_bwd_dz_bf16(dy, T, slot_token, S, offsets, cap, E_, W2T, Wd, D, z, act, rgate, a, dgp, dZ,
+                                     st));
+  MOE_LAUNCH(MOE_K_BWD, st,
+             moe::launch_dgate_sum(dgp, (Wd + moe::kDgpColsHost - 1) / moe::kDgpColsHost, S, dgs, st));
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W1, E_, Wd, D, W13T, Zw, 0, st));
   if (swiglu) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W3, E_, Wd, D, W13T, Zw, Wd, st));
   MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_grouped_bf16(dZ, S, offsets, cap, E_, W13T, nullptr, D, Zw, dX, st));
@@ -587,8 +598,8 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   // router, dh, dW_r, db_r
   float* dl = at<float>(ws, pl.dl);
   MOE_LAUNCH(MOE_K_BWD, st,
-             moe::launch_router_backward(logits, b_r, bias_select, topk_idx, topk_gate, dgate, counts, T, E_, K,
-                                         d.gate, daux, dl, st));
+             moe::launch_router_backward(logits, b_r, bias_select, topk_idx, topk_gate, dgs, dyb, token_slot,
+                                         counts, T, E_, K, d.gate, daux, dl, st));
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dh(dX, token_slot, dl, W_r, T, D, E_, K, dh, st));
   MOE_LAUNCH(MOE_K_BWD, st,
              moe::launch_dwr(h, dl, T, D, E_, at<float>(ws, pl.wr_part), dW_r, bias_select ? nullptr : db_r, st));

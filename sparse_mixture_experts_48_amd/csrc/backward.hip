@@ -139,30 +139,38 @@ __global__ __launch_bounds__(256) void transpose_weights_kernel(const bf16_t* __
   }
 }
 
-// One block per (token, slot j): dO[s] = g dy[t] and dgate[t][j] = dy[t] . o[s]
-// (fixed-order sum: per-thread strided partials, then a tree). Dropped slots:
-// dgate 0 and no row.
-__global__ __launch_bounds__(256) void dout_kernel(const bf16_t* __restrict__ dy, const float* __restrict__ o_perm,
+// One block per routing slot (t, j) with grouped row s: dO[s] = g dy[t]
+// (bfloat16, for the dW2 GEMM), rgate[s] = g, and dyb = dy[t] . b2[e], the
+// bias part of the gate gradient (its other part, a[s] . (dy W2), comes from
+// the dZ GEMM), summed by a fixed-order tree. A dropped slot gets dyb = 0.
+__global__ __launch_bounds__(256) void dout_kernel(const bf16_t* __restrict__ dy,
                                                    const int32_t* __restrict__ token_slot,
-                                                   const float* __restrict__ gate, int d, int K,
-                                                   bf16_t* __restrict__ dO, float* __restrict__ dgate) {
+                                                   const int32_t* __restrict__ topk_idx,
+                                                   const float* __restrict__ gate, const bf16_t* __restrict__ b2,
+                                                   int d, int K, bf16_t* __restrict__ dO, float* __restrict__ rgate,
+                                                   float* __restrict__ dyb) {
   __shared__ float red[256];
   const int tj = blockIdx.x;
   const int t = tj / K;
   const int s = token_slot[tj];
   if (s < 0) {
-    if (threadIdx.x == 0) dgate[tj] = 0.0f;
+    if (threadIdx.x == 0) dyb[tj] = 0.0f;
     return;
   }
   const float g = gate[tj];
+  if (threadIdx.x == 0) rgate[s] = g;
   const bf16_t* dyr = dy + static_cast<size_t>(t) * d;
-  const float* orow = o_perm + static_cast<size_t>(s) * d;
+  const bf16_t* br = b2 != nullptr ? b2 + static_cast<size_t>(topk_idx[tj]) * d : nullptr;
   bf16_t* dor = dO + static_cast<size_t>(s) * d;
   float acc = 0.0f;
   for (int n = threadIdx.x; n < d; n += 256) {
     const float v = bf16_to_f32(dyr[n]);
     dor[n] = f32_to_bf16(g * v);
-    acc = fmaf(v, orow[n], acc);
+    if (br != nullptr) acc = fmaf(v, bf16_to_f32(br[n]), acc);
+  }
+  if (b2 == nullptr) {
+    if (threadIdx.x == 0) dyb[tj] = 0.0f;
+    return;
   }
   red[threadIdx.x] = acc;
   __syncthreads();
@@ -170,18 +178,39 @@ __global__ __launch_bounds__(256) void dout_kernel(const bf16_t* __restrict__ dy
     if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dgate[tj] = red[0];
+  if (threadIdx.x == 0) dyb[tj] = red[0];
+}
+
+// One thread per grouped row: the dZ GEMM's 64-column partial sums of a . u,
+// as eight interleaved running sums (block c goes to sum c mod 8, eight loads
+// in flight) added pairwise at the end: a fixed order.
+__global__ __launch_bounds__(64) void dgate_sum_kernel(const float* __restrict__ dgp, int ncb, int S,
+                                                       float* __restrict__ dgs) {
+  const int s = blockIdx.x * 64 + threadIdx.x;
+  if (s >= S) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int c = 0;
+  for (; c + 8 <= ncb; c += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += dgp[static_cast<size_t>(c + u) * S + s];
+  }
+  for (int u = 0; c < ncb; ++c, ++u) acc[u] += dgp[static_cast<size_t>(c) * S + s];
+  dgs[s] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
 // One wave per token, lane = expert: d loss / d gate logits.
 __global__ __launch_bounds__(256) void router_backward_kernel(
     const float* __restrict__ logits, const float* __restrict__ br, int bias_select,
-    const int32_t* __restrict__ topk_idx, const float* __restrict__ gate, const float* __restrict__ dgate,
-    const int32_t* __restrict__ counts, int T, int E, int K, int gate_mode, float daux,
-    float* __restrict__ dl) {
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ gate, const float* __restrict__ dgs,
+    const float* __restrict__ dyb, const int32_t* __restrict__ token_slot, const int32_t* __restrict__ counts,
+    int T, int E, int K, int gate_mode, float daux, float* __restrict__ dl) {
   const int t = blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   if (t >= T) return;
+  auto dgate = [&](int j) {  // d loss / d g of slot (t, j): 0 for a dropped slot
+    const int s = token_slot[t * K + j];
+    return s >= 0 ? dgs[s] + dyb[t * K + j] : 0.0f;
+  };
   const bool on = lane < E;
   float gl = -INFINITY;
   if (on) {
@@ -197,12 +226,12 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
   float dlv = 0.0f, dp = 0.0f;
   if (gate_mode == 0) {  // renormalised: dl[c_j] = g_j (dg_j - sum_i g_i dg_i)
     float sdot = 0.0f;
-    for (int j = 0; j < K; ++j) sdot += gate[t * K + j] * dgate[t * K + j];
+    for (int j = 0; j < K; ++j) sdot += gate[t * K + j] * dgate(j);
     for (int j = 0; j < K; ++j)
-      if (topk_idx[t * K + j] == lane) dlv += gate[t * K + j] * (dgate[t * K + j] - sdot);
+      if (topk_idx[t * K + j] == lane) dlv += gate[t * K + j] * (dgate(j) - sdot);
   } else {  // raw: g_j = p[c_j]
     for (int j = 0; j < K; ++j)
-      if (topk_idx[t * K + j] == lane) dp += dgate[t * K + j];
+      if (topk_idx[t * K + j] == lane) dp += dgate(j);
   }
   if (on && daux != 0.0f) {
     const float f = static_cast<float>(counts[lane]) / (static_cast<float>(T) * static_cast<float>(K));
@@ -363,19 +392,26 @@ hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_dout(const void* dy, const float* o_perm, const int32_t* token_slot, const float* gate, int T,
-                       int d, int K, void* dO, float* dgate, hipStream_t st) {
+hipError_t launch_dout(const void* dy, const int32_t* token_slot, const int32_t* topk_idx, const float* gate,
+                       const void* b2, int T, int d, int K, void* dO, float* rgate, float* dyb, hipStream_t st) {
   hipLaunchKernelGGL(dout_kernel, dim3(static_cast<unsigned>(T * K)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(dy), o_perm, token_slot, gate, d, K, static_cast<bf16_t*>(dO),
-                     dgate);
+                     static_cast<const bf16_t*>(dy), token_slot, topk_idx, gate, static_cast<const bf16_t*>(b2), d, K,
+                     static_cast<bf16_t*>(dO), rgate, dyb);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgate_sum(const float* dgp, int ncb, int S, float* dgs, hipStream_t st) {
+  hipLaunchKernelGGL(dgate_sum_kernel, dim3(static_cast<unsigned>((S + 63) / 64)), dim3(64), 0, st, dgp, ncb, S,
+                     dgs);
   return hipGetLastError();
 }
 
 hipError_t launch_router_backward(const float* logits, const float* br, int bias_select, const int32_t* topk_idx,
-                                  const float* gate, const float* dgate, const int32_t* counts, int T, int E,
-                                  int K, int gate_mode, float daux, float* dl, hipStream_t st) {
+                                  const float* gate, const float* dgs, const float* dyb,
+                                  const int32_t* token_slot, const int32_t* counts, int T, int E, int K,
+                                  int gate_mode, float daux, float* dl, hipStream_t st) {
   hipLaunchKernelGGL(router_backward_kernel, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(256), 0, st, logits,
-                     br, bias_select, topk_idx, gate, dgate, counts, T, E, K, gate_mode, daux, dl);
+                     br, bias_select, topk_idx, gate, dgs, dyb, token_slot, counts, T, E, K, gate_mode, daux, dl);
   return hipGetLastError();
 }
 

@@ -69,7 +69,14 @@ struct GemmParams {
   float* out2;
   void* out_act;       // G1_*_Z: also the activation a = act(z), bfloat16 [S][N]
   const bf16_t* zin;   // G2_DZ_*: the pre-activations written by G1_*_Z
+  // G2_DZ_*: the reduction gives u = dy W2 for the grouped rows; the epilogue
+  // takes dA = rgate[s] u and writes, for every 64 columns c of a row, the
+  // sum over them of ain[s][c] u[c] to dgp[c / 64][s] (float32).
+  const float* rgate;
+  const bf16_t* ain;
+  float* dgp;
 };
+constexpr int kDgpCols = 64;  // columns per partial sum of the dZ GEMM's gate-gradient terms
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -400,6 +407,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // Epilogue. Accumulator (j, i), register r: token = i*32 + lane%32 of the
   // wave's rows; weight row = j*32 + (r/4)*8 + (lane/32)*4 + r%4.
   constexpr int TNO = TN / NMAT;  // output column tiles per wave
+  constexpr bool DZ = (MODE == G2_DZ_SWIGLU || MODE == G2_DZ_GELU);
+  // gate-gradient terms of a row: column tiles j hold columns j*32 .. j*32+31
+  // of the wave's WTN, so 64-column block b is j = 2b, 2b+1 (both lane halves)
+  constexpr int NDB = DZ ? (WTN + kDgpCols - 1) / kDgpCols : 1;
+  static_assert(!DZ || WTN % kDgpCols == 0, "dZ column blocks");
+  float dgs[TM][NDB];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) dgs[i][b] = 0.0f;
 #pragma unroll
   for (int j = 0; j < TNO; ++j)
 #pragma unroll
@@ -436,6 +453,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
           } else {
             v[q] = v1;
             if (p.bias != nullptr) v[q] += bf16_to_f32(p.bias[static_cast<size_t>(e) * N + n + q]);
+          }
+        }
+        if constexpr (DZ) {  // v = u: gate-gradient terms a u, then dA = g u
+          const u32x2_t ap = *reinterpret_cast<const u32x2_t*>(p.ain + static_cast<size_t>(s) * N + n);
+          const uint32_t aw[2] = {ap[0], ap[1]};
+          const float gs = p.rgate[s];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float av = __uint_as_float(q % 2 ? (aw[q / 2] & 0xFFFF0000u) : (aw[q / 2] << 16));
+            dgs[i][(j * 32) / kDgpCols] = fmaf(av, v[q], dgs[i][(j * 32) / kDgpCols]);
+            v[q] *= gs;
           }
         }
         if (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_GELU_Z) {
@@ -494,6 +522,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
         }
       }
     }
+  if constexpr (DZ) {
+    // lanes l and l ^ 32 hold the same rows: add the other half's columns
+    // (lower half first), then lanes 0..31 store one row each per block
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) {
+        const float other = __shfl_xor(dgs[i][b], 32);
+        dgs[i][b] = lane < 32 ? dgs[i][b] + other : other + dgs[i][b];
+      }
+    if (lane < 32) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rl = wm * WTM + i * 32 + lane;
+        if (rl >= rows) continue;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const int c0 = n0 + wn * WTN + b * kDgpCols;
+          if (c0 < N) p.dgp[static_cast<size_t>(c0 / kDgpCols) * p.S + row0 + rl] = dgs[i][b];
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------- streaming kernel
@@ -792,15 +843,20 @@ hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets,
   return launch_tile_auto<G2_OPERM>(p, S, st);
 }
 
-hipError_t launch_bwd_dz_bf16(const void* dO, int S, const int32_t* offsets, int cap, int E, const void* W2T, int N,
-                              int Kd, const void* z, int act, void* dZ, hipStream_t st) {
+hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, int S, const int32_t* offsets,
+                              int cap, int E, const void* W2T, int N, int Kd, const void* z, int act,
+                              const float* rgate, const void* a, float* dgp, void* dZ, hipStream_t st) {
   GemmParams p{};
-  p.x = static_cast<const bf16_t*>(dO);
-  p.x_nrows = S;
+  p.x = static_cast<const bf16_t*>(dy);
+  p.x_rows = slot_token;
+  p.x_nrows = T;
   p.cap = cap;
   p.offsets = offsets;
   p.B = static_cast<const bf16_t*>(W2T);
   p.zin = static_cast<const bf16_t*>(z);
+  p.rgate = rgate;
+  p.ain = static_cast<const bf16_t*>(a);
+  p.dgp = dgp;
   p.out = dZ;
   p.E = E;
   p.N = N;

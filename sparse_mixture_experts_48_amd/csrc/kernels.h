@@ -75,10 +75,14 @@ hipError_t launch_combine(const float* o_perm, const int32_t* token_slot, const 
 // First GEMM without its activation: SwiGLU z = [x W1 | x W3] as rows of 2*width,
 // GELU z = x W1 + b1; grouped rows as in launch_gemm1; also a = act(z) [S][width].
 hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, void* a, hipStream_t st);
-// dZ = (dO W2) * act'(z) for the grouped rows: W2T stored [E][N = width][Kd = d];
-// z as written by launch_bwd_z_bf16; dZ like z (bfloat16).
-hipError_t launch_bwd_dz_bf16(const void* dO, int S, const int32_t* offsets, int cap, int E, const void* W2T, int N,
-                              int Kd, const void* z, int act, void* dZ, hipStream_t st);
+// For the grouped rows s (dy rows read through slot_token): u = dy W2, dA = rgate[s] u,
+// dZ = dA * act'(z) (z as written by launch_bwd_z_bf16; dZ like z, bfloat16), and
+// dgp[c][s] = sum over the 64 columns 64c .. 64c+63 of a[s] u (the gate-gradient
+// terms; a [S][N] bfloat16). W2T stored [E][N = width][Kd = d]; dgp [ceil(N/64)][S].
+constexpr int kDgpColsHost = 64;
+hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, int S, const int32_t* offsets,
+                              int cap, int E, const void* W2T, int N, int Kd, const void* z, int act,
+                              const float* rgate, const void* a, float* dgp, void* dZ, hipStream_t st);
 // out[s] = x[s] . B_e^T (+ bias_e) (float32) for the grouped rows s of every
 // expert e (the first cap of each group); B stored [E][N][Kd], bias [E][N] or null.
 hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets, int cap, int E, const void* B,
@@ -95,11 +99,16 @@ hipError_t launch_transpose_groups(const void* src, const int32_t* src_rows, int
                                    hipStream_t st);
 hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* dst, int ldd, int coff,
                                     hipStream_t st);
-hipError_t launch_dout(const void* dy, const float* o_perm, const int32_t* token_slot, const float* gate, int T,
-                       int d, int K, void* dO, float* dgate, hipStream_t st);
+// Per routing slot: dO[s] = g dy[t] (bfloat16), rgate[s] = g, dyb = dy[t] . b2[e] (0 without b2).
+hipError_t launch_dout(const void* dy, const int32_t* token_slot, const int32_t* topk_idx, const float* gate,
+                       const void* b2, int T, int d, int K, void* dO, float* rgate, float* dyb, hipStream_t st);
+// dgs[s] = sum over c of dgp[c][s], c in order (the gate gradient of grouped row s, bias term aside).
+hipError_t launch_dgate_sum(const float* dgp, int ncb, int S, float* dgs, hipStream_t st);
+// Gate gradient of slot (t, j): dgs[token_slot] + dyb (0 for a dropped slot).
 hipError_t launch_router_backward(const float* logits, const float* br, int bias_select, const int32_t* topk_idx,
-                                  const float* gate, const float* dgate, const int32_t* counts, int T, int E,
-                                  int K, int gate_mode, float daux, float* dl, hipStream_t st);
+                                  const float* gate, const float* dgs, const float* dyb,
+                                  const int32_t* token_slot, const int32_t* counts, int T, int E, int K,
+                                  int gate_mode, float daux, float* dl, hipStream_t st);
 hipError_t launch_dh(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
                      int E, int K, void* dh, hipStream_t st);
 int dwr_chunks(int T);
