@@ -209,8 +209,9 @@ int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes);
  * differentiable), through p_i for raw gates (Lensa ML Step 3), and through
  * P of the aux loss, whose f is a count (Step 4: only P_i is
  * differentiable); the choice and the capacity drops are held fixed, and a
- * selection-only bias gets a zero gradient. The forward pass is recomputed
- * from the inputs (same routing, bit for bit).
+ * selection-only bias gets a zero gradient. The routing (bit for bit the
+ * same), the grouping and the first expert GEMM are recomputed from the
+ * inputs; the caller keeps no activations.
  * In:  the forward's inputs (h, W_r, b_r, W1, b1, W3, W2, b2), dy [T][d]
  *      dtype, daux (finite; the weight of aux in the loss).
  * Out: dh [T][d] dtype; dW_r [d][E], db_r [E] (nullable), dW1 [E][width][d],
