@@ -5,11 +5,16 @@ one batch of seeded synthetic input already resident in HBM.
 
 Headline (`value`): tokens/s on the Mixtral-shaped prefill layer (T=4096,
 d=4096, E=8, top-2, SwiGLU width 14336, bf16). The decode-shaped layer (T=16),
-the Switch-style top-1 layer (T=8192, E=64, width 1376) and the backward pass
-of the prefill layer are reported in extra objects of the same JSON line. Each carries a roofline for its dominant
-kernel: algorithmic flops or bytes per launch divided by that kernel's mean
-duration, measured with HIP events that the library records on the launch
-stream during the timed region.
+the Switch-style top-1 layer (T=8192, E=64, width 1376), the two small layers
+(micro fp32, skewed small experts) and the backward pass of the prefill layer
+are reported in extra objects of the same JSON line. The large layers carry a
+roofline for their dominant kernel: algorithmic flops or bytes per launch
+divided by that kernel's mean duration, measured with HIP events that the
+library records on the launch stream during the timed region. Every layer
+also reports per-step event times (median, minimum), launches per step and
+the layer's roofline fraction max(F / F_peak, B / B_peak) / t; decode and
+Switch also cold-cache times (two copies of the weights, alternated), and
+`context` the box's plain-copy rate and the vendor GEMM on one expert's shape.
 
 cpu_baseline: the CPU oracle (never tuned) on a bounded sample of the
 prefill workload: the same layer restricted to its first tokens.
@@ -56,11 +61,34 @@ def algorithmic(cfg, counts):
             "bytes": bytes_total, "weight_bytes_gemm1": w_g1, "weight_bytes_gemm2": w_g2, "experts_hit": hit}
 
 
-def time_workload(cfg, steps, warmup, label):
+def layer_roofline_frac(cfg, alg, ms):
+    """max(F / F_peak, B / B_peak) / t: the ideal time at the binding peak over the measured time."""
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == W.DT_BF16 else PEAK_F32_TFLOPS
+    return round(max(alg["flops"] / (peak * 1e12), alg["bytes"] / (PEAK_HBM_GBPS * 1e9)) / (ms * 1e-3), 4)
+
+
+def step_times(run, steps):
+    """Per-step durations (ms) of `run` from HIP events on the current stream
+    (the stream the library launches on)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def time_workload(cfg, steps, warmup, label, cold=False):
+    """Eager and graph-replayed steps of moe_forward, the library's per-launch
+    events, and per-step event times. cold: alternate between two copies of the
+    weights, so that no weight byte can still be in the 256 MB Infinity Cache
+    from the previous step (the step times are then the cold ones)."""
     sys.stderr.write("[bench] %s: generating inputs %s\n" % (label, cfg))
     sys.stderr.flush()
     inp = W.make_inputs(cfg)
     layer = moe.MoELayer(cfg, inp)
+    twin = moe.MoELayer(cfg, inp) if cold else None
     del inp
     for _ in range(warmup):
         layer.forward()
@@ -95,6 +123,16 @@ def time_workload(cfg, steps, warmup, label):
     torch.cuda.synchronize()
     ms_graph = (time.perf_counter() - tg0) * 1e3 / steps
     del g
+    per_step = step_times(layer.forward, steps)
+    cold_steps = None
+    if twin is not None:
+        flip = [0]
+
+        def alternate():
+            (layer if flip[0] % 2 == 0 else twin).forward()
+            flip[0] += 1
+        cold_steps = step_times(alternate, 2 * steps)
+        del twin
     per_kernel = {}
     for name, dur in events:
         per_kernel.setdefault(name, []).append(dur)
@@ -104,7 +142,14 @@ def time_workload(cfg, steps, warmup, label):
     aux = float(layer.aux.cpu()[0])
     del layer
     torch.cuda.empty_cache()
-    return ms, kernels, alg, counts, aux, ms_graph
+    stats = {"ms_median": round(float(np.median(per_step)), 4), "ms_min": round(float(np.min(per_step)), 4),
+             "launches_per_step": round(len(events) / steps, 2),
+             "layer_roofline_frac": layer_roofline_frac(cfg, alg, float(np.median(per_step)))}
+    if cold_steps is not None:
+        stats["cold_ms_median"] = round(float(np.median(cold_steps)), 4)
+        stats["cold_ms_min"] = round(float(np.min(cold_steps)), 4)
+        stats["cold_layer_roofline_frac"] = layer_roofline_frac(cfg, alg, float(np.median(cold_steps)))
+    return ms, kernels, alg, counts, aux, ms_graph, stats
 
 
 def time_backward(cfg, steps, warmup):
@@ -176,6 +221,43 @@ def roofline_hbm(nbytes, mean_ms, traffic=None):
             "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic}
 
 
+def small_workload(name, steps, warmup):
+    """The latency-bound layers (micro fp32, skewed small experts): step times,
+    launches and the roofline fraction, which is small by nature at these sizes."""
+    c = W.WORKLOADS[name]
+    ms, k, alg, counts, aux, ms_g, st = time_workload(c, steps, warmup, name)
+    return {"workload": name, "ms_per_step": round(ms, 4), "ms_per_step_graph": round(ms_g, 4),
+            "tokens_per_s": round(c.T / (st["ms_median"] * 1e-3), 1),
+            "tokens_per_s_graph": round(c.T / (ms_g * 1e-3), 1), **st,
+            "layer_tflops": round(alg["flops"] / (st["ms_median"] * 1e-3) / 1e12, 3),
+            "layer_hbm_GBps": round(alg["bytes"] / (st["ms_median"] * 1e-3) / 1e9, 1),
+            "aux_loss": round(aux, 6), "experts_hit": alg["experts_hit"], "idle_experts": int((counts == 0).sum()),
+            "max_expert_share": round(float(counts.max()) / max(c.S, 1), 4),
+            "kernels_ms": {kk: round(v["mean_ms"], 4) for kk, v in k.items()}}
+
+
+def context_ceilings():
+    """Practical ceilings on this machine, as context (not dependencies of the
+    path): a plain 1 GiB device copy, and torch.matmul (the vendor GEMM) on one
+    expert's first-GEMM shape, 1024 x 4096 x 28672 in bf16."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    t = float(np.median(step_times(lambda: dst.copy_(src), 10)))
+    copy_gbps = 2 * (1 << 30) / (t * 1e-3) / 1e9
+    del src, dst
+    a = torch.randn(1024, 4096, device="cuda").to(torch.bfloat16)
+    b = torch.randn(4096, 28672, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    t = float(np.median(step_times(lambda: torch.matmul(a, b), 10)))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_1GiB_GBps_read_plus_write": round(copy_gbps, 1),
+            "vendor_gemm_1024x4096x28672_bf16_tflops": round(2.0 * 1024 * 4096 * 28672 / (t * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(cfg, n_tokens):
     """The CPU oracle on the first n_tokens tokens of the workload (same weights)."""
     from oracle import moe_oracle as O
@@ -242,14 +324,14 @@ def main():
     if args.only is not None:
         name = {"prefill": "mixtral_prefill", "decode": "mixtral_decode", "switch": "switch_top1"}[args.only]
         c = W.WORKLOADS[name]
-        ms, kernels, alg, counts, aux, msg = time_workload(c, args.steps, args.warmup, args.only)
+        ms, kernels, alg, counts, aux, msg, _ = time_workload(c, args.steps, args.warmup, args.only)
         print(json.dumps({"workload": name, "ms_per_step": round(ms, 4), "ms_per_step_graph": round(msg, 4),
                           "tokens_per_s": round(c.T / (ms * 1e-3), 1),
                           "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in kernels.items()}}))
         return
 
     cfg = W.WORKLOADS["mixtral_prefill"]
-    ms, kernels, alg, counts, aux, ms_g = time_workload(cfg, args.steps, args.warmup, "prefill")
+    ms, kernels, alg, counts, aux, ms_g, pstats = time_workload(cfg, args.steps, args.warmup, "prefill")
     g1 = kernels["gemm1"]["mean_ms"]
     out = {
         "metric": METRIC,
@@ -273,14 +355,15 @@ def main():
                                                + cfg.S * cfg.width * bpe(cfg))),
         "layer_tflops": round(alg["flops"] / (ms * 1e-3) / 1e12, 2),
         "layer_mfma_frac": round(alg["flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        **pstats,
         "aux_loss": round(aux, 6),
         "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in kernels.items()},
     }
     if not args.no_extra:
         dcfg = W.WORKLOADS["mixtral_decode"]
         dsteps = max(args.steps, 50)
-        dms, dk, dalg, dcounts, _, dms_g = time_workload(dcfg, dsteps, args.warmup, "decode")
-        out["decode"] = {
+        dms, dk, dalg, dcounts, _, dms_g, dstats = time_workload(dcfg, dsteps, args.warmup, "decode", cold=True)
+        out["decode"] = {**dstats,
             "workload": dcfg.name, "steps": dsteps, "ms_per_step": round(dms, 4),
             "ms_per_step_graph": round(dms_g, 4), "tokens_per_s_graph": round(dcfg.T / (dms_g * 1e-3), 1),
             "layer_hbm_frac_graph": round(dalg["bytes"] / (dms_g * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
@@ -295,8 +378,9 @@ def main():
             "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in dk.items()},
         }
         scfg = W.WORKLOADS["switch_top1"]
-        sms, sk, salg, scounts, saux, sms_g = time_workload(scfg, args.steps, args.warmup, "switch")
-        out["switch_top1"] = {
+        sms, sk, salg, scounts, saux, sms_g, sstats = time_workload(scfg, args.steps, args.warmup, "switch",
+                                                                    cold=True)
+        out["switch_top1"] = {**sstats,
             "workload": scfg.name, "ms_per_step": round(sms, 4), "ms_per_step_graph": round(sms_g, 4),
             "tokens_per_s": round(scfg.T / (sms * 1e-3), 1),
             "layer_tflops": round(salg["flops"] / (sms * 1e-3) / 1e12, 2),
@@ -309,6 +393,9 @@ def main():
             "kernels_ms": {k: round(v["mean_ms"], 4) for k, v in sk.items()},
         }
     if not args.no_extra:
+        out["micro"] = small_workload("micro", max(args.steps, 200), args.warmup)
+        out["skewed"] = small_workload("skewed", max(args.steps, 200), args.warmup)
+        out["context"] = context_ceilings()
         bcfg = W.WORKLOADS["mixtral_prefill"]
         bms, bk = time_backward(bcfg, max(args.steps // 4, 3), 2)
         F = 2.0 * bcfg.S * bcfg.d * bcfg.width * 3  # forward expert flops (SwiGLU: 3 matrices)
