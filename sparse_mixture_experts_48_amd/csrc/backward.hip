@@ -8,11 +8,14 @@
 // load-balancing loss, whose f is a count (Step 4: only P_i is
 // differentiable). The choice and the capacity drops are held fixed.
 //
-// Loss = sum(dy * y) + daux * aux. With y[t] = sum_j g[t][j] o[slot(t, j)]:
-//   dO[s] = g dy[t],  dgate[t][j] = dy[t] . o[s]
-//   dA = dO W2 (rows of W2^T),  dZ = dA * act'(Z),  dX = dZ [W1; W3]
-//   (the pre-activation GEMM also writes A = act(Z); the dA GEMM applies
-//   act' in its epilogue and writes dZ)
+// Loss = sum(dy * y) + daux * aux. With y[t] = sum_j g[t][j] o[slot(t, j)]
+// and o[s] = A[s] W2^T + b2:
+//   u[s] = dy[t] W2 (rows of W2^T),  dA = g u,  dZ = dA * act'(Z),  dX = dZ [W1; W3]
+//   dgate[t][j] = dy[t] . o[s] = A[s] . u[s] + dy[t] . b2
+//   (the pre-activation GEMM also writes A = act(Z); the u GEMM forms dA and
+//   applies act' in its epilogue, writes dZ and the 64-column partial sums of
+//   A . u, so o is never recomputed)
+//   dO[s] = g dy[t] (for dW2)
 //   dh[t] = sum_j dX[slot(t, j)] + dlogits[t] W_r^T
 //   dW2_e = dO_e^T A_e,  dW1_e = dZ1_e^T X_e,  dW3_e = dZ3_e^T X_e
 //   dW_r = h^T dlogits,  db_r = sum_t dlogits   (not when the bias only steers the choice)

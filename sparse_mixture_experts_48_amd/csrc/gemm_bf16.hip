@@ -93,16 +93,18 @@ __device__ __forceinline__ float epilogue_g1(int mode, float v1, float v3, const
 // Block: WM x WN waves; tile = BM grouped rows x BN weight rows. k is staged
 // 64 at a time (one 128-byte line of every row) through LDS filled by direct
 // global-to-LDS loads (buffer_load_dwordx4 ... lds: no staging registers, no LDS
-// store instructions). The token tile has a ring of three LDS slots and the
-// weight tile a ring of two, which is what 160 KB of LDS holds for a 256 x 256
-// tile: token rows are loaded two stages ahead, weight rows one stage ahead.
+// store instructions). Each operand has a ring of LDS slots and is loaded one
+// stage ahead per slot beyond the first: at 256 x 256 three token slots and
+// two weight slots (all 160 KB of LDS: tokens two stages ahead, weights one),
+// at 128 x 256 three of each (both two stages ahead), at 128 x 128 three and
+// two (so that two blocks share a CU).
 // Per stage:
-//   wait until this wave's loads of the stage have landed (its newest batch of
-//   token loads stays in flight), barrier (so have every wave's)
+//   wait until this wave's loads of the stage have landed (the loads issued
+//   after them may stay in flight), barrier (so have every wave's)
 //   -> for each of the four 16-k steps: issue a quarter of the loads of the
-//      following stages (weights of stage kt+1 first, then tokens of stage
-//      kt+2, into the slots freed by stage kt-1), read the next step's MFMA
-//      fragments, run this step's MFMAs.
+//      following stages (the operand loaded fewer stages ahead first), into
+//      the slots freed by stage kt-1, read the next step's MFMA fragments,
+//      run this step's MFMAs.
 // The loads are spread over the MFMAs because a wave issues in order: a load
 // that waits for room in the memory pipeline holds up every MFMA behind it.
 // A compiler fence after each batch keeps the compiler from sinking the loads
