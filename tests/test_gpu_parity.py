@@ -279,6 +279,37 @@ def test_group_size_boundaries(act):
             assert err <= H.Y_TOL[cfg.dtype], (e, n, err)
 
 
+def test_max_operand_size():
+    """The largest layer the 32-bit offsets allow: T*K*d = 2^31 - 2^22 elements
+    of h rows read through the grouping (T = 261632 tokens, d = 4096, top-2),
+    so the byte offsets of the last rows' loads sit at the limit. Routing of
+    every token bit-exact; y on the first and last tokens and a seeded sample.
+    (About 35 s of host time for the inputs and the oracle.)"""
+    cfg = L("max_offsets", 261632, 4096, 8, 2, 512, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 51)
+    assert cfg.T * cfg.K * cfg.d == 2 ** 31 - 2 ** 22
+    H.say("[gpu] max operand size %s" % (cfg,))
+    inp = W.make_inputs(cfg)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(cfg.T - 8, cfg.T),
+                                     rng.choice(cfg.T, size=24, replace=False)])).astype(np.int64)
+    r = H.run_oracle(cfg, inp, tokens=rows)
+    dev = H.to_dev(inp)
+    del inp
+    _check_route(cfg, dev, r)
+    layer_desc = moe.desc_of(cfg)
+    y, aux, counts = moe.forward(layer_desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"],
+                                 dev["W2"], dev["b2"])
+    torch.cuda.synchronize()
+    H.check_bits_equal("expert_counts", H.to_np(counts), r["counts"])
+    assert abs(float(H.to_np(aux)[0]) - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0)
+    yg = H.to_np(y[torch.from_numpy(rows).cuda()])
+    raw, net = H.layer_err(yg, r["y"], cfg.dtype)
+    H.say("[gpu] max operand size y: max|d|/rms = %.4f (raw), %.4f (net)" % (raw, net))
+    assert net <= H.Y_TOL[cfg.dtype], (raw, net)
+    del dev, y
+    torch.cuda.empty_cache()
+
+
 FULL = ["micro", "skewed", "mixtral_prefill", "mixtral_decode", "switch_top1"]
 
 
