@@ -25,6 +25,8 @@
 //    weight rows over the whole reduction with v_mfma_f32_16x16x32_bf16, the
 //    weights as the M operand and up to 32 token rows as N; weights are read
 //    from HBM exactly once, which is what bounds decode-sized batches.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -332,7 +334,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr bool kPrio = BM == 256 && BN == 256 && NW == 8;
   // Stage kt: MFMAs on slots (As, Bs); loads of weights (kt+DB) into Bn and of
   // tokens (kt+DA) into An.
-  auto run_stage = [&](int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* Bn, u32x4_t* An) {
+  // mf: std::true_type for a wave that holds rows of the tile, std::false_type
+  // for one that does not (it only issues its share of the loads and waits).
+  auto run_stage = [&](auto mf, int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* Bn, u32x4_t* An) {
+    constexpr bool MF = decltype(mf)::value;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAITN));  // this wave's loads for stage kt landed
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();                   // ... and every wave's
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) xf[ks][i] = as_bf16x8(As[swz(wm * WTM + i * 32 + frow, c)]);
     };
-    read(0);
+    if constexpr (MF) read(0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -360,14 +365,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
         }
       }
       asm volatile("" ::: "memory");  // keep the loads ahead of the later fragment reads
-      if (ks + 1 < NKS) read(ks + 1);
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
+      if constexpr (MF) {
+        if (ks + 1 < NKS) read(ks + 1);
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks][j], xf[ks][i], acc[j][i], 0, 0, 0);
-      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+          for (int i = 0; i < TM; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks][j], xf[ks][i], acc[j][i], 0, 0, 0);
+        if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+      }
     }
   };
 
@@ -394,15 +401,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // the loop. Stage i uses token slot i % NAS and weight slot i % NBS and fills
   // token slot (i + DA) % NAS and weight slot (i + DB) % NBS.
   constexpr int RING = NAS == NBS ? NAS : NAS * NBS;
-  int kt = 0;
-  for (; kt + RING <= nk; kt += RING) {
+  auto ring = [&](auto mf) {
+    int kt = 0;
+    for (; kt + RING <= nk; kt += RING) {
 #pragma unroll
-    for (int i = 0; i < RING; ++i)
-      run_stage(kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
-  }
+      for (int i = 0; i < RING; ++i)
+        run_stage(mf, kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
+    }
 #pragma unroll
-  for (int i = 0; i + 1 < RING; ++i)
-    if (kt + i < nk) run_stage(kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
+    for (int i = 0; i + 1 < RING; ++i)
+      if (kt + i < nk) run_stage(mf, kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
+  };
+  // A tile with few rows (a small expert, the last tile of a group) leaves the
+  // waves past its rows without work: they skip the fragment reads and MFMAs
+  // (wave-uniform choice, once per tile).
+  if (wm * WTM < rows) ring(std::true_type{});
+  else ring(std::false_type{});
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
   asm volatile("" ::: "memory");
 
