@@ -65,6 +65,24 @@ Function -> passage it follows -> what pins it (tests/test_oracle_pins.py):
                          not move with a bias that leaves the choice alone; a
                          forcing bias picks its expert for every token with
                          the unbiased gate ratio.
+  moe_forward(noise=...)
+                      [AJ] "Load Balancing" (Shazeer's noisy top-K: tuned
+                      Gaussian noise on the router logits; the pages give no
+                      scale or form). Reading: the caller draws the noise and
+                      passes it, already scaled, as a [T][E] float32 input;
+                      it is added to the logits after the bias (a separate
+                      float32 add) and enters the choice, the gates and P
+                      -> zero noise equals the default path bit for bit; a
+                         per-expert constant noise equals that router bias
+                         bit for bit; a forcing noise picks its expert.
+  z_loss              [AJ] "Mixtral and the Open MoE Era" (ST-MoE's router
+                      z-loss, a penalty on large router logits; the formula
+                      is not on the pages). Reading: the ST-MoE form, the mean
+                      over tokens of the squared log-sum-exp of the logits
+                      the softmax sees
+                      -> uniform logits give (ln E)^2 exactly; a per-token
+                         shift c moves each term to (lse + c)^2; the gradient
+                         2 lse p / T by central differences.
   param_counts        [CUR] "Parameters you hold..."; [LENSA] Steps 1 and 6
                       -> the printed 4.46M / 1.32M / 3.39x / 25.2x,
                          37.0B / 11.1B / 3.3x and 176M / 45.1B.
@@ -312,7 +330,7 @@ def drop_stats(counts: Sequence[int], C: int) -> Dict[str, float]:
 def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int,
                 act: int, gate: int, tokens: Optional[Sequence[int]] = None,
                 capacity: Optional[int] = None, bias_select_only: bool = False,
-                logits_f64: bool = False) -> Dict[str, np.ndarray]:
+                logits_f64: bool = False, noise: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """The whole layer. `inp` holds float32 arrays of the exact input values.
 
     Routing, grouping and the aux loss cover all T tokens. The expert FFNs and
@@ -332,6 +350,13 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
     logits_f64: router logits in float64 instead of the float32 contract (a
     smooth function of the inputs, for finite-difference checks of the
     backward pass).
+
+    noise: [T][E] values added to the logits after the bias (noisy top-K;
+    drawn and scaled by the caller), in the logits' precision; they enter the
+    choice, the gates and P (with bias_select_only too: only the bias is
+    choice-only).
+
+    Also returns z_loss: mean over tokens of (log sum_e exp gate_logits)^2.
     """
     h32 = np.asarray(inp["h"], np.float32).reshape(T, d)
     router = router_logits_f64 if logits_f64 else router_logits_f32
@@ -341,12 +366,18 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
         gate_logits = router(hin, inp["W_r"], None)
     else:
         gate_logits = logits
+    if noise is not None:
+        nz = np.asarray(noise, logits.dtype).reshape(T, E)
+        same = gate_logits is logits
+        logits = logits + nz           # one rounding in the logits' precision, after the bias
+        gate_logits = logits if same else gate_logits + nz
     idx = select_topk(logits, K)
     p = router_probs(gate_logits)
     g = gates(gate_logits, idx, gate)
     counts = expert_counts(idx, E)
     offsets, slot_token, token_slot = stable_permutation(idx, E)
     aux = aux_loss(counts, p, K)
+    zl = z_loss(gate_logits)
     keep = np.ones((T, K), dtype=bool) if capacity is None else capacity_keep(idx, E, capacity)
     rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     y = np.zeros((len(rows), d), dtype=np.float64)
@@ -362,10 +393,32 @@ def moe_forward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K:
             "counts": counts,
             "offsets": offsets, "slot_token": slot_token, "token_slot": token_slot,
             "token_slot_kept": np.where(keep, token_slot, -1).astype(np.int32), "keep": keep,
-            "aux": aux, "y": y, "rows": rows}
+            "aux": aux, "z_loss": zl, "y": y, "rows": rows}
+
+
+def logsumexp_rows(l: np.ndarray) -> np.ndarray:
+    """log sum_e exp l[t, e] per row, float64, shifted by the row maximum."""
+    l = np.asarray(l, np.float64)
+    m = l.max(axis=1)
+    return m + np.log(np.exp(l - m[:, None]).sum(axis=1))
+
+
+def z_loss(gate_logits: np.ndarray) -> float:
+    """Router z-loss (ST-MoE form): the mean over tokens of the squared
+    log-sum-exp of the logits the softmax sees."""
+    if gate_logits.shape[0] == 0:
+        return 0.0
+    return float(np.mean(logsumexp_rows(gate_logits) ** 2))
 
 
 # ----------------------------------------------------------------------------- backward
+
+def z_loss_logit_grad(gate_logits: np.ndarray, p: np.ndarray) -> np.ndarray:
+    """d z_loss / d gate_logits: the derivative of lse_t^2 is 2 lse_t times
+    the softmax of row t; the mean over T tokens divides by T."""
+    T = gate_logits.shape[0]
+    return (2.0 / T) * logsumexp_rows(gate_logits)[:, None] * p
+
 
 def gelu_grad(z: np.ndarray) -> np.ndarray:
     """d GELU / dz = Phi(z) + z phi(z) (exact GELU; Phi, phi: normal cdf and density)."""
@@ -409,10 +462,12 @@ def gate_logit_grad(gl: np.ndarray, idx: np.ndarray, g: np.ndarray, p: np.ndarra
 def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K: int, act: int, gate: int,
                  dy: np.ndarray, daux: float = 0.0, capacity: Optional[int] = None,
                  bias_select_only: bool = False, logits_f64: bool = False,
-                 with_scales: bool = False) -> Dict[str, Optional[np.ndarray]]:
-    """Gradients of loss = sum(dy * y) + daux * aux with respect to every input
-    of the layer, float64 (reading: the expert choice and the capacity drops
-    are held fixed; see gate_logit_grad for the router).
+                 with_scales: bool = False, noise: Optional[np.ndarray] = None,
+                 dz_loss: float = 0.0) -> Dict[str, Optional[np.ndarray]]:
+    """Gradients of loss = sum(dy * y) + daux * aux + dz_loss * z_loss with respect
+    to every input of the layer, float64 (reading: the expert choice and the
+    capacity drops are held fixed; see gate_logit_grad for the router; the
+    noise is an input, not differentiated).
 
     Returns dh [T][d], dW_r [d][E], db_r [E] (zero when the bias only steers
     the choice; None without a bias), and per expert dW1, dW3 (SwiGLU), dW2 in
@@ -423,7 +478,7 @@ def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K
     rounding error of an implementation's sum is judged.
     """
     fwd = moe_forward(inp, T, d, E, K, act, gate, capacity=capacity, bias_select_only=bias_select_only,
-                      logits_f64=logits_f64)
+                      logits_f64=logits_f64, noise=noise)
     idx, g, p, keep = fwd["topk_idx"], fwd["topk_gate"], fwd["probs"], fwd["keep"]
     h = np.asarray(inp["h"], np.float64).reshape(T, d)
     dy = np.asarray(dy, np.float64).reshape(T, d)
@@ -488,6 +543,8 @@ def moe_backward(inp: Dict[str, Optional[np.ndarray]], T: int, d: int, E: int, K
                 sc["dh"][st] += np.abs(dz1) @ np.abs(W1[e]) + np.abs(dz3) @ np.abs(W3[e])
     f = fwd["counts"] / float(max(T * K, 1))
     dl = gate_logit_grad(fwd["gate_logits"].astype(np.float64), idx, g, p, dg, gate, daux, f)
+    if dz_loss != 0.0 and T > 0:
+        dl = dl + dz_loss * z_loss_logit_grad(fwd["gate_logits"], p)
     W_r = np.asarray(inp["W_r"], np.float64)
     out["dh"] += dl @ W_r.T                          # gate logits = h W_r (+ b_r)
     out["dW_r"] = h.T @ dl

@@ -517,19 +517,23 @@ def _bw_case(seed, T, d, E, K, w, act, bias=True, ffn_bias=False):
     return rng, inp
 
 
-def _fd_backward(seed, T, d, E, K, w, act, gate, daux, n_probe=5, eps=1e-6, bias=True, ffn_bias=False, **kw):
+def _fd_backward(seed, T, d, E, K, w, act, gate, daux, n_probe=5, eps=1e-6, bias=True, ffn_bias=False, dz=0.0,
+                 noise_scale=0.0, **kw):
     rng, inp = _bw_case(seed, T, d, E, K, w, act, bias, ffn_bias)
     dy = rng.standard_normal((T, d))
+    noise = rng.standard_normal((T, E)) * noise_scale if noise_scale else None
 
     def loss(x):
-        r = O.moe_forward(x, T, d, E, K, act, gate, logits_f64=True, **kw)
-        return float(np.sum(dy * r["y"]) + daux * r["aux"])
+        r = O.moe_forward(x, T, d, E, K, act, gate, logits_f64=True, noise=noise, **kw)
+        return float(np.sum(dy * r["y"]) + daux * r["aux"] + dz * r["z_loss"])
 
     # the expert choice must not flip inside +-eps: keep clear top-K margins
     l = O.router_logits_f64(inp["h"], inp["W_r"], inp["b_r"])
+    if noise is not None:
+        l = l + noise
     srt = np.sort(l, axis=1)[:, ::-1]
     assert K == E or np.min(srt[:, K - 1] - srt[:, K]) > 1e-3
-    g = O.moe_backward(inp, T, d, E, K, act, gate, dy, daux=daux, logits_f64=True, **kw)
+    g = O.moe_backward(inp, T, d, E, K, act, gate, dy, daux=daux, logits_f64=True, noise=noise, dz_loss=dz, **kw)
     for pname, gname in (("h", "dh"), ("W_r", "dW_r"), ("b_r", "db_r"), ("W1", "dW1"), ("W3", "dW3"),
                          ("W2", "dW2"), ("b1", "db1"), ("b2", "db2")):
         if inp[pname] is None:
@@ -595,6 +599,88 @@ def check_backward_dense_reduction(seed=34):
         assert not g["dW_r"].any() and not g["db_r"].any()
 
 
+def check_noise_zero_and_bias_equivalence(seed=41):
+    """Zero noise is the default path bit for bit; a noise that is the same
+    per-expert vector for every token equals that router bias bit for bit
+    (both are one float32 add after the logits), so choice, gates, P and the
+    z-loss agree exactly."""
+    T, d, E, K = 37, 24, 7, 2
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((T, d)).astype(np.float32)
+    Wr = (rng.standard_normal((d, E)) * 0.3).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.5).astype(np.float32)
+    base = {"h": h, "W_r": Wr, "b_r": None, "W1": rng.standard_normal((E, 8, d)), "W2": rng.standard_normal((E, d, 8)),
+            "W3": rng.standard_normal((E, 8, d)), "b1": None, "b2": None}
+    for gate in (O.GATE_RENORM, O.GATE_RAW):
+        r0 = O.moe_forward(base, T, d, E, K, O.ACT_SWIGLU, gate)
+        rz = O.moe_forward(base, T, d, E, K, O.ACT_SWIGLU, gate, noise=np.zeros((T, E), np.float32))
+        assert np.array_equal(r0["logits"].view(np.uint32), rz["logits"].view(np.uint32))
+        assert np.array_equal(r0["topk_gate"], rz["topk_gate"]) and r0["z_loss"] == rz["z_loss"]
+        rb = O.moe_forward({**base, "b_r": b}, T, d, E, K, O.ACT_SWIGLU, gate)
+        rn = O.moe_forward(base, T, d, E, K, O.ACT_SWIGLU, gate, noise=np.tile(b, (T, 1)))
+        assert np.array_equal(rb["logits"].view(np.uint32), rn["logits"].view(np.uint32))
+        assert np.array_equal(rb["topk_idx"], rn["topk_idx"])
+        assert np.array_equal(rb["topk_gate"], rn["topk_gate"]) and np.array_equal(rb["probs"], rn["probs"])
+        assert rb["z_loss"] == rn["z_loss"] and np.allclose(rb["y"], rn["y"], rtol=0, atol=0)
+
+
+def check_noise_forcing(seed=42):
+    """A noise of +1e4 on one expert per token picks that expert as the first
+    choice of every token; with top-1 renormalised gates the gate is 1, with
+    raw gates p of that expert is 1 to float64 rounding. With a
+    selection-only bias the noise still reaches the gates (only the bias is
+    choice-only)."""
+    T, d, E = 29, 16, 5
+    rng = np.random.default_rng(seed)
+    inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+           "W_r": rng.standard_normal((d, E)).astype(np.float32), "b_r": rng.standard_normal(E).astype(np.float32),
+           "W1": rng.standard_normal((E, 4, d)), "W2": rng.standard_normal((E, d, 4)),
+           "W3": rng.standard_normal((E, 4, d)), "b1": None, "b2": None}
+    want = rng.integers(0, E, T)
+    noise = np.zeros((T, E), np.float32)
+    noise[np.arange(T), want] = 1e4
+    for gate, sel in ((O.GATE_RENORM, False), (O.GATE_RAW, False), (O.GATE_RAW, True)):
+        r = O.moe_forward(inp, T, d, E, 1, O.ACT_SWIGLU, gate, noise=noise, bias_select_only=sel)
+        assert np.array_equal(r["topk_idx"][:, 0], want)
+        assert np.allclose(r["topk_gate"][:, 0], 1.0, rtol=0, atol=1e-12)
+        assert np.allclose(r["probs"][np.arange(T), want], 1.0, rtol=0, atol=1e-12)
+
+
+def check_z_loss_closed_forms(seed=43):
+    """W_r = 0 and no bias: every logit is 0, log-sum-exp is ln E and the
+    z-loss (ln E)^2; a per-token constant c_t (as noise) gives the mean of
+    (ln E + c_t)^2; with E = 2 and bias (0, x) every token's log-sum-exp is
+    log(1 + e^x), so the z-loss is log1p(exp(x))^2."""
+    rng = np.random.default_rng(seed)
+    T, d = 23, 12
+    for E in (1, 2, 3, 8, 64):
+        inp = {"h": rng.standard_normal((T, d)).astype(np.float32), "W_r": np.zeros((d, E), np.float32),
+               "b_r": None, "W1": np.zeros((E, 4, d)), "W2": np.zeros((E, d, 4)), "W3": np.zeros((E, 4, d)),
+               "b1": None, "b2": None}
+        r = O.moe_forward(inp, T, d, E, 1, O.ACT_SWIGLU, O.GATE_RENORM)
+        assert abs(r["z_loss"] - math.log(E) ** 2) <= 1e-13 * max(1.0, math.log(E) ** 2), (E, r["z_loss"])
+        c = rng.integers(-8, 9, T).astype(np.float32) / 4  # exact in float32
+        r = O.moe_forward(inp, T, d, E, 1, O.ACT_SWIGLU, O.GATE_RENORM, noise=np.repeat(c[:, None], E, axis=1))
+        want = float(np.mean((math.log(E) + c.astype(np.float64)) ** 2))
+        assert abs(r["z_loss"] - want) <= 1e-12 * max(1.0, want), (E, r["z_loss"], want)
+    for x in (-3.0, 0.0, 0.75, 5.5):
+        inp = {"h": rng.standard_normal((T, d)).astype(np.float32), "W_r": np.zeros((d, 2), np.float32),
+               "b_r": np.array([0.0, x], np.float32), "W1": np.zeros((2, 4, d)), "W2": np.zeros((2, d, 4)),
+               "W3": np.zeros((2, 4, d)), "b1": None, "b2": None}
+        r = O.moe_forward(inp, T, d, 2, 1, O.ACT_SWIGLU, O.GATE_RENORM)
+        assert abs(r["z_loss"] - math.log1p(math.exp(x)) ** 2) <= 1e-13 * max(1.0, r["z_loss"]), (x, r["z_loss"])
+
+
+def check_backward_fd_zloss_noise(seed=44):
+    """The z-loss gradient and a noisy router: central differences of
+    sum(dy y) + daux aux + dz z_loss, with noise on the logits (held fixed:
+    an input, not a parameter) — SwiGLU, renormalised top-2, router bias."""
+    _fd_backward(seed, T=12, d=10, E=4, K=2, w=6, act=O.ACT_SWIGLU, gate=O.GATE_RENORM, daux=0.4, dz=0.8,
+                 noise_scale=0.3)
+    _fd_backward(seed + 1, T=10, d=8, E=5, K=1, w=6, act=O.ACT_GELU, gate=O.GATE_RAW, daux=0.0, dz=1.5,
+                 noise_scale=0.5, ffn_bias=True, bias_select_only=True)
+
+
 ALL_CHECKS = [check_router_logits_exact, check_router_logits_bound, check_topk_bruteforce,
               check_probs, check_gates_worked_example, check_gates_invariants,
               check_combine_worked_example, check_permutation_sorted, check_load_stats_page,
@@ -602,4 +688,6 @@ ALL_CHECKS = [check_router_logits_exact, check_router_logits_bound, check_topk_b
               check_soft_mixture_K_equals_E, check_forward_subset_consistency, check_param_counts,
               check_capacity_widget, check_capacity_order, check_capacity_slots_rounding,
               check_capacity_layer, check_bias_select_only, check_backward_fd_swiglu_renorm,
-              check_backward_fd_gelu_raw_capacity, check_backward_fd_switch_top1, check_backward_dense_reduction]
+              check_backward_fd_gelu_raw_capacity, check_backward_fd_switch_top1, check_backward_dense_reduction,
+              check_noise_zero_and_bias_equivalence, check_noise_forcing, check_z_loss_closed_forms,
+              check_backward_fd_zloss_noise]

@@ -12,7 +12,8 @@ from oracle import moe_oracle as O
 _orig = {name: getattr(O, name) for name in
          ("moe_forward", "gelu_grad", "silu_grad", "gate_logit_grad", "router_logits_f32", "select_topk", "router_probs", "gates", "stable_permutation",
           "aux_loss", "gelu", "silu", "expert_ffn", "combine", "param_counts_micro",
-          "param_counts_swiglu_model", "expert_counts", "capacity_keep", "capacity_slots", "drop_stats")}
+          "param_counts_swiglu_model", "expert_counts", "capacity_keep", "capacity_slots", "drop_stats",
+          "z_loss", "z_loss_logit_grad")}
 
 
 def _logits_no_bias(h, W, b):
@@ -198,7 +199,39 @@ def _drop_stats_over_T(counts, C):
     return {"dropped": st["dropped"], "percent": 100.0 * st["dropped"] / max(int(sum(counts)) // 2, 1)}
 
 
+def _zloss_not_squared(gl):
+    return float(np.mean(O.logsumexp_rows(gl))) if gl.shape[0] else 0.0
+
+
+def _zloss_sum_not_mean(gl):
+    return float(np.sum(O.logsumexp_rows(gl) ** 2))
+
+
+def _zloss_grad_factor_one(gl, p):
+    return 0.5 * _orig["z_loss_logit_grad"](gl, p)
+
+
+def _forward_noise_ignored(*a, noise=None, **kw):
+    return _orig["moe_forward"](*a, **kw)
+
+
+def _forward_noise_selection_only(inp, T, d, E, K, act, gate, *a, noise=None, **kw):
+    # the noise steers the choice but the gates and P come from noise-free logits
+    r = _orig["moe_forward"](inp, T, d, E, K, act, gate, *a, noise=noise, **kw)
+    if noise is None:
+        return r
+    r0 = _orig["moe_forward"](inp, T, d, E, K, act, gate, *a, **kw)
+    r["topk_gate"] = O.gates(r0["gate_logits"], r["topk_idx"], gate)
+    r["probs"] = O.router_probs(r0["gate_logits"])
+    return r
+
+
 MUTATIONS = {
+    "zloss_not_squared": ("z_loss", _zloss_not_squared),
+    "zloss_sum_not_mean": ("z_loss", _zloss_sum_not_mean),
+    "zloss_grad_factor_one": ("z_loss_logit_grad", _zloss_grad_factor_one),
+    "noise_ignored": ("moe_forward", _forward_noise_ignored),
+    "noise_selection_only": ("moe_forward", _forward_noise_selection_only),
     "capacity_later_tokens_win": ("capacity_keep", _keep_later_tokens_win),
     "capacity_off_by_one": ("capacity_keep", _keep_off_by_one),
     "capacity_rounded_down": ("capacity_slots", _capacity_floor),
