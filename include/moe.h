@@ -145,15 +145,21 @@ int moe_workspace_size(const moe_desc* desc, size_t* bytes);
 
 /* Router (Lensa ML Step 2: a linear layer and a softmax; Step 3: top-k and
  * gates; Step 4: slot counts and the load-balance loss).
- * In:  h, W_r, b_r (nullable).
+ * In:  h, W_r, b_r (nullable), noise [T][E] float32 (nullable): values added
+ *      to the logits after the bias, one float32 add each, which enter the
+ *      choice, the gates and P (noisy top-k routing, arjunjaggi.com "Load
+ *      Balancing": the caller draws and scales the noise).
  * Out: topk_idx, topk_gate, expert_counts, prob_mean [E] (P_e, nullable),
  *      aux_loss [1] (nullable), logits [T][E] float32 (nullable): the scores
- *      the choice is made on, h . W_r + b_r (with either bias_mode).
+ *      the choice is made on, h . W_r + b_r (+ noise) (with either bias_mode),
+ *      z_loss [1] (nullable): the router z-loss (arjunjaggi.com "Mixtral and
+ *      the Open MoE Era": ST-MoE's penalty on large router logits), the mean
+ *      over tokens of the squared log-sum-exp of the logits the softmax sees.
  * Returns a moe_status. */
 int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
               int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,
-              float* prob_mean, float* aux_loss, float* logits,
-              void* ws, size_t ws_bytes, void* stream);
+              float* prob_mean, float* aux_loss, float* logits, const float* noise,
+              float* z_loss, void* ws, size_t ws_bytes, void* stream);
 
 /* Grouping of the routing slots by expert (Lensa ML Step 5: experts take any
  * number of tokens). Stable: inside each expert's group tokens keep their order.
@@ -188,22 +194,24 @@ int moe_combine(const moe_desc* desc, const float* o_perm, const int32_t* token_
                 const float* topk_gate, void* y, void* stream);
 
 /* The whole layer: route -> group -> experts -> combine, plus the aux loss.
- * In:  h, W_r, b_r (nullable), W1, b1 (nullable), W3 (SwiGLU), W2, b2 (nullable).
- * Out: y, aux_loss [1] (nullable), expert_counts [E] (nullable).
+ * In:  h, W_r, b_r (nullable), W1, b1 (nullable), W3 (SwiGLU), W2, b2 (nullable),
+ *      noise [T][E] (nullable, as in moe_route).
+ * Out: y, aux_loss [1] (nullable), expert_counts [E] (nullable), z_loss [1]
+ *      (nullable, as in moe_route).
  * For K = 1 and no capacity the second expert GEMM writes gate * o straight
  * into y; with a capacity (desc->capacity > 0) dropped slots add nothing.
  * Returns a moe_status. */
 int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
                 const void* W1, const void* b1, const void* W3, const void* W2,
                 const void* b2, void* y, float* aux_loss, int32_t* expert_counts,
-                void* ws, size_t ws_bytes, void* stream);
+                const float* noise, float* z_loss, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace moe_backward needs for this layer shape (bfloat16 layers
  * only: MOE_ERR_UNSUPPORTED otherwise). Host-only; enqueues nothing. */
 int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes);
 
 /* Backward pass of the layer: gradients of loss = sum(dy * y) + daux * aux
- * with respect to every input, for bfloat16 layers. The gradient reaches the
+ * + dz * z_loss with respect to every input, for bfloat16 layers. The gradient reaches the
  * router only through the gate weights of the chosen experts (maptheai.com
  * "Mixture of Experts", "The difficulties": the top-k choice is not
  * differentiable), through p_i for raw gates (Lensa ML Step 3), and through
@@ -212,8 +220,9 @@ int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes);
  * selection-only bias gets a zero gradient. The routing (bit for bit the
  * same), the grouping and the first expert GEMM are recomputed from the
  * inputs; the caller keeps no activations.
- * In:  the forward's inputs (h, W_r, b_r, W1, b1, W3, W2, b2), dy [T][d]
- *      dtype, daux (finite; the weight of aux in the loss).
+ * In:  the forward's inputs (h, W_r, b_r, W1, b1, W3, W2, b2, noise
+ *      (nullable; held fixed: an input, not differentiated)), dy [T][d] dtype,
+ *      daux and dz (finite; the weights of aux and of z_loss in the loss).
  * Out: dh [T][d] dtype; dW_r [d][E], db_r [E] (nullable), dW1 [E][width][d],
  *      db1 [E][width] (nullable, GELU only), dW3 [E][width][d] (SwiGLU),
  *      dW2 [E][d][width], db2 [E][d] (nullable, GELU only), all float32.
@@ -221,12 +230,12 @@ int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes);
  * Sums over tokens and slots run in a fixed order: results are bitwise
  * reproducible. Returns a moe_status (MOE_ERR_UNSUPPORTED for float32 layers,
  * bias gradients of SwiGLU layers, or transposed operands past the 32-bit
- * offset range; MOE_ERR_SHAPE for a non-finite daux). */
+ * offset range; MOE_ERR_SHAPE for a non-finite daux or dz). */
 int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
                  const void* W1, const void* b1, const void* W3, const void* W2, const void* b2,
-                 const void* dy, float daux, void* dh, float* dW_r, float* db_r, float* dW1,
-                 float* db1, float* dW3, float* dW2, float* db2, void* ws, size_t ws_bytes,
-                 void* stream);
+                 const void* dy, float daux, const float* noise, float dz, void* dh, float* dW_r,
+                 float* db_r, float* dW1, float* db1, float* dW3, float* dW2, float* db2, void* ws,
+                 size_t ws_bytes, void* stream);
 
 /* Instrumentation (not part of the layer). While enabled, every kernel the
  * library launches is bracketed by two hipEvents recorded on its launch

@@ -44,16 +44,16 @@ _SIGS = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_workspace_size": (ctypes.c_int, [ctypes.POINTER(MoeDesc), ctypes.POINTER(ctypes.c_size_t)]),
-    "moe_route": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 9 + [_vp, ctypes.c_size_t, _vp]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 6 + [_vp, ctypes.c_size_t, _vp]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 4 + [_vp]),
-    "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]),
+    "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 13 + [_vp, ctypes.c_size_t, _vp]),
     "moe_capacity_slots": (ctypes.c_int, [ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.POINTER(ctypes.c_int32)]),
     "moe_backward_workspace_size": (ctypes.c_int, [ctypes.POINTER(MoeDesc), ctypes.POINTER(ctypes.c_size_t)]),
-    "moe_backward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 9 + [ctypes.c_float] + [_vp] * 8
-                     + [_vp, ctypes.c_size_t, _vp]),
+    "moe_backward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 9 + [ctypes.c_float, _vp, ctypes.c_float]
+                     + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]),
     "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_trace_read": (ctypes.c_int, [_vp, _vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
     "moe_trace_disable": (ctypes.c_int, []),
@@ -132,21 +132,23 @@ def workspace(desc: MoeDesc, device="cuda") -> torch.Tensor:
     return torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device)
 
 
-def route(desc: MoeDesc, h, W_r, b_r=None, ws=None, want_logits=False) -> Dict[str, torch.Tensor]:
+def route(desc: MoeDesc, h, W_r, b_r=None, ws=None, want_logits=False, noise=None) -> Dict[str, torch.Tensor]:
+    """moe_route; noise: [T][E] float32 added to the logits (or None). Also returns z_loss."""
     dev = h.device
     T, E, K = desc.T, desc.E, desc.K
     out = {"topk_idx": torch.empty((T, K), dtype=torch.int32, device=dev),
            "topk_gate": torch.empty((T, K), dtype=torch.float32, device=dev),
            "counts": torch.empty(E, dtype=torch.int32, device=dev),
            "prob_mean": torch.empty(E, dtype=torch.float32, device=dev),
-           "aux": torch.empty(1, dtype=torch.float32, device=dev)}
+           "aux": torch.empty(1, dtype=torch.float32, device=dev),
+           "z_loss": torch.empty(1, dtype=torch.float32, device=dev)}
     if want_logits:
         out["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
     ws = workspace(desc, dev) if ws is None else ws
     _check("moe_route", lib().moe_route(
         ctypes.byref(desc), _ptr(h), _ptr(W_r), _ptr(b_r), _ptr(out["topk_idx"]), _ptr(out["topk_gate"]),
-        _ptr(out["counts"]), _ptr(out["prob_mean"]), _ptr(out["aux"]), _ptr(out.get("logits")),
-        _ptr(ws), ws.numel(), _stream()))
+        _ptr(out["counts"]), _ptr(out["prob_mean"]), _ptr(out["aux"]), _ptr(out.get("logits")), _ptr(noise),
+        _ptr(out["z_loss"]), _ptr(ws), ws.numel(), _stream()))
     return out
 
 
@@ -182,7 +184,10 @@ def combine(desc: MoeDesc, o_perm, token_slot, topk_gate, dtype) -> torch.Tensor
 
 
 def forward(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, ws=None, y=None, aux=None,
-            counts=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+            counts=None, noise=None, z_loss=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """moe_forward: (y, aux, counts). noise: [T][E] float32 added to the logits
+    (or None); z_loss: a float32 tensor of one element to receive the router
+    z-loss (or None: not computed)."""
     dev = h.device
     y = torch.empty((desc.T, desc.d), dtype=h.dtype, device=dev) if y is None else y
     aux = torch.empty(1, dtype=torch.float32, device=dev) if aux is None else aux
@@ -190,7 +195,7 @@ def forward(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, ws=None, y=None, aux
     ws = workspace(desc, dev) if ws is None else ws
     _check("moe_forward", lib().moe_forward(
         ctypes.byref(desc), _ptr(h), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2), _ptr(b2),
-        _ptr(y), _ptr(aux), _ptr(counts), _ptr(ws), ws.numel(), _stream()))
+        _ptr(y), _ptr(aux), _ptr(counts), _ptr(noise), _ptr(z_loss), _ptr(ws), ws.numel(), _stream()))
     return y, aux, counts
 
 
@@ -201,8 +206,9 @@ def backward_workspace(desc: MoeDesc, device="cuda") -> torch.Tensor:
 
 
 def backward(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, dy, daux: float = 0.0, ws=None,
-             bias_grads: bool = True) -> Dict[str, Optional[torch.Tensor]]:
-    """Gradients of sum(dy * y) + daux * aux (moe_backward); float32 except dh."""
+             bias_grads: bool = True, noise=None, dz: float = 0.0) -> Dict[str, Optional[torch.Tensor]]:
+    """Gradients of sum(dy * y) + daux * aux + dz * z_loss (moe_backward), with
+    the router noise (or None) held fixed; float32 except dh."""
     dev = h.device
     E, d, w = desc.E, desc.d, desc.width
     f32 = dict(dtype=torch.float32, device=dev)
@@ -218,7 +224,7 @@ def backward(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, dy, daux: float = 0
     ws = backward_workspace(desc, dev) if ws is None else ws
     _check("moe_backward", lib().moe_backward(
         ctypes.byref(desc), _ptr(h), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2), _ptr(b2),
-        _ptr(dy), float(daux), _ptr(out["dh"]), _ptr(out["dW_r"]), _ptr(out["db_r"]), _ptr(out["dW1"]),
+        _ptr(dy), float(daux), _ptr(noise), float(dz), _ptr(out["dh"]), _ptr(out["dW_r"]), _ptr(out["db_r"]), _ptr(out["dW1"]),
         _ptr(out["db1"]), _ptr(out["dW3"]), _ptr(out["dW2"]), _ptr(out["db2"]), _ptr(ws), ws.numel(), _stream()))
     return out
 

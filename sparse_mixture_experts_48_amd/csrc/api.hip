@@ -42,7 +42,7 @@ size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Plan {
   RouteTiling rt;
-  size_t blk_hist, blk_psum, blk_base;
+  size_t blk_hist, blk_psum, blk_base, blk_z;
   size_t topk_idx, topk_gate, token_slot, slot_token;
   size_t counts, offsets, pmean, aux;
   size_t act, o_perm;
@@ -64,6 +64,7 @@ Plan make_plan(const moe_desc& d) {
   p.blk_hist = take(nbe * 4);
   p.blk_psum = take(nbe * 4);
   p.blk_base = take(nbe * 4);
+  p.blk_z = take(static_cast<size_t>(p.rt.NB) * 4);
   p.topk_idx = take(S * 4);
   p.topk_gate = take(S * 4);
   p.token_slot = take(S * 4);
@@ -85,7 +86,8 @@ struct BwdPlan {
   RouteTiling rt;
   int64_t S, Zw, ldk;
   int nwr;
-  size_t blk_hist, blk_psum, blk_base, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux, logits;
+  size_t blk_hist, blk_psum, blk_base, blk_z, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux,
+      logits;
   size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
   size_t total;
 };
@@ -109,6 +111,7 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   p.blk_hist = take(nbe * 4);
   p.blk_psum = take(nbe * 4);
   p.blk_base = take(nbe * 4);
+  p.blk_z = take(static_cast<size_t>(p.rt.NB) * 4);
   p.topk_idx = take(S * 4);
   p.topk_gate = take(S * 4);
   p.token_slot = take(S * 4);
@@ -288,7 +291,7 @@ int moe_workspace_size(const moe_desc* desc, size_t* bytes) {
 
 int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, int32_t* topk_idx,
               float* topk_gate, int32_t* expert_counts, float* prob_mean, float* aux_loss, float* logits,
-              void* ws, size_t ws_bytes, void* stream) {
+              const float* noise, float* z_loss, void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_desc(desc));
   const moe_desc& d = *desc;
   const bool any = d.T > 0;
@@ -301,21 +304,26 @@ int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float
   MOE_CHECK(check_ptr(prob_mean, false));
   MOE_CHECK(check_ptr(aux_loss, false));
   MOE_CHECK(check_ptr(logits, false));
+  MOE_CHECK(check_ptr(noise, false));
+  MOE_CHECK(check_ptr(z_loss, false));
   const Plan pl = make_plan(d);
   MOE_CHECK(check_ws(pl, ws, ws_bytes));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!any) {
-    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, expert_counts, nullptr, prob_mean, aux_loss, st));
+    MOE_LAUNCH(MOE_K_ZERO, st,
+               moe::launch_zero_outputs(d.E, expert_counts, nullptr, prob_mean, aux_loss, z_loss, st));
     return MOE_OK;
   }
   moe::RouteArgs ra{h, W_r, b_r, static_cast<int>(d.T), static_cast<int>(d.d), static_cast<int>(d.E),
                     static_cast<int>(d.K), d.gate, topk_idx, topk_gate, logits,
                     at<int32_t>(ws, pl.blk_hist), at<float>(ws, pl.blk_psum)};
   ra.bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
+  ra.noise = noise;
+  ra.blk_z = z_loss != nullptr ? at<float>(ws, pl.blk_z) : nullptr;
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, d.dtype == MOE_BF16, st));
   MOE_LAUNCH(MOE_K_FINALIZE, st,
-             moe::launch_finalize(ra.blk_hist, ra.blk_psum, pl.rt.NB, ra.T, ra.E, ra.K, nullptr, expert_counts,
-                                  nullptr, prob_mean, aux_loss, st));
+             moe::launch_finalize(ra.blk_hist, ra.blk_psum, ra.blk_z, pl.rt.NB, ra.T, ra.E, ra.K, nullptr,
+                                  expert_counts, nullptr, prob_mean, aux_loss, z_loss, st));
   return MOE_OK;
 }
 
@@ -335,7 +343,7 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h, in
   MOE_CHECK(check_ws(pl, ws, ws_bytes));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!any) {
-    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, nullptr, expert_offsets, nullptr, nullptr, st));
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, nullptr, expert_offsets, nullptr, nullptr, nullptr, st));
     return MOE_OK;
   }
   const int T = static_cast<int>(d.T), E = static_cast<int>(d.E), K = static_cast<int>(d.K);
@@ -344,8 +352,8 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h, in
   const size_t row_bytes = static_cast<size_t>(d.d) * (d.dtype == MOE_BF16 ? 2 : 4);
   MOE_LAUNCH(MOE_K_HIST, st, moe::launch_hist(topk_idx, T, E, K, pl.rt, blk_hist, st));
   MOE_LAUNCH(MOE_K_FINALIZE, st,
-             moe::launch_finalize(blk_hist, nullptr, pl.rt.NB, T, E, K, blk_base, nullptr, expert_offsets,
-                                  nullptr, nullptr, st));
+             moe::launch_finalize(blk_hist, nullptr, nullptr, pl.rt.NB, T, E, K, blk_base, nullptr, expert_offsets,
+                                  nullptr, nullptr, nullptr, st));
   MOE_LAUNCH(MOE_K_PERMUTE, st,
              moe::launch_permute(topk_idx, blk_base, expert_offsets, T, E, K, cap_of(d), pl.rt, h, row_bytes,
                                  h_perm, slot_token, token_slot, st));
@@ -406,7 +414,8 @@ int moe_combine(const moe_desc* desc, const float* o_perm, const int32_t* token_
 
 int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, const void* W1,
                 const void* b1, const void* W3, const void* W2, const void* b2, void* y, float* aux_loss,
-                int32_t* expert_counts, void* ws, size_t ws_bytes, void* stream) {
+                int32_t* expert_counts, const float* noise, float* z_loss, void* ws, size_t ws_bytes,
+                void* stream) {
   MOE_CHECK(check_desc(desc));
   const moe_desc& d = *desc;
   const bool any = d.T > 0;
@@ -417,11 +426,13 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
   MOE_CHECK(check_ptr(y, any));
   MOE_CHECK(check_ptr(aux_loss, false));
   MOE_CHECK(check_ptr(expert_counts, false));
+  MOE_CHECK(check_ptr(noise, false));
+  MOE_CHECK(check_ptr(z_loss, false));
   const Plan pl = make_plan(d);
   MOE_CHECK(check_ws(pl, ws, ws_bytes));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!any) {
-    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, expert_counts, nullptr, nullptr, aux_loss, st));
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, expert_counts, nullptr, nullptr, aux_loss, z_loss, st));
     return MOE_OK;
   }
   const int T = static_cast<int>(d.T), E = static_cast<int>(d.E), K = static_cast<int>(d.K);
@@ -439,10 +450,12 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
   moe::RouteArgs ra{h, W_r, b_r, T, static_cast<int>(d.d), E, K, d.gate, topk_idx, topk_gate, nullptr,
                     blk_hist, blk_psum};
   ra.bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
+  ra.noise = noise;
+  ra.blk_z = z_loss != nullptr ? at<float>(ws, pl.blk_z) : nullptr;
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
   MOE_LAUNCH(MOE_K_FINALIZE, st,
-             moe::launch_finalize(blk_hist, blk_psum, pl.rt.NB, T, E, K, blk_base, counts, offsets, nullptr,
-                                  aux_loss, st));
+             moe::launch_finalize(blk_hist, blk_psum, ra.blk_z, pl.rt.NB, T, E, K, blk_base, counts, offsets,
+                                  nullptr, aux_loss, z_loss, st));
   const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
   const int cap = cap_of(d);
   MOE_LAUNCH(MOE_K_PERMUTE, st,
@@ -487,8 +500,8 @@ int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes) {
 
 int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, const void* W1,
                  const void* b1, const void* W3, const void* W2, const void* b2, const void* dy, float daux,
-                 void* dh, float* dW_r, float* db_r, float* dW1, float* db1, float* dW3, float* dW2, float* db2,
-                 void* ws, size_t ws_bytes, void* stream) {
+                 const float* noise, float dz, void* dh, float* dW_r, float* db_r, float* dW1, float* db1,
+                 float* dW3, float* dW2, float* db2, void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_desc(desc));
   const moe_desc& d = *desc;
   MOE_CHECK(check_bwd_desc(d));
@@ -508,7 +521,8 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   MOE_CHECK(check_ptr(db2, false));
   if (swiglu) MOE_CHECK(check_ptr(dW3, true));
   if (swiglu && (db1 != nullptr || db2 != nullptr || b1 != nullptr || b2 != nullptr)) return MOE_ERR_UNSUPPORTED;
-  if (!std::isfinite(daux)) return MOE_ERR_SHAPE;
+  if (!std::isfinite(daux) || !std::isfinite(dz)) return MOE_ERR_SHAPE;
+  MOE_CHECK(check_ptr(noise, false));
   const BwdPlan pl = make_bwd_plan(d);
   if (ws_bytes < pl.total || ws == nullptr || reinterpret_cast<uintptr_t>(ws) % 256 != 0) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -543,10 +557,11 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   // forward: routing (with the logits), grouping, the expert GEMMs
   moe::RouteArgs ra{h, W_r, b_r, T, D, E_, K, d.gate, topk_idx, topk_gate, logits, blk_hist, blk_psum};
   ra.bias_select = bias_select;
+  ra.noise = noise;
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, true, st));
   MOE_LAUNCH(MOE_K_FINALIZE, st,
-             moe::launch_finalize(blk_hist, blk_psum, pl.rt.NB, T, E_, K, blk_base, counts, offsets, nullptr,
-                                  at<float>(ws, pl.aux), st));
+             moe::launch_finalize(blk_hist, blk_psum, nullptr, pl.rt.NB, T, E_, K, blk_base, counts, offsets, nullptr,
+                                  at<float>(ws, pl.aux), nullptr, st));
   MOE_LAUNCH(MOE_K_PERMUTE, st,
              moe::launch_permute(topk_idx, blk_base, offsets, T, E_, K, cap, pl.rt, h, dd * 2, nullptr, slot_token,
                                  token_slot, st));
@@ -599,7 +614,7 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   float* dl = at<float>(ws, pl.dl);
   MOE_LAUNCH(MOE_K_BWD, st,
              moe::launch_router_backward(logits, b_r, bias_select, topk_idx, topk_gate, dgs, dyb, token_slot,
-                                         counts, T, E_, K, d.gate, daux, dl, st));
+                                         counts, T, E_, K, d.gate, daux, dz, dl, st));
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dh(dX, token_slot, dl, W_r, T, D, E_, K, dh, st));
   MOE_LAUNCH(MOE_K_BWD, st,
              moe::launch_dwr(h, dl, T, D, E_, at<float>(ws, pl.wr_part), dW_r, bias_select ? nullptr : db_r, st));

@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
     const float* __restrict__ logits, const float* __restrict__ br, int bias_select,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ gate, const float* __restrict__ dgs,
     const float* __restrict__ dyb, const int32_t* __restrict__ token_slot, const int32_t* __restrict__ counts,
-    int T, int E, int K, int gate_mode, float daux, float* __restrict__ dl) {
+    int T, int E, int K, int gate_mode, float daux, float dz, float* __restrict__ dl) {
   const int t = blockIdx.x * 4 + threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   if (t >= T) return;
@@ -242,7 +242,9 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
   }
   float pdp = on ? p * dp : 0.0f;
   for (int off = 32; off > 0; off >>= 1) pdp += __shfl_xor(pdp, off);
-  if (on) dl[static_cast<size_t>(t) * E + lane] = dlv + p * (dp - pdp);
+  // z-loss: d (lse_t^2 / T) / d l = 2 lse_t p / T
+  const float dzl = dz != 0.0f ? dz * (2.0f / static_cast<float>(T)) * (m + logf(sum)) * p : 0.0f;
+  if (on) dl[static_cast<size_t>(t) * E + lane] = dlv + p * (dp - pdp) + dzl;
 }
 
 // dh[t] = sum_j dX[slot(t, j)] (ascending j, kept slots) + sum_e dl[t][e] W_r[k][e].
@@ -412,9 +414,10 @@ hipError_t launch_dgate_sum(const float* dgp, int ncb, int S, float* dgs, hipStr
 hipError_t launch_router_backward(const float* logits, const float* br, int bias_select, const int32_t* topk_idx,
                                   const float* gate, const float* dgs, const float* dyb,
                                   const int32_t* token_slot, const int32_t* counts, int T, int E, int K,
-                                  int gate_mode, float daux, float* dl, hipStream_t st) {
+                                  int gate_mode, float daux, float dz, float* dl, hipStream_t st) {
   hipLaunchKernelGGL(router_backward_kernel, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(256), 0, st, logits,
-                     br, bias_select, topk_idx, gate, dgs, dyb, token_slot, counts, T, E, K, gate_mode, daux, dl);
+                     br, bias_select, topk_idx, gate, dgs, dyb, token_slot, counts, T, E, K, gate_mode, daux, dz,
+                     dl);
   return hipGetLastError();
 }
 

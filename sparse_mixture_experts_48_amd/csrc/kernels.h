@@ -29,16 +29,19 @@ struct RouteArgs {
   int32_t* blk_hist;  // [NB][E]
   float* blk_psum;    // [NB][E]
   int bias_select = 0;  // 1: br steers the choice only; softmax and gates use h . W_r
+  const float* noise = nullptr;  // [T][E] added to the logits after the bias, or null
+  float* blk_z = nullptr;        // [NB] per-block sums of lse^2 (z-loss), or null
 };
 
 hipError_t launch_route(const RouteArgs& a, const RouteTiling& rt, bool bf16, hipStream_t st);
 hipError_t launch_hist(const int32_t* topk_idx, int T, int E, int K, const RouteTiling& rt,
                        int32_t* blk_hist, hipStream_t st);
-hipError_t launch_finalize(const int32_t* blk_hist, const float* blk_psum, int NB, int T, int E, int K,
-                           int32_t* blk_base, int32_t* counts, int32_t* offsets, float* prob_mean,
-                           float* aux, hipStream_t st);
+// z_loss (nullable) = sum of blk_z / T; blk_z may be null when z_loss is.
+hipError_t launch_finalize(const int32_t* blk_hist, const float* blk_psum, const float* blk_z, int NB, int T,
+                           int E, int K, int32_t* blk_base, int32_t* counts, int32_t* offsets, float* prob_mean,
+                           float* aux, float* z_loss, hipStream_t st);
 hipError_t launch_zero_outputs(int E, int32_t* counts, int32_t* offsets, float* prob_mean, float* aux,
-                               hipStream_t st);
+                               float* z_loss, hipStream_t st);
 
 // Stable grouping: slot ranks, token_slot, slot_token and the gathered rows.
 // With cap < INT_MAX, a slot whose rank in its expert's group is cap or more is
@@ -105,10 +108,11 @@ hipError_t launch_dout(const void* dy, const int32_t* token_slot, const int32_t*
 // dgs[s] = sum over c of dgp[c][s], c in order (the gate gradient of grouped row s, bias term aside).
 hipError_t launch_dgate_sum(const float* dgp, int ncb, int S, float* dgs, hipStream_t st);
 // Gate gradient of slot (t, j): dgs[token_slot] + dyb (0 for a dropped slot).
+// Also the z-loss term dz * 2 lse p / T when dz != 0 (lse and p of the gate logits).
 hipError_t launch_router_backward(const float* logits, const float* br, int bias_select, const int32_t* topk_idx,
                                   const float* gate, const float* dgs, const float* dyb,
                                   const int32_t* token_slot, const int32_t* counts, int T, int E, int K,
-                                  int gate_mode, float daux, float* dl, hipStream_t st);
+                                  int gate_mode, float daux, float dz, float* dl, hipStream_t st);
 hipError_t launch_dh(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
                      int E, int K, void* dh, hipStream_t st);
 int dwr_chunks(int T);

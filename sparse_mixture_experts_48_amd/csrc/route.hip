@@ -90,9 +90,9 @@ template <> struct HVec<bf16_t> {
 template <typename Tin, int EP, int TE, int TPT, int BK, int NS>
 __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
-    int T, int d, int E, int K, int gate_mode,
+    const float* __restrict__ noise, int T, int d, int E, int K, int gate_mode,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
-    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, int bias_select) {
+    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, float* __restrict__ blk_z, int bias_select) {
   constexpr int LE = EP / TE;             // expert lanes per chain
   constexpr int LG = 4 * LE;              // lanes per token group: chain-major, then expert lane
   constexpr int G = kRouteThreads / LG;   // token groups per block
@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   __shared__ __align__(16) float h_s[2][TB][HP];
   __shared__ __align__(16) float w_s[2][BK][WP];
   __shared__ float psum_s[G][EP];
+  __shared__ float z_s[G];
   __shared__ int hist_s[EP];
 
   const int tid = threadIdx.x;
@@ -251,14 +252,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   float psum_local[TE];
 #pragma unroll
   for (int q = 0; q < TE; ++q) psum_local[q] = 0.0f;
+  float z_local = 0.0f;  // sum of lse^2 over this token group's tokens (z-loss)
 
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int t = t0 + tg + i * G;
     const bool tok_ok = t < T;  // uniform across the lanes of this token group
-    // l: the score the choice is made on (logit + bias); lg: the logit of the
-    // softmax and the gates (l, or the unbiased logit when the bias only
-    // steers the choice)
+    // l: the score the choice is made on (logit + bias, + noise); lg: the
+    // logit of the softmax and the gates (l, or logit + noise when the bias
+    // only steers the choice)
     float l[TE], lg[TE];
 #pragma unroll
     for (int q = 0; q < TE; ++q) {
@@ -270,6 +272,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
         l[q] = c0123;
         if (br != nullptr) l[q] = l[q] + br[e];
         lg[q] = bias_select ? c0123 : l[q];
+        if (noise != nullptr && tok_ok) {
+          const float nz = noise[static_cast<size_t>(t) * E + e];
+          l[q] = l[q] + nz;
+          lg[q] = lg[q] + nz;
+        }
       } else {
         l[q] = -INFINITY;
         lg[q] = -INFINITY;
@@ -335,6 +342,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     if (tok_ok) {
 #pragma unroll
       for (int q = 0; q < TE; ++q) psum_local[q] += ex[q] / s;
+      const float lse = m + logf(s);
+      z_local += lse * lse;
     }
     if (tok_ok && cj == 0 && el == 0) {
       float ec[8];
@@ -361,12 +370,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
 #pragma unroll
   for (int q = 0; q < TE; ++q)
     if (cj == 0) psum_s[tg][expert_of(q)] = psum_local[q];
+  if (cj == 0 && el == 0) z_s[tg] = z_local;
   __syncthreads();
   if (tid < E) {
     float s = 0.0f;
     for (int g = 0; g < G; ++g) s += psum_s[g][tid];
     blk_psum[static_cast<size_t>(blockIdx.x) * E + tid] = s;
     blk_hist[static_cast<size_t>(blockIdx.x) * E + tid] = hist_s[tid];
+  }
+  if (tid == 0 && blk_z != nullptr) {
+    float z = 0.0f;
+    for (int g = 0; g < G; ++g) z += z_s[g];  // fixed order
+    blk_z[blockIdx.x] = z;
   }
 }
 
@@ -377,9 +392,9 @@ constexpr int kNarrowNW = 4;
 template <typename Tin, int EP, int NW>
 __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
     const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
-    int T, int d, int E, int K, int gate_mode,
+    const float* __restrict__ noise, int T, int d, int E, int K, int gate_mode,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
-    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, int bias_select) {
+    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, float* __restrict__ blk_z, int bias_select) {
   constexpr int KC = kNarrowKC;
   constexpr int NT = NW * 64;
   constexpr int WF4 = KC * EP / 4;         // float4 slots of a W_r chunk buffer
@@ -395,6 +410,7 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
   __shared__ __align__(16) float wA[EP * KP];  // W_r chunk transposed: [e][k - k0]
   __shared__ __align__(16) float wB[EP * KP];
   __shared__ float psum_s[NW][EP];
+  __shared__ float z_s[NW];
   __shared__ int hist_s[EP];
 
   const int tid = threadIdx.x;
@@ -518,15 +534,20 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
   // lanes of inactive chains or experts hold +0 and are not used
   float part = acc + __shfl_xor(acc, EP);  // chains 0/1: c0 + c1; chains 2/3: c2 + c3
   part = part + __shfl_xor(part, 2 * EP);
-  // top-K by (score descending, expert ascending) on l = logit (+ bias);
-  // softmax and gates on lg, which is l, or the unbiased logit when the bias
-  // only steers the choice
+  // top-K by (score descending, expert ascending) on l = logit (+ bias)
+  // (+ noise); softmax and gates on lg, which is l, or logit + noise when the
+  // bias only steers the choice
   float l = -INFINITY;
   float lg = -INFINITY;
   if (lane < E) {
     l = part;
     if (br != nullptr) l = l + br[lane];
     lg = bias_select ? part : l;
+    if (noise != nullptr && tok_ok) {
+      const float nz = noise[static_cast<size_t>(t) * E + lane];
+      l = l + nz;
+      lg = lg + nz;
+    }
   }
   if (tok_ok && logits_out != nullptr && lane < E) logits_out[static_cast<size_t>(t) * E + lane] = l;
   bool taken = false;
@@ -562,6 +583,10 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
 #pragma unroll
   for (int off = 1; off < EP; off <<= 1) s += __shfl_xor(s, off, EP);
   if (lane < EP) psum_s[wave][lane] = tok_ok ? ex / s : 0.0f;
+  if (lane == 0) {
+    const float lse = m + logf(s);
+    z_s[wave] = tok_ok ? lse * lse : 0.0f;
+  }
   if (tok_ok && lane == 0) {
     float ec[8];
     float se = 0.0f;
@@ -589,6 +614,11 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
     blk_psum[static_cast<size_t>(blockIdx.x) * E + tid] = sum;
     blk_hist[static_cast<size_t>(blockIdx.x) * E + tid] = hist_s[tid];
   }
+  if (tid == 0 && blk_z != nullptr) {
+    float z = 0.0f;
+    for (int w = 0; w < NW; ++w) z += z_s[w];  // fixed order
+    blk_z[blockIdx.x] = z;
+  }
 }
 
 // Per-block expert histogram of topk_idx, with the router's token tiling.
@@ -613,11 +643,13 @@ constexpr int kFinThreads = 1024;
 constexpr int kFinParts = kFinThreads / 64;
 
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
-    const int32_t* __restrict__ blk_hist, const float* __restrict__ blk_psum, int NB, int T, int E,
-    int K, int32_t* __restrict__ blk_base, int32_t* __restrict__ counts_out,
-    int32_t* __restrict__ offsets_out, float* __restrict__ prob_mean, float* __restrict__ aux_out) {
+    const int32_t* __restrict__ blk_hist, const float* __restrict__ blk_psum, const float* __restrict__ blk_z,
+    int NB, int T, int E, int K, int32_t* __restrict__ blk_base, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, float* __restrict__ prob_mean, float* __restrict__ aux_out,
+    float* __restrict__ z_out) {
   __shared__ int part_cnt[kFinParts][64];
   __shared__ float part_p[kFinParts][64];
+  __shared__ float part_z[kFinParts];
   __shared__ int tot_s[64];
   __shared__ int off_s[65];
   __shared__ float P_s[64];
@@ -649,6 +681,12 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   }
   part_cnt[part][e] = c;
   part_p[part][e] = ps;
+  if (e == 0) {  // z-loss partials of this part's blocks, in block order
+    float zs = 0.0f;
+    if (blk_z != nullptr)
+      for (int b = b0; b < b1; ++b) zs += blk_z[b];
+    part_z[part] = zs;
+  }
   __syncthreads();
   if (threadIdx.x < 64) {
     int tot = 0;
@@ -675,6 +713,11 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     if (prob_mean != nullptr) prob_mean[e] = P_s[e];
   }
   if (threadIdx.x <= E && offsets_out != nullptr) offsets_out[threadIdx.x] = off_s[threadIdx.x];
+  if (threadIdx.x == 0 && z_out != nullptr) {
+    float z = 0.0f;
+    for (int p = 0; p < kFinParts; ++p) z += part_z[p];  // fixed order
+    *z_out = (T > 0) ? z / static_cast<float>(T) : 0.0f;
+  }
   if (threadIdx.x == 0 && aux_out != nullptr) {
     float a = 0.0f;
     const float S = static_cast<float>(T) * static_cast<float>(K);
@@ -699,27 +742,28 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 }
 
 __global__ void zero_outputs_kernel(int E, int32_t* counts, int32_t* offsets, float* prob_mean,
-                                    float* aux) {
+                                    float* aux, float* z_loss) {
   const int i = threadIdx.x;
   if (counts != nullptr && i < E) counts[i] = 0;
   if (prob_mean != nullptr && i < E) prob_mean[i] = 0.0f;
   if (offsets != nullptr && i <= E) offsets[i] = 0;
   if (aux != nullptr && i == 0) *aux = 0.0f;
+  if (z_loss != nullptr && i == 0) *z_loss = 0.0f;
 }
 
 template <typename Tin, int EP, int TE, int TPT, int BK, int NS>
 hipError_t launch_route_wide(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
   hipLaunchKernelGGL((route_wide_kernel<Tin, EP, TE, TPT, BK, NS>), dim3(rt.NB), dim3(kRouteThreads), 0, st,
-                     static_cast<const Tin*>(a.h), a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
-                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.bias_select);
+                     static_cast<const Tin*>(a.h), a.Wr, a.br, a.noise, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
+                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.blk_z, a.bias_select);
   return hipGetLastError();
 }
 
 template <typename Tin, int EP, int NW>
 hipError_t launch_route_narrow(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
   hipLaunchKernelGGL((route_narrow_kernel<Tin, EP, NW>), dim3(rt.NB), dim3(NW * 64), 0, st,
-                     static_cast<const Tin*>(a.h), a.Wr, a.br, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
-                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.bias_select);
+                     static_cast<const Tin*>(a.h), a.Wr, a.br, a.noise, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
+                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.blk_z, a.bias_select);
   return hipGetLastError();
 }
 
@@ -774,17 +818,17 @@ hipError_t launch_hist(const int32_t* topk_idx, int T, int E, int K, const Route
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const int32_t* blk_hist, const float* blk_psum, int NB, int T, int E, int K,
-                           int32_t* blk_base, int32_t* counts, int32_t* offsets, float* prob_mean,
-                           float* aux, hipStream_t st) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kFinThreads), 0, st, blk_hist, blk_psum, NB, T, E,
-                     K, blk_base, counts, offsets, prob_mean, aux);
+hipError_t launch_finalize(const int32_t* blk_hist, const float* blk_psum, const float* blk_z, int NB, int T,
+                           int E, int K, int32_t* blk_base, int32_t* counts, int32_t* offsets, float* prob_mean,
+                           float* aux, float* z_loss, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kFinThreads), 0, st, blk_hist, blk_psum, blk_z, NB, T, E,
+                     K, blk_base, counts, offsets, prob_mean, aux, z_loss);
   return hipGetLastError();
 }
 
 hipError_t launch_zero_outputs(int E, int32_t* counts, int32_t* offsets, float* prob_mean, float* aux,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(zero_outputs_kernel, dim3(1), dim3(128), 0, st, E, counts, offsets, prob_mean, aux);
+                               float* z_loss, hipStream_t st) {
+  hipLaunchKernelGGL(zero_outputs_kernel, dim3(1), dim3(128), 0, st, E, counts, offsets, prob_mean, aux, z_loss);
   return hipGetLastError();
 }
 

@@ -45,9 +45,9 @@ def oracle_params(inp: Dict[str, Optional[torch.Tensor]]) -> Dict[str, object]:
 
 
 def run_oracle(cfg: W.LayerShape, inp, tokens: Optional[Sequence[int]] = None, capacity: Optional[int] = None,
-               bias_select_only: bool = False):
+               bias_select_only: bool = False, noise: Optional[np.ndarray] = None):
     return O.moe_forward(oracle_params(inp), cfg.T, cfg.d, cfg.E, cfg.K, cfg.act, cfg.gate, tokens=tokens,
-                         capacity=capacity, bias_select_only=bias_select_only)
+                         capacity=capacity, bias_select_only=bias_select_only, noise=noise)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

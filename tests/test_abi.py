@@ -85,7 +85,13 @@ def test_workspace_size_and_null_desc():
 def _forward(desc, h=FAKE, Wr=FAKE, br=None, W1=FAKE, b1=None, W3=FAKE, W2=FAKE, b2=None, y=FAKE,
              aux=None, counts=None, ws=FAKE, ws_bytes=None):
     wsb = _ws(desc) if ws_bytes is None else ws_bytes
-    return moe.lib().moe_forward(ctypes.byref(desc), h, Wr, br, W1, b1, W3, W2, b2, y, aux, counts, ws, wsb, None)
+    return moe.lib().moe_forward(ctypes.byref(desc), h, Wr, br, W1, b1, W3, W2, b2, y, aux, counts, None, None, ws,
+                                 wsb, None)
+
+
+def _forward_nz(desc, noise=None, z_loss=None):
+    return moe.lib().moe_forward(ctypes.byref(desc), FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, None, None,
+                                 noise, z_loss, FAKE, _ws(desc), None)
 
 
 def test_forward_error_paths():
@@ -100,8 +106,9 @@ def test_forward_error_paths():
     assert _forward(d, ws_bytes=_ws(d) - 1) == WS
     assert _forward(d, ws=None) == WS
     assert _forward(d, ws=FAKE + 16) == WS        # workspace must be 256-byte aligned
-    assert moe.lib().moe_forward(None, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, None, None,
-                                 FAKE, 1 << 30, None) == NULL
+    assert moe.lib().moe_forward(None, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, None, None, None,
+                                 None, FAKE, 1 << 30, None) == NULL
+    assert _forward_nz(d, noise=FAKE + 4) == UNSUP  # misaligned noise
 
 
 def test_stage_error_paths():
@@ -109,9 +116,13 @@ def test_stage_error_paths():
     d = _d()
     wsb = _ws(d)
     by = ctypes.byref
-    assert L.moe_route(by(d), None, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, wsb, None) == NULL
-    assert L.moe_route(by(d), FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, FAKE, wsb, None) == NULL
-    assert L.moe_route(by(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE, 0, None) == WS
+    assert L.moe_route(by(d), None, FAKE, None, FAKE, FAKE, FAKE, None, None, None, None, None, FAKE, wsb,
+                       None) == NULL
+    assert L.moe_route(by(d), FAKE, FAKE, None, FAKE, FAKE, None, None, None, None, None, None, FAKE, wsb,
+                       None) == NULL
+    assert L.moe_route(by(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, None, None, FAKE, 0, None) == WS
+    assert L.moe_route(by(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, FAKE + 4, None, FAKE, wsb,
+                       None) == UNSUP  # misaligned noise
     assert L.moe_permute(by(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsb, None) == NULL
     assert L.moe_permute(by(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, wsb, None) == NULL
     assert L.moe_expert_ffn(by(d), FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, wsb, None) == UNSUP
@@ -138,10 +149,11 @@ def _bws(desc):
 
 
 def _backward(desc, h=FAKE, Wr=FAKE, br=None, W1=FAKE, b1=None, W3=FAKE, W2=FAKE, b2=None, dy=FAKE, daux=0.0,
-              dh=FAKE, dWr=FAKE, dbr=None, dW1=FAKE, db1=None, dW3=FAKE, dW2=FAKE, db2=None, ws=FAKE, ws_bytes=None):
+              noise=None, dz=0.0, dh=FAKE, dWr=FAKE, dbr=None, dW1=FAKE, db1=None, dW3=FAKE, dW2=FAKE, db2=None,
+              ws=FAKE, ws_bytes=None):
     wsb = _bws(desc) if ws_bytes is None else ws_bytes
-    return moe.lib().moe_backward(ctypes.byref(desc), h, Wr, br, W1, b1, W3, W2, b2, dy, daux, dh, dWr, dbr, dW1,
-                                  db1, dW3, dW2, db2, ws, wsb, None)
+    return moe.lib().moe_backward(ctypes.byref(desc), h, Wr, br, W1, b1, W3, W2, b2, dy, daux, noise, dz, dh, dWr,
+                                  dbr, dW1, db1, dW3, dW2, db2, ws, wsb, None)
 
 
 def test_backward_error_paths():
@@ -160,6 +172,8 @@ def test_backward_error_paths():
     assert _backward(d, dW3=None) == NULL                     # SwiGLU needs dW3
     assert _backward(d, db1=FAKE) == UNSUP                    # SwiGLU layers have no biases
     assert _backward(d, daux=float("inf")) == SHAPE
+    assert _backward(d, dz=float("nan")) == SHAPE
+    assert _backward(d, noise=FAKE + 4) == UNSUP              # misaligned noise
     assert _backward(d, dh=FAKE + 8) == UNSUP                 # misaligned
     assert _backward(d, ws_bytes=_bws(d) - 1) == WS
     assert _backward(_d(dtype=0), ws_bytes=1 << 30) == UNSUP

@@ -100,6 +100,40 @@ def test_backward_matches_oracle(name):
     assert not bad, bad
 
 
+def test_backward_z_loss_and_noise():
+    """loss = sum(dy y) + daux aux + dz z_loss with noise on the router logits
+    (an input, held fixed): both router layouts, both bias modes."""
+    for cfg, bias_mode, dz in ((L("bw_znoise", 160, 128, 8, 2, 192, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16,
+                                  "normal2", 89), 0, 0.7),
+                               (L("bw_znoise_sel", 300, 64, 24, 2, 96, W.ACT_GELU, W.GATE_RAW, W.DT_BF16,
+                                  "normal2", 90), 1, 2.0)):
+        H.say("[gpu] backward z-loss/noise %s bias_mode=%d dz=%g" % (cfg, bias_mode, dz))
+        inp = W.make_inputs(cfg)
+        dev = H.to_dev(inp)
+        dy = _dy(cfg, cfg.seed + 1000)
+        noise = (np.random.default_rng(cfg.seed).standard_normal((cfg.T, cfg.E)) * 0.5).astype(np.float32)
+        desc = moe.desc_of(cfg, bias_mode=bias_mode)
+        out = moe.backward(desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"], dev["W2"],
+                           dev["b2"], dy.cuda(), 0.3, noise=torch.from_numpy(noise).cuda(), dz=dz)
+        torch.cuda.synchronize()
+        ref = O.moe_backward(H.oracle_params(inp), cfg.T, cfg.d, cfg.E, cfg.K, cfg.act, cfg.gate,
+                             W.as_float32(dy).astype(np.float64), daux=0.3, bias_select_only=bias_mode == 1,
+                             with_scales=True, noise=noise, dz_loss=dz)
+        for k in ("dh", "dW_r", "db_r", "dW1", "db1", "dW3", "dW2", "db2"):
+            got, want = out[k], ref[k]
+            if got is None or want is None:
+                continue
+            g = H.to_np(got).astype(np.float64)
+            if k == "db_r" and bias_mode == 1:
+                assert not g.any()
+                continue
+            err = float(np.linalg.norm(g - want) / max(np.linalg.norm(want), 1e-30))
+            scale = ref["scale"][k]
+            per_elem = float(np.max(np.abs(g - want) / np.maximum(scale, 1e-6 * max(float(scale.max()), 1e-30))))
+            H.say("[gpu] %s %s: |d|/|ref| = %.5f (max |d|/sum|terms| %.4f)" % (cfg.name, k, err, per_elem))
+            assert (per_elem if k == "db_r" else err) <= TOL, (k, err, per_elem)
+
+
 def test_backward_no_tokens():
     cfg = CASES["gelu_raw_bias"][0]
     cfg0 = L("bw_empty", 0, cfg.d, cfg.E, cfg.K, cfg.width, cfg.act, cfg.gate, cfg.dtype, cfg.router_bias, 88)

@@ -1,0 +1,114 @@
+"""Noisy router logits and the router z-loss (arjunjaggi.com "Mixture of
+Experts in LLMs", "Load Balancing": Shazeer's noisy top-k; "Mixtral and the
+Open MoE Era": ST-MoE's router z-loss).
+
+The caller's noise [T][E] (float32, drawn and scaled by the caller) is added to
+the logits after the bias, one float32 add; the z-loss is the mean over tokens
+of the squared log-sum-exp of the logits the softmax sees. Against the CPU
+oracle on the same seeded inputs and noise: the scores (noise included) bit for
+bit, the choice and counts exactly, gates within 1e-6, P, aux and z-loss within
+1e-5 relative, y within the layer tolerance. Both router layouts, both bias
+modes, renormalised and raw gates, float32 and bfloat16; a forcing noise; no
+tokens. The backward with noise and a z-loss weight is in test_gpu_backward.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import sparse_mixture_experts_48_amd as moe
+from sparse_mixture_experts_48_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - the CPU suite deselects these
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+L = W.LayerShape
+Z_RTOL = 1e-5
+CASES = {
+    # name: (shape, bias_mode, noise scale)
+    "narrow_e8_k2": (L("nz_narrow", 16, 512, 8, 2, 1376, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 91), 0,
+                     0.5),
+    "narrow_e16_sel": (L("nz_narrow16", 200, 256, 16, 3, 264, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 92),
+                       1, 1.0),
+    "wide_e8_k2": (L("nz_wide8", 700, 256, 8, 2, 512, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 93), 0, 0.3),
+    "wide_e64_raw_sel": (L("nz_wide64", 300, 128, 64, 2, 256, W.ACT_GELU, W.GATE_RAW, W.DT_BF16, "zipf1.1", 94),
+                         1, 2.0),
+    "wide_e40_k1": (L("nz_k1", 517, 256, 40, 1, 344, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16, "zipf1.1", 95), 0, 0.7),
+    "f32_e12_k2": (L("nz_f32", 97, 72, 12, 2, 136, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2", 96), 0, 0.5),
+    "no_noise": (L("nz_none", 333, 256, 8, 2, 680, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 97), 0, 0.0),
+}
+
+
+def _noise(cfg, scale, seed):
+    if scale == 0.0:
+        return None
+    return (np.random.default_rng(seed).standard_normal((cfg.T, cfg.E)) * scale).astype(np.float32)
+
+
+def _check(cfg, inp, dev, bias_mode, noise):
+    r = H.run_oracle(cfg, inp, bias_select_only=bias_mode == 1, noise=noise)
+    desc = moe.desc_of(cfg, bias_mode=bias_mode)
+    nz = None if noise is None else torch.from_numpy(noise).cuda()
+    g = moe.route(desc, dev["h"], dev["W_r"], dev["b_r"], want_logits=True, noise=nz)
+    torch.cuda.synchronize()
+    H.check_logits_bits(H.to_np(g["logits"]), r["logits"])
+    H.check_bits_equal("topk_idx", H.to_np(g["topk_idx"]), r["topk_idx"])
+    H.check_bits_equal("expert_counts", H.to_np(g["counts"]), r["counts"])
+    gate_err = float(np.max(np.abs(H.to_np(g["topk_gate"]) - r["topk_gate"]))) if cfg.T else 0.0
+    assert gate_err <= H.GATE_ATOL, gate_err
+    P = r["probs"].mean(axis=0) if cfg.T else np.zeros(cfg.E)
+    assert np.max(np.abs(H.to_np(g["prob_mean"]) - P)) <= H.PROB_RTOL * max(P.max(), 1e-30) + 1e-7
+    assert abs(float(H.to_np(g["aux"])[0]) - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0)
+    z = float(H.to_np(g["z_loss"])[0])
+    assert abs(z - r["z_loss"]) <= Z_RTOL * max(abs(r["z_loss"]), 1.0), (z, r["z_loss"])
+    zt = torch.empty(1, dtype=torch.float32, device="cuda")
+    y, aux, counts = moe.forward(desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"],
+                                 dev["W2"], dev["b2"], noise=nz, z_loss=zt)
+    torch.cuda.synchronize()
+    H.check_bits_equal("expert_counts (forward)", H.to_np(counts), r["counts"])
+    assert abs(float(H.to_np(aux)[0]) - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0)
+    assert float(H.to_np(zt)[0]) == z, "forward and route z-loss differ"
+    if cfg.T:
+        raw, net = H.layer_err(H.to_np(y), r["y"], cfg.dtype)
+        H.say("[gpu] %s y: max|d|/rms = %.4f (raw), %.4f (net); z_loss %.6f (oracle %.6f)" % (
+            cfg.name, raw, net, z, r["z_loss"]))
+        assert net <= H.Y_TOL[cfg.dtype], (raw, net)
+    return r
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_noise_and_z_loss(name):
+    cfg, bias_mode, scale = CASES[name]
+    H.say("[gpu] noise/z-loss %s %s bias_mode=%d scale=%g" % (name, cfg, bias_mode, scale))
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    _check(cfg, inp, dev, bias_mode, _noise(cfg, scale, cfg.seed + 7))
+
+
+def test_forcing_noise():
+    """+1e4 on one expert per token: that expert is every token's first choice,
+    with gate 1 for renormalised top-1."""
+    cfg = L("nz_force", 300, 128, 16, 1, 128, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 98)
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    want = np.random.default_rng(5).integers(0, cfg.E, cfg.T)
+    noise = np.zeros((cfg.T, cfg.E), np.float32)
+    noise[np.arange(cfg.T), want] = 1e4
+    r = _check(cfg, inp, dev, 0, noise)
+    assert np.array_equal(r["topk_idx"][:, 0], want)
+
+
+def test_no_tokens_zero_z_loss():
+    cfg = L("nz_empty", 0, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 99)
+    H.say("[gpu] noise/z-loss T=0")
+    dev = H.to_dev(W.make_inputs(cfg))
+    desc = moe.desc_of(cfg)
+    zt = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    nz = torch.empty((0, cfg.E), dtype=torch.float32, device="cuda")
+    moe.forward(desc, dev["h"], dev["W_r"], None, dev["W1"], None, dev["W3"], dev["W2"], None, noise=nz,
+                z_loss=zt)
+    g = moe.route(desc, dev["h"], dev["W_r"], None, noise=nz)
+    torch.cuda.synchronize()
+    assert float(zt.cpu()[0]) == 0.0 and float(g["z_loss"].cpu()[0]) == 0.0
