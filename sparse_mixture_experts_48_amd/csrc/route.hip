@@ -57,12 +57,31 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 }
 
 // 8 consecutive h values of one token as raw bits (bf16: one 16-byte load).
+// Raw buffer over `bytes` bytes at `base`: loads at byte offsets >= bytes
+// return zeros. The router's loads go through these, with no branch around
+// them, so that the compiler's wait counts keep several stages of loads in
+// flight (a load behind a branch makes it wait for every load before a use).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t route_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load16f(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const uint4 v = load16(r, byte_off);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
 template <typename Tin> struct HVec;
 template <> struct HVec<float> {
   typedef float4 raw[2];
-  __device__ __forceinline__ static void load(const float* p, raw& r) {
-    r[0] = *reinterpret_cast<const float4*>(p);
-    r[1] = *reinterpret_cast<const float4*>(p + 4);
+  // 8 values at element offset `off` of the buffer (zeros past its end)
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t off, raw& x) {
+    x[0] = load16f(r, 4 * off);
+    x[1] = load16f(r, 4 * off + 16);
   }
   __device__ __forceinline__ static void zero(raw& r) { r[0] = r[1] = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ static void to_f32(const raw& r, float* out) {
@@ -72,7 +91,9 @@ template <> struct HVec<float> {
 };
 template <> struct HVec<bf16_t> {
   typedef uint4 raw[1];
-  __device__ __forceinline__ static void load(const bf16_t* p, raw& r) { r[0] = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t off, raw& x) {
+    x[0] = load16(r, 2 * off);
+  }
   __device__ __forceinline__ static void zero(raw& r) { r[0] = make_uint4(0u, 0u, 0u, 0u); }
   __device__ __forceinline__ static void to_f32(const raw& r, float* out) {
     const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
@@ -125,27 +146,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   typename HVec<Tin>::raw hreg[NS][HV];
   float4 wreg[NS][WV];
 
-  // Issue the global loads of stage c into register slot `slot`.
+  // The block's token rows (rows past T read zeros) and all of W_r as buffers.
+  const int rows = max(0, min(TB, T - t0));
+  const __amdgpu_buffer_rsrc_t hbuf =
+      route_rsrc(h + static_cast<size_t>(min(t0, max(T - 1, 0))) * d, static_cast<uint32_t>(rows) * d * sizeof(Tin));
+  const __amdgpu_buffer_rsrc_t wbuf = route_rsrc(Wr, static_cast<uint32_t>(d) * E * 4);
+  // Issue the global loads of stage c into register slot `slot`. Stages past
+  // the end are allowed (zeros or values that are never stored). In the last
+  // stage, h values at k >= d of a row come from the next row: never read
+  // (the chains stop at d) — rows past the block's last one read zeros.
   auto load_stage = [&](int c, int slot) {
     const int k0 = c * BK;
-    const int kn = min(BK, d - k0);
 #pragma unroll
     for (int v = 0; v < HV; ++v) {
       const int i = tid + v * kRouteThreads;
       const int r = i / (BK / 8);
       const int cc = (i % (BK / 8)) * 8;
-      const int t = t0 + r;
-      const bool mine = HN % kRouteThreads == 0 || i < HN;
-      if (mine && t < T && cc < kn) HVec<Tin>::load(h + static_cast<size_t>(t) * d + k0 + cc, hreg[slot][v]);
-      else HVec<Tin>::zero(hreg[slot][v]);
+      HVec<Tin>::load(hbuf, static_cast<uint32_t>(r) * d + k0 + cc, hreg[slot][v]);
     }
-    // rows k0 .. k0+kn of W_r are one contiguous run of kn*E floats
-    const float4* wsrc = reinterpret_cast<const float4*>(Wr + static_cast<size_t>(k0) * E);
-    const int n4 = kn * E / 4;
+    // rows k0 .. of W_r are one contiguous run of floats; values past the
+    // stage's run are never stored, values past W_r are zeros
 #pragma unroll
     for (int v = 0; v < WV; ++v) {
       const int i = tid + v * kRouteThreads;
-      wreg[slot][v] = (i < n4) ? wsrc[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      wreg[slot][v] = load16f(wbuf, (static_cast<uint32_t>(k0) * E + 4 * i) * 4);
     }
   };
   // Move register slot `slot` (stage c) into LDS buffer `buf`.
@@ -231,21 +255,29 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     }
   };
 
-  // Pipeline: stage c is loaded into registers NS-1 steps before it is
-  // stored to LDS buffer c&1 and consumed; one barrier per stage.
+  // Pipeline: stage c is loaded into register slot c % NS, NS-1 stages before
+  // it is stored to LDS buffer c % 2 and consumed; one barrier per stage. The
+  // main loop issues its loads with no condition (past the end they are
+  // unused); the tail, fewer than NS stages, has all of its stages loaded.
+  static_assert(NS % 2 == 0, "slot parity selects the LDS buffer");
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nc) load_stage(s, s);
-  for (int c0 = 0; c0 < nc; c0 += NS) {
+  for (int s = 0; s < NS - 1; ++s) load_stage(s, s);
+  int c0 = 0;
+  for (; c0 + NS <= nc; c0 += NS) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int c = c0 + s;
-      if (c < nc) {
-        store_stage(c, s, c & 1);
-        __syncthreads();
-        if (c + NS - 1 < nc) load_stage(c + NS - 1, (s + NS - 1) % NS);
-        compute_stage(c, c & 1);
-      }
+      store_stage(c0 + s, s, s & 1);
+      __syncthreads();
+      load_stage(c0 + s + NS - 1, (s + NS - 1) % NS);
+      compute_stage(c0 + s, s & 1);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+    if (c0 + s < nc) {
+      store_stage(c0 + s, s, s & 1);
+      __syncthreads();
+      compute_stage(c0 + s, s & 1);
     }
   }
 
@@ -385,9 +417,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   }
 }
 
-// Narrow layout: kNarrowNW waves per block, one token per wave; chunks of kNarrowKC k.
+// Narrow layout: kNarrowNW waves per block, one token per wave; chunks of kNarrowKC k,
+// the global loads of kNarrowPD chunks in flight. (A deeper ring measured no
+// faster: a chunk's fmaf chains, not its loads, set the pace.)
 constexpr int kNarrowKC = 512;
 constexpr int kNarrowNW = 4;
+constexpr int kNarrowPD = 2;
 
 template <typename Tin, int EP, int NW>
 __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
@@ -420,38 +455,41 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
   const int t = blockIdx.x * NW + wave;
   const bool tok_ok = t < T;                                 // wave-uniform
   const Tin* hrow = h + static_cast<size_t>(min(t, T - 1)) * d;  // rows past T are dropped
+  const __amdgpu_buffer_rsrc_t hbuf = route_rsrc(hrow, static_cast<uint32_t>(d) * sizeof(Tin));
+  const __amdgpu_buffer_rsrc_t wbuf = route_rsrc(Wr, static_cast<uint32_t>(d) * E * 4);
   const int nc = (d + KC - 1) / KC;
 
-  typename HVec<Tin>::raw hreg;
-  float4 wreg[WI];
-  // Registers <- chunk c: this lane's 8 h values, and the block's share of W_r.
-  auto load_chunk = [&](int c) {
+  constexpr int PD = kNarrowPD;  // register ring of chunks in flight; even, so chunk c uses LDS buffer c % 2
+  static_assert(PD % 2 == 0, "ring slot parity selects the LDS buffer");
+  typename HVec<Tin>::raw hreg[PD];
+  float4 wreg[PD][WI];
+  // Register slot `slot` <- chunk c: this lane's 8 h values (zeros past d),
+  // and the block's share of W_r (rows k0.. are one run of floats; values past
+  // the chunk's run are never stored, values past W_r are zeros). Chunks past
+  // the end are allowed.
+  auto load_chunk = [&](int c, int slot) {
     const int k0 = c * KC;
-    const int kh = k0 + 8 * lane;
-    if (kh < d) HVec<Tin>::load(hrow + kh, hreg);  // d is a multiple of 8
-    else HVec<Tin>::zero(hreg);
-    const int n4 = min(KC, d - k0) * E / 4;        // W_r rows k0.. are one run of floats
-    const float4* src = reinterpret_cast<const float4*>(Wr + static_cast<size_t>(k0) * E);
+    HVec<Tin>::load(hbuf, k0 + 8 * lane, hreg[slot]);
 #pragma unroll
     for (int v = 0; v < WI; ++v) {
       const int i = tid + v * NT;
-      wreg[v] = (i < n4) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      wreg[slot][v] = load16f(wbuf, (static_cast<uint32_t>(k0) * E + 4 * i) * 4);
     }
   };
   // LDS <- registers: h as float32 in this wave's row; W_r transposed into the
   // block's buffer (element f of the chunk run is row f / E, expert f % E; the
   // quotient is (f * ceil(2^32 / E)) >> 32 in 64 bits, exact for f < 2^16).
   const uint64_t e_recip = (0x100000000ull + E - 1) / E;
-  auto store_chunk = [&](float (*hs)[HP], float* ws) {
+  auto store_chunk = [&](int slot, float (*hs)[HP], float* ws) {
     float x[8];
-    HVec<Tin>::to_f32(hreg, x);
+    HVec<Tin>::to_f32(hreg[slot], x);
     *reinterpret_cast<float4*>(&hs[wave][8 * lane]) = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4*>(&hs[wave][8 * lane + 4]) = make_float4(x[4], x[5], x[6], x[7]);
 #pragma unroll
     for (int v = 0; v < WI; ++v) {
       const int i = tid + v * NT;
       if (i < WF4) {
-        const float q[4] = {wreg[v].x, wreg[v].y, wreg[v].z, wreg[v].w};
+        const float q[4] = {wreg[slot][v].x, wreg[slot][v].y, wreg[slot][v].z, wreg[slot][v].w};
         int k = static_cast<int>((static_cast<uint64_t>(4 * i) * e_recip) >> 32);
         int e = 4 * i - k * E;
 #pragma unroll
@@ -512,22 +550,34 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
     }
   };
 
-  load_chunk(0);
-  int c = 0;
-  for (; c + 2 <= nc; c += 2) {
-    store_chunk(hA, wA);
-    __syncthreads();  // chunk c in LDS; buffers B no longer read (chunk c-1 done)
-    load_chunk(c + 1);
-    compute(c, hA, wA);
-    store_chunk(hB, wB);
-    __syncthreads();
-    if (c + 2 < nc) load_chunk(c + 2);
-    compute(c + 1, hB, wB);
+  // Chunk c sits in register slot c % PD and LDS buffer c % 2 (A even, B odd).
+  // Storing chunk c into a buffer is safe: every wave passed the barrier of
+  // chunk c - 1 only after computing chunk c - 2 from that buffer.
+  // The main loop issues its loads with no condition (past the end they are
+  // unused); the tail, fewer than PD chunks, has all of its chunks loaded.
+#pragma unroll
+  for (int s = 0; s < PD; ++s) load_chunk(s, s);
+  int c0 = 0;
+  for (; c0 + PD <= nc; c0 += PD) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      if (s % 2 == 0) store_chunk(s, hA, wA);
+      else store_chunk(s, hB, wB);
+      __syncthreads();
+      load_chunk(c0 + s + PD, s);
+      if (s % 2 == 0) compute(c0 + s, hA, wA);
+      else compute(c0 + s, hB, wB);
+    }
   }
-  if (c < nc) {
-    store_chunk(hA, wA);
-    __syncthreads();
-    compute(c, hA, wA);
+#pragma unroll
+  for (int s = 0; s < PD - 1; ++s) {
+    if (c0 + s < nc) {
+      if (s % 2 == 0) store_chunk(s, hA, wA);
+      else store_chunk(s, hB, wB);
+      __syncthreads();
+      if (s % 2 == 0) compute(c0 + s, hA, wA);
+      else compute(c0 + s, hB, wB);
+    }
   }
 
   // logit = (c0 + c1) + (c2 + c3) on the lanes of chain 0 (lane = expert);
@@ -778,10 +828,10 @@ hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStre
     return rt.EP == 8 ? launch_route_narrow_nw<Tin, 8>(a, rt, st) : launch_route_narrow_nw<Tin, 16>(a, rt, st);
   }
   switch (rt.EP) {  // wide layout: wide_tb<EP>() tokens x EP experts per block of 256 threads
-    case 8: return launch_route_wide<Tin, 8, WideCfg<8>::TE, WideCfg<8>::TPT, WideCfg<8>::BK, 4>(a, rt, st);
-    case 16: return launch_route_wide<Tin, 16, WideCfg<16>::TE, WideCfg<16>::TPT, WideCfg<16>::BK, 4>(a, rt, st);
-    case 32: return launch_route_wide<Tin, 32, WideCfg<32>::TE, WideCfg<32>::TPT, WideCfg<32>::BK, 4>(a, rt, st);
-    default: return launch_route_wide<Tin, 64, WideCfg<64>::TE, WideCfg<64>::TPT, WideCfg<64>::BK, 4>(a, rt, st);
+    case 8: return launch_route_wide<Tin, 8, WideCfg<8>::TE, WideCfg<8>::TPT, WideCfg<8>::BK, 2>(a, rt, st);
+    case 16: return launch_route_wide<Tin, 16, WideCfg<16>::TE, WideCfg<16>::TPT, WideCfg<16>::BK, 2>(a, rt, st);
+    case 32: return launch_route_wide<Tin, 32, WideCfg<32>::TE, WideCfg<32>::TPT, WideCfg<32>::BK, 2>(a, rt, st);
+    default: return launch_route_wide<Tin, 64, WideCfg<64>::TE, WideCfg<64>::TPT, WideCfg<64>::BK, 2>(a, rt, st);
   }
 }
 
