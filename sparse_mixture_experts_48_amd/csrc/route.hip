@@ -708,13 +708,17 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const int per = (NB + kFinParts - 1) / kFinParts;
   const int b0 = min(NB, part * per);
   const int b1 = min(NB, b0 + per);
-  // Loads in batches of 8 (independent, in flight together), sums in block order.
-  constexpr int kU = 8;
+  // Loads in batches of kU (independent, in flight together), sums in block
+  // order. A part of at most kU blocks (NB <= 512) is one batch, and its
+  // counts stay in registers for the bases below.
+  constexpr int kU = 32;
   int c = 0;
   float ps = 0.0f;
+  int hv[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) hv[u] = 0;
   if (e < E) {
     for (int b = b0; b < b1; b += kU) {
-      int hv[kU];
       float pv[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -733,8 +737,16 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   part_p[part][e] = ps;
   if (e == 0) {  // z-loss partials of this part's blocks, in block order
     float zs = 0.0f;
-    if (blk_z != nullptr)
-      for (int b = b0; b < b1; ++b) zs += blk_z[b];
+    if (blk_z != nullptr) {
+      for (int b = b0; b < b1; b += kU) {
+        float zv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) zv[u] = (b + u < b1) ? blk_z[b + u] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (b + u < b1) zs += zv[u];
+      }
+    }
     part_z[part] = zs;
   }
   __syncthreads();
@@ -778,14 +790,21 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     // base[b][e] = offsets[e] + slots of e in blocks before b
     int pre = off_s[e];
     for (int p = 0; p < part; ++p) pre += part_cnt[p][e];
-    for (int b = b0; b < b1; b += kU) {
-      int hv[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) hv[u] = (b + u < b1) ? blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
+    if (b1 - b0 <= kU) {  // the part's counts are still in hv
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        if (b + u < b1) blk_base[static_cast<size_t>(b + u) * E + e] = pre;
+        if (b0 + u < b1) blk_base[static_cast<size_t>(b0 + u) * E + e] = pre;
         pre += hv[u];
+      }
+    } else {
+      for (int b = b0; b < b1; b += kU) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) hv[u] = (b + u < b1) ? blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (b + u < b1) blk_base[static_cast<size_t>(b + u) * E + e] = pre;
+          pre += hv[u];
+        }
       }
     }
   }
