@@ -453,14 +453,29 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
   ra.noise = noise;
   ra.blk_z = z_loss != nullptr ? at<float>(ws, pl.blk_z) : nullptr;
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
-  MOE_LAUNCH(MOE_K_FINALIZE, st,
-             moe::launch_finalize(blk_hist, blk_psum, ra.blk_z, pl.rt.NB, T, E, K, blk_base, counts, offsets,
-                                  nullptr, aux_loss, z_loss, st));
   const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
   const int cap = cap_of(d);
-  MOE_LAUNCH(MOE_K_PERMUTE, st,
-             moe::launch_permute(topk_idx, blk_base, offsets, T, E, K, cap, pl.rt, h, row_bytes, nullptr,
-                                 slot_token, token_slot, st));
+  if (moe::permute_one_block(pl.rt)) {  // up to 256 tokens: statistics and grouping in one launch
+    moe::FinArgs fin;
+    fin.blk_hist = blk_hist;
+    fin.blk_psum = blk_psum;
+    fin.blk_z = ra.blk_z;
+    fin.NB = pl.rt.NB;
+    fin.counts = counts;
+    fin.offsets = offsets;
+    fin.aux = aux_loss;
+    fin.z_loss = z_loss;
+    MOE_LAUNCH(MOE_K_PERMUTE, st,
+               moe::launch_finalize_permute(fin, topk_idx, T, E, K, cap, pl.rt, h, row_bytes, nullptr, slot_token,
+                                            token_slot, st));
+  } else {
+    MOE_LAUNCH(MOE_K_FINALIZE, st,
+               moe::launch_finalize(blk_hist, blk_psum, ra.blk_z, pl.rt.NB, T, E, K, blk_base, counts, offsets,
+                                    nullptr, aux_loss, z_loss, st));
+    MOE_LAUNCH(MOE_K_PERMUTE, st,
+               moe::launch_permute(topk_idx, blk_base, offsets, T, E, K, cap, pl.rt, h, row_bytes, nullptr,
+                                   slot_token, token_slot, st));
+  }
   // GEMM1 reads the rows of h through slot_token: the grouped copy of h is never written.
   moe::FfnArgs f{};
   f.S = T * K;

@@ -43,12 +43,33 @@ hipError_t launch_finalize(const int32_t* blk_hist, const float* blk_psum, const
 hipError_t launch_zero_outputs(int E, int32_t* counts, int32_t* offsets, float* prob_mean, float* aux,
                                float* z_loss, hipStream_t st);
 
+// The router's per-block partials and what the finalize kernel forms from them
+// (outputs nullable), for the fused statistics-and-grouping launch below.
+struct FinArgs {
+  const int32_t* blk_hist = nullptr;
+  const float* blk_psum = nullptr;
+  const float* blk_z = nullptr;
+  int NB = 0;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  float* prob_mean = nullptr;
+  float* aux = nullptr;
+  float* z_loss = nullptr;
+};
+
 // Stable grouping: slot ranks, token_slot, slot_token and the gathered rows.
 // With cap < INT_MAX, a slot whose rank in its expert's group is cap or more is
 // dropped: its token_slot entry is -1.
 hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, const int32_t* offsets, int T,
                           int E, int K, int cap, const RouteTiling& rt, const void* h, size_t row_bytes,
                           void* h_perm, int32_t* slot_token, int32_t* token_slot, hipStream_t st);
+// True when the grouping of a router tiling is a single block (at most 256 tokens).
+bool permute_one_block(const RouteTiling& rt);
+// That single block forms the statistics first (bit for bit as launch_finalize,
+// without the per-block bases) and then groups: one launch instead of two.
+hipError_t launch_finalize_permute(const FinArgs& fin, const int32_t* topk_idx, int T, int E, int K, int cap,
+                                   const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
+                                   int32_t* slot_token, int32_t* token_slot, hipStream_t st);
 
 // Expert GEMMs over the grouped rows.
 struct FfnArgs {

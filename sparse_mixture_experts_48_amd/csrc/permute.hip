@@ -17,6 +17,7 @@
 // its slot adds the counts of earlier waves.
 #include "common.h"
 #include "kernels.h"
+#include "stats.h"
 
 namespace moe {
 
@@ -25,25 +26,37 @@ namespace {
 constexpr int kPermThreads = 256;  // 4 waves x 64 tokens
 constexpr int kMaxK = 8;
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+// FUSED: the only grouping block (the batch fits one block) first forms the
+// router statistics itself, as the finalize kernel would, with kFinThreads
+// threads; its base rows are then the offsets. Threads past kPermThreads
+// take part in the statistics and in every barrier, and group nothing.
+template <bool FUSED>
+__global__ __launch_bounds__(FUSED ? kFinThreads : kPermThreads) void permute_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_base,
     const int32_t* __restrict__ offsets, int T, int E, int K, int cap,
     int TB, int M, const char* __restrict__ h, size_t row_bytes, char* __restrict__ h_perm,
-    int32_t* __restrict__ slot_token, int32_t* __restrict__ token_slot) {
+    int32_t* __restrict__ slot_token, int32_t* __restrict__ token_slot, FinArgs fin) {
   __shared__ int cnt_s[kPermThreads / 64][64];
   __shared__ int slots_s[kPermThreads][kMaxK];
   __shared__ int base_s[64];
-  __shared__ int off_s[64];
-  if (threadIdx.x < E) {  // one coalesced read instead of one read per expert below
-    base_s[threadIdx.x] = blk_base[static_cast<size_t>(blockIdx.x) * M * E + threadIdx.x];
-    off_s[threadIdx.x] = offsets[threadIdx.x];
+  __shared__ int off_s[65];
+  if constexpr (FUSED) {
+    finalize_block(fin.blk_hist, fin.blk_psum, fin.blk_z, fin.NB, T, E, K, nullptr, fin.counts, fin.offsets,
+                   fin.prob_mean, fin.aux, fin.z_loss, off_s);
+    if (threadIdx.x < E) base_s[threadIdx.x] = off_s[threadIdx.x];
+  } else {
+    if (threadIdx.x < E) {  // one coalesced read instead of one read per expert below
+      base_s[threadIdx.x] = blk_base[static_cast<size_t>(blockIdx.x) * M * E + threadIdx.x];
+      off_s[threadIdx.x] = offsets[threadIdx.x];
+    }
   }
   const int wave = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
+  const bool grp = threadIdx.x < kPermThreads;  // wave-uniform
   const int t0 = blockIdx.x * TB;
   const int lt = threadIdx.x;
   const int t = t0 + lt;
-  const bool ok = lt < TB && t < T;
+  const bool ok = grp && lt < TB && t < T;
   int ids[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) ids[j] = (ok && j < K) ? topk_idx[static_cast<size_t>(t) * K + j] : -1;
@@ -53,7 +66,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   // layer): the lanes holding it get their rank among the wave's tokens that
   // chose it (popcount of those below), and the wave's count is recorded.
   // Slot ids outside [0, E) are skipped.
-  cnt_s[wave][lane] = 0;
+  if (grp) cnt_s[wave][lane] = 0;
   uint32_t rem = 0;  // bit j: slot j of this lane still to rank
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
@@ -109,7 +122,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   constexpr int kU = 8;
   const int ntok = min(TB, T - t0);
   const int nvec = static_cast<int>(row_bytes / 16);
-  for (int r = wave; r < ntok; r += kPermThreads / 64) {
+  for (int r = wave; grp && r < ntok; r += kPermThreads / 64) {
     const uint4* src = reinterpret_cast<const uint4*>(h + static_cast<size_t>(t0 + r) * row_bytes);
     int sl[kMaxK];
 #pragma unroll
@@ -144,9 +157,24 @@ hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, cons
   if (rt.TB < 1 || rt.TB > kPermThreads) return hipErrorInvalidValue;
   const int M = kPermThreads / rt.TB;  // router blocks per permute block
   const int nb = (rt.NB + M - 1) / M;
-  hipLaunchKernelGGL(permute_kernel, dim3(nb), dim3(kPermThreads), 0, st, topk_idx, blk_base, offsets, T,
+  hipLaunchKernelGGL(permute_kernel<false>, dim3(nb), dim3(kPermThreads), 0, st, topk_idx, blk_base, offsets, T,
                      E, K, cap, M * rt.TB, M, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
-                     slot_token, token_slot);
+                     slot_token, token_slot, FinArgs{});
+  return hipGetLastError();
+}
+
+bool permute_one_block(const RouteTiling& rt) {
+  return rt.TB >= 1 && rt.TB <= kPermThreads && rt.NB <= kPermThreads / rt.TB;
+}
+
+hipError_t launch_finalize_permute(const FinArgs& fin, const int32_t* topk_idx, int T, int E, int K, int cap,
+                                   const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
+                                   int32_t* slot_token, int32_t* token_slot, hipStream_t st) {
+  if (!permute_one_block(rt) || fin.NB != rt.NB || fin.blk_hist == nullptr) return hipErrorInvalidValue;
+  const int M = kPermThreads / rt.TB;
+  hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(kFinThreads), 0, st, topk_idx, nullptr, nullptr, T, E,
+                     K, cap, M * rt.TB, M, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
+                     slot_token, token_slot, fin);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@
 //    batches. Two butterflies over the chain index form the sums.
 #include "common.h"
 #include "kernels.h"
+#include "stats.h"
 
 namespace moe {
 
@@ -687,127 +688,14 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ t
   if (threadIdx.x < E) blk_hist[static_cast<size_t>(blockIdx.x) * E + threadIdx.x] = hist_s[threadIdx.x];
 }
 
-// One block: expert counts, offsets, per-block bases for the stable grouping,
-// P_e, and the aux loss. Fixed summation orders only.
-constexpr int kFinThreads = 1024;
-constexpr int kFinParts = kFinThreads / 64;
-
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t* __restrict__ blk_hist, const float* __restrict__ blk_psum, const float* __restrict__ blk_z,
     int NB, int T, int E, int K, int32_t* __restrict__ blk_base, int32_t* __restrict__ counts_out,
     int32_t* __restrict__ offsets_out, float* __restrict__ prob_mean, float* __restrict__ aux_out,
     float* __restrict__ z_out) {
-  __shared__ int part_cnt[kFinParts][64];
-  __shared__ float part_p[kFinParts][64];
-  __shared__ float part_z[kFinParts];
-  __shared__ int tot_s[64];
   __shared__ int off_s[65];
-  __shared__ float P_s[64];
-  const int e = threadIdx.x % 64;
-  const int part = threadIdx.x / 64;
-  const int per = (NB + kFinParts - 1) / kFinParts;
-  const int b0 = min(NB, part * per);
-  const int b1 = min(NB, b0 + per);
-  // Loads in batches of kU (independent, in flight together), sums in block
-  // order. A part of at most kU blocks (NB <= 512) is one batch, and its
-  // counts stay in registers for the bases below.
-  constexpr int kU = 32;
-  int c = 0;
-  float ps = 0.0f;
-  int hv[kU];
-#pragma unroll
-  for (int u = 0; u < kU; ++u) hv[u] = 0;
-  if (e < E) {
-    for (int b = b0; b < b1; b += kU) {
-      float pv[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const bool in = b + u < b1;
-        hv[u] = in ? blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
-        pv[u] = (in && blk_psum != nullptr) ? blk_psum[static_cast<size_t>(b + u) * E + e] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        c += hv[u];
-        if (b + u < b1) ps += pv[u];
-      }
-    }
-  }
-  part_cnt[part][e] = c;
-  part_p[part][e] = ps;
-  if (e == 0) {  // z-loss partials of this part's blocks, in block order
-    float zs = 0.0f;
-    if (blk_z != nullptr) {
-      for (int b = b0; b < b1; b += kU) {
-        float zv[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) zv[u] = (b + u < b1) ? blk_z[b + u] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-          if (b + u < b1) zs += zv[u];
-      }
-    }
-    part_z[part] = zs;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    int tot = 0;
-    float ptot = 0.0f;
-    for (int p = 0; p < kFinParts; ++p) {  // fixed order
-      tot += part_cnt[p][e];
-      ptot += part_p[p][e];
-    }
-    tot_s[e] = tot;
-    P_s[e] = (T > 0) ? ptot / static_cast<float>(T) : 0.0f;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int x = 0; x < E; ++x) {
-      off_s[x] = run;
-      run += tot_s[x];
-    }
-    off_s[E] = run;
-  }
-  __syncthreads();
-  if (threadIdx.x < E) {
-    if (counts_out != nullptr) counts_out[e] = tot_s[e];
-    if (prob_mean != nullptr) prob_mean[e] = P_s[e];
-  }
-  if (threadIdx.x <= E && offsets_out != nullptr) offsets_out[threadIdx.x] = off_s[threadIdx.x];
-  if (threadIdx.x == 0 && z_out != nullptr) {
-    float z = 0.0f;
-    for (int p = 0; p < kFinParts; ++p) z += part_z[p];  // fixed order
-    *z_out = (T > 0) ? z / static_cast<float>(T) : 0.0f;
-  }
-  if (threadIdx.x == 0 && aux_out != nullptr) {
-    float a = 0.0f;
-    const float S = static_cast<float>(T) * static_cast<float>(K);
-    for (int x = 0; x < E; ++x) a += (static_cast<float>(tot_s[x]) / S) * P_s[x];
-    *aux_out = (T > 0) ? static_cast<float>(E) * a : 0.0f;
-  }
-  if (blk_base != nullptr && e < E) {
-    // base[b][e] = offsets[e] + slots of e in blocks before b
-    int pre = off_s[e];
-    for (int p = 0; p < part; ++p) pre += part_cnt[p][e];
-    if (b1 - b0 <= kU) {  // the part's counts are still in hv
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        if (b0 + u < b1) blk_base[static_cast<size_t>(b0 + u) * E + e] = pre;
-        pre += hv[u];
-      }
-    } else {
-      for (int b = b0; b < b1; b += kU) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u) hv[u] = (b + u < b1) ? blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          if (b + u < b1) blk_base[static_cast<size_t>(b + u) * E + e] = pre;
-          pre += hv[u];
-        }
-      }
-    }
-  }
+  finalize_block(blk_hist, blk_psum, blk_z, NB, T, E, K, blk_base, counts_out, offsets_out, prob_mean, aux_out,
+                 z_out, off_s);
 }
 
 __global__ void zero_outputs_kernel(int E, int32_t* counts, int32_t* offsets, float* prob_mean,

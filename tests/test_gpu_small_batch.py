@@ -35,6 +35,9 @@ CASES = {
     "t16_e8_noise": (L("sb_noise", 16, 256, 8, 2, 256, SW, RN, BF, "none", 68), 0, 0, 0.5),
     "t17_e8_k2_boundary": (L("sb_t17", 17, 256, 8, 2, 256, SW, RN, BF, "normal2", 69), 3, 0, 0.3),
     "t13_e12_f32_d72": (L("sb_f32_d72", 13, 72, 12, 2, 136, GE, RN, F32, "normal2", 70), 0, 0, 0.0),
+    # d / 512 odd: the router's chunk loop ends in its one-chunk tail
+    "t10_e8_d1536": (L("sb_d1536", 10, 1536, 8, 2, 128, SW, RN, BF, "normal2", 71), 0, 0, 0.0),
+    "t200_e16_d2560_f32": (L("sb_d2560_f32", 200, 2560, 16, 2, 64, GE, RAW, F32, "normal2", 72), 0, 0, 0.0),
 }
 
 
