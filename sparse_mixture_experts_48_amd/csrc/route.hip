@@ -173,6 +173,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
       wreg[slot][v] = load16f(wbuf, (static_cast<uint32_t>(k0) * E + 4 * i) * 4);
     }
   };
+  // Padded experts read zeros; no stage writes their columns, so both buffers
+  // are cleared once (the first stage's barrier orders this before any read).
+  if (E < EP) {
+    const int pad = EP - E;
+    for (int i = tid; i < 2 * BK * pad; i += kRouteThreads) {
+      const int b = i / (BK * pad);
+      const int r = i - b * (BK * pad);
+      w_s[b][r / pad][E + r % pad] = 0.0f;
+    }
+  }
+  // Row of element f of a stage's W_r run: f / E as (f * ceil(2^32 / E)) >> 32,
+  // exact for f < 2^16 (a stage holds at most BK * E <= 8192 floats).
+  const uint64_t e_recip = (0x100000000ull + E - 1) / E;
   // Move register slot `slot` (stage c) into LDS buffer `buf`.
   auto store_stage = [&](int c, int slot, int buf) {
     const int kn = min(BK, d - c * BK);
@@ -184,24 +197,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
       if (HN % kRouteThreads != 0 && i >= HN) continue;
       float x[8];
       HVec<Tin>::to_f32(hreg[slot][v], x);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) h_s[buf][r][cc + u] = x[u];
+      *reinterpret_cast<float4*>(&h_s[buf][r][cc]) = make_float4(x[0], x[1], x[2], x[3]);  // HP % 4 == 0
+      *reinterpret_cast<float4*>(&h_s[buf][r][cc + 4]) = make_float4(x[4], x[5], x[6], x[7]);
     }
     const int n4 = kn * E / 4;
 #pragma unroll
     for (int v = 0; v < WV; ++v) {
       const int i = tid + v * kRouteThreads;
       if (i < n4) {
-        const float x[4] = {wreg[slot][v].x, wreg[slot][v].y, wreg[slot][v].z, wreg[slot][v].w};
+        int k = static_cast<int>((static_cast<uint64_t>(4 * i) * e_recip) >> 32);
+        int e = 4 * i - k * E;
+        if (E % 4 == 0) {  // the four floats sit in one row: one 16-byte store (WP % 4 == 0)
+          *reinterpret_cast<float4*>(&w_s[buf][k][e]) = wreg[slot][v];
+        } else {
+          const float x[4] = {wreg[slot][v].x, wreg[slot][v].y, wreg[slot][v].z, wreg[slot][v].w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int f = 4 * i + u;
-          w_s[buf][f / E][f % E] = x[u];
+          for (int u = 0; u < 4; ++u) {
+            w_s[buf][k][e] = x[u];
+            if (++e == E) { e = 0; ++k; }
+          }
         }
       }
-    }
-    if (E < EP) {  // padded experts read zeros
-      for (int i = tid; i < BK * (EP - E); i += kRouteThreads) w_s[buf][i / (EP - E)][E + i % (EP - E)] = 0.0f;
     }
   };
 
