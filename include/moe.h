@@ -245,7 +245,8 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
  * (moe_kernel_id) and duration in milliseconds, sets *n, and rewinds the
  * buffer; moe_trace_disable frees the events. Not thread-safe. */
 typedef enum moe_kernel_id {
-  MOE_K_ROUTE = 0, MOE_K_FINALIZE = 1, MOE_K_HIST = 2, MOE_K_PERMUTE = 3,
+  MOE_K_ROUTE = 0, MOE_K_FINALIZE = 1, MOE_K_HIST = 2,
+  MOE_K_PERMUTE = 3,  /* grouping; in moe_forward for T <= 256 also the finalize statistics (one launch) */
   MOE_K_GEMM1 = 4, MOE_K_GEMM2 = 5, MOE_K_COMBINE = 6, MOE_K_ZERO = 7,
   MOE_K_BWD = 8,   /* backward pass: elementwise, transpose and reduction kernels */
   MOE_K_WGRAD = 9  /* backward pass: weight-gradient GEMMs */
