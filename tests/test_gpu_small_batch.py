@@ -1,6 +1,8 @@
-"""Decode-sized batches (T = 1 ... 17 tokens, E <= 16 experts: the router's
-one-token-per-wave layout), with capacity drops, both bias modes, noise,
-float32 and bfloat16. Against the CPU oracle on the same seeded inputs: scores
+"""Small batches: T = 1 ... 17 tokens with E <= 16 (the router's
+one-token-per-wave layout), and up to 257 tokens around the size where
+moe_forward forms the routing statistics inside its single grouping block
+(both router layouts), with capacity drops, both bias modes, noise, float32
+and bfloat16. Against the CPU oracle on the same seeded inputs: scores
 bit for bit, choice and counts exactly, gates 1e-6, P, aux and z-loss 1e-5
 relative, y within the layer tolerance (so every grouped row went to the right
 expert and every dropped slot was dropped); moe_route and moe_forward give the
@@ -38,6 +40,11 @@ CASES = {
     # d / 512 odd: the router's chunk loop ends in its one-chunk tail
     "t10_e8_d1536": (L("sb_d1536", 10, 1536, 8, 2, 128, SW, RN, BF, "normal2", 71), 0, 0, 0.0),
     "t200_e16_d2560_f32": (L("sb_d2560_f32", 200, 2560, 16, 2, 64, GE, RAW, F32, "normal2", 72), 0, 0, 0.0),
+    # where moe_forward forms the statistics inside the single grouping block, and where it stops
+    "t256_e8_one_group_block": (L("sb_t256", 256, 256, 8, 2, 128, SW, RN, BF, "normal2", 73), 40, 0, 0.0),
+    "t257_e8_two_launches": (L("sb_t257", 257, 256, 8, 2, 128, SW, RN, BF, "normal2", 74), 0, 0, 0.2),
+    "t200_e40_wide_one_block": (L("sb_t200_e40", 200, 128, 40, 2, 64, GE, RAW, BF, "zipf1.1", 75), 12, 1, 0.0),
+    "t256_e64_wide_one_block": (L("sb_t256_e64", 256, 128, 64, 1, 64, SW, RAW, BF, "zipf1.1", 76), 0, 0, 0.5),
 }
 
 
