@@ -103,22 +103,25 @@ def test_backward_matches_oracle(name):
 def test_backward_z_loss_and_noise():
     """loss = sum(dy y) + daux aux + dz z_loss with noise on the router logits
     (an input, held fixed): both router layouts, both bias modes."""
-    for cfg, bias_mode, dz in ((L("bw_znoise", 160, 128, 8, 2, 192, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16,
-                                  "normal2", 89), 0, 0.7),
-                               (L("bw_znoise_sel", 300, 64, 24, 2, 96, W.ACT_GELU, W.GATE_RAW, W.DT_BF16,
-                                  "normal2", 90), 1, 2.0)):
-        H.say("[gpu] backward z-loss/noise %s bias_mode=%d dz=%g" % (cfg, bias_mode, dz))
+    for cfg, bias_mode, dz, cap in ((L("bw_znoise", 160, 128, 8, 2, 192, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16,
+                                       "normal2", 89), 0, 0.7, 0),
+                                    (L("bw_znoise_sel", 300, 64, 24, 2, 96, W.ACT_GELU, W.GATE_RAW, W.DT_BF16,
+                                       "normal2", 90), 1, 2.0, 0),
+                                    # everything at once: top-1 raw gates, drops, selection-only bias, noise, dz
+                                    (L("bw_znoise_cap", 240, 64, 16, 1, 64, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
+                                       "zipf1.1", 91), 1, 1.3, 24)):
+        H.say("[gpu] backward z-loss/noise %s bias_mode=%d dz=%g capacity=%d" % (cfg, bias_mode, dz, cap))
         inp = W.make_inputs(cfg)
         dev = H.to_dev(inp)
         dy = _dy(cfg, cfg.seed + 1000)
         noise = (np.random.default_rng(cfg.seed).standard_normal((cfg.T, cfg.E)) * 0.5).astype(np.float32)
-        desc = moe.desc_of(cfg, bias_mode=bias_mode)
+        desc = moe.desc_of(cfg, capacity=cap, bias_mode=bias_mode)
         out = moe.backward(desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"], dev["W2"],
                            dev["b2"], dy.cuda(), 0.3, noise=torch.from_numpy(noise).cuda(), dz=dz)
         torch.cuda.synchronize()
         ref = O.moe_backward(H.oracle_params(inp), cfg.T, cfg.d, cfg.E, cfg.K, cfg.act, cfg.gate,
-                             W.as_float32(dy).astype(np.float64), daux=0.3, bias_select_only=bias_mode == 1,
-                             with_scales=True, noise=noise, dz_loss=dz)
+                             W.as_float32(dy).astype(np.float64), daux=0.3, capacity=cap if cap > 0 else None,
+                             bias_select_only=bias_mode == 1, with_scales=True, noise=noise, dz_loss=dz)
         for k in ("dh", "dW_r", "db_r", "dW1", "db1", "dW3", "dW2", "db2"):
             got, want = out[k], ref[k]
             if got is None or want is None:
