@@ -671,6 +671,25 @@ def check_z_loss_closed_forms(seed=43):
         assert abs(r["z_loss"] - math.log1p(math.exp(x)) ** 2) <= 1e-13 * max(1.0, r["z_loss"]), (x, r["z_loss"])
 
 
+def check_z_loss_ignores_selection_bias(seed=45):
+    """A bias that only steers the choice never reaches the softmax, so the
+    z-loss is the same bits as without that bias (any bias vector, chosen to
+    change the choice), while the same bias added to the logits changes it: the
+    z-loss is taken on the logits the softmax sees, not on the choice scores."""
+    rng = np.random.default_rng(seed)
+    T, d, E = 31, 16, 6
+    inp = {"h": rng.standard_normal((T, d)).astype(np.float32),
+           "W_r": (rng.standard_normal((d, E)) * 0.3).astype(np.float32), "b_r": None,
+           "W1": np.zeros((E, 4, d)), "W2": np.zeros((E, d, 4)), "W3": np.zeros((E, 4, d)), "b1": None, "b2": None}
+    r0 = O.moe_forward(inp, T, d, E, 2, O.ACT_SWIGLU, O.GATE_RENORM)
+    b = (rng.standard_normal(E) * 3).astype(np.float32)
+    sel = O.moe_forward(dict(inp, b_r=b), T, d, E, 2, O.ACT_SWIGLU, O.GATE_RENORM, bias_select_only=True)
+    lgt = O.moe_forward(dict(inp, b_r=b), T, d, E, 2, O.ACT_SWIGLU, O.GATE_RENORM)
+    assert not np.array_equal(sel["topk_idx"], r0["topk_idx"]), "the bias should change the choice"
+    assert sel["z_loss"] == r0["z_loss"], (sel["z_loss"], r0["z_loss"])
+    assert lgt["z_loss"] != r0["z_loss"]
+
+
 def check_backward_fd_zloss_noise(seed=44):
     """The z-loss gradient and a noisy router: central differences of
     sum(dy y) + daux aux + dz z_loss, with noise on the logits (held fixed:
@@ -690,4 +709,5 @@ ALL_CHECKS = [check_router_logits_exact, check_router_logits_bound, check_topk_b
               check_capacity_layer, check_bias_select_only, check_backward_fd_swiglu_renorm,
               check_backward_fd_gelu_raw_capacity, check_backward_fd_switch_top1, check_backward_dense_reduction,
               check_noise_zero_and_bias_equivalence, check_noise_forcing, check_z_loss_closed_forms,
+              check_z_loss_ignores_selection_bias,
               check_backward_fd_zloss_noise]

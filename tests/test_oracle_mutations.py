@@ -226,7 +226,16 @@ def _forward_noise_selection_only(inp, T, d, E, K, act, gate, *a, noise=None, **
     return r
 
 
+def _forward_zloss_on_choice_scores(*a, **kw):
+    # the z-loss taken on the scores the choice is made on (bias included even
+    # when it only steers the choice) instead of the softmax's logits
+    r = _orig["moe_forward"](*a, **kw)
+    r["z_loss"] = _orig["z_loss"](np.asarray(r["logits"], np.float64))
+    return r
+
+
 MUTATIONS = {
+    "zloss_on_choice_scores": ("moe_forward", _forward_zloss_on_choice_scores),
     "zloss_not_squared": ("z_loss", _zloss_not_squared),
     "zloss_sum_not_mean": ("z_loss", _zloss_sum_not_mean),
     "zloss_grad_factor_one": ("z_loss_logit_grad", _zloss_grad_factor_one),
