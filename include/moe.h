@@ -41,7 +41,9 @@
  *  b_r      [E]             float32  optional router bias (see moe_bias_mode)
  *  W1, W3   [E][width][d]   dtype    row n of expert e = column n of the d x width
  *                                    matrix of the math (output-major: the reduction
- *                                    dimension d is contiguous)
+ *                                    dimension d is contiguous). The input-major
+ *                                    layout [E][d][width] is not accepted: a caller
+ *                                    holding it transposes once per weight load.
  *  b1       [E][width]      dtype    GELU experts only (optional)
  *  W2       [E][d][width]   dtype    row j of expert e = column j of the width x d matrix
  *  b2       [E][d]          dtype    GELU experts only (optional)
@@ -180,6 +182,9 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h,
  * Out: o_perm (ungated float32 expert outputs, one row per grouped slot).
  * With desc->capacity = C > 0 only the first C rows of each group are
  * computed; the o_perm rows of dropped slots are left as they were.
+ * expert_offsets must be non-decreasing from 0 to S = T*K (as moe_permute
+ * writes them); otherwise the outputs are unspecified, but every expert's row
+ * range is clamped into [0, S), so no access leaves the buffers.
  * Returns a moe_status. */
 int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expert_offsets,
                    const void* W1, const void* b1, const void* W3, const void* W2,
@@ -189,7 +194,8 @@ int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expe
  * Step 3; maptheai.com "The mechanism"), accumulated in float32 in ascending j
  * and rounded once to dtype. A gather: each y row is written by one owner.
  * Entries of token_slot that are negative (slots dropped at capacity) are
- * skipped. Needs no workspace. Returns a moe_status. */
+ * skipped; entries of S = T*K or more give unspecified values in y but are
+ * clamped, so no access leaves o_perm. Needs no workspace. Returns a moe_status. */
 int moe_combine(const moe_desc* desc, const float* o_perm, const int32_t* token_slot,
                 const float* topk_gate, void* y, void* stream);
 

@@ -90,7 +90,6 @@ Function -> passage it follows -> what pins it (tests/test_oracle_pins.py):
 from __future__ import annotations
 
 import ctypes
-import itertools
 import math
 import os
 from fractions import Fraction
@@ -599,12 +598,3 @@ def load_stats(counts: Sequence[int], T: int, K: int) -> Dict[str, float]:
     return {"slots": int(c.sum()), "balanced": S / len(c), "busiest_share": float(c.max() / S),
             "top2_share": float(top2 / S), "idle": int((c == 0).sum())}
 
-
-def brute_force_topk_set(logits_row: np.ndarray, K: int):
-    """The K-subset with the largest logit sum; ties -> lexicographically smallest index set."""
-    best, best_sum = None, None
-    for sub in itertools.combinations(range(len(logits_row)), K):  # lexicographic order
-        s = float(sum(float(logits_row[i]) for i in sub))
-        if best_sum is None or s > best_sum:
-            best, best_sum = sub, s
-    return best

@@ -27,6 +27,18 @@ def say(msg: str):
     sys.__stderr__.flush()
 
 
+# Error figures of the comparisons, printed at the end of the session by the
+# pytest_terminal_summary hook in conftest.py, so that the run's own output
+# (not only its pass/fail dots) carries them.
+RESULTS = []
+
+
+def record(kind: str, case: str, full: bool = False, **figures):
+    """Keep one comparison's figures (kind: 'y', 'grad', ...) for the session
+    summary; full-size workloads (full=True) are printed last."""
+    RESULTS.append((kind, case, full, figures))
+
+
 class PerExpert:
     """Lazily upcasts one expert's slice of a CPU tensor to float32 numpy (exact)."""
 
@@ -102,13 +114,3 @@ def check_logits_bits(got: np.ndarray, ref: np.ndarray):
     r = np.ascontiguousarray(ref, np.float32).view(np.uint32)
     check_bits_equal("router logits (float32 bits)", g, r)
 
-
-def sample_tokens(r: dict, T: int, n_random: int = 32, seed: int = 0) -> np.ndarray:
-    """First and last tokens, a seeded random set, and the first token of every used expert."""
-    rng = np.random.default_rng(seed)
-    pick = set(range(min(4, T))) | set(range(max(0, T - 4), T))
-    pick |= set(rng.choice(T, size=min(n_random, T), replace=False).tolist())
-    idx = r["topk_idx"]
-    for e in np.unique(idx):
-        pick.add(int(np.nonzero((idx == e).any(axis=1))[0][0]))
-    return np.array(sorted(pick), dtype=np.int64)

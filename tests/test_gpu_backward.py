@@ -48,7 +48,45 @@ CASES = {
     "decode_T16": (L("bw_dec", 16, 256, 8, 2, 512, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 86), 0.1, 0, 0),
     "tiles_e4": (L("bw_tiles", 2048, 256, 4, 2, 512, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 87), 0.0, 0,
                  0),
+    # shapes whose backward GEMMs run on the tiles of the full-size layers
+    # (see TILES): the recompute and dZ GEMMs on 256 x 256 ...
+    "tiles_256_swiglu": (L("bw_t256", 4096, 256, 4, 2, 4096, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 92),
+                         0.25, 0, 0),
+    # ... on 128 x 256 (about 100 rows per expert, top-1) ...
+    "tiles_128x256_k1": (L("bw_t128x256", 1600, 128, 16, 1, 4608, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16, "zipf1.1",
+                           93), 0.5, 0, 0),
+    # ... and the dX GEMM on 256 x 256 (d = 4096)
+    "tiles_256_dx_gelu": (L("bw_t256dx", 4096, 4096, 4, 2, 512, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 94),
+                          0.1, 0, 0),
 }
+
+# Tile (rows x weight rows) each backward GEMM must run on, for the cases that
+# are there to cover the larger tiles: (recompute, dZ, dX).
+TILES = {
+    "tiles_256_swiglu": ((256, 256), (256, 256), (128, 128)),
+    "tiles_128x256_k1": ((128, 256), (128, 256), (128, 128)),
+    "tiles_256_dx_gelu": ((128, 128), (128, 128), (256, 256)),
+}
+
+
+def _tile(S, E, N, nmat):
+    """The tile shape the library picks for a grouped GEMM of S rows over E
+    experts and N output columns (nmat = 2 when W1 and W3 share a tile): 256 x
+    256 with at least 512 rows per expert on average and two blocks per CU,
+    else 128 x 256 with two blocks per CU, else 128 x 128."""
+    def blocks(bm, bn):
+        return ((S + bm - 1) // bm + min(E, S)) * ((N + bn // nmat - 1) // (bn // nmat))
+    if S // max(E, 1) >= 512 and blocks(256, 256) >= 2 * 256:
+        return (256, 256)
+    if blocks(128, 256) >= 2 * 256:
+        return (128, 256)
+    return (128, 128)
+
+
+def _backward_tiles(cfg):
+    nmat = 2 if cfg.act == W.ACT_SWIGLU else 1
+    return (_tile(cfg.S, cfg.E, cfg.width, nmat), _tile(cfg.S, cfg.E, cfg.width, 1),
+            _tile(cfg.S, cfg.E, cfg.d, 1))
 
 
 def _dy(cfg, seed):
@@ -68,6 +106,8 @@ def _run(cfg, dev, dy, daux, cap, bias_mode):
 def test_backward_matches_oracle(name):
     cfg, daux, cap, bias_mode = CASES[name]
     H.say("[gpu] backward %s %s daux=%g capacity=%d bias_mode=%d" % (name, cfg, daux, cap, bias_mode))
+    if name in TILES:
+        assert _backward_tiles(cfg) == TILES[name], (name, _backward_tiles(cfg))
     inp = W.make_inputs(cfg)
     dev = H.to_dev(inp)
     dy = _dy(cfg, cfg.seed + 1000)
@@ -95,6 +135,7 @@ def test_backward_matches_oracle(name):
         per_elem = float(np.max(np.abs(g - want) / np.maximum(scale, floor)))
         H.say("[gpu] %s %s: |d|/|ref| = %.5f (max |d|/sum|terms| %.4f, max|d|/rms %.4f)" % (
             name, k, err, per_elem, H.rel_err(g, want)))
+        H.record("grad", "%s %s" % (name, k), rel=err, per_term=per_elem)
         if (per_elem if k == "db_r" else err) > TOL:
             bad.append((k, err, per_elem))
     assert not bad, bad
@@ -134,6 +175,7 @@ def test_backward_z_loss_and_noise():
             scale = ref["scale"][k]
             per_elem = float(np.max(np.abs(g - want) / np.maximum(scale, 1e-6 * max(float(scale.max()), 1e-30))))
             H.say("[gpu] %s %s: |d|/|ref| = %.5f (max |d|/sum|terms| %.4f)" % (cfg.name, k, err, per_elem))
+            H.record("grad", "%s %s" % (cfg.name, k), rel=err, per_term=per_elem)
             assert (per_elem if k == "db_r" else err) <= TOL, (k, err, per_elem)
 
 

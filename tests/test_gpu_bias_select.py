@@ -53,6 +53,7 @@ def _check(cfg, inp, dev):
     assert abs(float(H.to_np(aux)[0]) - r["aux"]) <= H.AUX_RTOL * max(abs(r["aux"]), 1.0)
     raw, net = H.layer_err(H.to_np(y), r["y"], cfg.dtype)
     H.say("[gpu] %s y: max|d|/rms = %.4f (raw), %.4f (net of output rounding)" % (cfg.name, raw, net))
+    H.record("y", cfg.name, raw=raw, net=net)
     assert net <= H.Y_TOL[cfg.dtype], (raw, net)
     return r
 

@@ -74,6 +74,7 @@ def _check(cfg, inp, dev, bias_mode, noise):
         raw, net = H.layer_err(H.to_np(y), r["y"], cfg.dtype)
         H.say("[gpu] %s y: max|d|/rms = %.4f (raw), %.4f (net); z_loss %.6f (oracle %.6f)" % (
             cfg.name, raw, net, z, r["z_loss"]))
+        H.record("y", cfg.name, raw=raw, net=net, z_rel=abs(z - r["z_loss"]) / max(abs(r["z_loss"]), 1e-30))
         assert net <= H.Y_TOL[cfg.dtype], (raw, net)
     return r
 

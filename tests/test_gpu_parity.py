@@ -8,9 +8,10 @@ an ulp of the output dtype) is discounted; the combine stage within one
 rounding of its float32 sum.
 
 Small cases run the whole oracle and span several tiles with ragged tails;
-the five full-size workloads compare all routing outputs and a sample of y
-rows (every used expert is represented), in the same launch configuration as
-the benchmark.
+the five full-size workloads compare every routing output, every grouped
+expert row and every y row, element by element, in the same launch
+configuration as the benchmark. Only the largest-operand test samples y rows
+(its oracle would take minutes).
 """
 import numpy as np
 import pytest
@@ -107,7 +108,7 @@ def _check_permute(cfg, dev, r):
                        want.view(torch.int16) if want.dtype == torch.bfloat16 else want), "h_perm rows differ"
 
 
-def _check_expert_ffn(cfg, inp, dev, r, slots=None):
+def _check_expert_ffn(cfg, inp, dev, r, slots=None, full=False):
     desc = moe.desc_of(cfg)
     h_perm = dev["h"][torch.from_numpy(r["slot_token"].astype(np.int64)).cuda()].contiguous()
     offs = torch.from_numpy(r["offsets"]).cuda()
@@ -124,6 +125,7 @@ def _check_expert_ffn(cfg, inp, dev, r, slots=None):
         x = p["h"][r["slot_token"][slots[sel]]]
         ref[sel] = O.expert_ffn(x, int(e), p, cfg.act)
     err = H.rel_err(got, ref)
+    H.record("o", cfg.name, full=full, slots=len(slots), err=err, bar=H.Y_TOL[cfg.dtype])
     assert err <= H.Y_TOL[cfg.dtype], err
 
 
@@ -149,7 +151,7 @@ def _check_combine(cfg, r):
     assert np.all(diff <= bound), ("combine outside one-rounding bound", worst, diff[worst], bound[worst])
 
 
-def _check_forward(cfg, dev, r, rows=None, repeats=3):
+def _check_forward(cfg, dev, r, rows=None, repeats=3, full=False):
     layer_desc = moe.desc_of(cfg)
     ws = moe.workspace(layer_desc)
     outs = []
@@ -170,8 +172,12 @@ def _check_forward(cfg, dev, r, rows=None, repeats=3):
         yg = yg[rows]
     raw, net = H.layer_err(yg, r["y"], cfg.dtype)
     H.say("[gpu] %s y: max|d|/rms = %.4f (raw), %.4f (net of output rounding)" % (cfg.name, raw, net))
+    raw_bar = H.Y_TOL[cfg.dtype]
+    if cfg.dtype == W.DT_BF16 and r["y"].size:
+        raw_bar += (2.0 ** -8) * np.abs(r["y"]).max() / np.sqrt(np.mean(r["y"] ** 2))
+    H.record("y", cfg.name, full=full, rows=len(yg), raw=raw, net=net, bar=H.Y_TOL[cfg.dtype], raw_bar=raw_bar)
     assert net <= H.Y_TOL[cfg.dtype], (raw, net)
-    assert raw <= H.Y_TOL[cfg.dtype] + (2.0 ** -8) * np.abs(r["y"]).max() / np.sqrt(np.mean(r["y"] ** 2))
+    assert raw <= raw_bar, (raw, raw_bar)
     return raw
 
 
@@ -315,23 +321,17 @@ FULL = ["micro", "skewed", "mixtral_prefill", "mixtral_decode", "switch_top1"]
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_workload(name):
+    """Every token and every grouped row of the workload against the oracle."""
     cfg = W.WORKLOADS[name]
     H.say("[gpu] full workload %s %s" % (name, cfg))
     inp = W.make_inputs(cfg)
-    rows = None
-    r = H.run_oracle(cfg, inp, tokens=[])  # routing for every token; y below
-    if cfg.T * cfg.d * cfg.width > 2 ** 31:
-        rows = H.sample_tokens(r, cfg.T)
-    r = H.run_oracle(cfg, inp, tokens=rows)
+    r = H.run_oracle(cfg, inp)
     dev = H.to_dev(inp)
     _check_route(cfg, dev, r)
     _check_permute(cfg, dev, r)
-    slots = None
-    if rows is not None:
-        slots = np.unique(r["token_slot"][rows].reshape(-1))
-    _check_expert_ffn(cfg, inp, dev, r, slots=slots)
+    _check_expert_ffn(cfg, inp, dev, r, full=True)
     _check_combine(cfg, r)
-    err = _check_forward(cfg, dev, r, rows=rows)
+    err = _check_forward(cfg, dev, r, full=True)
     H.say("[gpu] %s y max|d|/rms = %.3e, aux = %.6f, idle experts = %d, max share = %.3f" % (
         name, err, r["aux"], int((r["counts"] == 0).sum()), r["counts"].max() / cfg.S))
     del dev

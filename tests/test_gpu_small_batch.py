@@ -87,6 +87,7 @@ def test_small_batch(name):
     raw, net = H.layer_err(ys[0], r["y"], cfg.dtype)
     dropped = int((~r["keep"]).sum()) if "keep" in r else 0
     H.say("[gpu] %s y: max|d|/rms = %.4f (raw), %.4f (net); %d slots dropped" % (cfg.name, raw, net, dropped))
+    H.record("y", cfg.name, raw=raw, net=net, dropped=dropped)
     assert net <= H.Y_TOL[cfg.dtype], (raw, net)
     if cap:
         assert dropped > 0, "the capacity case should drop slots"
