@@ -22,7 +22,8 @@
  *    the call only. All tensors are contiguous, row-major, 16-byte aligned.
  *  - The library never allocates device memory and never synchronises the
  *    host. Scratch comes from the caller's workspace `ws` (`ws_bytes` long,
- *    256-byte aligned), sized by moe_workspace_size(). All work is enqueued on
+ *    256-byte aligned), sized by moe_workspace_size(), or for
+ *    moe_forward_noalloc from a static device array. All work is enqueued on
  *    `stream` (a hipStream_t; NULL = the null stream) and is complete once the
  *    stream is; outputs are not valid before that.
  *  - Arguments are validated on the host before anything is enqueued. On any
@@ -211,6 +212,30 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
                 const void* W1, const void* b1, const void* W3, const void* W2,
                 const void* b2, void* y, float* aux_loss, int32_t* expert_counts,
                 const float* noise, float* z_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* Size in bytes of the static device scratch of moe_forward_noalloc (one
+ * array per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): it calls no allocating routine. Its scratch is a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES that each GPU holds from the
+ * library's first call on it until the process ends; make that first call
+ * outside stream capture (it looks up the array's device address once per
+ * device). Layers whose moe_workspace_size() exceeds MOE_NOALLOC_SCRATCH_BYTES
+ * (the Mixtral-shaped prefill layer needs about 0.43 GB; decode batches and the
+ * Switch-style layer fit) return MOE_ERR_WORKSPACE with nothing enqueued.
+ * All calls on one GPU share the array and it keeps the last call's contents:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and give unspecified results; calls ordered on one stream are safe. The
+ * kernels write every scratch byte before they read it, so nothing needs
+ * clearing between calls. Arguments, outputs and numerics as moe_forward
+ * (bitwise the same results). Returns a moe_status. */
+int moe_forward_noalloc(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
+                        const void* W1, const void* b1, const void* W3, const void* W2,
+                        const void* b2, void* y, float* aux_loss, int32_t* expert_counts,
+                        const float* noise, float* z_loss, void* stream);
 
 /* Bytes of workspace moe_backward needs for this layer shape (bfloat16 layers
  * only: MOE_ERR_UNSUPPORTED otherwise). Host-only; enqueues nothing. */

@@ -6,5 +6,5 @@ seeded synthetic workloads.
 """
 from . import workloads  # noqa: F401
 from .binding import (MoeDesc, MoeError, MoELayer, Trace, backward, backward_workspace, capacity_slots,  # noqa: F401
-                      combine, desc_of, expert_ffn, forward, header_symbols, lib, permute, route, workspace,
-                      workspace_size)
+                      combine, desc_of, expert_ffn, forward, forward_noalloc, header_symbols, lib, permute, route,
+                      workspace, workspace_size)

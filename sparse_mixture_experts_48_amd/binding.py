@@ -49,6 +49,7 @@ _SIGS = {
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]),
     "moe_combine": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 4 + [_vp]),
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 13 + [_vp, ctypes.c_size_t, _vp]),
+    "moe_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeDesc)] + [_vp] * 13 + [_vp]),
     "moe_capacity_slots": (ctypes.c_int, [ctypes.c_double, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.POINTER(ctypes.c_int32)]),
     "moe_backward_workspace_size": (ctypes.c_int, [ctypes.POINTER(MoeDesc), ctypes.POINTER(ctypes.c_size_t)]),
@@ -197,6 +198,20 @@ def forward(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, ws=None, y=None, aux
         ctypes.byref(desc), _ptr(h), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2), _ptr(b2),
         _ptr(y), _ptr(aux), _ptr(counts), _ptr(noise), _ptr(z_loss), _ptr(ws), ws.numel(), _stream()))
     return y, aux, counts
+
+
+# Bytes of the static device scratch of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES in include/moe.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(desc: MoeDesc, h, W_r, b_r, W1, b1, W3, W2, b2, y, aux=None, counts=None, noise=None,
+                    z_loss=None) -> None:
+    """moe_forward_noalloc: the layer into the caller's y (and aux, counts,
+    z_loss if given) with the library's static scratch; nothing is allocated
+    here or in the library."""
+    _check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        ctypes.byref(desc), _ptr(h), _ptr(W_r), _ptr(b_r), _ptr(W1), _ptr(b1), _ptr(W3), _ptr(W2), _ptr(b2),
+        _ptr(y), _ptr(aux), _ptr(counts), _ptr(noise), _ptr(z_loss), _stream()))
 
 
 def backward_workspace(desc: MoeDesc, device="cuda") -> torch.Tensor:

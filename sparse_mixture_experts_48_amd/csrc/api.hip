@@ -7,10 +7,17 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "moe.h"
 #include "kernels.h"
+
+// Scratch of moe_forward_noalloc: one array per GPU, held from the library's
+// first call on that GPU until the process ends. In host code `scratch` names
+// a host-side stand-in, never the device memory: kernels and copies get the
+// address hipGetSymbolAddress returns for the current device (noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace moe {
 hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st);
@@ -239,6 +246,129 @@ hipError_t traced(int kid, hipStream_t st, F&& launch) {
     if (_e != hipSuccess) return MOE_ERR_HIP;                     \
   } while (0)
 
+// Every argument of moe_forward / moe_forward_noalloc except the workspace.
+int check_forward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, const void* W1,
+                  const void* b1, const void* W3, const void* W2, const void* b2, const void* y,
+                  const float* aux_loss, const int32_t* expert_counts, const float* noise, const float* z_loss) {
+  MOE_CHECK(check_desc(desc));
+  const moe_desc& d = *desc;
+  const bool any = d.T > 0;
+  MOE_CHECK(check_ptr(h, any));
+  MOE_CHECK(check_ptr(W_r, true));
+  MOE_CHECK(check_ptr(b_r, false));
+  MOE_CHECK(check_experts(d, W1, b1, W3, W2, b2));
+  MOE_CHECK(check_ptr(y, any));
+  MOE_CHECK(check_ptr(aux_loss, false));
+  MOE_CHECK(check_ptr(expert_counts, false));
+  MOE_CHECK(check_ptr(noise, false));
+  MOE_CHECK(check_ptr(z_loss, false));
+  return MOE_OK;
+}
+
+// The whole layer on stream st, with scratch at ws (laid out by pl); the
+// arguments have passed check_forward.
+int enqueue_forward(const moe_desc& d, const Plan& pl, const void* h, const float* W_r, const float* b_r,
+                    const void* W1, const void* b1, const void* W3, const void* W2, const void* b2, void* y,
+                    float* aux_loss, int32_t* expert_counts, const float* noise, float* z_loss, void* ws,
+                    hipStream_t st) {
+  const bool any = d.T > 0;
+  if (!any) {
+    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, expert_counts, nullptr, nullptr, aux_loss, z_loss, st));
+    return MOE_OK;
+  }
+  const int T = static_cast<int>(d.T), E = static_cast<int>(d.E), K = static_cast<int>(d.K);
+  const bool bf16 = d.dtype == MOE_BF16;
+  int32_t* topk_idx = at<int32_t>(ws, pl.topk_idx);
+  float* topk_gate = at<float>(ws, pl.topk_gate);
+  int32_t* blk_hist = at<int32_t>(ws, pl.blk_hist);
+  float* blk_psum = at<float>(ws, pl.blk_psum);
+  int32_t* blk_base = at<int32_t>(ws, pl.blk_base);
+  int32_t* offsets = at<int32_t>(ws, pl.offsets);
+  int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
+  int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
+  int32_t* counts = expert_counts != nullptr ? expert_counts : at<int32_t>(ws, pl.counts);
+
+  moe::RouteArgs ra{h, W_r, b_r, T, static_cast<int>(d.d), E, K, d.gate, topk_idx, topk_gate, nullptr,
+                    blk_hist, blk_psum};
+  ra.bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
+  ra.noise = noise;
+  ra.blk_z = z_loss != nullptr ? at<float>(ws, pl.blk_z) : nullptr;
+  MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
+  const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
+  const int cap = cap_of(d);
+  if (moe::permute_one_block(pl.rt)) {  // up to 256 tokens: statistics and grouping in one launch
+    moe::FinArgs fin;
+    fin.blk_hist = blk_hist;
+    fin.blk_psum = blk_psum;
+    fin.blk_z = ra.blk_z;
+    fin.NB = pl.rt.NB;
+    fin.counts = counts;
+    fin.offsets = offsets;
+    fin.aux = aux_loss;
+    fin.z_loss = z_loss;
+    MOE_LAUNCH(MOE_K_PERMUTE, st,
+               moe::launch_finalize_permute(fin, topk_idx, T, E, K, cap, pl.rt, h, row_bytes, nullptr, slot_token,
+                                            token_slot, st));
+  } else {
+    MOE_LAUNCH(MOE_K_FINALIZE, st,
+               moe::launch_finalize(blk_hist, blk_psum, ra.blk_z, pl.rt.NB, T, E, K, blk_base, counts, offsets,
+                                    nullptr, aux_loss, z_loss, st));
+    MOE_LAUNCH(MOE_K_PERMUTE, st,
+               moe::launch_permute(topk_idx, blk_base, offsets, T, E, K, cap, pl.rt, h, row_bytes, nullptr,
+                                   slot_token, token_slot, st));
+  }
+  // GEMM1 reads the rows of h through slot_token: the grouped copy of h is never written.
+  moe::FfnArgs f{};
+  f.S = T * K;
+  f.d = static_cast<int>(d.d);
+  f.E = E;
+  f.K = K;
+  f.width = static_cast<int>(d.width);
+  f.act = d.act;
+  f.bf16 = bf16;
+  f.x = h;
+  f.x_rows = slot_token;
+  f.offsets = offsets;
+  f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
+  f.a = at<char>(ws, pl.act);
+  f.o_perm = at<float>(ws, pl.o_perm);
+  f.fused_y = K == 1 && d.capacity == 0;  // with drops, the combine writes the tokens that lost their slot
+  f.y = y;
+  f.slot_token = slot_token;
+  f.topk_gate = topk_gate;
+  f.cap = cap;
+  f.max_rows_per_expert = std::min(T, cap);
+  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_gemm1(f, st));
+  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_gemm2(f, st));
+  if (!f.fused_y) {
+    MOE_LAUNCH(MOE_K_COMBINE, st, moe::launch_combine(f.o_perm, token_slot, topk_gate, T, f.d, K, bf16, y, st));
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------- static scratch
+
+constexpr size_t kNoallocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device id; null until looked up
+
+// Device address of the current GPU's scratch array (looked up once per device).
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (static_cast<size_t>(dev) >= g_scratch_ptr.size()) g_scratch_ptr.resize(static_cast<size_t>(dev) + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MOE_ERR_HIP;
+    if (reinterpret_cast<uintptr_t>(ptr) % 256 != 0) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -416,93 +546,23 @@ int moe_forward(const moe_desc* desc, const void* h, const float* W_r, const flo
                 const void* b1, const void* W3, const void* W2, const void* b2, void* y, float* aux_loss,
                 int32_t* expert_counts, const float* noise, float* z_loss, void* ws, size_t ws_bytes,
                 void* stream) {
-  MOE_CHECK(check_desc(desc));
-  const moe_desc& d = *desc;
-  const bool any = d.T > 0;
-  MOE_CHECK(check_ptr(h, any));
-  MOE_CHECK(check_ptr(W_r, true));
-  MOE_CHECK(check_ptr(b_r, false));
-  MOE_CHECK(check_experts(d, W1, b1, W3, W2, b2));
-  MOE_CHECK(check_ptr(y, any));
-  MOE_CHECK(check_ptr(aux_loss, false));
-  MOE_CHECK(check_ptr(expert_counts, false));
-  MOE_CHECK(check_ptr(noise, false));
-  MOE_CHECK(check_ptr(z_loss, false));
-  const Plan pl = make_plan(d);
+  MOE_CHECK(check_forward(desc, h, W_r, b_r, W1, b1, W3, W2, b2, y, aux_loss, expert_counts, noise, z_loss));
+  const Plan pl = make_plan(*desc);
   MOE_CHECK(check_ws(pl, ws, ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!any) {
-    MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_zero_outputs(d.E, expert_counts, nullptr, nullptr, aux_loss, z_loss, st));
-    return MOE_OK;
-  }
-  const int T = static_cast<int>(d.T), E = static_cast<int>(d.E), K = static_cast<int>(d.K);
-  const bool bf16 = d.dtype == MOE_BF16;
-  int32_t* topk_idx = at<int32_t>(ws, pl.topk_idx);
-  float* topk_gate = at<float>(ws, pl.topk_gate);
-  int32_t* blk_hist = at<int32_t>(ws, pl.blk_hist);
-  float* blk_psum = at<float>(ws, pl.blk_psum);
-  int32_t* blk_base = at<int32_t>(ws, pl.blk_base);
-  int32_t* offsets = at<int32_t>(ws, pl.offsets);
-  int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
-  int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
-  int32_t* counts = expert_counts != nullptr ? expert_counts : at<int32_t>(ws, pl.counts);
+  return enqueue_forward(*desc, pl, h, W_r, b_r, W1, b1, W3, W2, b2, y, aux_loss, expert_counts, noise, z_loss, ws,
+                         static_cast<hipStream_t>(stream));
+}
 
-  moe::RouteArgs ra{h, W_r, b_r, T, static_cast<int>(d.d), E, K, d.gate, topk_idx, topk_gate, nullptr,
-                    blk_hist, blk_psum};
-  ra.bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
-  ra.noise = noise;
-  ra.blk_z = z_loss != nullptr ? at<float>(ws, pl.blk_z) : nullptr;
-  MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
-  const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
-  const int cap = cap_of(d);
-  if (moe::permute_one_block(pl.rt)) {  // up to 256 tokens: statistics and grouping in one launch
-    moe::FinArgs fin;
-    fin.blk_hist = blk_hist;
-    fin.blk_psum = blk_psum;
-    fin.blk_z = ra.blk_z;
-    fin.NB = pl.rt.NB;
-    fin.counts = counts;
-    fin.offsets = offsets;
-    fin.aux = aux_loss;
-    fin.z_loss = z_loss;
-    MOE_LAUNCH(MOE_K_PERMUTE, st,
-               moe::launch_finalize_permute(fin, topk_idx, T, E, K, cap, pl.rt, h, row_bytes, nullptr, slot_token,
-                                            token_slot, st));
-  } else {
-    MOE_LAUNCH(MOE_K_FINALIZE, st,
-               moe::launch_finalize(blk_hist, blk_psum, ra.blk_z, pl.rt.NB, T, E, K, blk_base, counts, offsets,
-                                    nullptr, aux_loss, z_loss, st));
-    MOE_LAUNCH(MOE_K_PERMUTE, st,
-               moe::launch_permute(topk_idx, blk_base, offsets, T, E, K, cap, pl.rt, h, row_bytes, nullptr,
-                                   slot_token, token_slot, st));
-  }
-  // GEMM1 reads the rows of h through slot_token: the grouped copy of h is never written.
-  moe::FfnArgs f{};
-  f.S = T * K;
-  f.d = static_cast<int>(d.d);
-  f.E = E;
-  f.K = K;
-  f.width = static_cast<int>(d.width);
-  f.act = d.act;
-  f.bf16 = bf16;
-  f.x = h;
-  f.x_rows = slot_token;
-  f.offsets = offsets;
-  f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
-  f.a = at<char>(ws, pl.act);
-  f.o_perm = at<float>(ws, pl.o_perm);
-  f.fused_y = K == 1 && d.capacity == 0;  // with drops, the combine writes the tokens that lost their slot
-  f.y = y;
-  f.slot_token = slot_token;
-  f.topk_gate = topk_gate;
-  f.cap = cap;
-  f.max_rows_per_expert = std::min(T, cap);
-  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_gemm1(f, st));
-  MOE_LAUNCH(MOE_K_GEMM2, st, moe::launch_gemm2(f, st));
-  if (!f.fused_y) {
-    MOE_LAUNCH(MOE_K_COMBINE, st, moe::launch_combine(f.o_perm, token_slot, topk_gate, T, f.d, K, bf16, y, st));
-  }
-  return MOE_OK;
+int moe_forward_noalloc(const moe_desc* desc, const void* h, const float* W_r, const float* b_r, const void* W1,
+                        const void* b1, const void* W3, const void* W2, const void* b2, void* y, float* aux_loss,
+                        int32_t* expert_counts, const float* noise, float* z_loss, void* stream) {
+  MOE_CHECK(check_forward(desc, h, W_r, b_r, W1, b1, W3, W2, b2, y, aux_loss, expert_counts, noise, z_loss));
+  const Plan pl = make_plan(*desc);
+  if (pl.total > kNoallocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  MOE_CHECK(noalloc_scratch(&ws));
+  return enqueue_forward(*desc, pl, h, W_r, b_r, W1, b1, W3, W2, b2, y, aux_loss, expert_counts, noise, z_loss, ws,
+                         static_cast<hipStream_t>(stream));
 }
 
 int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes) {

@@ -178,3 +178,32 @@ def test_backward_error_paths():
     assert _backward(d, ws_bytes=_bws(d) - 1) == WS
     assert _backward(_d(dtype=0), ws_bytes=1 << 30) == UNSUP
     assert _backward(_d(K=0), ws_bytes=1 << 30) == SHAPE
+
+
+def _noalloc(desc, h=FAKE, y=FAKE, noise=None):
+    return moe.lib().moe_forward_noalloc(ctypes.byref(desc), h, FAKE, None, FAKE, None, FAKE, FAKE, None, y, None,
+                                         None, noise, None, None)
+
+
+def test_forward_noalloc_error_paths():
+    """The entry point without a workspace: its scratch limit matches the
+    header's, layers past it are refused before any HIP call, and the other
+    argument checks are moe_forward's."""
+    import re
+    with open(moe.binding.HEADER_PATH) as f:
+        m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.binding.NOALLOC_SCRATCH_BYTES
+    prefill = _d(T=4096, d=4096, E=8, K=2, w=14336)
+    assert _ws(prefill) > moe.binding.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(prefill) == WS
+    # the decode batch and the Switch-style layer fit
+    assert _ws(_d(T=16, d=4096, E=8, K=2, w=14336)) <= moe.binding.NOALLOC_SCRATCH_BYTES
+    assert _ws(_d(T=8192, d=4096, E=64, K=1, w=1376, gate=1)) <= moe.binding.NOALLOC_SCRATCH_BYTES
+    d = _d()
+    assert _noalloc(d, h=None) == NULL
+    assert _noalloc(d, y=None) == NULL
+    assert _noalloc(d, h=FAKE + 8) == UNSUP
+    assert _noalloc(d, noise=FAKE + 4) == UNSUP
+    assert _noalloc(_d(K=0)) == SHAPE
+    assert moe.lib().moe_forward_noalloc(None, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, None, FAKE, None, None,
+                                         None, None, None) == NULL
