@@ -21,10 +21,11 @@
 //  * gemm_tile_kernel: BM x BN tiles on v_mfma_f32_32x32x16_bf16, LDS rings
 //    fed by direct loads, tiles enumerated over (expert m-tiles) x (n-tiles) on the device
 //    from expert_offsets, so no host synchronisation is needed.
-//  * gemm_stream_kernel (rows per expert <= 32): every wave streams NR x 16
+//  * gemm_slab_kernel (rows per expert <= 32): every wave streams slabs of 16
 //    weight rows over the whole reduction with v_mfma_f32_16x16x32_bf16, the
 //    weights as the M operand and up to 32 token rows as N; weights are read
 //    from HBM exactly once, which is what bounds decode-sized batches.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -563,140 +564,300 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------- streaming kernel
+// ---------------------------------------------------------------------------- slab kernel
+//
+// Decode-sized groups (at most MC * 16 rows per expert): the weights are read
+// from HBM exactly once and bound the time, so everything is arranged for the
+// weight stream. A slab is 16 weight rows (of W1 and W3 for SwiGLU) of one
+// hit expert over the whole reduction; slabs of all hit experts are numbered
+// expert by expert and wave g of G takes slabs g, g + G, ... (the host sizes
+// G so that they divide evenly when every expert is hit), running one
+// software pipeline over the stages (64 k) of all its slabs, so no wave waits
+// at a slab boundary and none is left over at the end.
+// Weights: each stage of a slab is 16 rows x 128 bytes; two non-temporal
+// direct-to-LDS loads per matrix, each covering 8 rows with 8 lanes per
+// 128-byte line (whole lines per instruction: measured on the Mixtral decode
+// weights, 6.85 TB/s against 6.10 for half lines per instruction and plain
+// loads). The wave's private LDS ring holds NBUF stages, loaded NBUF - 1
+// ahead; the MFMA fragments are read back with the same chunk swizzle as the
+// tiled kernel. One wave per block: no barriers.
+// Tokens: each stage's token rows (at most MC * 16; cached, reused by every
+// slab of the expert) are loaded into the same ring slot, each lane fetching
+// exactly the 16 bytes it later reads as its MFMA fragment (rows past the
+// expert's count and k past the end read zeros through the range check). No
+// load of the loop writes a register, so no compiler-inserted wait drains
+// the pipeline (with a register ring for the tokens the compiler waited for
+// all loads at the top of the loop). Stages past the wave's last issue the
+// same loads at offsets past the end (zeros, no memory traffic), so every
+// stage waits for the same count.
+// MFMA v_mfma_f32_16x16x32_bf16, weights as the M operand: lane (a = l / 16,
+// b = l % 16) reads weight row b and token row b at k chunk 4u + a of the
+// stage for the u-th MFMA, so both operands agree on which k a slot holds.
+// IDX: how grouped row s finds its row of x. 0: row s itself; 1: x_rows[s],
+// with all S <= 256 ids held in four registers per lane and picked by lane
+// shuffles (no memory access at a slab switch); 2: x_rows[s] loaded at the
+// switch.
+constexpr int kSlabRows = 16;
+// Ring depth: two stages (one in flight while one is computed), with as many
+// waves per CU as the LDS allows (up to 8). Measured on the Mixtral decode
+// layer (first / second GEMM): depth 2: 285 / 144 us; 3: 287 / 158 us;
+// 4 and 5: 296 / 170 us (with deeper rings the compiler adds waits of its own
+// for direct loads into other slots before some fragment reads).
+constexpr int kSlabBuf1 = 2;
+constexpr int kSlabBuf2 = 2;
+constexpr int kSlabIdsMax = 256;
 
-constexpr int kStreamWaves = 4;
+// 16 bytes per lane into LDS, non-temporal (the nt cache-policy bit).
+__device__ __forceinline__ void lds_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, u32x4_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_wave_base), 16,
+                                           static_cast<int>(voff), 0, 0, 2);
+}
 
-// KU: k per step = KU runs of 32 contiguous k (8 per lane group) per row.
-template <int MODE, int NR, int MC, int NBUF, int KU>
-__global__ __launch_bounds__(kStreamWaves * 64) void gemm_stream_kernel(GemmParams p, int n_groups) {
+// Store through a pointer the compiler knows to be global: stores through a
+// generic pointer may write LDS, and then every later LDS read waits for them.
+template <typename T>
+__device__ __forceinline__ void store_global(void* ptr, T v) {
+  *(__attribute__((address_space(1))) T*)(ptr) = v;
+}
+
+template <int MODE, int MC, int NBUF, int IDX>
+__global__ __launch_bounds__(64) void gemm_slab_kernel(GemmParams p) {
   constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
-  constexpr int kKS = KU * 32;
-  const int e = blockIdx.x / n_groups;
-  const int grp = blockIdx.x % n_groups;
-  int beg, end_row;
-  expert_rows(p.offsets, e, p.S, p.cap, &beg, &end_row);
-  const int rows = min(end_row - beg, MC * 16);  // the host guarantees <= MC * 16 rows per expert
-  if (rows <= 0) return;
-  const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
-  const int n_base = (grp * kStreamWaves + wave) * NR * 16;
+  constexpr int WSLOT = NMAT * kSlabRows * kCH;   // u32x4 of weights per ring stage
+  constexpr int SLOT = WSLOT + MC * 2 * 64;       // + the token fragments (two per 16 rows)
+  constexpr int L = 2 * NMAT + 2 * MC;          // loads per stage
+  constexpr int WAIT = (NBUF - 1) * L;          // loads that may stay in flight past a stage's own
+  static_assert(WAIT <= 63, "vmcnt range");
+  static_assert(NBUF >= 2 && NBUF <= 6, "ring depth");
+  // One array per ring slot, so that the fragment reads of one slot are known
+  // not to alias the direct loads in flight into the others.
+  __shared__ u32x4_t R0[SLOT], R1[SLOT];
+  u32x4_t *R2p = nullptr, *R3p = nullptr, *R4p = nullptr, *R5p = nullptr;
+  if constexpr (NBUF > 2) {
+    __shared__ u32x4_t R2[SLOT];
+    R2p = R2;
+  }
+  if constexpr (NBUF > 3) {
+    __shared__ u32x4_t R3[SLOT];
+    R3p = R3;
+  }
+  if constexpr (NBUF > 4) {
+    __shared__ u32x4_t R4[SLOT];
+    R4p = R4;
+  }
+  if constexpr (NBUF > 5) {
+    __shared__ u32x4_t R5[SLOT];
+    R5p = R5;
+  }
+  // (slot is a constant wherever this is called: the loops over slots are unrolled)
+  auto ring = [&](int slot) {
+    return slot == 0 ? R0 : slot == 1 ? R1 : slot == 2 ? R2p : slot == 3 ? R3p : slot == 4 ? R4p : R5p;
+  };
+  const int lane = threadIdx.x;
+  const int la = lane / 16, lb = lane % 16;
   const int N = p.N, Kd = p.Kd;
-  if (n_base >= N) return;
-  const int lr = lane % 16;     // row inside a 16-row fragment
-  const int lg = lane / 16;     // lane group: 8 k values inside each 32-wide run
+  const int G = static_cast<int>(gridDim.x), gw = static_cast<int>(blockIdx.x);
 
-  const bf16_t* wsrc[NMAT][NR];
-#pragma unroll
-  for (int q = 0; q < NR; ++q) {
-    const int n = min(n_base + q * 16 + lr, N - 1);
-    wsrc[0][q] = p.B + (static_cast<size_t>(e) * N + n) * Kd + lg * 8;
-    if (NMAT == 2) wsrc[NMAT - 1][q] = p.B3 + (static_cast<size_t>(e) * N + n) * Kd + lg * 8;
+  // hit experts: lane e holds expert e's first row and row count
+  int rbeg = 0, rcnt = 0;
+  if (lane < p.E) {
+    int b, en;
+    expert_rows(p.offsets, lane, p.S, p.cap, &b, &en);
+    rbeg = b;
+    rcnt = min(en - b, MC * 16);  // the host guarantees at most MC * 16 rows per expert
   }
-  const bf16_t* xsrc[MC];
-  bool xok[MC];
+  const uint64_t hit = __ballot(rcnt > 0);
+  const int hrank = __popcll(hit & ((uint64_t{1} << lane) - 1));  // rank of this lane among hit experts
+  const int nsl = (N + kSlabRows - 1) / kSlabRows;
+  const int total = __popcll(hit) * nsl;
+  const int my = gw < total ? (total - 1 - gw) / G + 1 : 0;
+  if (my == 0) return;
+  const int nks = (Kd + kBK - 1) / kBK;
+  const int nstage = my * nks;
+  int ids[4] = {0, 0, 0, 0};
+  if constexpr (IDX == 1) {
 #pragma unroll
-  for (int c = 0; c < MC; ++c) {
-    const int r = c * 16 + lr;
-    xok[c] = r < rows;
-    const int s = beg + min(r, rows - 1);
-    xsrc[c] = p.x + static_cast<size_t>(p.x_rows != nullptr ? p.x_rows[s] : s) * Kd + lg * 8;
+    for (int q = 0; q < 4; ++q) ids[q] = lane + 64 * q < p.S ? p.x_rows[lane + 64 * q] : 0;
   }
 
-  f32x4_t acc[NMAT][NR][MC];
+  const uint32_t w_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(Kd) * 2u;
+  const uint32_t x_bytes = static_cast<uint32_t>(p.x_nrows) * static_cast<uint32_t>(Kd) * 2u;
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.x, x_bytes);
+
+  // Slab i of this wave -> expert, first weight row, token rows (wave-uniform).
+  struct Slab {
+    int e, n0, beg, rows;
+  };
+  auto slab = [&](int i) {
+    const int s = gw + min(i, my - 1) * G;
+    const int h = s / nsl;
+    Slab r;
+    r.e = __ffsll(static_cast<unsigned long long>(__ballot(rcnt > 0 && hrank == h))) - 1;
+    r.n0 = (s - h * nsl) * kSlabRows;
+    r.beg = __shfl(rbeg, r.e);
+    r.rows = __shfl(rcnt, r.e);
+    return r;
+  };
+
+  // Load side: the slab being loaded and its per-lane offsets.
+  // Weight instruction j covers rows 8j .. 8j+7 of the slab: lane l reads row
+  // 8j + l / 8, physical chunk l % 8 = logical chunk (l % 8) ^ swz_key(row).
+  __amdgpu_buffer_rsrc_t rw[NMAT];
+  uint32_t wvo[2];   // byte offset of this lane's weight chunk at k = 0 (or past the end)
+  int wkc[2];        // its logical chunk's first k
+  uint32_t xvo[MC];  // byte offset of this lane's token row at k = 0 (or past the end)
+  int li = 0, lkk = 0;
+  auto set_load_slab = [&](const Slab& sl) {
+    rw[0] = buffer_rsrc(p.B + static_cast<size_t>(sl.e) * N * Kd, w_bytes);
+    if constexpr (NMAT == 2) rw[NMAT - 1] = buffer_rsrc(p.B3 + static_cast<size_t>(sl.e) * N * Kd, w_bytes);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * j + lane / 8;
+      wkc[j] = ((lane % 8) ^ swz_key(r)) * 8;
+      const int n = sl.n0 + r;
+      wvo[j] = n < N ? (static_cast<uint32_t>(n) * static_cast<uint32_t>(Kd) + static_cast<uint32_t>(wkc[j])) * 2u
+                     : w_bytes;
+    }
+#pragma unroll
+    for (int c = 0; c < MC; ++c) {
+      const int r = c * 16 + lb;
+      const int s = sl.beg + min(r, sl.rows - 1);  // a grouped row of the expert (rows >= 1)
+      int src = s;
+      if constexpr (IDX == 1) {
+        int v = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = __shfl(ids[q], s & 63);
+          if ((s >> 6) == q) v = t;
+        }
+        src = v;
+      } else if constexpr (IDX == 2) {
+        src = p.x_rows[s];
+      }
+      xvo[c] = r < sl.rows
+                   ? (static_cast<uint32_t>(src) * static_cast<uint32_t>(Kd) + static_cast<uint32_t>(la * 8)) * 2u
+                   : x_bytes;
+    }
+  };
+  set_load_slab(slab(0));
+
+  // The loads of the next stage of the load side into ring slot `slot`; past
+  // the wave's last stage the same loads at offsets past the end.
+  // (Conditions below combine with & rather than &&: short-circuit forms
+  // became branches, each with its own copy of the load.)
+  auto issue = [&](int slot) {
+    const bool live = li < my;
+    const int k0 = lkk * kBK;
+    u32x4_t* base = ring(slot);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool ok = live & (wvo[j] < w_bytes) & (k0 + wkc[j] < Kd);
+        lds_load16_nt(rw[m], ok ? wvo[j] + k0 * 2 : w_bytes, base + m * kSlabRows * kCH + j * 64);
+      }
+#pragma unroll
+    for (int c = 0; c < MC; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int k = k0 + u * 32;
+        const bool ok = live & (xvo[c] < x_bytes) & (k + la * 8 < Kd);
+        lds_load16(rx, ok ? xvo[c] + k * 2 : x_bytes, 0, base + WSLOT + (c * 2 + u) * 64);
+      }
+    if (live && ++lkk == nks) {
+      lkk = 0;
+      if (++li < my) set_load_slab(slab(li));
+    }
+  };
+
+  // Compute side.
+  f32x4_t acc[NMAT][MC];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int q = 0; q < NR; ++q)
-#pragma unroll
-      for (int c = 0; c < MC; ++c) acc[m][q][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  u32x4_t wreg[NBUF][NMAT][NR][KU];
-  u32x4_t xreg[NBUF][MC][KU];
-  auto load = [&](int slot, int k0) {
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const bool kin = k0 + u * 32 + lg * 8 < Kd;
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int q = 0; q < NR; ++q)
-          wreg[slot][m][q][u] = kin ? *reinterpret_cast<const u32x4_t*>(wsrc[m][q] + k0 + u * 32)
-                                    : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < MC; ++c)
-        xreg[slot][c][u] = (kin && xok[c]) ? *reinterpret_cast<const u32x4_t*>(xsrc[c] + k0 + u * 32)
-                                           : u32x4_t{0, 0, 0, 0};
-    }
-  };
+    for (int c = 0; c < MC; ++c) acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int slot) {
+    const u32x4_t* base = ring(slot);
+    bf16x8_t wf[NMAT][2];
 #pragma unroll
-    for (int u = 0; u < KU; ++u)
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) wf[m][u] = as_bf16x8(base[m * kSlabRows * kCH + swz(lb, 4 * u + la)]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int q = 0; q < NR; ++q)
-#pragma unroll
-          for (int c = 0; c < MC; ++c)
-            acc[m][q][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(wreg[slot][m][q][u]), as_bf16x8(xreg[slot][c][u]), acc[m][q][c], 0, 0, 0);
+        for (int c = 0; c < MC; ++c)
+          acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              wf[m][u], as_bf16x8(base[WSLOT + (c * 2 + u) * 64 + lane]), acc[m][c], 0, 0, 0);
   };
-
-  const int nk = (Kd + kKS - 1) / kKS;
-  if constexpr (NBUF == 2) {
-    // explicit register double buffer: one k-step in flight per wave
-    load(0, 0);
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      load(1, (kt + 1) * kKS);
-      compute(0);
-      if (kt + 2 < nk) load(0, (kt + 2) * kKS);
-      compute(1);
-    }
-    if (kt < nk) compute(0);
-  } else {
-    // single buffer: fewer registers, more waves per SIMD to keep loads in flight
-    for (int kt = 0; kt < nk; ++kt) {
-      load(0, kt * kKS);
-      compute(0);
-    }
-  }
-
-  // 16x16 accumulator layout: lane l holds column l%16 (a token row) and
-  // rows (l/16)*4 + r (four consecutive output columns n).
-#pragma unroll
-  for (int q = 0; q < NR; ++q) {
-    const int n = n_base + q * 16 + lg * 4;
-    if (n >= N) continue;  // N is a multiple of 8: a group of four is all in or all out
+  // 16x16 accumulator: lane l holds token row c * 16 + l % 16 and weight rows
+  // 4 (l / 16) + i, i = 0..3 (four consecutive output columns).
+  auto epilogue = [&](const Slab& sl) {
+    const int n = sl.n0 + la * 4;
+    if (n >= N) return;  // N % 8 == 0: four columns are all in or all out
 #pragma unroll
     for (int c = 0; c < MC; ++c) {
-      const int r = c * 16 + lr;
-      if (r >= rows) continue;
-      const int s = beg + r;
+      const int r = c * 16 + lb;
+      if (r >= sl.rows) continue;
+      const int s = sl.beg + r;
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (MODE == G1_SWIGLU || MODE == G1_GELU) {
-          v[i] = epilogue_g1(MODE, acc[0][q][c][i], acc[NMAT - 1][q][c][i], p.bias, e, N, n + i);
+          v[i] = epilogue_g1(MODE, acc[0][c][i], acc[NMAT - 1][c][i], p.bias, sl.e, N, n + i);
         } else {
-          v[i] = acc[0][q][c][i];
-          if (p.bias != nullptr) v[i] += bf16_to_f32(p.bias[static_cast<size_t>(e) * N + n + i]);
+          v[i] = acc[0][c][i];
+          if (p.bias != nullptr) v[i] += bf16_to_f32(p.bias[static_cast<size_t>(sl.e) * N + n + i]);
         }
       }
       if (MODE == G1_SWIGLU || MODE == G1_GELU) {
-        *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n) =
-            u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        store_global(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n,
+                     u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
       } else if (MODE == G2_OPERM) {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + static_cast<size_t>(s) * N + n) =
-            f32x4_t{v[0], v[1], v[2], v[3]};
+        store_global(static_cast<float*>(p.out) + static_cast<size_t>(s) * N + n, f32x4_t{v[0], v[1], v[2], v[3]});
       } else {
         const int t = p.slot_token[s];
         const float g = p.gate[t];
-        *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(t) * N + n) =
-            u32x2_t{pack_bf16x2(g * v[0], g * v[1]), pack_bf16x2(g * v[2], g * v[3])};
+        store_global(static_cast<bf16_t*>(p.out) + static_cast<size_t>(t) * N + n,
+                     u32x2_t{pack_bf16x2(g * v[0], g * v[1]), pack_bf16x2(g * v[2], g * v[3])});
+      }
+    }
+  };
+
+  // Prologue: stages 0 .. NBUF - 2 into slots 0 .. NBUF - 2. (Every loop over
+  // ring slots is fully unrolled, so the register ring's index is a constant.)
+#pragma unroll
+  for (int sl = 0; sl + 1 < NBUF; ++sl) issue(sl);
+
+  Slab cs = slab(0);
+  int ci = 0, ckk = 0;
+  // Stage t uses slot t % NBUF and loads stage t + NBUF - 1 into slot
+  // (t - 1) % NBUF, read by stage t - 1 (whose fragment reads have completed:
+  // its MFMAs consumed them).
+  for (int t0 = 0; t0 < nstage; t0 += NBUF) {
+#pragma unroll
+    for (int sl = 0; sl < NBUF; ++sl) {
+      if (t0 + sl < nstage) {
+        issue((sl + NBUF - 1) % NBUF);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT));
+        asm volatile("" ::: "memory");
+        compute(sl);
+        if (++ckk == nks) {
+          epilogue(cs);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int c = 0; c < MC; ++c) acc[m][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          ckk = 0;
+          if (++ci < my) cs = slab(ci);
+        }
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------- launch
@@ -742,28 +903,34 @@ hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
   return launch_tile<128, 128, 2, 2, MODE>(p, S, st);
 }
 
-template <int MODE, int NR, int NBUF, int KU>
-hipError_t launch_stream(GemmParams p, int max_rows, hipStream_t st) {
-  const int n_groups = (p.N + kStreamWaves * NR * 16 - 1) / (kStreamWaves * NR * 16);
-  const dim3 grid(static_cast<unsigned>(p.E * n_groups));
-  if (max_rows <= 16) {
-    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 1, NBUF, KU>), grid, dim3(kStreamWaves * 64), 0, st, p,
-                       n_groups);
+// Waves of the slab kernel: as many as fit (LDS ring and registers allow
+// `per_cu` per CU), but cut so that every wave gets the same number of slabs
+// when every expert is hit.
+template <int MODE, int MC, int NBUF>
+hipError_t launch_slab_mc(GemmParams p, hipStream_t st) {
+  constexpr int NMAT = (MODE == G1_SWIGLU) ? 2 : 1;
+  constexpr int ring_bytes = NBUF * (NMAT * kSlabRows * kCH + MC * 2 * 64) * 16;
+  const int per_cu = std::min(8, 160 * 1024 / ring_bytes);
+  const long slabs = static_cast<long>(p.E) * ((p.N + kSlabRows - 1) / kSlabRows);
+  const long cap = 256L * per_cu;
+  const long per_wave = (slabs + cap - 1) / cap;
+  const dim3 grid(static_cast<unsigned>((slabs + per_wave - 1) / per_wave));
+  if (p.x_rows == nullptr) {
+    hipLaunchKernelGGL((gemm_slab_kernel<MODE, MC, NBUF, 0>), grid, dim3(64), 0, st, p);
+  } else if (p.S <= kSlabIdsMax) {
+    hipLaunchKernelGGL((gemm_slab_kernel<MODE, MC, NBUF, 1>), grid, dim3(64), 0, st, p);
   } else {
-    hipLaunchKernelGGL((gemm_stream_kernel<MODE, NR, 2, NBUF, KU>), grid, dim3(kStreamWaves * 64), 0, st, p,
-                       n_groups);
+    hipLaunchKernelGGL((gemm_slab_kernel<MODE, MC, NBUF, 2>), grid, dim3(64), 0, st, p);
   }
   return hipGetLastError();
 }
 
-constexpr int kStreamMaxRows = 32;
-// Measured on the Mixtral-shaped decode layer: one 16-row weight fragment per
-// wave, with a register double buffer of 64-k steps for GEMM1 (96 registers:
-// five waves per SIMD, so its 7168 waves run in 1.4 rounds; 128-k steps took 144
-// registers and 2.3 rounds and were 1.5 % slower, 32-k steps no faster) and a
-// single buffer of 128-k steps (more waves per SIMD) for GEMM2.
-constexpr int kStreamNR1 = 1, kStreamBuf1 = 2, kStreamKU1 = 2;  // fragments per wave, buffers, 32-k runs per step
-constexpr int kStreamNR2 = 1, kStreamBuf2 = 1, kStreamKU2 = 4;
+template <int MODE, int NBUF>
+hipError_t launch_slab(GemmParams p, int max_rows, hipStream_t st) {
+  return max_rows <= 16 ? launch_slab_mc<MODE, 1, NBUF>(p, st) : launch_slab_mc<MODE, 2, NBUF>(p, st);
+}
+
+constexpr int kSlabMaxRows = 32;  // rows per expert up to which the slab kernel runs
 
 }  // namespace
 
@@ -783,9 +950,9 @@ hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st) {
   p.Kd = f.d;
   p.S = f.S;
   const bool swiglu = f.act == 1;
-  if (f.max_rows_per_expert <= kStreamMaxRows) {
-    return swiglu ? launch_stream<G1_SWIGLU, kStreamNR1, kStreamBuf1, kStreamKU1>(p, f.max_rows_per_expert, st)
-                  : launch_stream<G1_GELU, kStreamNR1, kStreamBuf1, kStreamKU1>(p, f.max_rows_per_expert, st);
+  if (f.max_rows_per_expert <= kSlabMaxRows) {
+    return swiglu ? launch_slab<G1_SWIGLU, kSlabBuf1>(p, f.max_rows_per_expert, st)
+                  : launch_slab<G1_GELU, kSlabBuf1>(p, f.max_rows_per_expert, st);
   }
   return swiglu ? launch_tile_auto<G1_SWIGLU>(p, f.S, st) : launch_tile_auto<G1_GELU>(p, f.S, st);
 }
@@ -810,9 +977,9 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
   } else {
     p.out = f.o_perm;
   }
-  if (f.max_rows_per_expert <= kStreamMaxRows) {
-    return f.fused_y ? launch_stream<G2_FUSED_Y, kStreamNR2, kStreamBuf2, kStreamKU2>(p, f.max_rows_per_expert, st)
-                     : launch_stream<G2_OPERM, kStreamNR2, kStreamBuf2, kStreamKU2>(p, f.max_rows_per_expert, st);
+  if (f.max_rows_per_expert <= kSlabMaxRows) {
+    return f.fused_y ? launch_slab<G2_FUSED_Y, kSlabBuf2>(p, f.max_rows_per_expert, st)
+                     : launch_slab<G2_OPERM, kSlabBuf2>(p, f.max_rows_per_expert, st);
   }
   return f.fused_y ? launch_tile_auto<G2_FUSED_Y>(p, f.S, st) : launch_tile_auto<G2_OPERM>(p, f.S, st);
 }
