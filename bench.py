@@ -96,15 +96,20 @@ def time_workload(cfg, steps, warmup, label, cold=False):
     counts = layer.counts.cpu().numpy()
     sys.stderr.write("[bench] %s: timing %d steps\n" % (label, steps))
     sys.stderr.flush()
+    # wall-clock steps with the library's tracing off (the headline figure) ...
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+    # ... then the same steps again with HIP events around every launch (per-kernel times)
     with moe.Trace(capacity=16 * steps + 16) as tr:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for _ in range(steps):
             layer.forward()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         events = tr.read()
-    ms = (t1 - t0) * 1e3 / steps
     # the same step replayed from a captured HIP graph (no per-kernel launch gaps)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -173,13 +178,16 @@ def time_backward(cfg, steps, warmup):
     torch.cuda.synchronize()
     sys.stderr.write("[bench] backward: timing %d steps\n" % steps)
     sys.stderr.flush()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps  # tracing off
     with moe.Trace(capacity=64 * steps + 64) as tr:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for _ in range(steps):
             step()
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
         events = tr.read()
     per_call = len(events) // steps
     calls = [events[i * per_call:(i + 1) * per_call] for i in range(steps)]
