@@ -69,6 +69,14 @@ SMALL = {
     # scatter into y from a grid far smaller than the chip
     "ragged_fused_k1": L("ragged_fused_k1", 400, 2048, 64, 1, 520, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
                          "zipf1.1", 60),
+    # many experts with large matrices and Zipf-ragged groups (17 or 21 with
+    # 1..32 rows beside 6 or 8 with hundreds): one tiled launch, in which the
+    # weight-bound tiles of the small experts run beside the large experts'
+    # compute-bound tiles; top-1 with the gated scatter, and top-2 GELU with biases
+    "ragged_large_k1": L("ragged_large_k1", 2048, 2048, 32, 1, 1024, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
+                         "zipf1.1", 61),
+    "ragged_large_gelu_k2": L("ragged_large_gelu_k2", 1024, 2048, 32, 2, 1024, W.ACT_GELU, W.GATE_RENORM,
+                              W.DT_BF16, "zipf1.1", 62),
 }
 
 
