@@ -237,12 +237,15 @@ int moe_forward_noalloc(const moe_desc* desc, const void* h, const float* W_r, c
                         const void* b2, void* y, float* aux_loss, int32_t* expert_counts,
                         const float* noise, float* z_loss, void* stream);
 
-/* Bytes of workspace moe_backward needs for this layer shape (bfloat16 layers
- * only: MOE_ERR_UNSUPPORTED otherwise). Host-only; enqueues nothing. */
+/* Bytes of workspace moe_backward needs for this layer shape. Host-only;
+ * enqueues nothing. */
 int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes);
 
 /* Backward pass of the layer: gradients of loss = sum(dy * y) + daux * aux
- * + dz * z_loss with respect to every input, for bfloat16 layers. The gradient reaches the
+ * + dz * z_loss with respect to every input, for bfloat16 and float32 layers
+ * (bfloat16 layers round the recomputed pre-activations, the hidden
+ * activation and the intermediate gradients to bfloat16; float32 layers keep
+ * everything in float32). The gradient reaches the
  * router only through the gate weights of the chosen experts (maptheai.com
  * "Mixture of Experts", "The difficulties": the top-k choice is not
  * differentiable), through p_i for raw gates (Lensa ML Step 3), and through
@@ -259,9 +262,9 @@ int moe_backward_workspace_size(const moe_desc* desc, size_t* bytes);
  *      dW2 [E][d][width], db2 [E][d] (nullable, GELU only), all float32.
  *      With T = 0 every gradient is zero.
  * Sums over tokens and slots run in a fixed order: results are bitwise
- * reproducible. Returns a moe_status (MOE_ERR_UNSUPPORTED for float32 layers,
- * bias gradients of SwiGLU layers, or transposed operands past the 32-bit
- * offset range; MOE_ERR_SHAPE for a non-finite daux or dz). */
+ * reproducible. Returns a moe_status (MOE_ERR_UNSUPPORTED for bias gradients
+ * of SwiGLU layers, or transposed operands past the 32-bit offset range;
+ * MOE_ERR_SHAPE for a non-finite daux or dz). */
 int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
                  const void* W1, const void* b1, const void* W3, const void* W2, const void* b2,
                  const void* dy, float daux, const float* noise, float dz, void* dh, float* dW_r,

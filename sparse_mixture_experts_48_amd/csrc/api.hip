@@ -96,6 +96,7 @@ struct BwdPlan {
   size_t blk_hist, blk_psum, blk_base, blk_z, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux,
       logits;
   size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
+  size_t u;  // float32 layers: dy W2 of the grouped rows
   size_t total;
 };
 
@@ -127,6 +128,21 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   p.offsets = take((E + 1) * 4);
   p.aux = take(4);
   p.logits = take(static_cast<size_t>(d.T) * E * 4);
+  if (d.dtype == MOE_F32) {  // float32 intermediates, no transposed copies
+    p.z = take(S * Zw * 4);
+    p.a = take(S * w * 4);
+    p.rgate = take(S * 4);
+    p.dyb = take(S * 4);
+    p.dgs = take(S * 4);
+    p.dO = take(S * dd * 4);
+    p.u = take(S * w * 4);
+    p.dZ = take(S * Zw * 4);
+    p.dX = take(S * dd * 4);
+    p.dl = take(static_cast<size_t>(d.T) * E * 4);
+    p.wr_part = take(static_cast<size_t>(p.nwr) * dd * E * 4);
+    p.total = off;
+    return p;
+  }
   p.z = take(S * Zw * 2);
   p.a = take(S * w * 2);
   p.rgate = take(S * 4);
@@ -149,10 +165,9 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   return p;
 }
 
-// Shapes moe_backward supports beyond check_desc: bfloat16, and every
-// transposed or widened operand within the 32-bit offset range of the GEMMs.
+// Shapes moe_backward supports beyond check_desc: every transposed or widened
+// operand within the 32-bit offset range of the GEMMs.
 int check_bwd_desc(const moe_desc& d) {
-  if (d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const int64_t S = d.T * d.K, Zw = d.act == MOE_ACT_SWIGLU ? 2 * d.width : d.width;
   const int64_t ldk = 64 * ((S + 63) / 64 + d.E);
   if (S > 0 && S > kMaxElems / Zw) return MOE_ERR_UNSUPPORTED;
@@ -343,6 +358,83 @@ int enqueue_forward(const moe_desc& d, const Plan& pl, const void* h, const floa
   if (!f.fused_y) {
     MOE_LAUNCH(MOE_K_COMBINE, st, moe::launch_combine(f.o_perm, token_slot, topk_gate, T, f.d, K, bf16, y, st));
   }
+  return MOE_OK;
+}
+
+// Backward pass of a float32 layer after the routing and grouping (shared
+// with the bfloat16 path): the same gradients from float32 kernels, with no
+// transposed copies (the GEMMs read the weights with k as the row index).
+int backward_f32(const moe_desc& d, const BwdPlan& pl, const void* h, const float* W_r, const float* b_r,
+                 const void* W1, const void* b1, const void* W3, const void* W2, const void* b2, const void* dy,
+                 float daux, float dz, void* dh, float* dW_r, float* db_r, float* dW1, float* db1, float* dW3,
+                 float* dW2, float* db2, void* ws, hipStream_t st) {
+  const int T = static_cast<int>(d.T), E_ = static_cast<int>(d.E), K = static_cast<int>(d.K);
+  const int D = static_cast<int>(d.d), Wd = static_cast<int>(d.width), S = static_cast<int>(pl.S);
+  const int Zw = static_cast<int>(pl.Zw);
+  const bool swiglu = d.act == MOE_ACT_SWIGLU;
+  const int cap = cap_of(d);
+  const int bias_select = d.bias_mode == MOE_BIAS_SELECT && b_r != nullptr;
+  const int32_t* topk_idx = at<int32_t>(ws, pl.topk_idx);
+  const float* topk_gate = at<float>(ws, pl.topk_gate);
+  const int32_t* offsets = at<int32_t>(ws, pl.offsets);
+  const int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
+  const int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
+  const int32_t* counts = at<int32_t>(ws, pl.counts);
+  const float* logits = at<float>(ws, pl.logits);
+  float* z = at<float>(ws, pl.z);
+  float* a = at<float>(ws, pl.a);
+  float* rgate = at<float>(ws, pl.rgate);
+  float* dyb = at<float>(ws, pl.dyb);
+  float* dgs = at<float>(ws, pl.dgs);
+  float* dO = at<float>(ws, pl.dO);
+  float* u = at<float>(ws, pl.u);
+  float* dZ = at<float>(ws, pl.dZ);
+  float* dX = at<float>(ws, pl.dX);
+  float* dl = at<float>(ws, pl.dl);
+
+  moe::FfnArgs f{};
+  f.S = S;
+  f.d = D;
+  f.E = E_;
+  f.K = K;
+  f.width = Wd;
+  f.act = d.act;
+  f.bf16 = false;
+  f.x = h;
+  f.x_rows = slot_token;
+  f.offsets = offsets;
+  f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
+  f.cap = cap;
+  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_z_f32(f, z, a, st));
+  MOE_LAUNCH(MOE_K_BWD, st,
+             moe::launch_dout(dy, token_slot, topk_idx, topk_gate, b2, T, D, K, dO, rgate, dyb, false, st));
+  // u = dy W2 for every grouped row (W2 [E][d][width]: k = d is its row index)
+  MOE_LAUNCH(MOE_K_GEMM2, st,
+             moe::launch_bwd_grouped_f32(static_cast<const float*>(dy), slot_token, D, S, offsets, cap, E_,
+                                         static_cast<const float*>(W2), nullptr, 0, Wd, D, u, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dz_f32(u, z, a, rgate, S, Wd, swiglu ? 1 : 0, dZ, dgs, st));
+  // dX = dZ [W1; W3] (W1, W3 [E][width][d]: k = width is their row index)
+  MOE_LAUNCH(MOE_K_GEMM1, st,
+             moe::launch_bwd_grouped_f32(dZ, nullptr, Zw, S, offsets, cap, E_, static_cast<const float*>(W1),
+                                         swiglu ? static_cast<const float*>(W3) : nullptr, Wd, D, Wd, dX, st));
+  MOE_LAUNCH(MOE_K_BWD, st,
+             moe::launch_router_backward(logits, b_r, bias_select, topk_idx, topk_gate, dgs, dyb, token_slot,
+                                         counts, T, E_, K, d.gate, daux, dz, dl, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dh(dX, token_slot, dl, W_r, T, D, E_, K, dh, false, st));
+  MOE_LAUNCH(MOE_K_BWD, st,
+             moe::launch_dwr(h, dl, T, D, E_, at<float>(ws, pl.wr_part), dW_r, bias_select ? nullptr : db_r, false,
+                             st));
+  if (bias_select) MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(db_r, static_cast<size_t>(E_) * 4, st));
+  // weight gradients: dW2[e] = sum_s dO[s]^T a[s]; [dW1; dW3][e] = sum_s dZ[s]^T x[s]
+  MOE_LAUNCH(MOE_K_WGRAD, st,
+             moe::launch_bwd_wgrad_f32(dO, D, a, nullptr, Wd, offsets, S, cap, E_, dW2, nullptr, D, st));
+  MOE_LAUNCH(MOE_K_WGRAD, st,
+             moe::launch_bwd_wgrad_f32(dZ, Zw, static_cast<const float*>(h), slot_token, D, offsets, S, cap, E_, dW1,
+                                       dW3, Wd, st));
+  if (db1 != nullptr)
+    MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dZ, Wd, offsets, E_, S, cap, db1, false, st));
+  if (db2 != nullptr)
+    MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dO, D, offsets, E_, S, cap, db2, false, st));
   return MOE_OK;
 }
 
@@ -633,13 +725,17 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   moe::RouteArgs ra{h, W_r, b_r, T, D, E_, K, d.gate, topk_idx, topk_gate, logits, blk_hist, blk_psum};
   ra.bias_select = bias_select;
   ra.noise = noise;
-  MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, true, st));
+  const bool bf16 = d.dtype == MOE_BF16;
+  MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
   MOE_LAUNCH(MOE_K_FINALIZE, st,
              moe::launch_finalize(blk_hist, blk_psum, nullptr, pl.rt.NB, T, E_, K, blk_base, counts, offsets, nullptr,
                                   at<float>(ws, pl.aux), nullptr, st));
   MOE_LAUNCH(MOE_K_PERMUTE, st,
-             moe::launch_permute(topk_idx, blk_base, offsets, T, E_, K, cap, pl.rt, h, dd * 2, nullptr, slot_token,
-                                 token_slot, st));
+             moe::launch_permute(topk_idx, blk_base, offsets, T, E_, K, cap, pl.rt, h, dd * (bf16 ? 2 : 4), nullptr,
+                                 slot_token, token_slot, st));
+  if (d.dtype == MOE_F32)
+    return backward_f32(d, pl, h, W_r, b_r, W1, b1, W3, W2, b2, dy, daux, dz, dh, dW_r, db_r, dW1, db1, dW3, dW2, db2,
+                        ws, st);
   int32_t* kofs = at<int32_t>(ws, pl.kofs);
   MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_pad_offsets(offsets, E_, S, cap, kofs, st));
   moe::FfnArgs f{};
@@ -674,7 +770,7 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   void* W2T = at<char>(ws, pl.W2T);
   void* W13T = at<char>(ws, pl.W13T);
   MOE_LAUNCH(MOE_K_BWD, st,
-             moe::launch_dout(dy, token_slot, topk_idx, topk_gate, b2, T, D, K, dO, rgate, dyb, st));
+             moe::launch_dout(dy, token_slot, topk_idx, topk_gate, b2, T, D, K, dO, rgate, dyb, true, st));
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W2, E_, D, Wd, W2T, D, 0, st));
   MOE_LAUNCH(MOE_K_GEMM2, st,
              moe::launch_bwd_dz_bf16(dy, T, slot_token, S, offsets, cap, E_, W2T, Wd, D, z, act, rgate, a, dgp, dZ,
@@ -690,9 +786,10 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   MOE_LAUNCH(MOE_K_BWD, st,
              moe::launch_router_backward(logits, b_r, bias_select, topk_idx, topk_gate, dgs, dyb, token_slot,
                                          counts, T, E_, K, d.gate, daux, dz, dl, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dh(dX, token_slot, dl, W_r, T, D, E_, K, dh, st));
+  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_dh(dX, token_slot, dl, W_r, T, D, E_, K, dh, true, st));
   MOE_LAUNCH(MOE_K_BWD, st,
-             moe::launch_dwr(h, dl, T, D, E_, at<float>(ws, pl.wr_part), dW_r, bias_select ? nullptr : db_r, st));
+             moe::launch_dwr(h, dl, T, D, E_, at<float>(ws, pl.wr_part), dW_r, bias_select ? nullptr : db_r, true,
+                             st));
   if (bias_select) MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(db_r, E * 4, st));
 
   // weight gradients: sums over each expert's kept rows of transposed operands
@@ -706,8 +803,10 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(dZ, nullptr, Zw, offsets, kofs, E_, S, cap, dZT, ldk, st));
   MOE_LAUNCH(MOE_K_WGRAD, st, moe::launch_bwd_wgrad_bf16(dOT, D, aT, Wd, ldk, kofs, E_, dW2, nullptr, D, st));
   MOE_LAUNCH(MOE_K_WGRAD, st, moe::launch_bwd_wgrad_bf16(dZT, Zw, xT, D, ldk, kofs, E_, dW1, dW3, Wd, st));
-  if (db1 != nullptr) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dZ, Wd, offsets, E_, S, cap, db1, st));
-  if (db2 != nullptr) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dO, D, offsets, E_, S, cap, db2, st));
+  if (db1 != nullptr)
+    MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dZ, Wd, offsets, E_, S, cap, db1, true, st));
+  if (db2 != nullptr)
+    MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dO, D, offsets, E_, S, cap, db2, true, st));
   return MOE_OK;
 }
 

@@ -146,11 +146,12 @@ __global__ __launch_bounds__(256) void transpose_weights_kernel(const bf16_t* __
 // (bfloat16, for the dW2 GEMM), rgate[s] = g, and dyb = dy[t] . b2[e], the
 // bias part of the gate gradient (its other part, a[s] . (dy W2), comes from
 // the dZ GEMM), summed by a fixed-order tree. A dropped slot gets dyb = 0.
-__global__ __launch_bounds__(256) void dout_kernel(const bf16_t* __restrict__ dy,
-                                                   const int32_t* __restrict__ token_slot,
+// T: the layer's element type (bfloat16 or float32) of dy, b2 and dO.
+template <typename T>
+__global__ __launch_bounds__(256) void dout_kernel(const T* __restrict__ dy, const int32_t* __restrict__ token_slot,
                                                    const int32_t* __restrict__ topk_idx,
-                                                   const float* __restrict__ gate, const bf16_t* __restrict__ b2,
-                                                   int d, int K, bf16_t* __restrict__ dO, float* __restrict__ rgate,
+                                                   const float* __restrict__ gate, const T* __restrict__ b2, int d,
+                                                   int K, T* __restrict__ dO, float* __restrict__ rgate,
                                                    float* __restrict__ dyb) {
   __shared__ float red[256];
   const int tj = blockIdx.x;
@@ -162,14 +163,14 @@ __global__ __launch_bounds__(256) void dout_kernel(const bf16_t* __restrict__ dy
   }
   const float g = gate[tj];
   if (threadIdx.x == 0) rgate[s] = g;
-  const bf16_t* dyr = dy + static_cast<size_t>(t) * d;
-  const bf16_t* br = b2 != nullptr ? b2 + static_cast<size_t>(topk_idx[tj]) * d : nullptr;
-  bf16_t* dor = dO + static_cast<size_t>(s) * d;
+  const T* dyr = dy + static_cast<size_t>(t) * d;
+  const T* br = b2 != nullptr ? b2 + static_cast<size_t>(topk_idx[tj]) * d : nullptr;
+  T* dor = dO + static_cast<size_t>(s) * d;
   float acc = 0.0f;
   for (int n = threadIdx.x; n < d; n += 256) {
-    const float v = bf16_to_f32(dyr[n]);
-    dor[n] = f32_to_bf16(g * v);
-    if (br != nullptr) acc = fmaf(v, bf16_to_f32(br[n]), acc);
+    const float v = Elem<T>::load(dyr + n);
+    Elem<T>::store(dor + n, g * v);
+    if (br != nullptr) acc = fmaf(v, Elem<T>::load(br + n), acc);
   }
   if (b2 == nullptr) {
     if (threadIdx.x == 0) dyb[tj] = 0.0f;
@@ -253,10 +254,10 @@ __global__ __launch_bounds__(256) void router_backward_kernel(
 // consecutive features (16-byte loads of dX when KV = 4) and keeps their W_r
 // rows in registers across the block's tokens.
 constexpr int kDhTokens = 16;
-template <int EP, int KV>
+template <int EP, int KV, typename Tout>
 __global__ __launch_bounds__(256) void dh_kernel(const float* __restrict__ dX, const int32_t* __restrict__ token_slot,
                                                  const float* __restrict__ dl, const float* __restrict__ Wr, int T,
-                                                 int d, int E, int K, bf16_t* __restrict__ dh) {
+                                                 int d, int E, int K, Tout* __restrict__ dh) {
   __shared__ float dl_s[kDhTokens][EP];
   __shared__ int slot_s[kDhTokens][8];
   const int t0 = blockIdx.x * kDhTokens;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void dh_kernel(const float* __restrict__ dX, c
         float r = 0.0f;
 #pragma unroll
         for (int e = 0; e < EP; ++e) r = fmaf(dl_s[i][e], wr[v][e], r);
-        dh[static_cast<size_t>(t) * d + k0 + v] = f32_to_bf16(acc[v] + r);
+        Elem<Tout>::store(dh + static_cast<size_t>(t) * d + k0 + v, acc[v] + r);
       }
     }
   }
@@ -307,8 +308,8 @@ __global__ __launch_bounds__(256) void dh_kernel(const float* __restrict__ dX, c
 // Partial sums over chunks of kWrChunk tokens: part[c][k][e] = sum_t h[t][k] dl[t][e];
 // column e of chunk c, row k: one thread, tokens in order.
 constexpr int kWrChunk = 256;
-template <int EP>
-__global__ __launch_bounds__(256) void dwr_partial_kernel(const bf16_t* __restrict__ h, const float* __restrict__ dl,
+template <int EP, typename Tin>
+__global__ __launch_bounds__(256) void dwr_partial_kernel(const Tin* __restrict__ h, const float* __restrict__ dl,
                                                           int T, int d, int E, float* __restrict__ part) {
   __shared__ float dl_s[kWrChunk][EP + 1];
   const int c = blockIdx.y;
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const bf16_t* __restri
 #pragma unroll
   for (int e = 0; e < EP; ++e) acc[e] = 0.0f;
   for (int tt = 0; tt < nt; ++tt) {
-    const float hv = bf16_to_f32(h[static_cast<size_t>(t0 + tt) * d + k]);
+    const float hv = Elem<Tin>::load(h + static_cast<size_t>(t0 + tt) * d + k);
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[e] = fmaf(hv, dl_s[tt][e], acc[e]);  // padding columns are 0
   }
@@ -354,7 +355,8 @@ __global__ __launch_bounds__(256) void dwr_final_kernel(const float* __restrict_
 }
 
 // out[e][c] = sum over the kept grouped rows of expert e of src[row][c] (in order).
-__global__ __launch_bounds__(256) void group_colsum_kernel(const bf16_t* __restrict__ src, int C,
+template <typename T>
+__global__ __launch_bounds__(256) void group_colsum_kernel(const T* __restrict__ src, int C,
                                                            const int32_t* __restrict__ offsets, int S, int cap,
                                                            float* __restrict__ out) {
   const int e = blockIdx.y;
@@ -363,8 +365,51 @@ __global__ __launch_bounds__(256) void group_colsum_kernel(const bf16_t* __restr
   int beg, end;
   expert_rows(offsets, e, S, cap, &beg, &end);
   float s = 0.0f;
-  for (int r = beg; r < end; ++r) s += bf16_to_f32(src[static_cast<size_t>(r) * C + c]);
+  for (int r = beg; r < end; ++r) s += Elem<T>::load(src + static_cast<size_t>(r) * C + c);
   out[static_cast<size_t>(e) * C + c] = s;
+}
+
+// Float32 layers, one block per grouped row s: from u = dy W2 of the row
+// (the second GEMM's input gradient before the gate), dA = g u,
+// dgs[s] = sum_j a[s][j] u[s][j] (the gate gradient's term from the expert
+// output; a fixed-order tree), and dZ = dA * act'(z): SwiGLU [dz1 | dz3] with
+// dz1 = dA z3 SiLU'(z1), dz3 = dA SiLU(z1); GELU dz = dA GELU'(z). Rows of
+// dropped slots hold values that nothing reads.
+__global__ __launch_bounds__(256) void dz_f32_kernel(const float* __restrict__ u, const float* __restrict__ z,
+                                                     const float* __restrict__ a, const float* __restrict__ rgate,
+                                                     int w, int act, float* __restrict__ dZ,
+                                                     float* __restrict__ dgs) {
+  __shared__ float red[256];
+  const int s = blockIdx.x;
+  const float g = rgate[s];
+  const float* ur = u + static_cast<size_t>(s) * w;
+  const float* ar = a + static_cast<size_t>(s) * w;
+  const int zw = act == 1 ? 2 * w : w;
+  const float* zr = z + static_cast<size_t>(s) * zw;
+  float* dzr = dZ + static_cast<size_t>(s) * zw;
+  float acc = 0.0f;
+  for (int j = threadIdx.x; j < w; j += 256) {
+    const float uv = ur[j];
+    acc = fmaf(ar[j], uv, acc);
+    const float da = g * uv;
+    if (act == 1) {
+      const float z1 = zr[j], z3 = zr[w + j];
+      const float sg = 1.0f / (1.0f + expf(-z1));
+      dzr[j] = da * z3 * (sg * (1.0f + z1 * (1.0f - sg)));
+      dzr[w + j] = da * (z1 * sg);
+    } else {
+      const float x = zr[j];
+      dzr[j] = da * (0.5f * (1.0f + erff(x * 0.70710678118654752440f)) +
+                     x * expf(-0.5f * x * x) * 0.39894228040143267794f);
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dgs[s] = red[0];
 }
 
 unsigned grid1d(size_t n) {
@@ -398,10 +443,17 @@ hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* 
 }
 
 hipError_t launch_dout(const void* dy, const int32_t* token_slot, const int32_t* topk_idx, const float* gate,
-                       const void* b2, int T, int d, int K, void* dO, float* rgate, float* dyb, hipStream_t st) {
-  hipLaunchKernelGGL(dout_kernel, dim3(static_cast<unsigned>(T * K)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(dy), token_slot, topk_idx, gate, static_cast<const bf16_t*>(b2), d, K,
-                     static_cast<bf16_t*>(dO), rgate, dyb);
+                       const void* b2, int T, int d, int K, void* dO, float* rgate, float* dyb, bool bf16,
+                       hipStream_t st) {
+  if (bf16) {
+    hipLaunchKernelGGL(dout_kernel<bf16_t>, dim3(static_cast<unsigned>(T * K)), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(dy), token_slot, topk_idx, gate, static_cast<const bf16_t*>(b2), d,
+                       K, static_cast<bf16_t*>(dO), rgate, dyb);
+  } else {
+    hipLaunchKernelGGL(dout_kernel<float>, dim3(static_cast<unsigned>(T * K)), dim3(256), 0, st,
+                       static_cast<const float*>(dy), token_slot, topk_idx, gate, static_cast<const float*>(b2), d, K,
+                       static_cast<float*>(dO), rgate, dyb);
+  }
   return hipGetLastError();
 }
 
@@ -421,43 +473,69 @@ hipError_t launch_router_backward(const float* logits, const float* br, int bias
   return hipGetLastError();
 }
 
-template <int EP>
+template <int EP, typename Tout>
 hipError_t launch_dh_ep(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
                         int E, int K, void* dh, hipStream_t st) {
   constexpr int KV = EP <= 16 ? 4 : 1;
-  hipLaunchKernelGGL((dh_kernel<EP, KV>), dim3(static_cast<unsigned>((T + kDhTokens - 1) / kDhTokens)), dim3(256), 0,
-                     st, dX, token_slot, dl, Wr, T, d, E, K, static_cast<bf16_t*>(dh));
+  hipLaunchKernelGGL((dh_kernel<EP, KV, Tout>), dim3(static_cast<unsigned>((T + kDhTokens - 1) / kDhTokens)),
+                     dim3(256), 0, st, dX, token_slot, dl, Wr, T, d, E, K, static_cast<Tout*>(dh));
   return hipGetLastError();
 }
 
+template <typename Tout>
+hipError_t launch_dh_t(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
+                       int E, int K, void* dh, hipStream_t st) {
+  if (E <= 8) return launch_dh_ep<8, Tout>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+  if (E <= 16) return launch_dh_ep<16, Tout>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+  if (E <= 32) return launch_dh_ep<32, Tout>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+  return launch_dh_ep<64, Tout>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+}
+
 hipError_t launch_dh(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
-                     int E, int K, void* dh, hipStream_t st) {
-  if (E <= 8) return launch_dh_ep<8>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
-  if (E <= 16) return launch_dh_ep<16>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
-  if (E <= 32) return launch_dh_ep<32>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
-  return launch_dh_ep<64>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
+                     int E, int K, void* dh, bool bf16, hipStream_t st) {
+  return bf16 ? launch_dh_t<bf16_t>(dX, token_slot, dl, Wr, T, d, E, K, dh, st)
+              : launch_dh_t<float>(dX, token_slot, dl, Wr, T, d, E, K, dh, st);
 }
 
 int dwr_chunks(int T) { return (T + kWrChunk - 1) / kWrChunk; }
 
+template <typename Tin>
+void launch_dwr_partial(const Tin* hb, const float* dl, int T, int d, int E, float* part, dim3 grid,
+                        hipStream_t st) {
+  if (E <= 8) hipLaunchKernelGGL((dwr_partial_kernel<8, Tin>), grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+  else if (E <= 16) hipLaunchKernelGGL((dwr_partial_kernel<16, Tin>), grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+  else if (E <= 32) hipLaunchKernelGGL((dwr_partial_kernel<32, Tin>), grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+  else hipLaunchKernelGGL((dwr_partial_kernel<64, Tin>), grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+}
+
 hipError_t launch_dwr(const void* h, const float* dl, int T, int d, int E, float* part, float* dWr, float* dbr,
-                      hipStream_t st) {
+                      bool bf16, hipStream_t st) {
   const int nc = dwr_chunks(T);
   const dim3 grid(static_cast<unsigned>((d + 255) / 256), static_cast<unsigned>(nc));
-  const bf16_t* hb = static_cast<const bf16_t*>(h);
-  if (E <= 8) hipLaunchKernelGGL(dwr_partial_kernel<8>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
-  else if (E <= 16) hipLaunchKernelGGL(dwr_partial_kernel<16>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
-  else if (E <= 32) hipLaunchKernelGGL(dwr_partial_kernel<32>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
-  else hipLaunchKernelGGL(dwr_partial_kernel<64>, grid, dim3(256), 0, st, hb, dl, T, d, E, part);
+  if (bf16) launch_dwr_partial(static_cast<const bf16_t*>(h), dl, T, d, E, part, grid, st);
+  else launch_dwr_partial(static_cast<const float*>(h), dl, T, d, E, part, grid, st);
   hipLaunchKernelGGL(dwr_final_kernel, dim3(static_cast<unsigned>((static_cast<size_t>(d) * E + 255) / 256)),
                      dim3(256), 0, st, part, nc, dl, T, d, E, dWr, dbr);
   return hipGetLastError();
 }
 
 hipError_t launch_group_colsum(const void* src, int C, const int32_t* offsets, int E, int S, int cap, float* out,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(group_colsum_kernel, dim3(static_cast<unsigned>((C + 255) / 256), static_cast<unsigned>(E)),
-                     dim3(256), 0, st, static_cast<const bf16_t*>(src), C, offsets, S, cap, out);
+                               bool bf16, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((C + 255) / 256), static_cast<unsigned>(E));
+  if (bf16) {
+    hipLaunchKernelGGL(group_colsum_kernel<bf16_t>, grid, dim3(256), 0, st, static_cast<const bf16_t*>(src), C,
+                       offsets, S, cap, out);
+  } else {
+    hipLaunchKernelGGL(group_colsum_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(src), C,
+                       offsets, S, cap, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dz_f32(const float* u, const float* z, const float* a, const float* rgate, int S, int width,
+                         int act, float* dZ, float* dgs, hipStream_t st) {
+  hipLaunchKernelGGL(dz_f32_kernel, dim3(static_cast<unsigned>(S)), dim3(256), 0, st, u, z, a, rgate, width, act, dZ,
+                     dgs);
   return hipGetLastError();
 }
 

@@ -125,7 +125,8 @@ hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* 
                                     hipStream_t st);
 // Per routing slot: dO[s] = g dy[t] (bfloat16), rgate[s] = g, dyb = dy[t] . b2[e] (0 without b2).
 hipError_t launch_dout(const void* dy, const int32_t* token_slot, const int32_t* topk_idx, const float* gate,
-                       const void* b2, int T, int d, int K, void* dO, float* rgate, float* dyb, hipStream_t st);
+                       const void* b2, int T, int d, int K, void* dO, float* rgate, float* dyb, bool bf16,
+                       hipStream_t st);
 // dgs[s] = sum over c of dgp[c][s], c in order (the gate gradient of grouped row s, bias term aside).
 hipError_t launch_dgate_sum(const float* dgp, int ncb, int S, float* dgs, hipStream_t st);
 // Gate gradient of slot (t, j): dgs[token_slot] + dyb (0 for a dropped slot).
@@ -135,12 +136,28 @@ hipError_t launch_router_backward(const float* logits, const float* br, int bias
                                   const int32_t* token_slot, const int32_t* counts, int T, int E, int K,
                                   int gate_mode, float daux, float dz, float* dl, hipStream_t st);
 hipError_t launch_dh(const float* dX, const int32_t* token_slot, const float* dl, const float* Wr, int T, int d,
-                     int E, int K, void* dh, hipStream_t st);
+                     int E, int K, void* dh, bool bf16, hipStream_t st);
 int dwr_chunks(int T);
 hipError_t launch_dwr(const void* h, const float* dl, int T, int d, int E, float* part, float* dWr, float* dbr,
-                      hipStream_t st);
+                      bool bf16, hipStream_t st);
 hipError_t launch_group_colsum(const void* src, int C, const int32_t* offsets, int E, int S, int cap, float* out,
-                               hipStream_t st);
+                               bool bf16, hipStream_t st);
+// ---- backward pass of float32 layers
+// z and a = act(z) of the grouped rows (SwiGLU: z = [x W1 | x W3] in rows of 2 width).
+hipError_t launch_bwd_z_f32(const FfnArgs& f, void* z, void* a, hipStream_t st);
+// out[s][n] = sum_k x[row(s)][k] B_e[k][n] (B [E][Kd][N]), plus with B3 the same
+// over columns koff2 .. koff2 + Kd - 1 of x against B3 (grouped rows, first cap of each expert).
+hipError_t launch_bwd_grouped_f32(const float* x, const int32_t* x_rows, int lda, int S, const int32_t* offsets,
+                                  int cap, int E, const float* B, const float* B3, int koff2, int N, int Kd,
+                                  float* out, hipStream_t st);
+// C_e[m][n] = sum over expert e's kept rows s of A[s][m] Bx[row(s)][n], rows m < split to
+// out [E][split][N], the others to out2.
+hipError_t launch_bwd_wgrad_f32(const float* A, int M, const float* Bx, const int32_t* b_rows, int N,
+                                const int32_t* offsets, int S, int cap, int E, float* out, float* out2, int split,
+                                hipStream_t st);
+// Per grouped row: dA = g u, dgs = sum a u, dZ = dA * act'(z) (float32).
+hipError_t launch_dz_f32(const float* u, const float* z, const float* a, const float* rgate, int S, int width,
+                         int act, float* dZ, float* dgs, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace moe

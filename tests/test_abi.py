@@ -161,7 +161,8 @@ def test_backward_error_paths():
     L = moe.lib()
     d = _d()
     n = ctypes.c_size_t(0)
-    assert L.moe_backward_workspace_size(ctypes.byref(_d(dtype=0)), ctypes.byref(n)) == UNSUP  # bfloat16 only
+    assert L.moe_backward_workspace_size(ctypes.byref(_d(dtype=0)), ctypes.byref(n)) == OK  # float32 layers too
+    assert L.moe_backward_workspace_size(ctypes.byref(_d(dtype=7)), ctypes.byref(n)) == UNSUP
     assert L.moe_backward_workspace_size(ctypes.byref(d), None) == NULL
     assert _bws(d) > _ws(d)
     assert _backward(d, dy=None) == NULL
@@ -176,7 +177,8 @@ def test_backward_error_paths():
     assert _backward(d, noise=FAKE + 4) == UNSUP              # misaligned noise
     assert _backward(d, dh=FAKE + 8) == UNSUP                 # misaligned
     assert _backward(d, ws_bytes=_bws(d) - 1) == WS
-    assert _backward(_d(dtype=0), ws_bytes=1 << 30) == UNSUP
+    assert _backward(_d(dtype=0), ws_bytes=_bws(_d(dtype=0)) - 1) == WS
+    assert _backward(_d(dtype=0), ws_bytes=_bws(_d(dtype=0)), db1=FAKE) == UNSUP  # SwiGLU layers have no biases
     assert _backward(_d(K=0), ws_bytes=1 << 30) == SHAPE
 
 

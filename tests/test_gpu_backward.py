@@ -16,6 +16,11 @@ element against the sum of its terms' magnitudes (which the oracle returns):
 with renormalised gates a token's terms sum to zero over the experts, so the
 whole vector is small next to its terms. That per-element figure is printed
 for every gradient.
+Float32 layers keep every intermediate in float32, so their bar is 1e-4
+(per tensor, and per element of db_r against its terms): each gradient is a
+chain of a few float32 sums over at most max(d, width, T) terms, whose
+rounding (2^-24 per operation, growing like the square root of the terms)
+stays near 1e-6 at these sizes.
 Also: a second call gives the same bits, and with no tokens every gradient is
 zero.
 """
@@ -35,6 +40,7 @@ if not torch.cuda.is_available():  # pragma: no cover - the CPU suite deselects 
 
 L = W.LayerShape
 TOL = 2e-2
+TOL_F32 = 1e-4
 CASES = {
     # name: (shape, daux, capacity, bias_mode)
     "swiglu_renorm": (L("bw_swiglu", 200, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "normal2", 81),
@@ -58,6 +64,13 @@ CASES = {
     # ... and the dX GEMM on 256 x 256 (d = 4096)
     "tiles_256_dx_gelu": (L("bw_t256dx", 4096, 4096, 4, 2, 512, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 94),
                           0.1, 0, 0),
+    # float32 layers: the micro workload itself (GELU with biases), SwiGLU with
+    # raw gates and capacity drops, top-1 with a selection-only bias
+    "f32_micro": (W.WORKLOADS["micro"], 0.5, 0, 0),
+    "f32_swiglu_raw_cap": (L("bw_f32_sw", 300, 96, 6, 2, 160, W.ACT_SWIGLU, W.GATE_RAW, W.DT_F32, "normal2", 95),
+                           0.3, 80, 0),
+    "f32_top1_select": (L("bw_f32_k1", 200, 64, 16, 1, 128, W.ACT_GELU, W.GATE_RAW, W.DT_F32, "zipf1.1", 96), 1.0,
+                        0, 1),
 }
 
 # Tile (rows x weight rows) each backward GEMM must run on, for the cases that
@@ -91,7 +104,7 @@ def _backward_tiles(cfg):
 
 def _dy(cfg, seed):
     g = torch.Generator().manual_seed(seed)
-    return torch.randn((cfg.T, cfg.d), generator=g).to(torch.bfloat16)
+    return torch.randn((cfg.T, cfg.d), generator=g).to(cfg.torch_dtype)
 
 
 def _run(cfg, dev, dy, daux, cap, bias_mode):
@@ -136,7 +149,8 @@ def test_backward_matches_oracle(name):
         H.say("[gpu] %s %s: |d|/|ref| = %.5f (max |d|/sum|terms| %.4f, max|d|/rms %.4f)" % (
             name, k, err, per_elem, H.rel_err(g, want)))
         H.record("grad", "%s %s" % (name, k), rel=err, per_term=per_elem)
-        if (per_elem if k == "db_r" else err) > TOL:
+        tol = TOL if cfg.dtype == W.DT_BF16 else TOL_F32
+        if (per_elem if k == "db_r" else err) > tol:
             bad.append((k, err, per_elem))
     assert not bad, bad
 
