@@ -12,9 +12,15 @@ Two kinds of summary, both short Markdown files:
   of the source file of the kernels it measured; ``traffic_bytes`` returns
   nothing once that file has changed.
 
+* counters (``rocprofv3 --pmc`` passes of SQ/GRBM counters): mean totals per
+  launch of chosen kernels and the shares derived from them (MFMA busy, LDS
+  bytes per clock, waiting wave-cycles).
+
 Command line::
 
     python -m sparse_mixture_experts_48_amd.profiling trace STATS_CSV --command "..." > out.md
+    python -m sparse_mixture_experts_48_amd.profiling counters A.csv B.csv --kernel gemm1=PATTERN \\
+        --workload NAME --command "..." > out.md
     python -m sparse_mixture_experts_48_amd.profiling traffic FETCH_CSV WRITE_CSV --copy-mib 1024 \\
         --kernel gemm1=PATTERN --source FILE --workload NAME --command "..." > out.md
 """
@@ -151,6 +157,63 @@ def traffic_bytes(summary_md: str, label: str, repo_root: str):
     return None
 
 
+# Per-dispatch normalisation of the counters summarised by `counters`: what each
+# counter's total is divided by to give a per-unit figure on the MI355X (8
+# XCDs, 256 CUs, 1024 SIMDs). GRBM_GUI_ACTIVE sums the active cycles of the 8
+# XCDs; SQ_VALU_MFMA_BUSY_CYCLES sums over the SIMDs; the SQ_WAIT_* and
+# SQ_WAVE_CYCLES counters count wave-cycles in units of 4 cycles.
+def derived_counters(tot: dict) -> "OrderedDict[str, float]":
+    """Figures derived from one dispatch's counter totals (those available)."""
+    out = OrderedDict()
+    cycles = tot.get("GRBM_GUI_ACTIVE")
+    if cycles:
+        cyc = cycles / 8.0  # per XCD: the kernel's duration in GPU clocks
+        out["clock cycles (GRBM_GUI_ACTIVE / 8)"] = cyc
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in tot:
+            out["MFMA busy share (per SIMD)"] = tot["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024.0 / cyc
+        if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in tot:
+            out["LDS bytes read per CU per clock"] = tot["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64.0 / 256.0 / cyc
+        if "SQ_LDS_CMD_FIFO_FULL" in tot:
+            out["LDS command FIFO full share (per CU)"] = tot["SQ_LDS_CMD_FIFO_FULL"] / 256.0 / cyc
+    if tot.get("SQ_WAVE_CYCLES"):
+        for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"):
+            if c in tot:
+                out["%s / SQ_WAVE_CYCLES" % c] = tot[c] / tot["SQ_WAVE_CYCLES"]
+    return out
+
+
+def summarize_counters(csvs: list, kernels: dict, workload: str, command: str) -> str:
+    """Mean per-dispatch totals of every counter in the given --pmc CSVs for
+    each kernel pattern, and the figures derived from them."""
+    lines = ["# Counters per launch: %s" % workload, "", "Commands (one pass per CSV):", "", "```", command, "```", ""]
+    for label, pattern in kernels.items():
+        rx = re.compile(pattern)
+        tot = OrderedDict()
+        launches = {}
+        for path in csvs:
+            per = {}
+            for r in csv.DictReader(open(path)):
+                if not rx.search(r["Kernel_Name"]):
+                    continue
+                d = per.setdefault(r["Dispatch_Id"], {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if not per:
+                raise ValueError("kernel %s (%s) not found in %s" % (label, pattern, path))
+            for c in sorted({c for d in per.values() for c in d}):
+                vals = [d[c] for d in per.values() if c in d]
+                if c in tot:  # the same counter in two passes (the clock): average them
+                    tot[c] = 0.5 * (tot[c] + sum(vals) / len(vals))
+                else:
+                    tot[c] = sum(vals) / len(vals)
+                launches[c] = len(vals)
+        lines += ["## %s (`%s`)" % (label, pattern), "", "| counter | mean per launch | launches |", "|---|---:|---:|"]
+        lines += ["| %s | %.4g | %d |" % (c, v, launches[c]) for c, v in tot.items()]
+        lines += ["", "| derived | value |", "|---|---:|"]
+        lines += ["| %s | %.4g |" % (k, v) for k, v in derived_counters(tot).items()]
+        lines.append("")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -167,8 +230,17 @@ def main():
     f.add_argument("--source", required=True)
     f.add_argument("--workload", required=True)
     f.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", action="append", required=True, metavar="LABEL=REGEX")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
     a = ap.parse_args()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if a.what == "counters":
+        print(summarize_counters(a.csv, OrderedDict(kv.split("=", 1) for kv in a.kernel), a.workload, a.command),
+              end="")
+        return
     if a.what == "trace":
         print(summarize_trace(a.stats_csv, a.command, a.title, a.trace_csv), end="")
     else:

@@ -64,3 +64,41 @@ def test_trace_medians(tmp_path):
     assert med == {"void k_a(int)": 100, "void k_b(int)": 150.0}
     md = profiling.summarize_trace(str(stats), "cmd", "T", str(trace))
     assert "| `k_a` | 3 | 0.2 | 0.1 | 0.1 | 0.5 | 70.0 % |" in md
+
+
+def test_counter_summary(tmp_path):
+    """Per-launch means over dispatches, rows of one dispatch summed, the clock
+    of two passes averaged, and the derived shares from their definitions."""
+    gemm = "void moe::(anonymous namespace)::gemm_tile_kernel<256, 256, 4, 2, 0>(moe::GemmParams)"
+    other = "void moe::(anonymous namespace)::combine_kernel<unsigned short>(moe::CombineParams)"
+    a, b = tmp_path / "a.csv", tmp_path / "b.csv"
+    with open(a, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d, busy in ((5, 400_000), (6, 600_000)):
+            # GRBM_GUI_ACTIVE reported per XCD (summed: 8 x 1000 clocks)
+            for _ in range(8):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": gemm, "Counter_Name": "GRBM_GUI_ACTIVE",
+                            "Counter_Value": 1000})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": gemm, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES",
+                        "Counter_Value": busy})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": gemm, "Counter_Name": "SQ_INSTS_LDS_LOAD_BANDWIDTH",
+                        "Counter_Value": 16_000})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": gemm, "Counter_Name": "SQ_WAVE_CYCLES", "Counter_Value": 200})
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": gemm, "Counter_Name": "SQ_WAIT_ANY", "Counter_Value": 50})
+        w.writerow({"Dispatch_Id": 7, "Kernel_Name": other, "Counter_Name": "SQ_WAVE_CYCLES", "Counter_Value": 1})
+    with open(b, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        w.writerow({"Dispatch_Id": 9, "Kernel_Name": gemm, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 24_000})
+    md = profiling.summarize_counters([str(a), str(b)], {"gemm1": r"gemm_tile_kernel<256, 256, 4, 2, 0>"}, "w", "cmd")
+    # clock: pass A 8000, pass B 24000 per launch -> 16000, i.e. 2000 cycles per XCD
+    assert "| GRBM_GUI_ACTIVE | 1.6e+04 | 1 |" in md
+    assert "| SQ_VALU_MFMA_BUSY_CYCLES | 5e+05 | 2 |" in md
+    d = profiling.derived_counters({"GRBM_GUI_ACTIVE": 16_000, "SQ_VALU_MFMA_BUSY_CYCLES": 500_000,
+                                    "SQ_INSTS_LDS_LOAD_BANDWIDTH": 16_000, "SQ_WAVE_CYCLES": 200, "SQ_WAIT_ANY": 50})
+    assert d["clock cycles (GRBM_GUI_ACTIVE / 8)"] == 2000
+    assert abs(d["MFMA busy share (per SIMD)"] - 500_000 / 1024 / 2000) < 1e-12
+    assert abs(d["LDS bytes read per CU per clock"] - 16_000 * 64 / 256 / 2000) < 1e-12
+    assert d["SQ_WAIT_ANY / SQ_WAVE_CYCLES"] == 0.25
+    assert "combine" not in md
