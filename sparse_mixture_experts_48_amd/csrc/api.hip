@@ -95,7 +95,7 @@ struct BwdPlan {
   int nwr;
   size_t blk_hist, blk_psum, blk_base, blk_z, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux,
       logits;
-  size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, aT, dOT, dZT, W2T, W13T, dl, wr_part;
+  size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, aT, dOT, dZT, dl, wr_part;
   size_t u;  // float32 layers: dy W2 of the grouped rows
   size_t total;
 };
@@ -157,8 +157,6 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   p.aT = take(w * ldk * 2);
   p.dOT = take(dd * ldk * 2);
   p.dZT = take(Zw * ldk * 2);
-  p.W2T = take(E * w * dd * 2);
-  p.W13T = take(E * dd * Zw * 2);
   p.dl = take(static_cast<size_t>(d.T) * E * 4);
   p.wr_part = take(static_cast<size_t>(p.nwr) * dd * E * 4);
   p.total = off;
@@ -171,7 +169,7 @@ int check_bwd_desc(const moe_desc& d) {
   const int64_t S = d.T * d.K, Zw = d.act == MOE_ACT_SWIGLU ? 2 * d.width : d.width;
   const int64_t ldk = 64 * ((S + 63) / 64 + d.E);
   if (S > 0 && S > kMaxElems / Zw) return MOE_ERR_UNSUPPORTED;
-  if (ldk > kMaxElems / Zw || ldk > kMaxElems / d.d || d.d > kMaxElems / Zw) return MOE_ERR_UNSUPPORTED;
+  if (ldk > kMaxElems / Zw || ldk > kMaxElems / d.d) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -767,19 +765,16 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   void* dO = at<char>(ws, pl.dO);
   void* dZ = at<char>(ws, pl.dZ);
   float* dX = at<float>(ws, pl.dX);
-  void* W2T = at<char>(ws, pl.W2T);
-  void* W13T = at<char>(ws, pl.W13T);
   MOE_LAUNCH(MOE_K_BWD, st,
              moe::launch_dout(dy, token_slot, topk_idx, topk_gate, b2, T, D, K, dO, rgate, dyb, true, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W2, E_, D, Wd, W2T, D, 0, st));
+  // the dZ and dX GEMMs read W2 and [W1; W3] as stored, with k as the row index
   MOE_LAUNCH(MOE_K_GEMM2, st,
-             moe::launch_bwd_dz_bf16(dy, T, slot_token, S, offsets, cap, E_, W2T, Wd, D, z, act, rgate, a, dgp, dZ,
+             moe::launch_bwd_dz_bf16(dy, T, slot_token, S, offsets, cap, E_, W2, Wd, D, z, act, rgate, a, dgp, dZ,
                                      st));
   MOE_LAUNCH(MOE_K_BWD, st,
              moe::launch_dgate_sum(dgp, (Wd + moe::kDgpColsHost - 1) / moe::kDgpColsHost, S, dgs, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W1, E_, Wd, D, W13T, Zw, 0, st));
-  if (swiglu) MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_weights(W3, E_, Wd, D, W13T, Zw, Wd, st));
-  MOE_LAUNCH(MOE_K_GEMM1, st, moe::launch_bwd_grouped_bf16(dZ, S, offsets, cap, E_, W13T, nullptr, D, Zw, dX, st));
+  MOE_LAUNCH(MOE_K_GEMM1, st,
+             moe::launch_bwd_dx_bf16(dZ, S, offsets, cap, E_, W1, swiglu ? W3 : nullptr, D, Wd, dX, st));
 
   // router, dh, dW_r, db_r
   float* dl = at<float>(ws, pl.dl);

@@ -19,8 +19,10 @@
 //   dh[t] = sum_j dX[slot(t, j)] + dlogits[t] W_r^T
 //   dW2_e = dO_e^T A_e,  dW1_e = dZ1_e^T X_e,  dW3_e = dZ3_e^T X_e
 //   dW_r = h^T dlogits,  db_r = sum_t dlogits   (not when the bias only steers the choice)
-// Weight gradients need sums over each expert's grouped rows; the rows of
-// the operands are transposed into [feature][slot] matrices in which every
+// The u and dX GEMMs read W2 and [W1; W3] as stored for the forward pass,
+// with k as the row index (transposed in the LDS fragment reads). Weight
+// gradients need sums over each expert's grouped rows; the rows of the
+// operands are transposed into [feature][slot] matrices in which every
 // expert's slots start at a multiple of 64 and are padded with zeros to a
 // whole number of GEMM stages.
 #include "common.h"
@@ -46,7 +48,7 @@ __global__ void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, i
   kofs[E] = run;
 }
 
-// Both transposes move 64 x 64 tiles through LDS in 16-byte pieces: a thread
+// The transpose moves 64 x 64 tiles through LDS in 16-byte pieces: a thread
 // loads two runs of 8 elements along a source row and stores two runs of 8
 // along a destination row (every row length and offset is a multiple of 8).
 constexpr int kTP = kTile + 8;  // LDS row stride of a tile (elements)
@@ -113,32 +115,6 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(
     const int r = q / 8, c8 = (q % 8) * 8;
     if (r0 + r < R)
       *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r0 + r) * ldk + c0 + c8) = tile_get8_column(tile, c8, r);
-  }
-}
-
-// dst[e][c][coff + r] = src[e][r][c]: src [E][R][C], dst rows of length ldd.
-__global__ __launch_bounds__(256) void transpose_weights_kernel(const bf16_t* __restrict__ src, int R, int C,
-                                                                bf16_t* __restrict__ dst, int ldd, int coff) {
-  __shared__ uint16_t tile[kTile][kTP];  // [r][c]
-  const int e = blockIdx.z;
-  const int c0 = blockIdx.x * kTile, r0 = blockIdx.y * kTile;
-  const bf16_t* sp = src + static_cast<size_t>(e) * R * C;
-  bf16_t* dp = dst + static_cast<size_t>(e) * C * ldd;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    const int q = threadIdx.x + 256 * h2;
-    const int r = q / 8, c8 = (q % 8) * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r0 + r < R && c0 + c8 < C) v = *reinterpret_cast<const uint4*>(sp + static_cast<size_t>(r0 + r) * C + c0 + c8);
-    tile_put8(tile, r, c8, v);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    const int q = threadIdx.x + 256 * h2;
-    const int c = q / 8, r8 = (q % 8) * 8;
-    if (c0 + c < C && r0 + r8 < R)
-      *reinterpret_cast<uint4*>(dp + static_cast<size_t>(c0 + c) * ldd + coff + r0 + r8) = tile_get8_column(tile, r8, c);
   }
 }
 
@@ -430,15 +406,6 @@ hipError_t launch_transpose_groups(const void* src, const int32_t* src_rows, int
   const dim3 grid(static_cast<unsigned>(ldk / kTile), static_cast<unsigned>((R + kTile - 1) / kTile));
   hipLaunchKernelGGL(transpose_groups_kernel, grid, dim3(256), 0, st, static_cast<const bf16_t*>(src), src_rows,
                      R, offsets, kofs, E, S, cap, static_cast<bf16_t*>(dst), ldk);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* dst, int ldd, int coff,
-                                   hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((C + kTile - 1) / kTile), static_cast<unsigned>((R + kTile - 1) / kTile),
-                  static_cast<unsigned>(E));
-  hipLaunchKernelGGL(transpose_weights_kernel, grid, dim3(256), 0, st, static_cast<const bf16_t*>(src), R, C,
-                     static_cast<bf16_t*>(dst), ldd, coff);
   return hipGetLastError();
 }
 

@@ -78,6 +78,10 @@ struct GemmParams {
   const float* rgate;
   const bf16_t* ain;
   float* dgp;
+  // Weights stored with k as the row index (gemm_tile_kernel<..., BT = true>):
+  // B is [E][Kd1][N] with N contiguous, Kd1 = kb3 > 0 rows of B followed by
+  // kb3 rows of B3 (the SwiGLU input gradient dZ [W1; W3]), or Kd1 = Kd.
+  int kb3;
 };
 constexpr int kDgpCols = 64;  // columns per partial sum of the dZ GEMM's gate-gradient terms
 
@@ -143,6 +147,38 @@ constexpr int kTileGroupN = 4;   // n-tiles per group in the XCD-aware block ord
 __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kCH + (chunk ^ swz_key(row)); }
 
+// Weights stored with k as the row index (the backward pass reads W2 and
+// [W1; W3] this way, as stored for the forward pass): a weight slot holds 64
+// rows k of BN columns, 16-byte chunk c of row k at c ^ bt_key(k). An MFMA
+// fragment (32 columns x 16 k; lane l: column l % 32, k 8 (l / 32) .. + 7) is
+// two ds_read_b64_tr_b16. That instruction works on groups of 16 lanes:
+// element j of lane i of a group is element i % 4 of the 8 bytes lane
+// 4 j + i / 4 addresses (lane layout checked on the hardware). So lane
+// s = 16 G + 4 j + q addresses row 8 (G / 2) + 4 r + j, columns
+// 16 (G % 2) + 4 q .. + 3 of the fragment, and read r = 0, 1 delivers the
+// fragment's k 8 (l / 32) + 4 r .. + 3. With the XOR key, the 16 (row, chunk)
+// pairs of either half-wave of a read fall in distinct 16-byte bank groups.
+template <int BN> constexpr int kBtCPR = BN / 8;          // chunks per row
+template <int BN> constexpr int kBtRows = 64 / (BN / 8);  // rows per direct-load instruction
+__device__ __forceinline__ int bt_key(int k) { return 4 * (k & 3); }
+
+template <int BN>
+__device__ __forceinline__ int bt_lane_offset(int lane, int col0) {
+  const int G = lane / 16, j = (lane % 16) / 4, q = lane % 4;
+  const int k = 8 * (G / 2) + j;
+  const int c = col0 / 8 + 2 * (G % 2) + q / 2;
+  return k * BN * 2 + (c ^ bt_key(k)) * 16 + (q % 2) * 8;
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t bt_fragment(const u32x4_t* slot, int off, int row_bytes) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const char* base = reinterpret_cast<const char*>(slot);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off + 4 * row_bytes));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Buffer resource over `bytes` bytes at `base` (raw dword buffer; loads at
 // byte offsets >= bytes return zeros).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
@@ -161,10 +197,11 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
+  static_assert(!BT || (NMAT == 1 && MODE != G_WGRAD), "k-major weights: single-matrix forward-style modes");
   constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_SWIGLU_Z || MODE == G1_GELU_Z);
   constexpr bool WGRAD = (MODE == G_WGRAD);
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -283,9 +320,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const uint32_t a_bytes = static_cast<uint32_t>(WGRAD ? p.M : p.x_nrows) * static_cast<uint32_t>(stride) * 2u;
   const uint32_t b_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(stride) * 2u;
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.x, a_bytes);
-  const __amdgpu_buffer_rsrc_t rb1 = buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * N * Kd), b_bytes);
+  // k-major weights: Kd1 rows of B per expert (then as many of B3)
+  const int Kd1 = (BT && p.kb3 > 0) ? p.kb3 : Kd;
+  const uint32_t bt_bytes = static_cast<uint32_t>(Kd1) * static_cast<uint32_t>(N) * 2u;
+  const __amdgpu_buffer_rsrc_t rb1 =
+      BT ? buffer_rsrc(p.B + static_cast<size_t>(e) * Kd1 * N, bt_bytes)
+         : buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * N * Kd), b_bytes);
   const __amdgpu_buffer_rsrc_t rb3 =
-      (NMAT == 2) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * N * Kd, b_bytes) : rb1;
+      (NMAT == 2) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * N * Kd, b_bytes)
+                  : ((BT && p.kb3 > 0) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * Kd1 * N, bt_bytes) : rb1);
   // per lane: offset for every stage, and for the last one (out of range past the end of k)
   uint32_t a_vo[A_IN], a_vl[A_IN], b_vo[B_IN], b_vl[B_IN];
 #pragma unroll
@@ -299,22 +342,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   }
 #pragma unroll
   for (int u = 0; u < B_IN; ++u) {
-    int mat;
-    const int r = (wid * B_IN + u) * kRPI + lane / kCH;
-    const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
-    const int n = min(brow_col(r, &mat), N - 1);
-    b_vo[u] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
-    b_vl[u] = (WGRAD || k_last + kc < Kd) ? b_vo[u] : b_bytes;
+    if constexpr (BT) {
+      // LDS slot [k][BN] (rows of BN columns, 16-byte chunks): instruction u
+      // fills rows (wid * B_IN + u) * RB ..; lane l takes row-in-instruction
+      // l / CPR and physical chunk l % CPR, i.e. the global chunk
+      // (l % CPR) ^ bt_key(row) of the block's columns (columns past N read a
+      // valid chunk whose outputs are never stored).
+      const int lr = lane / kBtCPR<BN>;
+      const int r = (wid * B_IN + u) * kBtRows<BN> + lr;
+      const int gc = (lane % kBtCPR<BN>) ^ bt_key(r);
+      const int n = min(n0 + gc * 8, N - 8);
+      b_vo[u] = (static_cast<uint32_t>(lr) * static_cast<uint32_t>(N) + static_cast<uint32_t>(n)) * 2u;
+      b_vl[u] = b_vo[u];
+    } else {
+      int mat;
+      const int r = (wid * B_IN + u) * kRPI + lane / kCH;
+      const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
+      const int n = min(brow_col(r, &mat), N - 1);
+      b_vo[u] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
+      b_vl[u] = (WGRAD || k_last + kc < Kd) ? b_vo[u] : b_bytes;
+    }
   }
   // Load u of the token rows of the stage starting at k0.
   auto load_a = [&](int u, int k0, u32x4_t* As) {
     lds_load16(ra, k0 >= k_last ? a_vl[u] : a_vo[u], (kb + min(k0, k_last)) * 2, As + (wid * A_IN + u) * 64);
   };
   auto load_b = [&](int u, int k0, u32x4_t* Bs) {
-    int mat;
-    (void)brow_col((wid * B_IN + u) * kRPI, &mat);  // the 8 rows of one instruction share a matrix
-    lds_load16((NMAT == 2 && mat) ? rb3 : rb1, k0 >= k_last ? b_vl[u] : b_vo[u], (kb + min(k0, k_last)) * 2,
-               Bs + (wid * B_IN + u) * 64);
+    if constexpr (BT) {
+      // rows k0 + (wid * B_IN + u) * RB .. of the reduction: all in B, all in
+      // B3 (Kd1 is a multiple of 8, RB <= 4) or all past Kd (zeros, no traffic)
+      const int kr = k0 + (wid * B_IN + u) * kBtRows<BN>;
+      const bool second = p.kb3 > 0 && kr >= Kd1;
+      // byte offsets below 2^32 (the matrix bytes are); passed on as the same 32 bits
+      const uint32_t soff = kr >= Kd ? bt_bytes : static_cast<uint32_t>(second ? kr - Kd1 : kr) * N * 2u;
+      lds_load16(second ? rb3 : rb1, b_vo[u], static_cast<int>(soff), Bs + (wid * B_IN + u) * 64);
+    } else {
+      int mat;
+      (void)brow_col((wid * B_IN + u) * kRPI, &mat);  // the 8 rows of one instruction share a matrix
+      lds_load16((NMAT == 2 && mat) ? rb3 : rb1, k0 >= k_last ? b_vl[u] : b_vo[u], (kb + min(k0, k_last)) * 2,
+                 Bs + (wid * B_IN + u) * 64);
+    }
   };
 
   f32x16_t acc[TN][TM];
@@ -327,6 +394,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 
   const int frow = lane % 32;
   const int fsub = lane / 32;  // which of the two 8-wide k chunks of a 16-k step
+  // k-major weight fragments: byte offset in the slot of this lane's first
+  // transposed read for fragment j (k-step 0)
+  int bt_off[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bt_off[j] = BT ? bt_lane_offset<BN>(lane, wn * WTN + j * 32) : 0;
 
   // 256 x 256 tiles on 8 waves (two per SIMD): a wave issuing its MFMA batch
   // runs at raised priority, so the SIMD's other wave does not take the issue
@@ -364,7 +436,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     auto read = [&](int ks) {
       const int c = ks * 2 + fsub;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) wf[ks][j] = as_bf16x8(Bs[swz(wn * WTN + j * 32 + frow, c)]);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (BT) {
+          wf[ks][j] = bt_fragment(Bs, bt_off[j] + ks * 16 * BN * 2, BN * 2);
+        } else {
+          wf[ks][j] = as_bf16x8(Bs[swz(wn * WTN + j * 32 + frow, c)]);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) xf[ks][i] = as_bf16x8(As[swz(wm * WTM + i * 32 + frow, c)]);
     };
@@ -887,14 +965,14 @@ __global__ __launch_bounds__(64) void gemm_slab_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------- launch
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false>
 hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   p.n_mt = MODE == G_WGRAD ? p.E * ((p.M + BM - 1) / BM) : (S + BM - 1) / BM + min(p.E, S);
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
   const size_t total = static_cast<size_t>(n_nt) * p.n_mt;
   const size_t grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE, BT>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
 }
@@ -912,7 +990,7 @@ hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
 // on the first GEMM; on the second 5 % faster than 128 x 128 tiles at two
 // blocks per CU). Small grids fall back to 128 x 128 so that the chip is
 // still covered.
-template <int MODE>
+template <int MODE, bool BT = false>
 hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
   constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_SWIGLU_Z || MODE == G1_GELU_Z);
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
@@ -921,11 +999,11 @@ hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
     return static_cast<long>((S + bm - 1) / bm + min(p.E, S)) * ((p.N + bn / NMAT - 1) / (bn / NMAT));
   };
   if (mean_rows >= 512 && blocks(256, 256) >= 2 * 256) {
-    return (G1 || MODE == G2_OPERM || MODE == G2_FUSED_Y) ? launch_tile<256, 256, 4, 2, MODE>(p, S, st)
-                                                          : launch_tile<256, 256, 2, 2, MODE>(p, S, st);
+    return (G1 || MODE == G2_OPERM || MODE == G2_FUSED_Y) ? launch_tile<256, 256, 4, 2, MODE, BT>(p, S, st)
+                                                          : launch_tile<256, 256, 2, 2, MODE, BT>(p, S, st);
   }
-  if (blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, 4, 2, MODE>(p, S, st);
-  return launch_tile<128, 128, 2, 2, MODE>(p, S, st);
+  if (blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, 4, 2, MODE, BT>(p, S, st);
+  return launch_tile<128, 128, 2, 2, MODE, BT>(p, S, st);
 }
 
 // Waves of the slab kernel: as many as fit (LDS ring and registers allow
@@ -1034,25 +1112,26 @@ hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, void* a, hipStream_t st)
   return f.act == 1 ? launch_tile_auto<G1_SWIGLU_Z>(p, f.S, st) : launch_tile_auto<G1_GELU_Z>(p, f.S, st);
 }
 
-hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets, int cap, int E, const void* B,
-                                   const void* bias, int N, int Kd, float* out, hipStream_t st) {
+hipError_t launch_bwd_dx_bf16(const void* dZ, int S, const int32_t* offsets, int cap, int E, const void* W1,
+                              const void* W3, int N, int Kd1, float* out, hipStream_t st) {
   GemmParams p{};
-  p.x = static_cast<const bf16_t*>(x);
-  p.bias = static_cast<const bf16_t*>(bias);
+  p.x = static_cast<const bf16_t*>(dZ);
   p.x_nrows = S;
   p.cap = cap;
   p.offsets = offsets;
-  p.B = static_cast<const bf16_t*>(B);
+  p.B = static_cast<const bf16_t*>(W1);
+  p.B3 = static_cast<const bf16_t*>(W3);
+  p.kb3 = W3 != nullptr ? Kd1 : 0;
   p.out = out;
   p.E = E;
   p.N = N;
-  p.Kd = Kd;
+  p.Kd = W3 != nullptr ? 2 * Kd1 : Kd1;
   p.S = S;
-  return launch_tile_auto<G2_OPERM>(p, S, st);
+  return launch_tile_auto<G2_OPERM, true>(p, S, st);
 }
 
 hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, int S, const int32_t* offsets,
-                              int cap, int E, const void* W2T, int N, int Kd, const void* z, int act,
+                              int cap, int E, const void* W2, int N, int Kd, const void* z, int act,
                               const float* rgate, const void* a, float* dgp, void* dZ, hipStream_t st) {
   GemmParams p{};
   p.x = static_cast<const bf16_t*>(dy);
@@ -1060,7 +1139,7 @@ hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, 
   p.x_nrows = T;
   p.cap = cap;
   p.offsets = offsets;
-  p.B = static_cast<const bf16_t*>(W2T);
+  p.B = static_cast<const bf16_t*>(W2);
   p.zin = static_cast<const bf16_t*>(z);
   p.rgate = rgate;
   p.ain = static_cast<const bf16_t*>(a);
@@ -1070,7 +1149,7 @@ hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, 
   p.N = N;
   p.Kd = Kd;
   p.S = S;
-  return act == 1 ? launch_tile_auto<G2_DZ_SWIGLU>(p, S, st) : launch_tile_auto<G2_DZ_GELU>(p, S, st);
+  return act == 1 ? launch_tile_auto<G2_DZ_SWIGLU, true>(p, S, st) : launch_tile_auto<G2_DZ_GELU, true>(p, S, st);
 }
 
 hipError_t launch_bwd_wgrad_bf16(const void* A, int M, const void* B, int N, int ldk, const int32_t* kofs, int E,

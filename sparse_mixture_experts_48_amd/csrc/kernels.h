@@ -102,15 +102,18 @@ hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, void* a, hipStream_t st)
 // For the grouped rows s (dy rows read through slot_token): u = dy W2, dA = rgate[s] u,
 // dZ = dA * act'(z) (z as written by launch_bwd_z_bf16; dZ like z, bfloat16), and
 // dgp[c][s] = sum over the 64 columns 64c .. 64c+63 of a[s] u (the gate-gradient
-// terms; a [S][N] bfloat16). W2T stored [E][N = width][Kd = d]; dgp [ceil(N/64)][S].
+// terms; a [S][N] bfloat16). W2 as stored for the forward pass, [E][Kd = d][N = width]
+// (read with k as the row index); dgp [ceil(N/64)][S].
 constexpr int kDgpColsHost = 64;
 hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, int S, const int32_t* offsets,
-                              int cap, int E, const void* W2T, int N, int Kd, const void* z, int act,
+                              int cap, int E, const void* W2, int N, int Kd, const void* z, int act,
                               const float* rgate, const void* a, float* dgp, void* dZ, hipStream_t st);
-// out[s] = x[s] . B_e^T (+ bias_e) (float32) for the grouped rows s of every
-// expert e (the first cap of each group); B stored [E][N][Kd], bias [E][N] or null.
-hipError_t launch_bwd_grouped_bf16(const void* x, int S, const int32_t* offsets, int cap, int E, const void* B,
-                                   const void* bias, int N, int Kd, float* out, hipStream_t st);
+// dX[s] = dZ[s] . [W1_e; W3_e] (float32) for the grouped rows s of every expert e
+// (the first cap of each group): W1, W3 as stored for the forward pass,
+// [E][Kd1 = width][N = d], read with k as the row index; dZ rows of 2 Kd1
+// (SwiGLU, [dz1 | dz3]) or Kd1 (W3 null).
+hipError_t launch_bwd_dx_bf16(const void* dZ, int S, const int32_t* offsets, int cap, int E, const void* W1,
+                              const void* W3, int N, int Kd1, float* out, hipStream_t st);
 // Weight gradients: C_e[m][n] = sum over k in [kofs[e], kofs[e+1]) of A[m][k] B[n][k];
 // A [M][ldk], B [N][ldk] bfloat16, every range whole 64-k stages (zero padded);
 // rows m < split to out [E][split][N], the rest to out2 [E][M - split][N] (float32).
@@ -121,8 +124,6 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int S, int cap, int
 hipError_t launch_transpose_groups(const void* src, const int32_t* src_rows, int R, const int32_t* offsets,
                                    const int32_t* kofs, int E, int S, int cap, void* dst, int ldk,
                                    hipStream_t st);
-hipError_t launch_transpose_weights(const void* src, int E, int R, int C, void* dst, int ldd, int coff,
-                                    hipStream_t st);
 // Per routing slot: dO[s] = g dy[t] (bfloat16), rgate[s] = g, dyb = dy[t] . b2[e] (0 without b2).
 hipError_t launch_dout(const void* dy, const int32_t* token_slot, const int32_t* topk_idx, const float* gate,
                        const void* b2, int T, int d, int K, void* dO, float* rgate, float* dyb, bool bf16,
