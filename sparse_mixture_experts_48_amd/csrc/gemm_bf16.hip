@@ -517,7 +517,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // (wave-uniform choice, once per tile).
   if (wm * WTM < rows) {
     ring(std::true_type{});
-    if constexpr (kDefer) mfma_step(dwf, dxf);  // the last stage's last step
+    if constexpr (kDefer) {
+      if (nk > 0) mfma_step(dwf, dxf);  // the last stage's last step (none for an empty reduction)
+    }
   } else {
     ring(std::false_type{});
   }
