@@ -95,7 +95,7 @@ struct BwdPlan {
   int nwr;
   size_t blk_hist, blk_psum, blk_base, blk_z, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux,
       logits;
-  size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, aT, dOT, dZT, dl, wr_part;
+  size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, dl, wr_part;
   size_t u;  // float32 layers: dy W2 of the grouped rows
   size_t total;
 };
@@ -154,9 +154,6 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   p.dX = take(S * dd * 4);
   p.kofs = take((E + 1) * 4);
   p.xT = take(dd * ldk * 2);
-  p.aT = take(w * ldk * 2);
-  p.dOT = take(dd * ldk * 2);
-  p.dZT = take(Zw * ldk * 2);
   p.dl = take(static_cast<size_t>(d.T) * E * 4);
   p.wr_part = take(static_cast<size_t>(p.nwr) * dd * E * 4);
   p.total = off;
@@ -169,7 +166,7 @@ int check_bwd_desc(const moe_desc& d) {
   const int64_t S = d.T * d.K, Zw = d.act == MOE_ACT_SWIGLU ? 2 * d.width : d.width;
   const int64_t ldk = 64 * ((S + 63) / 64 + d.E);
   if (S > 0 && S > kMaxElems / Zw) return MOE_ERR_UNSUPPORTED;
-  if (ldk > kMaxElems / Zw || ldk > kMaxElems / d.d) return MOE_ERR_UNSUPPORTED;
+  if (ldk > kMaxElems / d.d) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -787,17 +784,16 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
                              st));
   if (bias_select) MOE_LAUNCH(MOE_K_ZERO, st, moe::launch_fill_zero(db_r, E * 4, st));
 
-  // weight gradients: sums over each expert's kept rows of transposed operands
+  // weight gradients: sums over each expert's kept grouped slots. dO, a and dZ
+  // are read as written, with the slots as rows; h, gathered through
+  // slot_token, is first transposed into [feature][slot] with every expert's
+  // slots padded to whole 64-k stages.
   void* xT = at<char>(ws, pl.xT);
-  void* aT = at<char>(ws, pl.aT);
-  void* dOT = at<char>(ws, pl.dOT);
-  void* dZT = at<char>(ws, pl.dZT);
   MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(h, slot_token, D, offsets, kofs, E_, S, cap, xT, ldk, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(a, nullptr, Wd, offsets, kofs, E_, S, cap, aT, ldk, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(dO, nullptr, D, offsets, kofs, E_, S, cap, dOT, ldk, st));
-  MOE_LAUNCH(MOE_K_BWD, st, moe::launch_transpose_groups(dZ, nullptr, Zw, offsets, kofs, E_, S, cap, dZT, ldk, st));
-  MOE_LAUNCH(MOE_K_WGRAD, st, moe::launch_bwd_wgrad_bf16(dOT, D, aT, Wd, ldk, kofs, E_, dW2, nullptr, D, st));
-  MOE_LAUNCH(MOE_K_WGRAD, st, moe::launch_bwd_wgrad_bf16(dZT, Zw, xT, D, ldk, kofs, E_, dW1, dW3, Wd, st));
+  MOE_LAUNCH(MOE_K_WGRAD, st,
+             moe::launch_bwd_wgrad_bf16(dO, D, a, true, Wd, ldk, kofs, offsets, S, cap, E_, dW2, nullptr, D, st));
+  MOE_LAUNCH(MOE_K_WGRAD, st,
+             moe::launch_bwd_wgrad_bf16(dZ, Zw, xT, false, D, ldk, kofs, offsets, S, cap, E_, dW1, dW3, Wd, st));
   if (db1 != nullptr)
     MOE_LAUNCH(MOE_K_BWD, st, moe::launch_group_colsum(dZ, Wd, offsets, E_, S, cap, db1, true, st));
   if (db2 != nullptr)

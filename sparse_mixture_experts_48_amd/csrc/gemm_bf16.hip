@@ -197,11 +197,18 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int BM, int BN, int WM, int WN, int MODE, bool BT = false>
+// BT: the weight operand stored with k as the row index (forward-style modes:
+// [E][Kd][N] per expert; G_WGRAD: [S][N], rows = grouped slots). XT (G_WGRAD
+// only): the x operand stored [S][M] with the grouped slots as rows; each
+// expert's reduction then runs over its own slots [beg, end) (expert_rows),
+// rows past end reading zeros.
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
-  static_assert(!BT || (NMAT == 1 && MODE != G_WGRAD), "k-major weights: single-matrix forward-style modes");
+  static_assert(!BT || NMAT == 1, "k-major weights: single-matrix modes");
+  static_assert(!XT || MODE == G_WGRAD, "k-major x: weight-gradient GEMMs");
+  static_assert(MODE != G_WGRAD || !BT || XT, "k-major weights of a weight-gradient GEMM need k-major x");
   constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_SWIGLU_Z || MODE == G1_GELU_Z);
   constexpr bool WGRAD = (MODE == G_WGRAD);
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -316,15 +323,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const int stride = WGRAD ? p.ldk : Kd;
   const int kb = WGRAD ? p.kofs[e] : 0;
   const int nk = WGRAD ? (p.kofs[e + 1] - kb) / kBK : (Kd + kBK - 1) / kBK;
+  // k-major weight-gradient operands: expert e's grouped slots (the same
+  // count of stages as its padded range kofs[e] .. kofs[e+1])
+  int kbeg = 0, kend = 0;
+  if constexpr (XT) expert_rows(p.offsets, e, p.S, p.cap, &kbeg, &kend);
   const int k_last = WGRAD ? (1 << 30) : (nk - 1) * kBK;  // first k of the last stage
-  const uint32_t a_bytes = static_cast<uint32_t>(WGRAD ? p.M : p.x_nrows) * static_cast<uint32_t>(stride) * 2u;
+  const uint32_t a_bytes = XT ? static_cast<uint32_t>(p.S) * static_cast<uint32_t>(p.M) * 2u
+                              : static_cast<uint32_t>(WGRAD ? p.M : p.x_nrows) * static_cast<uint32_t>(stride) * 2u;
   const uint32_t b_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(stride) * 2u;
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.x, a_bytes);
   // k-major weights: Kd1 rows of B per expert (then as many of B3)
   const int Kd1 = (BT && p.kb3 > 0) ? p.kb3 : Kd;
-  const uint32_t bt_bytes = static_cast<uint32_t>(Kd1) * static_cast<uint32_t>(N) * 2u;
+  const uint32_t bt_bytes = static_cast<uint32_t>(WGRAD ? p.S : Kd1) * static_cast<uint32_t>(N) * 2u;
   const __amdgpu_buffer_rsrc_t rb1 =
-      BT ? buffer_rsrc(p.B + static_cast<size_t>(e) * Kd1 * N, bt_bytes)
+      BT ? buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * Kd1 * N), bt_bytes)
          : buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * N * Kd), b_bytes);
   const __amdgpu_buffer_rsrc_t rb3 =
       (NMAT == 2) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * N * Kd, b_bytes)
@@ -333,12 +345,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   uint32_t a_vo[A_IN], a_vl[A_IN], b_vo[B_IN], b_vl[B_IN];
 #pragma unroll
   for (int u = 0; u < A_IN; ++u) {
-    const int r = (wid * A_IN + u) * kRPI + lane / kCH;
-    const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
-    const int s = row0 + min(r, rows - 1);
-    const int src_row = (p.x_rows != nullptr) ? p.x_rows[s] : s;
-    a_vo[u] = (static_cast<uint32_t>(src_row) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
-    a_vl[u] = (WGRAD || k_last + kc < Kd) ? a_vo[u] : a_bytes;
+    if constexpr (XT) {  // the slot layout of k-major weights, over the block's M columns
+      const int lr = lane / kBtCPR<BM>;
+      const int r = (wid * A_IN + u) * kBtRows<BM> + lr;
+      const int gc = (lane % kBtCPR<BM>) ^ bt_key(r);
+      const int m = min(row0 + gc * 8, p.M - 8);
+      a_vo[u] = (static_cast<uint32_t>(lr) * static_cast<uint32_t>(p.M) + static_cast<uint32_t>(m)) * 2u;
+      a_vl[u] = a_vo[u];
+    } else {
+      const int r = (wid * A_IN + u) * kRPI + lane / kCH;
+      const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
+      const int s = row0 + min(r, rows - 1);
+      const int src_row = (p.x_rows != nullptr) ? p.x_rows[s] : s;
+      a_vo[u] = (static_cast<uint32_t>(src_row) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
+      a_vl[u] = (WGRAD || k_last + kc < Kd) ? a_vo[u] : a_bytes;
+    }
   }
 #pragma unroll
   for (int u = 0; u < B_IN; ++u) {
@@ -363,12 +384,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       b_vl[u] = (WGRAD || k_last + kc < Kd) ? b_vo[u] : b_bytes;
     }
   }
+  // k-major slot rows: the lane's row kbeg + k0 + (first row of instruction
+  // u) + lane / CPR, zeros (an offset past the buffer) at or past kend
+  auto kmajor_off = [&](uint32_t vo, int rbase, int lr, uint32_t ld, uint32_t bytes) {
+    return kbeg + rbase + lr < kend ? vo + static_cast<uint32_t>(kbeg + rbase) * ld * 2u : bytes;
+  };
   // Load u of the token rows of the stage starting at k0.
   auto load_a = [&](int u, int k0, u32x4_t* As) {
-    lds_load16(ra, k0 >= k_last ? a_vl[u] : a_vo[u], (kb + min(k0, k_last)) * 2, As + (wid * A_IN + u) * 64);
+    if constexpr (XT) {
+      const int rbase = k0 + (wid * A_IN + u) * kBtRows<BM>;
+      lds_load16(ra, kmajor_off(a_vo[u], rbase, lane / kBtCPR<BM>, p.M, a_bytes), 0, As + (wid * A_IN + u) * 64);
+    } else {
+      lds_load16(ra, k0 >= k_last ? a_vl[u] : a_vo[u], (kb + min(k0, k_last)) * 2, As + (wid * A_IN + u) * 64);
+    }
   };
   auto load_b = [&](int u, int k0, u32x4_t* Bs) {
-    if constexpr (BT) {
+    if constexpr (BT && WGRAD) {
+      const int rbase = k0 + (wid * B_IN + u) * kBtRows<BN>;
+      lds_load16(rb1, kmajor_off(b_vo[u], rbase, lane / kBtCPR<BN>, N, bt_bytes), 0, Bs + (wid * B_IN + u) * 64);
+    } else if constexpr (BT) {
       // rows k0 + (wid * B_IN + u) * RB .. of the reduction: all in B, all in
       // B3 (Kd1 is a multiple of 8, RB <= 4) or all past Kd (zeros, no traffic)
       const int kr = k0 + (wid * B_IN + u) * kBtRows<BN>;
@@ -396,9 +430,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const int fsub = lane / 32;  // which of the two 8-wide k chunks of a 16-k step
   // k-major weight fragments: byte offset in the slot of this lane's first
   // transposed read for fragment j (k-step 0)
-  int bt_off[TN];
+  int bt_off[TN], xt_off[TM];
 #pragma unroll
   for (int j = 0; j < TN; ++j) bt_off[j] = BT ? bt_lane_offset<BN>(lane, wn * WTN + j * 32) : 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) xt_off[i] = XT ? bt_lane_offset<BM>(lane, wm * WTM + i * 32) : 0;
 
   // 256 x 256 tiles on 8 waves (two per SIMD): a wave issuing its MFMA batch
   // runs at raised priority, so the SIMD's other wave does not take the issue
@@ -444,7 +480,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
         }
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) xf[ks][i] = as_bf16x8(As[swz(wm * WTM + i * 32 + frow, c)]);
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (XT) {
+          xf[ks][i] = bt_fragment(As, xt_off[i] + ks * 16 * BM * 2, BM * 2);
+        } else {
+          xf[ks][i] = as_bf16x8(As[swz(wm * WTM + i * 32 + frow, c)]);
+        }
+      }
     };
     if constexpr (MF) {
       read(0);
@@ -967,14 +1009,14 @@ __global__ __launch_bounds__(64) void gemm_slab_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------- launch
 
-template <int BM, int BN, int WM, int WN, int MODE, bool BT = false>
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false>
 hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   p.n_mt = MODE == G_WGRAD ? p.E * ((p.M + BM - 1) / BM) : (S + BM - 1) / BM + min(p.E, S);
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
   const size_t total = static_cast<size_t>(n_nt) * p.n_mt;
   const size_t grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE, BT>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE, BT, XT>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
 }
@@ -1154,12 +1196,16 @@ hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, 
   return act == 1 ? launch_tile_auto<G2_DZ_SWIGLU, true>(p, S, st) : launch_tile_auto<G2_DZ_GELU, true>(p, S, st);
 }
 
-hipError_t launch_bwd_wgrad_bf16(const void* A, int M, const void* B, int N, int ldk, const int32_t* kofs, int E,
-                                 float* out, float* out2, int split, hipStream_t st) {
+hipError_t launch_bwd_wgrad_bf16(const void* X, int M, const void* B, bool b_kmajor, int N, int ldk,
+                                 const int32_t* kofs, const int32_t* offsets, int S, int cap, int E, float* out,
+                                 float* out2, int split, hipStream_t st) {
   GemmParams p{};
-  p.x = static_cast<const bf16_t*>(A);
+  p.x = static_cast<const bf16_t*>(X);
   p.B = static_cast<const bf16_t*>(B);
   p.kofs = kofs;
+  p.offsets = offsets;
+  p.S = S;
+  p.cap = cap;
   p.M = M;
   p.ldk = ldk;
   p.split = split;
@@ -1168,7 +1214,8 @@ hipError_t launch_bwd_wgrad_bf16(const void* A, int M, const void* B, int N, int
   p.E = E;
   p.N = N;
   p.Kd = ldk;
-  return launch_tile<256, 256, 4, 2, G_WGRAD>(p, 0, st);
+  return b_kmajor ? launch_tile<256, 256, 4, 2, G_WGRAD, true, true>(p, 0, st)
+                  : launch_tile<256, 256, 4, 2, G_WGRAD, false, true>(p, 0, st);
 }
 
 }  // namespace moe

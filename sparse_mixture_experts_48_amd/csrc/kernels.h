@@ -114,11 +114,15 @@ hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, 
 // (SwiGLU, [dz1 | dz3]) or Kd1 (W3 null).
 hipError_t launch_bwd_dx_bf16(const void* dZ, int S, const int32_t* offsets, int cap, int E, const void* W1,
                               const void* W3, int N, int Kd1, float* out, hipStream_t st);
-// Weight gradients: C_e[m][n] = sum over k in [kofs[e], kofs[e+1]) of A[m][k] B[n][k];
-// A [M][ldk], B [N][ldk] bfloat16, every range whole 64-k stages (zero padded);
-// rows m < split to out [E][split][N], the rest to out2 [E][M - split][N] (float32).
-hipError_t launch_bwd_wgrad_bf16(const void* A, int M, const void* B, int N, int ldk, const int32_t* kofs, int E,
-                                 float* out, float* out2, int split, hipStream_t st);
+// Weight gradients: C_e[m][n] = sum over expert e's kept grouped slots s of X[s][m] B[s][n]
+// (X [S][M] bfloat16, read with the slots as rows). B is either the same kind
+// of k-major matrix [S][N] (b_kmajor) or a transposed copy [N][ldk] in which
+// expert e's slots sit at columns kofs[e] .. kofs[e+1] (whole 64-k stages, zero
+// padded). Rows m < split to out [E][split][N], the rest to out2 [E][M - split][N]
+// (float32).
+hipError_t launch_bwd_wgrad_bf16(const void* X, int M, const void* B, bool b_kmajor, int N, int ldk,
+                                 const int32_t* kofs, const int32_t* offsets, int S, int cap, int E, float* out,
+                                 float* out2, int split, hipStream_t st);
 // Elementwise, transpose and reduction kernels of the backward pass (csrc/backward.hip).
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int S, int cap, int32_t* kofs, hipStream_t st);
 hipError_t launch_transpose_groups(const void* src, const int32_t* src_rows, int R, const int32_t* offsets,
