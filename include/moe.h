@@ -158,6 +158,12 @@ int moe_workspace_size(const moe_desc* desc, size_t* bytes);
  *      z_loss [1] (nullable): the router z-loss (arjunjaggi.com "Mixtral and
  *      the Open MoE Era": ST-MoE's penalty on large router logits), the mean
  *      over tokens of the squared log-sum-exp of the logits the softmax sees.
+ * A NaN score never wins the choice: a token with fewer than K scores that
+ * are not NaN gets id 0x7fffffff in its remaining slots, which are not
+ * counted and get no grouped row (moe_permute skips them; moe_forward's y then
+ * has nothing from them: 0 for a token with none left when K > 1 or with a
+ * capacity, unwritten for K = 1 without one); P, aux and the z-loss come out
+ * NaN. Memory-safe: no access depends on a score's value.
  * Returns a moe_status. */
 int moe_route(const moe_desc* desc, const void* h, const float* W_r, const float* b_r,
               int32_t* topk_idx, float* topk_gate, int32_t* expert_counts,

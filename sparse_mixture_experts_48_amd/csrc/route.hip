@@ -410,7 +410,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
           const float g = (gate_mode == 0) ? ec[j] / se : ec[j] / s;
           topk_idx[static_cast<size_t>(t) * K + j] = cidx[j];
           topk_gate[static_cast<size_t>(t) * K + j] = g;
-          atomicAdd(&hist_s[cidx[j]], 1);
+          // a token whose scores are NaN chooses no expert (id 0x7fffffff): not counted
+          if (static_cast<unsigned>(cidx[j]) < static_cast<unsigned>(E)) atomicAdd(&hist_s[cidx[j]], 1);
         }
       }
     }
@@ -623,9 +624,12 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < K) {
-      float bv = (!taken && lane < E) ? l : -INFINITY;
-      int bi = (!taken && lane < E) ? lane : 0x7fffffff;
-      float bg = (!taken && lane < E) ? lg : -INFINITY;
+      // a lane is a candidate if its score beats the empty choice (-inf, no
+      // expert): any score but NaN, as in the wide layout
+      const bool cand = !taken && lane < E && better(l, lane, -INFINITY, 0x7fffffff);
+      float bv = cand ? l : -INFINITY;
+      int bi = cand ? lane : 0x7fffffff;
+      float bg = cand ? lg : -INFINITY;
 #pragma unroll
       for (int off = 1; off < EP; off <<= 1) {
         const float ov = __shfl_xor(bv, off, EP);
@@ -670,7 +674,8 @@ __global__ __launch_bounds__(NW * 64) void route_narrow_kernel(
         const float g = (gate_mode == 0) ? ec[j] / se : ec[j] / s;
         topk_idx[static_cast<size_t>(t) * K + j] = cidx[j];
         topk_gate[static_cast<size_t>(t) * K + j] = g;
-        atomicAdd(&hist_s[cidx[j]], 1);
+        // a token whose scores are NaN chooses no expert (id 0x7fffffff): not counted
+        if (static_cast<unsigned>(cidx[j]) < static_cast<unsigned>(E)) atomicAdd(&hist_s[cidx[j]], 1);
       }
     }
   }
