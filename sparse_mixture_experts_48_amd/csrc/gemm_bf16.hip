@@ -581,8 +581,97 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int b = 0; b < NDB; ++b) dgs[i][b] = 0.0f;
+  if constexpr (DZ) {
+    // Per column tile j: every load of its rows and column groups is issued
+    // first (rows and columns past the tile's end clamped into it, so no load
+    // sits behind a branch), then the math and the stores. Loads placed after
+    // a store would wait for it (the output may alias them as far as the
+    // compiler knows), which made every group of four columns two round trips.
+    constexpr int ZR = MODE == G2_DZ_SWIGLU ? 2 : 1;  // z row length in units of N
 #pragma unroll
-  for (int j = 0; j < TNO; ++j)
+    for (int j = 0; j < TNO; ++j) {
+      u32x2_t ap[TM][4], z1p[TM][4], z3p[TM][4];
+      float gsv[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int s = row0 + min(wm * WTM + i * 32 + (lane % 32), rows - 1);
+        gsv[i] = p.rgate[s];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = min(n0 + wn * WTN + j * 32 + g * 8 + (lane / 32) * 4, N - 4);
+          ap[i][g] = *reinterpret_cast<const u32x2_t*>(p.ain + static_cast<size_t>(s) * N + n);
+          const bf16_t* zr = p.zin + static_cast<size_t>(s) * ZR * N;
+          z1p[i][g] = *reinterpret_cast<const u32x2_t*>(zr + n);
+          if constexpr (ZR == 2) z3p[i][g] = *reinterpret_cast<const u32x2_t*>(zr + N + n);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int rl = wm * WTM + i * 32 + (lane % 32);
+        if (rl >= rows) continue;
+        const int s = row0 + rl;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WTN + j * 32 + g * 8 + (lane / 32) * 4;
+          if (n >= N) continue;  // N % 8 == 0: four columns are all in or all out
+          // v = u: gate-gradient terms a u, then dA = g u
+          float v[4];
+          const uint32_t aw[2] = {ap[i][g][0], ap[i][g][1]};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] = acc[j][i][g * 4 + q];
+            const float av = __uint_as_float(q % 2 ? (aw[q / 2] & 0xFFFF0000u) : (aw[q / 2] << 16));
+            dgs[i][(j * 32) / kDgpCols] = fmaf(av, v[q], dgs[i][(j * 32) / kDgpCols]);
+            v[q] *= gsv[i];
+          }
+          const uint32_t z1w[2] = {z1p[i][g][0], z1p[i][g][1]};
+          if constexpr (MODE == G2_DZ_SWIGLU) {  // dz1 = dA z3 silu'(z1), dz3 = dA silu(z1)
+            const uint32_t z3w[2] = {z3p[i][g][0], z3p[i][g][1]};
+            float d1[4], d3[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t a1 = z1w[q / 2], a3 = z3w[q / 2];
+              const float z1 = __uint_as_float(q % 2 ? (a1 & 0xFFFF0000u) : (a1 << 16));
+              const float z3 = __uint_as_float(q % 2 ? (a3 & 0xFFFF0000u) : (a3 << 16));
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1 * -1.4426950408889634f));
+              d1[q] = v[q] * z3 * (sg * (1.0f + z1 * (1.0f - sg)));
+              d3[q] = v[q] * (z1 * sg);
+            }
+            bf16_t* orow = static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * 2 * N;
+            *reinterpret_cast<u32x2_t*>(orow + n) = u32x2_t{pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3])};
+            *reinterpret_cast<u32x2_t*>(orow + N + n) =
+                u32x2_t{pack_bf16x2(d3[0], d3[1]), pack_bf16x2(d3[2], d3[3])};
+          } else {  // dz = dA gelu'(z)
+            float dz[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t a = z1w[q / 2];
+              const float x = __uint_as_float(q % 2 ? (a & 0xFFFF0000u) : (a << 16));
+              const float gp = 0.5f * (1.0f + erff(x * 0.70710678118654752440f)) +
+                               x * expf(-0.5f * x * x) * 0.39894228040143267794f;
+              dz[q] = v[q] * gp;
+            }
+            *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n) =
+                u32x2_t{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
+          }
+        }
+      }
+    }
+  }
+  // K = 1 gated scatter: each row's token and gate, loaded once per row
+  // (not once per column group, where each would wait for the stores before it)
+  int fy_t[TM];
+  float fy_g[TM];
+  if constexpr (MODE == G2_FUSED_Y) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int s = row0 + min(wm * WTM + i * 32 + (lane % 32), rows - 1);
+      fy_t[i] = p.slot_token[s];
+      fy_g[i] = p.gate[fy_t[i]];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < (DZ ? 0 : TNO); ++j)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rl = wm * WTM + i * 32 + (lane % 32);
@@ -619,17 +708,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
             if (p.bias != nullptr) v[q] += bf16_to_f32(p.bias[static_cast<size_t>(e) * N + n + q]);
           }
         }
-        if constexpr (DZ) {  // v = u: gate-gradient terms a u, then dA = g u
-          const u32x2_t ap = *reinterpret_cast<const u32x2_t*>(p.ain + static_cast<size_t>(s) * N + n);
-          const uint32_t aw[2] = {ap[0], ap[1]};
-          const float gs = p.rgate[s];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float av = __uint_as_float(q % 2 ? (aw[q / 2] & 0xFFFF0000u) : (aw[q / 2] << 16));
-            dgs[i][(j * 32) / kDgpCols] = fmaf(av, v[q], dgs[i][(j * 32) / kDgpCols]);
-            v[q] *= gs;
-          }
-        }
         if (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_GELU_Z) {
           *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n) =
               u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -638,38 +716,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
                 u32x2_t{pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
                         pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
           }
-        } else if (MODE == G2_DZ_SWIGLU) {  // v = dA; dz1 = dA z3 silu'(z1), dz3 = dA silu(z1)
-          const bf16_t* zr = p.zin + static_cast<size_t>(s) * 2 * N;
-          const u32x2_t z1p = *reinterpret_cast<const u32x2_t*>(zr + n);
-          const u32x2_t z3p = *reinterpret_cast<const u32x2_t*>(zr + N + n);
-          const uint32_t z1w[2] = {z1p[0], z1p[1]}, z3w[2] = {z3p[0], z3p[1]};
-          float d1[4], d3[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t a1 = z1w[q / 2], a3 = z3w[q / 2];
-            const float z1 = __uint_as_float(q % 2 ? (a1 & 0xFFFF0000u) : (a1 << 16));
-            const float z3 = __uint_as_float(q % 2 ? (a3 & 0xFFFF0000u) : (a3 << 16));
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z1 * -1.4426950408889634f));
-            d1[q] = v[q] * z3 * (sg * (1.0f + z1 * (1.0f - sg)));
-            d3[q] = v[q] * (z1 * sg);
-          }
-          bf16_t* orow = static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * 2 * N;
-          *reinterpret_cast<u32x2_t*>(orow + n) = u32x2_t{pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3])};
-          *reinterpret_cast<u32x2_t*>(orow + N + n) = u32x2_t{pack_bf16x2(d3[0], d3[1]), pack_bf16x2(d3[2], d3[3])};
-        } else if (MODE == G2_DZ_GELU) {  // dz = dA gelu'(z)
-          const u32x2_t zp = *reinterpret_cast<const u32x2_t*>(p.zin + static_cast<size_t>(s) * N + n);
-          const uint32_t zw[2] = {zp[0], zp[1]};
-          float dz[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t a = zw[q / 2];
-            const float x = __uint_as_float(q % 2 ? (a & 0xFFFF0000u) : (a << 16));
-            const float gp = 0.5f * (1.0f + erff(x * 0.70710678118654752440f)) +
-                             x * expf(-0.5f * x * x) * 0.39894228040143267794f;
-            dz[q] = v[q] * gp;
-          }
-          *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(s) * N + n) =
-              u32x2_t{pack_bf16x2(dz[0], dz[1]), pack_bf16x2(dz[2], dz[3])};
         } else if (MODE == G_WGRAD) {
           float* dst = s < p.split
                            ? static_cast<float*>(p.out) + (static_cast<size_t>(e) * p.split + s) * N + n
@@ -679,8 +725,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
           *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + static_cast<size_t>(s) * N + n) =
               f32x4_t{v[0], v[1], v[2], v[3]};
         } else {
-          const int t = p.slot_token[s];
-          const float gt = p.gate[t];
+          const int t = fy_t[i];
+          const float gt = fy_g[i];
           *reinterpret_cast<u32x2_t*>(static_cast<bf16_t*>(p.out) + static_cast<size_t>(t) * N + n) =
               u32x2_t{pack_bf16x2(gt * v[0], gt * v[1]), pack_bf16x2(gt * v[2], gt * v[3])};
         }
