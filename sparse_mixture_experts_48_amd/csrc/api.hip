@@ -292,7 +292,6 @@ int enqueue_forward(const moe_desc& d, const Plan& pl, const void* h, const floa
   float* topk_gate = at<float>(ws, pl.topk_gate);
   int32_t* blk_hist = at<int32_t>(ws, pl.blk_hist);
   float* blk_psum = at<float>(ws, pl.blk_psum);
-  int32_t* blk_base = at<int32_t>(ws, pl.blk_base);
   int32_t* offsets = at<int32_t>(ws, pl.offsets);
   int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
   int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
@@ -306,7 +305,7 @@ int enqueue_forward(const moe_desc& d, const Plan& pl, const void* h, const floa
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
   const size_t row_bytes = static_cast<size_t>(d.d) * (bf16 ? 2 : 4);
   const int cap = cap_of(d);
-  if (moe::permute_one_block(pl.rt)) {  // up to 256 tokens: statistics and grouping in one launch
+  {  // statistics and grouping in one launch
     moe::FinArgs fin;
     fin.blk_hist = blk_hist;
     fin.blk_psum = blk_psum;
@@ -319,13 +318,6 @@ int enqueue_forward(const moe_desc& d, const Plan& pl, const void* h, const floa
     MOE_LAUNCH(MOE_K_PERMUTE, st,
                moe::launch_finalize_permute(fin, topk_idx, T, E, K, cap, pl.rt, h, row_bytes, nullptr, slot_token,
                                             token_slot, st));
-  } else {
-    MOE_LAUNCH(MOE_K_FINALIZE, st,
-               moe::launch_finalize(blk_hist, blk_psum, ra.blk_z, pl.rt.NB, T, E, K, blk_base, counts, offsets,
-                                    nullptr, aux_loss, z_loss, st));
-    MOE_LAUNCH(MOE_K_PERMUTE, st,
-               moe::launch_permute(topk_idx, blk_base, offsets, T, E, K, cap, pl.rt, h, row_bytes, nullptr,
-                                   slot_token, token_slot, st));
   }
   // GEMM1 reads the rows of h through slot_token: the grouped copy of h is never written.
   moe::FfnArgs f{};
@@ -708,7 +700,6 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   float* topk_gate = at<float>(ws, pl.topk_gate);
   int32_t* blk_hist = at<int32_t>(ws, pl.blk_hist);
   float* blk_psum = at<float>(ws, pl.blk_psum);
-  int32_t* blk_base = at<int32_t>(ws, pl.blk_base);
   int32_t* offsets = at<int32_t>(ws, pl.offsets);
   int32_t* slot_token = at<int32_t>(ws, pl.slot_token);
   int32_t* token_slot = at<int32_t>(ws, pl.token_slot);
@@ -722,12 +713,16 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   ra.noise = noise;
   const bool bf16 = d.dtype == MOE_BF16;
   MOE_LAUNCH(MOE_K_ROUTE, st, moe::launch_route(ra, pl.rt, bf16, st));
-  MOE_LAUNCH(MOE_K_FINALIZE, st,
-             moe::launch_finalize(blk_hist, blk_psum, nullptr, pl.rt.NB, T, E_, K, blk_base, counts, offsets, nullptr,
-                                  at<float>(ws, pl.aux), nullptr, st));
+  moe::FinArgs fin;
+  fin.blk_hist = blk_hist;
+  fin.blk_psum = blk_psum;
+  fin.NB = pl.rt.NB;
+  fin.counts = counts;
+  fin.offsets = offsets;
+  fin.aux = at<float>(ws, pl.aux);
   MOE_LAUNCH(MOE_K_PERMUTE, st,
-             moe::launch_permute(topk_idx, blk_base, offsets, T, E_, K, cap, pl.rt, h, dd * (bf16 ? 2 : 4), nullptr,
-                                 slot_token, token_slot, st));
+             moe::launch_finalize_permute(fin, topk_idx, T, E_, K, cap, pl.rt, h, dd * (bf16 ? 2 : 4), nullptr,
+                                          slot_token, token_slot, st));
   if (d.dtype == MOE_F32)
     return backward_f32(d, pl, h, W_r, b_r, W1, b1, W3, W2, b2, dy, daux, dz, dh, dW_r, db_r, dW1, db1, dW3, dW2, db2,
                         ws, st);

@@ -63,10 +63,9 @@ struct FinArgs {
 hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, const int32_t* offsets, int T,
                           int E, int K, int cap, const RouteTiling& rt, const void* h, size_t row_bytes,
                           void* h_perm, int32_t* slot_token, int32_t* token_slot, hipStream_t st);
-// True when the grouping of a router tiling is a single block (at most 256 tokens).
-bool permute_one_block(const RouteTiling& rt);
-// That single block forms the statistics first (bit for bit as launch_finalize,
-// without the per-block bases) and then groups: one launch instead of two.
+// Statistics and grouping in one launch: every grouping block forms the
+// statistics (bit for bit as launch_finalize; block 0 writes them) and its own
+// base rows, then groups.
 hipError_t launch_finalize_permute(const FinArgs& fin, const int32_t* topk_idx, int T, int E, int K, int cap,
                                    const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
                                    int32_t* slot_token, int32_t* token_slot, hipStream_t st);

@@ -26,10 +26,12 @@ namespace {
 constexpr int kPermThreads = 256;  // 4 waves x 64 tokens
 constexpr int kMaxK = 8;
 
-// FUSED: the only grouping block (the batch fits one block) first forms the
-// router statistics itself, as the finalize kernel would, with kFinThreads
-// threads; its base rows are then the offsets. Threads past kPermThreads
-// take part in the statistics and in every barrier, and group nothing.
+// FUSED: every grouping block first forms the router statistics itself, as
+// the finalize kernel would (the same function, so the same bits), with
+// kFinThreads threads; block 0 writes them. Its base row for expert e is then
+// offsets[e] plus the slots of e in the router blocks before its own, summed
+// over those blocks' histograms. Threads past kPermThreads take part in the
+// statistics and in every barrier, and group nothing.
 template <bool FUSED>
 __global__ __launch_bounds__(FUSED ? kFinThreads : kPermThreads) void permute_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_base,
@@ -41,9 +43,35 @@ __global__ __launch_bounds__(FUSED ? kFinThreads : kPermThreads) void permute_ke
   __shared__ int base_s[64];
   __shared__ int off_s[65];
   if constexpr (FUSED) {
-    finalize_block(fin.blk_hist, fin.blk_psum, fin.blk_z, fin.NB, T, E, K, nullptr, fin.counts, fin.offsets,
-                   fin.prob_mean, fin.aux, fin.z_loss, off_s);
-    if (threadIdx.x < E) base_s[threadIdx.x] = off_s[threadIdx.x];
+    const bool first = blockIdx.x == 0;
+    finalize_block(fin.blk_hist, fin.blk_psum, fin.blk_z, fin.NB, T, E, K, nullptr, first ? fin.counts : nullptr,
+                   first ? fin.offsets : nullptr, first ? fin.prob_mean : nullptr, first ? fin.aux : nullptr,
+                   first ? fin.z_loss : nullptr, off_s);
+    // slots of each expert in router blocks 0 .. blockIdx.x * M - 1: kFinParts
+    // parts of those blocks, one expert per lane, added in part order
+    __shared__ int pre_s[kFinParts][64];
+    const int e = threadIdx.x % 64, part = threadIdx.x / 64;
+    const int nb = min(fin.NB, static_cast<int>(blockIdx.x) * M);
+    const int per = (nb + kFinParts - 1) / kFinParts;
+    const int b0 = min(nb, part * per), b1 = min(nb, b0 + per);
+    int c = 0;
+    if (e < E) {
+      constexpr int kU = 32;  // loads in flight together
+      for (int b = b0; b < b1; b += kU) {
+        int hv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) hv[u] = (b + u < b1) ? fin.blk_hist[static_cast<size_t>(b + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) c += hv[u];
+      }
+    }
+    pre_s[part][e] = c;
+    __syncthreads();
+    if (threadIdx.x < E) {
+      int base = off_s[threadIdx.x];
+      for (int q = 0; q < kFinParts; ++q) base += pre_s[q][threadIdx.x];
+      base_s[threadIdx.x] = base;
+    }
   } else {
     if (threadIdx.x < E) {  // one coalesced read instead of one read per expert below
       base_s[threadIdx.x] = blk_base[static_cast<size_t>(blockIdx.x) * M * E + threadIdx.x];
@@ -163,16 +191,13 @@ hipError_t launch_permute(const int32_t* topk_idx, const int32_t* blk_base, cons
   return hipGetLastError();
 }
 
-bool permute_one_block(const RouteTiling& rt) {
-  return rt.TB >= 1 && rt.TB <= kPermThreads && rt.NB <= kPermThreads / rt.TB;
-}
-
 hipError_t launch_finalize_permute(const FinArgs& fin, const int32_t* topk_idx, int T, int E, int K, int cap,
                                    const RouteTiling& rt, const void* h, size_t row_bytes, void* h_perm,
                                    int32_t* slot_token, int32_t* token_slot, hipStream_t st) {
-  if (!permute_one_block(rt) || fin.NB != rt.NB || fin.blk_hist == nullptr) return hipErrorInvalidValue;
-  const int M = kPermThreads / rt.TB;
-  hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(kFinThreads), 0, st, topk_idx, nullptr, nullptr, T, E,
+  if (rt.TB < 1 || rt.TB > kPermThreads || fin.NB != rt.NB || fin.blk_hist == nullptr) return hipErrorInvalidValue;
+  const int M = kPermThreads / rt.TB;  // router blocks per grouping block
+  const int nb = (rt.NB + M - 1) / M;
+  hipLaunchKernelGGL(permute_kernel<true>, dim3(nb), dim3(kFinThreads), 0, st, topk_idx, nullptr, nullptr, T, E,
                      K, cap, M * rt.TB, M, static_cast<const char*>(h), row_bytes, static_cast<char*>(h_perm),
                      slot_token, token_slot, fin);
   return hipGetLastError();
