@@ -1069,12 +1069,11 @@ hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
 
 // Tile shape from the mean rows per expert (S / E): with about 1k rows per
 // expert, 256 x 256 tiles (the fewest bytes moved per flop) on 8 waves, two per
-// SIMD, so that one wave's MFMAs run while the other waits. The backward's dZ
-// GEMM (derivative of the activation in the epilogue) runs them on 4 waves of
-// 128 x 128, which read a third fewer LDS bytes per MFMA and hold their
-// accumulators in the AGPRs (measured: 8 waves 5 % slower there; on the
-// forward second GEMM 4 waves were 5 % faster until the 8-wave kernel raised
-// its priority around the MFMAs, now 8 waves are 2 % faster). With about 100
+// SIMD, so that one wave's MFMAs run while the other waits (4 waves of
+// 128 x 128, which read a third fewer LDS bytes per MFMA, measured slower on
+// every GEMM once the 8-wave kernel raised its priority around the MFMAs and
+// the dZ GEMM's epilogue issued its loads ahead of its stores: dZ GEMM
+// 1.47 -> 1.37 ms on 8 waves). With about 100
 // rows per expert, 128 x 256 tiles on 8 waves with the weights two stages
 // ahead (measured on the Switch-style layer: 21 % faster than one stage ahead
 // on the first GEMM; on the second 5 % faster than 128 x 128 tiles at two
@@ -1089,8 +1088,7 @@ hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
     return static_cast<long>((S + bm - 1) / bm + min(p.E, S)) * ((p.N + bn / NMAT - 1) / (bn / NMAT));
   };
   if (mean_rows >= 512 && blocks(256, 256) >= 2 * 256) {
-    return (G1 || MODE == G2_OPERM || MODE == G2_FUSED_Y) ? launch_tile<256, 256, 4, 2, MODE, BT>(p, S, st)
-                                                          : launch_tile<256, 256, 2, 2, MODE, BT>(p, S, st);
+    return launch_tile<256, 256, 4, 2, MODE, BT>(p, S, st);
   }
   if (blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, 4, 2, MODE, BT>(p, S, st);
   return launch_tile<128, 128, 2, 2, MODE, BT>(p, S, st);
