@@ -670,6 +670,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       fy_g[i] = p.gate[fy_t[i]];
     }
   }
+  // The bias of every column group of the wave, loaded once, 8 bytes per group
+  // (four 2-byte loads per group, each after the stores before it, took most
+  // of a short reduction's tile).
+  constexpr bool BIAS = MODE == G1_GELU || MODE == G1_GELU_Z || MODE == G2_OPERM || MODE == G2_FUSED_Y;
+  const bool has_bias = BIAS && p.bias != nullptr;
+  u32x2_t bias4[BIAS ? TNO : 1][4];
+  if constexpr (BIAS) {
+    if (has_bias) {
+#pragma unroll
+      for (int j = 0; j < TNO; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = min(n0 + wn * (WTN / NMAT) + j * 32 + g * 8 + (lane / 32) * 4, N - 4);
+          bias4[j][g] = *reinterpret_cast<const u32x2_t*>(p.bias + static_cast<size_t>(e) * N + n);
+        }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < (DZ ? 0 : TNO); ++j)
 #pragma unroll
@@ -701,11 +718,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float v1 = acc[j][i][g * 4 + q];
-          if (MODE == G1_SWIGLU || MODE == G1_GELU) {
-            v[q] = epilogue_g1(MODE, v1, acc[NMAT == 2 ? j + TNO : j][i][g * 4 + q], p.bias, e, N, n + q);
+          float bq = 0.0f;
+          if constexpr (BIAS) {
+            const uint32_t w = bias4[j][g][q / 2];
+            bq = __uint_as_float(q % 2 ? (w & 0xFFFF0000u) : (w << 16));
+          }
+          if constexpr (MODE == G1_SWIGLU) {
+            v[q] = silu(v1) * acc[j + TNO][i][g * 4 + q];
+          } else if constexpr (MODE == G1_GELU) {
+            v[q] = gelu_exact(has_bias ? v1 + bq : v1);
           } else {
-            v[q] = v1;
-            if (p.bias != nullptr) v[q] += bf16_to_f32(p.bias[static_cast<size_t>(e) * N + n + q]);
+            v[q] = has_bias ? v1 + bq : v1;
           }
         }
         if (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_GELU_Z) {
