@@ -157,10 +157,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
 
   if (rl >= rows) return;
   const int srow = row0 + rl;
+  // Inputs of the epilogue loaded before its first store (a load placed after a
+  // store waits for it): the bias of the four column groups (columns past N
+  // clamped) and, for the K = 1 scatter, the row's token and gate.
+  const bool has_bias = (MODE == F_G1_GELU || MODE == F_Z || MODE == F_G2_OPERM || MODE == F_G2_FUSED_Y) &&
+                        p.bias != nullptr && !swiglu_z;
+  float4 bias4[4];
+  if (has_bias) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      bias4[g] = *reinterpret_cast<const float4*>(p.bias + static_cast<size_t>(e) * N +
+                                                  min(n0 + g * 8 + (lane / 32) * 4, N - 4));
+  }
+  int fy_t = 0;
+  float fy_g = 0.0f;
+  if constexpr (MODE == F_G2_FUSED_Y) {
+    fy_t = p.slot_token[srow];
+    fy_g = p.gate[fy_t];
+  }
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int n = n0 + g * 8 + (lane / 32) * 4;
     if (n >= N) continue;  // N is a multiple of 8: four columns are all in or all out
+    const float bq[4] = {has_bias ? bias4[g].x : 0.0f, has_bias ? bias4[g].y : 0.0f, has_bias ? bias4[g].z : 0.0f,
+                         has_bias ? bias4[g].w : 0.0f};
     float v[4], v3[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -173,7 +193,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
     } else if constexpr (MODE == F_G1_GELU) {
       float z[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) z[q] = gelu_exact(v[q] + (p.bias != nullptr ? p.bias[static_cast<size_t>(e) * N + n + q] : 0.0f));
+      for (int q = 0; q < 4; ++q) z[q] = gelu_exact(has_bias ? v[q] + bq[q] : v[q]);
       store4(static_cast<float*>(p.out) + static_cast<size_t>(srow) * N + n, z[0], z[1], z[2], z[3]);
     } else if constexpr (MODE == F_Z) {
       float* zrow = static_cast<float*>(p.out) + static_cast<size_t>(srow) * (swiglu_z ? 2 * N : N);
@@ -185,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
       } else {
         float z[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) z[q] = v[q] + (p.bias != nullptr ? p.bias[static_cast<size_t>(e) * N + n + q] : 0.0f);
+        for (int q = 0; q < 4; ++q) z[q] = has_bias ? v[q] + bq[q] : v[q];
         store4(zrow + n, z[0], z[1], z[2], z[3]);
         store4(arow + n, gelu_exact(z[0]), gelu_exact(z[1]), gelu_exact(z[2]), gelu_exact(z[3]));
       }
@@ -194,14 +214,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(F32Params p) {
     } else {
       float o[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = v[q] + (p.bias != nullptr ? p.bias[static_cast<size_t>(e) * N + n + q] : 0.0f);
+      for (int q = 0; q < 4; ++q) o[q] = has_bias ? v[q] + bq[q] : v[q];
       if constexpr (MODE == F_G2_OPERM) {
         store4(static_cast<float*>(p.out) + static_cast<size_t>(srow) * N + n, o[0], o[1], o[2], o[3]);
       } else {
-        const int t = p.slot_token[srow];
-        const float gt = p.gate[t];
-        store4(static_cast<float*>(p.out) + static_cast<size_t>(t) * N + n, gt * o[0], gt * o[1], gt * o[2],
-               gt * o[3]);
+        store4(static_cast<float*>(p.out) + static_cast<size_t>(fy_t) * N + n, fy_g * o[0], fy_g * o[1],
+               fy_g * o[2], fy_g * o[3]);
       }
     }
   }
