@@ -17,8 +17,13 @@
 // chains per logit instead of one quarter the dependent-latency floor of a
 // small batch and give a large batch four times the independent fmas.
 //
-// Two layouts of the same chains:
-//  * wide (E > 16 or T > 256): a thread owns one chain of TPT tokens x TE
+// Three layouts of the same chains:
+//  * broadcast (17..64 experts): 16 tokens x four chains per wave, 16 experts
+//    per wave; h and W_r go straight from memory to registers and each fma
+//    takes its W_r value from another lane through a DPP row broadcast (see
+//    route_bcast_kernel); its chain sums go through LDS to the wide layout's
+//    per-token epilogue.
+//  * wide (up to 16 experts, T > 256): a thread owns one chain of TPT tokens x TE
 //    experts and walks that chain's k upward; lanes are laid out as [token
 //    group][chain][expert lane], so the four chains of a logit sit LE = EP/TE
 //    lanes apart (two xor-butterflies form the sums, identical in all four)
@@ -44,7 +49,8 @@ constexpr int kRouteThreads = 256;
 
 // Wide layout per padded expert count: TE experts and TPT tokens per thread
 // (one chain of each), BK k per LDS stage. A token group takes 4 * EP / TE
-// lanes; a block holds kRouteThreads / (4 * EP / TE) * TPT tokens.
+// lanes; a block holds kRouteThreads / (4 * EP / TE) * TPT tokens. For 32 and
+// 64 experts only the epilogue's tiling is used (by the broadcast layout).
 template <int EP> struct WideCfg;
 template <> struct WideCfg<8> { static constexpr int TE = 2, TPT = 1, BK = 128; };
 template <> struct WideCfg<16> { static constexpr int TE = 4, TPT = 2, BK = 128; };
@@ -62,7 +68,12 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 // return zeros. The router's loads go through these, with no branch around
 // them, so that the compiler's wait counts keep several stages of loads in
 // flight (a load behind a branch makes it wait for every load before a use).
+// The range is uniform, but where the compiler forms it with a vector
+// instruction (a clamp becomes v_med3) the descriptor would sit in vector
+// registers and every load through it would loop over the lanes; reading the
+// first lane puts it in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t route_rsrc(const void* base, uint32_t bytes) {
+  bytes = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bytes)));
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
 }
@@ -105,6 +116,174 @@ template <> struct HVec<bf16_t> {
     }
   }
 };
+
+// What a router block hands on.
+struct RouteOut {
+  const float* br;
+  const float* noise;
+  int T, E, K, gate_mode, bias_select;
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* logits_out;
+  int32_t* blk_hist;
+  float* blk_psum;
+  float* blk_z;
+};
+
+// Per-token epilogue of the wide layouts. lsum[i][q] is the float32 sum
+// (c0 + c1) + (c2 + c3) of token t0 + tg + i * G, expert expert_of(q), held
+// alike by the four chain lanes cj of that token group (lanes with cj == 0
+// write). Forms the scores, the top-K and its gates, the softmax's column sums
+// and lse^2, and the block's histogram (hist_s, cleared before a barrier that
+// precedes this call), then writes the block's partials (has a barrier).
+template <int EP, int TE, int TPT, int LE, int G, typename ExpertOf>
+__device__ __forceinline__ void route_epilogue(const float (&lsum)[TPT][TE], int tg, int cj, int el, int t0,
+                                               ExpertOf expert_of, const RouteOut& o, float (*psum_s)[EP],
+                                               float* z_s, int* hist_s) {
+  const int tid = threadIdx.x;
+  const float* br = o.br;
+  const float* noise = o.noise;
+  const int T = o.T, E = o.E, K = o.K, gate_mode = o.gate_mode, bias_select = o.bias_select;
+  int32_t* topk_idx = o.topk_idx;
+  float* topk_gate = o.topk_gate;
+  float* logits_out = o.logits_out;
+  int32_t* blk_hist = o.blk_hist;
+  float* blk_psum = o.blk_psum;
+  float* blk_z = o.blk_z;
+  float psum_local[TE];
+#pragma unroll
+  for (int q = 0; q < TE; ++q) psum_local[q] = 0.0f;
+  float z_local = 0.0f;  // sum of lse^2 over this token group's tokens (z-loss)
+
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int t = t0 + tg + i * G;
+    const bool tok_ok = t < T;  // uniform across the lanes of this token group
+    // l: the score the choice is made on (logit + bias, + noise); lg: the
+    // logit of the softmax and the gates (l, or logit + noise when the bias
+    // only steers the choice)
+    float l[TE], lg[TE];
+#pragma unroll
+    for (int q = 0; q < TE; ++q) {
+      const int e = expert_of(q);
+      const float c0123 = lsum[i][q];
+      if (e < E) {
+        l[q] = c0123;
+        if (br != nullptr) l[q] = l[q] + br[e];
+        lg[q] = bias_select ? c0123 : l[q];
+        if (noise != nullptr && tok_ok) {
+          const float nz = noise[static_cast<size_t>(t) * E + e];
+          l[q] = l[q] + nz;
+          lg[q] = lg[q] + nz;
+        }
+      } else {
+        l[q] = -INFINITY;
+        lg[q] = -INFINITY;
+      }
+    }
+    if (tok_ok && cj == 0 && logits_out != nullptr) {
+#pragma unroll
+      for (int q = 0; q < TE; ++q) {
+        const int e = expert_of(q);
+        if (e < E) logits_out[static_cast<size_t>(t) * E + e] = l[q];
+      }
+    }
+    // top-K by (logit descending, expert ascending)
+    bool taken[TE];
+#pragma unroll
+    for (int q = 0; q < TE; ++q) taken[q] = false;
+    int cidx[8];
+    float cval[8], cg[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < K) {
+        float bv = -INFINITY, bg = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < TE; ++q) {
+          const int e = expert_of(q);
+          if (!taken[q] && e < E && better(l[q], e, bv, bi)) { bv = l[q]; bi = e; bg = lg[q]; }
+        }
+#pragma unroll
+        for (int off = 1; off < LE; off <<= 1) {
+          const float ov = __shfl_xor(bv, off, LE);
+          const int oi = __shfl_xor(bi, off, LE);
+          const float og = __shfl_xor(bg, off, LE);
+          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; bg = og; }
+        }
+        cidx[j] = bi;
+        cval[j] = bv;
+        cg[j] = bg;
+#pragma unroll
+        for (int q = 0; q < TE; ++q)
+          if (expert_of(q) == bi) taken[q] = true;
+      }
+    }
+    // softmax over all E (the largest lg is the first choice, unless the
+    // bias steers the choice)
+    float m = cval[0];
+    if (bias_select) {
+      m = lg[0];
+#pragma unroll
+      for (int q = 1; q < TE; ++q) m = fmaxf(m, lg[q]);
+#pragma unroll
+      for (int off = 1; off < LE; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, LE));
+    }
+    float ex[TE];
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < TE; ++q) {
+      ex[q] = (expert_of(q) < E) ? expf(lg[q] - m) : 0.0f;
+      s += ex[q];
+    }
+#pragma unroll
+    for (int off = 1; off < LE; off <<= 1) s += __shfl_xor(s, off, LE);
+    if (tok_ok) {
+#pragma unroll
+      for (int q = 0; q < TE; ++q) psum_local[q] += ex[q] / s;
+      const float lse = m + logf(s);
+      z_local += lse * lse;
+    }
+    if (tok_ok && cj == 0 && el == 0) {
+      float ec[8];
+      float se = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < K) {
+          ec[j] = expf(cg[j] - m);
+          se += ec[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < K) {
+          const float g = (gate_mode == 0) ? ec[j] / se : ec[j] / s;
+          topk_idx[static_cast<size_t>(t) * K + j] = cidx[j];
+          topk_gate[static_cast<size_t>(t) * K + j] = g;
+          // a token whose scores are NaN chooses no expert (id 0x7fffffff): not counted
+          if (static_cast<unsigned>(cidx[j]) < static_cast<unsigned>(E)) atomicAdd(&hist_s[cidx[j]], 1);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int q = 0; q < TE; ++q)
+    if (cj == 0) psum_s[tg][expert_of(q)] = psum_local[q];
+  if (cj == 0 && el == 0) z_s[tg] = z_local;
+  __syncthreads();
+  if (tid < E) {
+    float s = 0.0f;
+    for (int g = 0; g < G; ++g) s += psum_s[g][tid];
+    blk_psum[static_cast<size_t>(blockIdx.x) * E + tid] = s;
+    blk_hist[static_cast<size_t>(blockIdx.x) * E + tid] = hist_s[tid];
+  }
+  if (tid == 0 && blk_z != nullptr) {
+    float z = 0.0f;
+    for (int g = 0; g < G; ++g) z += z_s[g];  // fixed order
+    blk_z[blockIdx.x] = z;
+  }
+}
 
 // EP: experts padded to a power of two; TE experts and TPT tokens per thread;
 // BK: k values per LDS stage; NS: pipeline depth (NS - 1 stages of global
@@ -298,141 +477,199 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
     }
   }
 
-  float psum_local[TE];
+  // (c0 + c1) + (c2 + c3): every chain's lane ends with the same sums
+  float lsum[TPT][TE];
 #pragma unroll
-  for (int q = 0; q < TE; ++q) psum_local[q] = 0.0f;
-  float z_local = 0.0f;  // sum of lse^2 over this token group's tokens (z-loss)
-
-#pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int t = t0 + tg + i * G;
-    const bool tok_ok = t < T;  // uniform across the lanes of this token group
-    // l: the score the choice is made on (logit + bias, + noise); lg: the
-    // logit of the softmax and the gates (l, or logit + noise when the bias
-    // only steers the choice)
-    float l[TE], lg[TE];
+  for (int i = 0; i < TPT; ++i)
 #pragma unroll
     for (int q = 0; q < TE; ++q) {
-      const int e = expert_of(q);
-      // (c0 + c1) + (c2 + c3): every chain's lane ends with the same sums
       const float c01 = acc[i][q] + __shfl_xor(acc[i][q], LE);
-      const float c0123 = c01 + __shfl_xor(c01, 2 * LE);
-      if (e < E) {
-        l[q] = c0123;
-        if (br != nullptr) l[q] = l[q] + br[e];
-        lg[q] = bias_select ? c0123 : l[q];
-        if (noise != nullptr && tok_ok) {
-          const float nz = noise[static_cast<size_t>(t) * E + e];
-          l[q] = l[q] + nz;
-          lg[q] = lg[q] + nz;
-        }
-      } else {
-        l[q] = -INFINITY;
-        lg[q] = -INFINITY;
-      }
+      lsum[i][q] = c01 + __shfl_xor(c01, 2 * LE);
     }
-    if (tok_ok && cj == 0 && logits_out != nullptr) {
+  const RouteOut o{br, noise, T, E, K, gate_mode, bias_select, topk_idx, topk_gate, logits_out,
+                   blk_hist, blk_psum, blk_z};
+  route_epilogue<EP, TE, TPT, LE, G>(lsum, tg, cj, el, t0, expert_of, o, psum_s, z_s, hist_s);
+}
+
+// Broadcast layout (17..64 experts, any batch): no LDS stage for h or W_r.
+// A wave holds 16 tokens x the four chains x 16 experts: lane = 16 * chain +
+// token, and each lane keeps its chain of its token for 16 experts in
+// registers. Per round of 16 k (four k per chain) a lane loads its token's
+// four h values of its chain (one 8-byte load for bfloat16) and one float4 of
+// W_r: lane i of chain row j holds W_r[k][e0 + 4 (i % 4) + c] for k =
+// 16 m + 4 j + i / 4 in component c, so the 16 lanes of a row hold the 64
+// weights its chain needs in that round. Every fma takes its weight from the
+// lane that holds it through a DPP row broadcast on the fma's first operand
+// (v_fmac_f32_dpp row_newbcast): 64 fmas per round and lane with no LDS
+// traffic and no data movement instructions; the fma's rounding is the same
+// as fmaf's. The wave's chain sums go through LDS to the wide layout's
+// epilogue (same per-token work, same block partials, same bits).
+constexpr int kBcastRing = 4;  // rounds of loads in flight per wave
+
+// acc[4 q + c] += W(lane 4 s + q of the row, component c) * hk[s] for s, q, c
+// in ascending order: 64 fmas, each expert's four in ascending k. The leading
+// s_nop covers the DPP read-after-VALU-write hazards (two wait states after a
+// VALU write of the broadcast register, five after a VALU write of EXEC),
+// which the compiler does not see through an asm statement.
+#define MOE_FMAC_BC(a, w, h, l) "v_fmac_f32_dpp %" #a ", %" #w ", %" #h " row_newbcast:" #l " row_mask:0xf bank_mask:0xf\n"
+#define MOE_FMAC_BC_Q(a0, a1, a2, a3, h, l) \
+  MOE_FMAC_BC(a0, 16, h, l) MOE_FMAC_BC(a1, 17, h, l) MOE_FMAC_BC(a2, 18, h, l) MOE_FMAC_BC(a3, 19, h, l)
+#define MOE_FMAC_BC_S(h, l0, l1, l2, l3)                                                        \
+  MOE_FMAC_BC_Q(0, 1, 2, 3, h, l0) MOE_FMAC_BC_Q(4, 5, 6, 7, h, l1) MOE_FMAC_BC_Q(8, 9, 10, 11, h, l2) \
+  MOE_FMAC_BC_Q(12, 13, 14, 15, h, l3)
+__device__ __forceinline__ void bcast_round(float (&acc)[16], const float4& w, const float (&hk)[4]) {
+  asm("s_nop 4\n"
+      MOE_FMAC_BC_S(20, 0, 1, 2, 3) MOE_FMAC_BC_S(21, 4, 5, 6, 7) MOE_FMAC_BC_S(22, 8, 9, 10, 11)
+      MOE_FMAC_BC_S(23, 12, 13, 14, 15)
+      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
+        "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]), "+v"(acc[12]), "+v"(acc[13]),
+        "+v"(acc[14]), "+v"(acc[15])
+      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(hk[0]), "v"(hk[1]), "v"(hk[2]), "v"(hk[3]));
+}
+#undef MOE_FMAC_BC_S
+#undef MOE_FMAC_BC_Q
+#undef MOE_FMAC_BC
+
+// Four h values of one token and chain (k .. k + 3).
+template <typename Tin> struct HQuad;
+template <> struct HQuad<bf16_t> {
+  typedef uint2 raw;
+  __device__ __forceinline__ static raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), soff, 0);
+    return make_uint2(v.x, v.y);
+  }
+  __device__ __forceinline__ static void to_f32(const raw& x, float (&out)[4]) {
+    out[0] = __uint_as_float(x.x << 16);
+    out[1] = __uint_as_float(x.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(x.y << 16);
+    out[3] = __uint_as_float(x.y & 0xFFFF0000u);
+  }
+};
+template <> struct HQuad<float> {
+  typedef float4 raw;
+  __device__ __forceinline__ static raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), soff, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
+  __device__ __forceinline__ static void to_f32(const raw& x, float (&out)[4]) {
+    out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+  }
+};
+
+template <typename Tin, int EP>
+__global__ __launch_bounds__(kRouteThreads) void route_bcast_kernel(
+    const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
+    const float* __restrict__ noise, int T, int d, int E, int K, int gate_mode,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
+    int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, float* __restrict__ blk_z, int bias_select) {
+  constexpr int NEG = EP / 16;               // expert groups of 16 (one per wave)
+  constexpr int NTS = kRouteThreads / 64 / NEG;  // token sets of 16 per block
+  constexpr int TB = 16 * NTS;               // tokens per block
+  // epilogue layout: the wide layout's for EP experts
+  constexpr int TE = WideCfg<EP>::TE, TPT = WideCfg<EP>::TPT;
+  constexpr int LE = EP / TE, LG = 4 * LE, G = kRouteThreads / LG;
+  static_assert(NEG >= 2 && NEG * NTS * 64 == kRouteThreads, "waves tile the block's experts and tokens");
+  static_assert(G * TPT == TB && TE == 4, "the epilogue covers the block's tokens, four experts per lane");
+  constexpr int R = kBcastRing;
+
+  __shared__ __align__(16) float lg_s[TB][EP + 4];
+  __shared__ float psum_s[G][EP];
+  __shared__ float z_s[G];
+  __shared__ int hist_s[EP];
+
+  const int tid = threadIdx.x;
+  const int wid = tid / 64, lane = tid % 64;
+  const int j = lane / 16, i = lane % 16;  // chain, token of the set
+  const int eg = wid % NEG, ts = wid / NEG;
+  const int t0 = blockIdx.x * TB;
+  if (tid < EP) hist_s[tid] = 0;
+
+  // The block's token rows (rows past T read zeros) and all of W_r as buffers;
+  // the round offset is the scalar operand, which the range check includes.
+  const int rows = max(0, min(TB, T - t0));
+  const __amdgpu_buffer_rsrc_t hbuf =
+      route_rsrc(h + static_cast<size_t>(min(t0, max(T - 1, 0))) * d, static_cast<uint32_t>(rows) * d * sizeof(Tin));
+  const __amdgpu_buffer_rsrc_t wbuf = route_rsrc(Wr, static_cast<uint32_t>(d) * E * 4);
+  const uint32_t hoff = (static_cast<uint32_t>(ts * 16 + i) * d + 4 * j) * sizeof(Tin);
+  const uint32_t woff = (static_cast<uint32_t>(4 * j + i / 4) * E + eg * 16 + 4 * (i % 4)) * 4;
+  const int hstep = 16 * static_cast<int>(sizeof(Tin));
+  const int wstep = 16 * E * 4;
+
+  typename HQuad<Tin>::raw hr[R];
+  float4 wr[R];
+  // Round m into ring slot `slot`. Rounds past the end read zeros (W_r) or
+  // values that are never used.
+  auto load_round = [&](int m, int slot) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    hr[slot] = HQuad<Tin>::load(hbuf, hoff, m * hstep);
+    const u4 w = __builtin_amdgcn_raw_buffer_load_b128(wbuf, static_cast<int>(woff), m * wstep, 0);
+    wr[slot] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+  };
+  float acc[16];
 #pragma unroll
-      for (int q = 0; q < TE; ++q) {
-        const int e = expert_of(q);
-        if (e < E) logits_out[static_cast<size_t>(t) * E + e] = l[q];
-      }
+  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+  auto compute_round = [&](int slot, bool half) {
+    float hk[4];
+    HQuad<Tin>::to_f32(hr[slot], hk);
+    if (half && j >= 2) {
+      // last half round (d % 16 == 8): chains 2 and 3 have no k left; their
+      // h values belong to the next row, their W_r values read zeros
+#pragma unroll
+      for (int s = 0; s < 4; ++s) hk[s] = 0.0f;
     }
-    // top-K by (logit descending, expert ascending)
-    bool taken[TE];
+    bcast_round(acc, wr[slot], hk);
+  };
+
+  const int nm = d / 16;          // whole rounds of the four chains
+  const bool half = (d % 16) != 0;  // d % 8 == 0: then a half round, chains 0 and 1
 #pragma unroll
-    for (int q = 0; q < TE; ++q) taken[q] = false;
-    int cidx[8];
-    float cval[8], cg[8];
+  for (int r = 0; r < R; ++r) load_round(r, r);
+  int m0 = 0;
+  for (; m0 + R <= nm; m0 += R) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < K) {
-        float bv = -INFINITY, bg = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int q = 0; q < TE; ++q) {
-          const int e = expert_of(q);
-          if (!taken[q] && e < E && better(l[q], e, bv, bi)) { bv = l[q]; bi = e; bg = lg[q]; }
-        }
-#pragma unroll
-        for (int off = 1; off < LE; off <<= 1) {
-          const float ov = __shfl_xor(bv, off, LE);
-          const int oi = __shfl_xor(bi, off, LE);
-          const float og = __shfl_xor(bg, off, LE);
-          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; bg = og; }
-        }
-        cidx[j] = bi;
-        cval[j] = bv;
-        cg[j] = bg;
-#pragma unroll
-        for (int q = 0; q < TE; ++q)
-          if (expert_of(q) == bi) taken[q] = true;
-      }
+    for (int r = 0; r < R; ++r) {
+      compute_round(r, false);
+      load_round(m0 + r + R, r);
+      // keep the refill here: sunk to the end of the loop body, the whole
+      // ring would be reissued at once and drained at the next round 0
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // softmax over all E (the largest lg is the first choice, unless the
-    // bias steers the choice)
-    float m = cval[0];
-    if (bias_select) {
-      m = lg[0];
+  }
+  // fewer than R whole rounds and the half round: all already in their slots
 #pragma unroll
-      for (int q = 1; q < TE; ++q) m = fmaxf(m, lg[q]);
-#pragma unroll
-      for (int off = 1; off < LE; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, LE));
-    }
-    float ex[TE];
-    float s = 0.0f;
-#pragma unroll
-    for (int q = 0; q < TE; ++q) {
-      ex[q] = (expert_of(q) < E) ? expf(lg[q] - m) : 0.0f;
-      s += ex[q];
-    }
-#pragma unroll
-    for (int off = 1; off < LE; off <<= 1) s += __shfl_xor(s, off, LE);
-    if (tok_ok) {
-#pragma unroll
-      for (int q = 0; q < TE; ++q) psum_local[q] += ex[q] / s;
-      const float lse = m + logf(s);
-      z_local += lse * lse;
-    }
-    if (tok_ok && cj == 0 && el == 0) {
-      float ec[8];
-      float se = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < K) {
-          ec[j] = expf(cg[j] - m);
-          se += ec[j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < K) {
-          const float g = (gate_mode == 0) ? ec[j] / se : ec[j] / s;
-          topk_idx[static_cast<size_t>(t) * K + j] = cidx[j];
-          topk_gate[static_cast<size_t>(t) * K + j] = g;
-          // a token whose scores are NaN chooses no expert (id 0x7fffffff): not counted
-          if (static_cast<unsigned>(cidx[j]) < static_cast<unsigned>(E)) atomicAdd(&hist_s[cidx[j]], 1);
-        }
-      }
-    }
+  for (int r = 0; r < R; ++r) {
+    if (m0 + r < nm) compute_round(r, false);
+    else if (m0 + r == nm && half) compute_round(r, true);
   }
 
+  // (c0 + c1) + (c2 + c3) in chain row 0; to LDS for the epilogue
 #pragma unroll
-  for (int q = 0; q < TE; ++q)
-    if (cj == 0) psum_s[tg][expert_of(q)] = psum_local[q];
-  if (cj == 0 && el == 0) z_s[tg] = z_local;
+  for (int q = 0; q < 16; ++q) {
+    const float c01 = acc[q] + __shfl_xor(acc[q], 16);
+    acc[q] = c01 + __shfl_xor(c01, 32);
+  }
+  if (j == 0) {
+#pragma unroll
+    for (int q = 0; q < 16; q += 4)
+      *reinterpret_cast<float4*>(&lg_s[ts * 16 + i][eg * 16 + q]) =
+          make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
+  }
   __syncthreads();
-  if (tid < E) {
-    float s = 0.0f;
-    for (int g = 0; g < G; ++g) s += psum_s[g][tid];
-    blk_psum[static_cast<size_t>(blockIdx.x) * E + tid] = s;
-    blk_hist[static_cast<size_t>(blockIdx.x) * E + tid] = hist_s[tid];
+  const int tg = tid / LG;
+  const int cj = (tid % LG) / LE;
+  const int el = tid % LE;
+  auto expert_of = [&](int q) { return el * 4 + q; };  // TE == 4: experts 4 el .. 4 el + 3
+  float lsum[TPT][TE];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const float4 v = *reinterpret_cast<const float4*>(&lg_s[tg + u * G][el * 4]);
+    lsum[u][0] = v.x; lsum[u][1] = v.y; lsum[u][2] = v.z; lsum[u][3] = v.w;
   }
-  if (tid == 0 && blk_z != nullptr) {
-    float z = 0.0f;
-    for (int g = 0; g < G; ++g) z += z_s[g];  // fixed order
-    blk_z[blockIdx.x] = z;
-  }
+  const RouteOut o{br, noise, T, E, K, gate_mode, bias_select, topk_idx, topk_gate, logits_out,
+                   blk_hist, blk_psum, blk_z};
+  route_epilogue<EP, TE, TPT, LE, G>(lsum, tg, cj, el, t0, expert_of, o, psum_s, z_s, hist_s);
 }
 
 // Narrow layout: kNarrowNW waves per block, one token per wave; chunks of kNarrowKC k,
@@ -737,6 +974,14 @@ hipError_t launch_route_wide(const RouteArgs& a, const RouteTiling& rt, hipStrea
   return hipGetLastError();
 }
 
+template <typename Tin, int EP>
+hipError_t launch_route_bcast(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
+  hipLaunchKernelGGL((route_bcast_kernel<Tin, EP>), dim3(rt.NB), dim3(kRouteThreads), 0, st,
+                     static_cast<const Tin*>(a.h), a.Wr, a.br, a.noise, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
+                     a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.blk_z, a.bias_select);
+  return hipGetLastError();
+}
+
 template <typename Tin, int EP, int NW>
 hipError_t launch_route_narrow(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
   hipLaunchKernelGGL((route_narrow_kernel<Tin, EP, NW>), dim3(rt.NB), dim3(NW * 64), 0, st,
@@ -758,8 +1003,8 @@ hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStre
   switch (rt.EP) {  // wide layout: wide_tb<EP>() tokens x EP experts per block of 256 threads
     case 8: return launch_route_wide<Tin, 8, WideCfg<8>::TE, WideCfg<8>::TPT, WideCfg<8>::BK, 2>(a, rt, st);
     case 16: return launch_route_wide<Tin, 16, WideCfg<16>::TE, WideCfg<16>::TPT, WideCfg<16>::BK, 2>(a, rt, st);
-    case 32: return launch_route_wide<Tin, 32, WideCfg<32>::TE, WideCfg<32>::TPT, WideCfg<32>::BK, 2>(a, rt, st);
-    default: return launch_route_wide<Tin, 64, WideCfg<64>::TE, WideCfg<64>::TPT, WideCfg<64>::BK, 2>(a, rt, st);
+    case 32: return launch_route_bcast<Tin, 32>(a, rt, st);
+    default: return launch_route_bcast<Tin, 64>(a, rt, st);
   }
 }
 
@@ -767,19 +1012,18 @@ hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStre
 
 // Narrow layout for small batches of few experts (T <= 256, E <= 16), where the
 // wide layout leaves most compute units idle: one token per wave, 4 waves per
-// block. Otherwise the wide layout, 32 tokens per block.
+// block. Otherwise the wide layout (up to 16 experts) or the broadcast layout
+// (17..64), wide_tb<EP>() tokens per block.
 constexpr int64_t kNarrowMaxT = 256;
 
 RouteTiling route_tiling(int64_t T, int64_t E) {
   RouteTiling rt;
   rt.EP = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
   if (rt.EP <= 16 && T <= kNarrowMaxT) {
-    rt.TPT = 1;
     rt.NW = kNarrowNW;
     rt.TB = kNarrowNW;
   } else {
-    rt.TPT = rt.EP >= 32 ? 2 : 1;
-    rt.NW = 0;  // wide layout
+    rt.NW = 0;  // wide or broadcast layout
     rt.TB = rt.EP == 8 ? wide_tb<8>() : rt.EP == 16 ? wide_tb<16>() : rt.EP == 32 ? wide_tb<32>() : wide_tb<64>();
   }
   rt.NB = static_cast<int>((T + rt.TB - 1) / rt.TB);

@@ -59,6 +59,14 @@ SMALL = {
     "bf16_short_k": L("bf16_short_k", 300, 40, 4, 2, 48, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 28),
     "T1": L("T1", 1, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 26),
     "f32_T1": L("f32_T1", 1, 64, 8, 2, 64, W.ACT_GELU, W.GATE_RENORM, W.DT_F32, "normal2", 27),
+    # router layouts over 17..64 experts with float32 h, expert counts that are
+    # not a multiple of 4 (W_r rows then start off 16-byte boundaries) and d = 8
+    # mod 16 (a last round of k that only two of the four chains reach)
+    "f32_e37_k2_d136": L("f32_e37_k2_d136", 300, 136, 37, 2, 200, W.ACT_GELU, W.GATE_RENORM, W.DT_F32,
+                         "normal2", 34),
+    "f32_e20_k1_d72": L("f32_e20_k1_d72", 150, 72, 20, 1, 64, W.ACT_SWIGLU, W.GATE_RAW, W.DT_F32, "zipf1.1", 35),
+    "bf16_e57_k2_d200": L("bf16_e57_k2_d200", 260, 200, 57, 2, 128, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16,
+                          "normal2", 36),
     # ragged groups of small mean size with long reductions: many one-tile
     # experts beside a few many-tile ones
     "ragged_switch_k1": L("ragged_switch_k1", 600, 1024, 16, 1, 1024, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
