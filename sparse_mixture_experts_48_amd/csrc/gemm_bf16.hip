@@ -398,7 +398,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       lds_load16(ra, k0 >= k_last ? a_vl[u] : a_vo[u], (kb + min(k0, k_last)) * 2, As + (wid * A_IN + u) * 64);
     }
   };
-  auto load_b = [&](int u, int k0, u32x4_t* Bs) {
+  auto load_b = [&](auto nt, int u, int k0, u32x4_t* Bs) {
     if constexpr (BT && WGRAD) {
       const int rbase = k0 + (wid * B_IN + u) * kBtRows<BN>;
       lds_load16(rb1, kmajor_off(b_vo[u], rbase, lane / kBtCPR<BN>, N, bt_bytes), 0, Bs + (wid * B_IN + u) * 64);
@@ -413,8 +413,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     } else {
       int mat;
       (void)brow_col((wid * B_IN + u) * kRPI, &mat);  // the 8 rows of one instruction share a matrix
-      lds_load16((NMAT == 2 && mat) ? rb3 : rb1, k0 >= k_last ? b_vl[u] : b_vo[u], (kb + min(k0, k_last)) * 2,
-                 Bs + (wid * B_IN + u) * 64);
+      const uint32_t vo = k0 >= k_last ? b_vl[u] : b_vo[u];
+      const int so = (kb + min(k0, k_last)) * 2;
+      if constexpr (decltype(nt)::value) {  // weights read once: non-temporal
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((NMAT == 2 && mat) ? rb3 : rb1,
+                                                 (__attribute__((address_space(3))) void*)(Bs + (wid * B_IN + u) * 64),
+                                                 16, static_cast<int>(vo), so, 0, 2);
+      } else {
+        lds_load16((NMAT == 2 && mat) ? rb3 : rb1, vo, so, Bs + (wid * B_IN + u) * 64);
+      }
     }
   };
 
@@ -462,7 +469,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       for (int i = 0; i < TM; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[j], x[i], acc[j][i], 0, 0, 0);
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
   };
-  auto run_stage = [&](auto mf, int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* Bn, u32x4_t* An) {
+  auto run_stage = [&](auto mf, auto nt, int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* Bn, u32x4_t* An) {
     constexpr bool MF = decltype(mf)::value;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAITN));  // this wave's loads for stage kt landed
     asm volatile("" ::: "memory");
@@ -498,11 +505,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       for (int q = 0; q < PER; ++q) {
         const int idx = ks * PER + q;
         if constexpr (BFIRST) {
-          if (idx < B_IN) load_b(idx, (kt + DB) * kBK, Bn);
+          if (idx < B_IN) load_b(nt, idx, (kt + DB) * kBK, Bn);
           else if (idx < A_IN + B_IN) load_a(idx - B_IN, (kt + DA) * kBK, An);
         } else {
           if (idx < A_IN) load_a(idx, (kt + DA) * kBK, An);
-          else if (idx < A_IN + B_IN) load_b(idx - A_IN, (kt + DB) * kBK, Bn);
+          else if (idx < A_IN + B_IN) load_b(nt, idx - A_IN, (kt + DB) * kBK, Bn);
         }
       }
       asm volatile("" ::: "memory");  // keep the loads ahead of the later fragment reads
@@ -524,46 +531,66 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   u32x4_t* const bs[3] = {B0, B1, B2};
   // Prologue: the loads of virtual stages -max(DA, DB) .. -1, in stage order
   // (those for stages >= 0 only), so that every stage wait counts the same.
+  auto prologue = [&](auto nt) {
 #pragma unroll
-  for (int j = -(DA > DB ? DA : DB); j < 0; ++j) {
-    if (BFIRST && j + DB >= 0) {
+    for (int j = -(DA > DB ? DA : DB); j < 0; ++j) {
+      if (BFIRST && j + DB >= 0) {
 #pragma unroll
-      for (int u = 0; u < B_IN; ++u) load_b(u, (j + DB) * kBK, bs[(j + DB) % NBS]);
+        for (int u = 0; u < B_IN; ++u) load_b(nt, u, (j + DB) * kBK, bs[(j + DB) % NBS]);
+      }
+      if (j + DA >= 0) {
+#pragma unroll
+        for (int u = 0; u < A_IN; ++u) load_a(u, (j + DA) * kBK, as[(j + DA) % NAS]);
+      }
+      if (!BFIRST && j + DB >= 0) {
+#pragma unroll
+        for (int u = 0; u < B_IN; ++u) load_b(nt, u, (j + DB) * kBK, bs[(j + DB) % NBS]);
+      }
     }
-    if (j + DA >= 0) {
-#pragma unroll
-      for (int u = 0; u < A_IN; ++u) load_a(u, (j + DA) * kBK, as[(j + DA) % NAS]);
-    }
-    if (!BFIRST && j + DB >= 0) {
-#pragma unroll
-      for (int u = 0; u < B_IN; ++u) load_b(u, (j + DB) * kBK, bs[(j + DB) % NBS]);
-    }
-  }
+  };
   // Straight-line ring over lcm(NAS, NBS) stages: no merge point for acc inside
   // the loop. Stage i uses token slot i % NAS and weight slot i % NBS and fills
   // token slot (i + DA) % NAS and weight slot (i + DB) % NBS.
   constexpr int RING = NAS == NBS ? NAS : NAS * NBS;
-  auto ring = [&](auto mf) {
+  auto ring = [&](auto mf, auto nt) {
     int kt = 0;
     for (; kt + RING <= nk; kt += RING) {
 #pragma unroll
       for (int i = 0; i < RING; ++i)
-        run_stage(mf, kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
+        run_stage(mf, nt, kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
     }
 #pragma unroll
     for (int i = 0; i + 1 < RING; ++i)
-      if (kt + i < nk) run_stage(mf, kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
+      if (kt + i < nk) run_stage(mf, nt, kt + i, as[i % NAS], bs[i % NBS], bs[(i + DB) % NBS], as[(i + DA) % NAS]);
   };
   // A tile with few rows (a small expert, the last tile of a group) leaves the
   // waves past its rows without work: they skip the fragment reads and MFMAs
   // (wave-uniform choice, once per tile).
-  if (wm * WTM < rows) {
-    ring(std::true_type{});
-    if constexpr (kDefer) {
-      if (nk > 0) mfma_step(dwf, dxf);  // the last stage's last step (none for an empty reduction)
+  auto run = [&](auto nt) {
+    prologue(nt);
+    if (wm * WTM < rows) {
+      ring(std::true_type{}, nt);
+      if constexpr (kDefer) {
+        if (nk > 0) mfma_step(dwf, dxf);  // the last stage's last step (none for an empty reduction)
+      }
+    } else {
+      ring(std::false_type{}, nt);
     }
+  };
+  // On 128-row tiles of the forward first GEMM, the only m-tile of an expert
+  // reads its weight slice exactly once: those loads go non-temporal (the
+  // streaming read pattern that measured fastest for weight-bound GEMMs), while
+  // experts with several m-tiles keep their slices in L2 for the other m-tiles.
+  // Measured on the Switch-style layer: first GEMM 0.353 -> 0.327 ms; the second
+  // GEMM (weight slices of 704 KB, its activations reused by 16 n-tiles) was
+  // slower with it (0.229 -> 0.244 ms), and all-non-temporal weight loads were
+  // slower everywhere (first GEMM 0.335 -> 0.366 ms, prefill 1.64 -> 1.79 ms).
+  constexpr bool kNtOnce = BM == 128 && !BT && (MODE == G1_SWIGLU || MODE == G1_GELU);
+  if constexpr (kNtOnce) {
+    if (__shfl(wt.cnt, e) <= BM) run(std::true_type{});
+    else run(std::false_type{});
   } else {
-    ring(std::false_type{});
+    run(std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
   asm volatile("" ::: "memory");
