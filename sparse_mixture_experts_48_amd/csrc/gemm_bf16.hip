@@ -196,6 +196,8 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt <= n only.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// ... for vmcnt <= n and for every LDS and scalar memory access (lgkmcnt 0).
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
 
 // BT: the weight operand stored with k as the row index (forward-style modes:
 // [E][Kd][N] per expert; G_WGRAD: [S][N], rows = grouped slots). XT (G_WGRAD
@@ -453,8 +455,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // mf: std::true_type for a wave that holds rows of the tile, std::false_type
   // for one that does not (it only issues its share of the loads and waits).
   // On 128-row tiles the MFMAs of a stage's last 16-k step run after the next
-  // stage's barrier and first fragment reads (their fragments are already in
-  // registers, so the slots they came from may be refilled): they cover the
+  // stage's barrier and first fragment reads (their fragments are in registers
+  // once the wait before that barrier has drained the LDS reads, so the slots
+  // they came from may be refilled): they cover the
   // latency of those reads (Switch-style layer, first GEMM 0.366 -> 0.355 ms;
   // on 256 x 256 tiles it was slower: prefill first GEMM 1.676 -> 1.706 ms,
   // second 0.984 -> 1.063 ms). Every accumulator still sees its k steps in
@@ -471,7 +474,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   };
   auto run_stage = [&](auto mf, auto nt, int kt, const u32x4_t* As, const u32x4_t* Bs, u32x4_t* Bn, u32x4_t* An) {
     constexpr bool MF = decltype(mf)::value;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAITN));  // this wave's loads for stage kt landed
+    // This wave's loads for stage kt landed. With deferred MFMAs, also the
+    // fragment reads of the previous stage's last step: the barrier lets the
+    // other waves refill the slots those reads come from, and the barrier does
+    // not wait for LDS reads in flight (left pending, an LDS queue backed up by
+    // eight waves' reads could let a refill land first: y then varied from run
+    // to run on 128-row tiles).
+    __builtin_amdgcn_s_waitcnt(kDefer ? vmcnt_lgkm0_imm(WAITN) : vmcnt_imm(WAITN));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();                   // ... and every wave's
     asm volatile("" ::: "memory");
@@ -585,7 +594,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // GEMM (weight slices of 704 KB, its activations reused by 16 n-tiles) was
   // slower with it (0.229 -> 0.244 ms), and all-non-temporal weight loads were
   // slower everywhere (first GEMM 0.335 -> 0.366 ms, prefill 1.64 -> 1.79 ms).
-  constexpr bool kNtOnce = BM == 128 && !BT && (MODE == G1_SWIGLU || MODE == G1_GELU);
+  constexpr bool kNtOnce = BM == 128 && BN == 256 && !BT && (MODE == G1_SWIGLU || MODE == G1_GELU);
   if constexpr (kNtOnce) {
     if (__shfl(wt.cnt, e) <= BM) run(std::true_type{});
     else run(std::false_type{});

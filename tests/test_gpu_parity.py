@@ -224,6 +224,36 @@ def test_all_slots_on_first_experts(dtype, act):
     _check_forward(cfg, dev, r)
 
 
+@pytest.mark.parametrize("name,runs", [("ragged_large_k1", 3000), ("tiles_128x256", 3000)])
+def test_forward_bitwise_repeatable_many(name, runs):
+    """Thousands of forward calls give the same bits. Both shapes run 128-row
+    tiles (128 x 128 and 128 x 256), whose last 16-k step of every stage is
+    multiplied after the next stage's barrier: the wait before that barrier
+    must also drain the LDS reads of those fragments, or another wave's refill
+    of the slot can land first (before that wait was added, about 1 call in
+    250 to 1000 of the first shape differed in one row)."""
+    shapes = {"ragged_large_k1": SMALL["ragged_large_k1"],
+              "tiles_128x256": L("tiles_128x256", 1600, 128, 16, 1, 4608, W.ACT_SWIGLU, W.GATE_RAW, W.DT_BF16,
+                                 "zipf1.1", 37)}
+    cfg = shapes[name]
+    H.say("[gpu] repeatability %s x %d %s" % (name, runs, cfg))
+    dev = H.to_dev(_case(cfg))
+    desc = moe.desc_of(cfg)
+    ws = moe.workspace(desc)
+    ref = None
+    differing = 0
+    for _ in range(runs):
+        y, aux, counts = moe.forward(desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"],
+                                     dev["W2"], dev["b2"], ws=ws)
+        yb = y.view(torch.int16).clone()
+        if ref is None:
+            ref = (yb, aux.clone(), counts.clone())
+        elif not (torch.equal(yb, ref[0]) and torch.equal(aux, ref[1]) and torch.equal(counts, ref[2])):
+            differing += 1
+    torch.cuda.synchronize()
+    assert differing == 0, "%d of %d calls differ from the first" % (differing, runs)
+
+
 def test_empty_batch():
     cfg = L("empty", 0, 128, 8, 2, 256, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 32)
     H.say("[gpu] T=0")
