@@ -18,11 +18,10 @@
 // small batch and give a large batch four times the independent fmas.
 //
 // Three layouts of the same chains:
-//  * broadcast (17..64 experts): 16 tokens x four chains per wave, 16 experts
-//    per wave; h and W_r go straight from memory to registers and each fma
-//    takes its W_r value from another lane through a DPP row broadcast (see
-//    route_bcast_kernel); its chain sums go through LDS to the wide layout's
-//    per-token epilogue.
+//  * MFMA (17..64 experts): the chains run on the float32 matrix cores, whose
+//    32x32x2 MFMA applies its two k as two correctly rounded fmas in order
+//    (route_mfma_kernel); one wave per chain and 32 experts of a 32-token
+//    block, chain sums through LDS, then the per-token epilogue.
 //  * wide (up to 16 experts, T > 256): a thread owns one chain of TPT tokens x TE
 //    experts and walks that chain's k upward; lanes are laid out as [token
 //    group][chain][expert lane], so the four chains of a logit sit LE = EP/TE
@@ -49,13 +48,11 @@ constexpr int kRouteThreads = 256;
 
 // Wide layout per padded expert count: TE experts and TPT tokens per thread
 // (one chain of each), BK k per LDS stage. A token group takes 4 * EP / TE
-// lanes; a block holds kRouteThreads / (4 * EP / TE) * TPT tokens. For 32 and
-// 64 experts only the epilogue's tiling is used (by the broadcast layout).
+// lanes; a block holds kRouteThreads / (4 * EP / TE) * TPT tokens. (More
+// experts run on the MFMA layout.)
 template <int EP> struct WideCfg;
 template <> struct WideCfg<8> { static constexpr int TE = 2, TPT = 1, BK = 128; };
 template <> struct WideCfg<16> { static constexpr int TE = 4, TPT = 2, BK = 128; };
-template <> struct WideCfg<32> { static constexpr int TE = 4, TPT = 4, BK = 64; };
-template <> struct WideCfg<64> { static constexpr int TE = 4, TPT = 4, BK = 64; };
 template <int EP>
 constexpr int wide_tb() { return kRouteThreads / (4 * EP / WideCfg<EP>::TE) * WideCfg<EP>::TPT; }
 
@@ -491,181 +488,222 @@ __global__ __launch_bounds__(kRouteThreads) void route_wide_kernel(
   route_epilogue<EP, TE, TPT, LE, G>(lsum, tg, cj, el, t0, expert_of, o, psum_s, z_s, hist_s);
 }
 
-// Broadcast layout (17..64 experts, any batch): no LDS stage for h or W_r.
-// A wave holds 16 tokens x the four chains x 16 experts: lane = 16 * chain +
-// token, and each lane keeps its chain of its token for 16 experts in
-// registers. Per round of 16 k (four k per chain) a lane loads its token's
-// four h values of its chain (one 8-byte load for bfloat16) and one float4 of
-// W_r: lane i of chain row j holds W_r[k][e0 + 4 (i % 4) + c] for k =
-// 16 m + 4 j + i / 4 in component c, so the 16 lanes of a row hold the 64
-// weights its chain needs in that round. Every fma takes its weight from the
-// lane that holds it through a DPP row broadcast on the fma's first operand
-// (v_fmac_f32_dpp row_newbcast): 64 fmas per round and lane with no LDS
-// traffic and no data movement instructions; the fma's rounding is the same
-// as fmaf's. The wave's chain sums go through LDS to the wide layout's
-// epilogue (same per-token work, same block partials, same bits).
-constexpr int kBcastRing = 4;  // rounds of loads in flight per wave
+// MFMA layout (17..64 experts): the four chains on the float32 matrix cores.
+// v_mfma_f32_32x32x2_f32 adds to each of its 32 x 32 outputs the products of
+// its two k in order, each with one rounding: an fmaf for the first k, then
+// one for the second (checked on the hardware against correctly rounded fmaf
+// chains, bit for bit, with denormals, infinities, NaN and signed zeros). So
+// chain j of a logit is a run of these MFMAs over its k pairs in ascending
+// order from a zero accumulator: the same bits as the fmaf chain.
+// A block holds 32 tokens; wave w runs chain w % 4 for experts 32 (w / 4) ..
+// + 31 with one 32 x 32 accumulator (16 registers). Per 16 k (one group of four
+// k per chain) a wave issues two MFMAs: k 4j, 4j+1 and k 4j+2, 4j+3. MFMA
+// operands: lane l gives A[token l % 32][k0 + l / 32] and B[k0 + l / 32][expert
+// l % 32]. Stages of 64 k of h and W_r go to LDS by direct loads, kMfmaRing - 1
+// stages ahead; h rows are stored in 16 units of four k per row, unit c of
+// token r at c ^ (r & 15), so the 32 tokens of a read fall in distinct banks
+// pairwise. The four chains meet in LDS as (c0 + c1) + (c2 + c3) and go to the
+// wide layout's per-token epilogue.
+constexpr int kMfmaBK = 64;   // k per stage
+constexpr int kMfmaRing = 3;  // register ring: stages loaded ahead of their store to LDS
+constexpr int kMfmaTB = 32;   // tokens per block
 
-// acc[4 q + c] += W(lane 4 s + q of the row, component c) * hk[s] for s, q, c
-// in ascending order: 64 fmas, each expert's four in ascending k. The leading
-// s_nop covers the DPP read-after-VALU-write hazards (two wait states after a
-// VALU write of the broadcast register, five after a VALU write of EXEC),
-// which the compiler does not see through an asm statement.
-#define MOE_FMAC_BC(a, w, h, l) "v_fmac_f32_dpp %" #a ", %" #w ", %" #h " row_newbcast:" #l " row_mask:0xf bank_mask:0xf\n"
-#define MOE_FMAC_BC_Q(a0, a1, a2, a3, h, l) \
-  MOE_FMAC_BC(a0, 16, h, l) MOE_FMAC_BC(a1, 17, h, l) MOE_FMAC_BC(a2, 18, h, l) MOE_FMAC_BC(a3, 19, h, l)
-#define MOE_FMAC_BC_S(h, l0, l1, l2, l3)                                                        \
-  MOE_FMAC_BC_Q(0, 1, 2, 3, h, l0) MOE_FMAC_BC_Q(4, 5, 6, 7, h, l1) MOE_FMAC_BC_Q(8, 9, 10, 11, h, l2) \
-  MOE_FMAC_BC_Q(12, 13, 14, 15, h, l3)
-__device__ __forceinline__ void bcast_round(float (&acc)[16], const float4& w, const float (&hk)[4]) {
-  asm("s_nop 4\n"
-      MOE_FMAC_BC_S(20, 0, 1, 2, 3) MOE_FMAC_BC_S(21, 4, 5, 6, 7) MOE_FMAC_BC_S(22, 8, 9, 10, 11)
-      MOE_FMAC_BC_S(23, 12, 13, 14, 15)
-      : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
-        "+v"(acc[7]), "+v"(acc[8]), "+v"(acc[9]), "+v"(acc[10]), "+v"(acc[11]), "+v"(acc[12]), "+v"(acc[13]),
-        "+v"(acc[14]), "+v"(acc[15])
-      : "v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w), "v"(hk[0]), "v"(hk[1]), "v"(hk[2]), "v"(hk[3]));
-}
-#undef MOE_FMAC_BC_S
-#undef MOE_FMAC_BC_Q
-#undef MOE_FMAC_BC
-
-// Four h values of one token and chain (k .. k + 3).
-template <typename Tin> struct HQuad;
-template <> struct HQuad<bf16_t> {
-  typedef uint2 raw;
-  __device__ __forceinline__ static raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), soff, 0);
-    return make_uint2(v.x, v.y);
-  }
-  __device__ __forceinline__ static void to_f32(const raw& x, float (&out)[4]) {
-    out[0] = __uint_as_float(x.x << 16);
-    out[1] = __uint_as_float(x.x & 0xFFFF0000u);
-    out[2] = __uint_as_float(x.y << 16);
-    out[3] = __uint_as_float(x.y & 0xFFFF0000u);
-  }
-};
-template <> struct HQuad<float> {
-  typedef float4 raw;
-  __device__ __forceinline__ static raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
-    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), soff, 0);
-    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-  }
-  __device__ __forceinline__ static void to_f32(const raw& x, float (&out)[4]) {
-    out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
-  }
-};
+template <int EP> constexpr int mfma_threads() { return EP / 32 * 4 * 64; }
 
 template <typename Tin, int EP>
-__global__ __launch_bounds__(kRouteThreads) void route_bcast_kernel(
+__global__ __launch_bounds__(mfma_threads<EP>()) void route_mfma_kernel(
     const Tin* __restrict__ h, const float* __restrict__ Wr, const float* __restrict__ br,
     const float* __restrict__ noise, int T, int d, int E, int K, int gate_mode,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, float* __restrict__ logits_out,
     int32_t* __restrict__ blk_hist, float* __restrict__ blk_psum, float* __restrict__ blk_z, int bias_select) {
-  constexpr int NEG = EP / 16;               // expert groups of 16 (one per wave)
-  constexpr int NTS = kRouteThreads / 64 / NEG;  // token sets of 16 per block
-  constexpr int TB = 16 * NTS;               // tokens per block
-  // epilogue layout: the wide layout's for EP experts
-  constexpr int TE = WideCfg<EP>::TE, TPT = WideCfg<EP>::TPT;
-  constexpr int LE = EP / TE, LG = 4 * LE, G = kRouteThreads / LG;
-  static_assert(NEG >= 2 && NEG * NTS * 64 == kRouteThreads, "waves tile the block's experts and tokens");
-  static_assert(G * TPT == TB && TE == 4, "the epilogue covers the block's tokens, four experts per lane");
-  constexpr int R = kBcastRing;
+  constexpr int NT = mfma_threads<EP>();
+  constexpr int TB = kMfmaTB;
+  constexpr int S = static_cast<int>(sizeof(Tin));
+  constexpr int UG = 4 * S;                  // bytes of one unit: four k of one token
+  constexpr int HROW = kMfmaBK * S;          // bytes of one token's stage (16 units)
+  constexpr int HB = TB * HROW;              // h bytes per stage
+  constexpr int WF = kMfmaBK * EP;           // W_r floats per stage ([64 k][EP])
+  constexpr int HP = HB / (NT * 8);          // 8-byte h pieces per thread per stage
+  constexpr int WL = WF / (NT * 4);          // float4 W_r pieces per thread per stage
+  constexpr int RD = kMfmaRing;              // register ring: stages loaded ahead
+  static_assert(HP * NT * 8 == HB && WL * NT * 4 == WF, "whole pieces per thread");
+  // epilogue: one token per group of LE lanes, four experts per lane (the
+  // chain sums are already formed, so no chain replicas)
+  constexpr int TE = 4, LE = EP / TE, G = NT / LE, TPT = TB / G;
+  static_assert(G * TPT == TB && TPT == 1, "the epilogue covers the block's tokens, one per lane group");
+  constexpr int CP = EP + 4;                 // chain-sum row stride (floats)
 
-  __shared__ __align__(16) float lg_s[TB][EP + 4];
+  // Three LDS slots: the stage whose operands are read (one stage before its
+  // MFMAs), the next one, and the one being stored from the register ring.
+  // h rows: unit c of token r at c ^ (r & 15).
+  __shared__ __align__(16) char hs[3][HB];
+  __shared__ __align__(16) float ws[3][WF];
+  __shared__ __align__(16) float cs[4][TB][CP];
   __shared__ float psum_s[G][EP];
   __shared__ float z_s[G];
   __shared__ int hist_s[EP];
+  auto hslot = [&](int b) { return &hs[b][0]; };
+  auto wslot = [&](int b) { return &ws[b][0]; };
 
   const int tid = threadIdx.x;
-  const int wid = tid / 64, lane = tid % 64;
-  const int j = lane / 16, i = lane % 16;  // chain, token of the set
-  const int eg = wid % NEG, ts = wid / NEG;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int j = wid % 4, eh = wid / 4;  // chain, expert half
+  const int q = lane / 32, li = lane % 32;
   const int t0 = blockIdx.x * TB;
   if (tid < EP) hist_s[tid] = 0;
 
   // The block's token rows (rows past T read zeros) and all of W_r as buffers;
-  // the round offset is the scalar operand, which the range check includes.
+  // a stage's offset is the scalar operand, which the range check includes.
   const int rows = max(0, min(TB, T - t0));
   const __amdgpu_buffer_rsrc_t hbuf =
-      route_rsrc(h + static_cast<size_t>(min(t0, max(T - 1, 0))) * d, static_cast<uint32_t>(rows) * d * sizeof(Tin));
+      route_rsrc(h + static_cast<size_t>(min(t0, max(T - 1, 0))) * d, static_cast<uint32_t>(rows) * d * S);
   const __amdgpu_buffer_rsrc_t wbuf = route_rsrc(Wr, static_cast<uint32_t>(d) * E * 4);
-  const uint32_t hoff = (static_cast<uint32_t>(ts * 16 + i) * d + 4 * j) * sizeof(Tin);
-  const uint32_t woff = (static_cast<uint32_t>(4 * j + i / 4) * E + eg * 16 + 4 * (i % 4)) * 4;
-  const int hstep = 16 * static_cast<int>(sizeof(Tin));
-  const int wstep = 16 * E * 4;
-
-  typename HQuad<Tin>::raw hr[R];
-  float4 wr[R];
-  // Round m into ring slot `slot`. Rounds past the end read zeros (W_r) or
-  // values that are never used.
-  auto load_round = [&](int m, int slot) {
-    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    hr[slot] = HQuad<Tin>::load(hbuf, hoff, m * hstep);
-    const u4 w = __builtin_amdgcn_raw_buffer_load_b128(wbuf, static_cast<int>(woff), m * wstep, 0);
-    wr[slot] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
-  };
-  float acc[16];
+  // Per thread: global byte offsets at stage 0 and LDS byte offsets of its
+  // pieces. h: consecutive threads take consecutive 8 bytes of a row (whole
+  // lines); W_r: float4 f of the stage's [64 k][EP] tile is W_r[k0 + f / EP]
+  // [f % EP] (experts past E land in padded columns that are never used).
+  uint32_t hvo[HP], hlo[HP], wvo[WL];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
-  auto compute_round = [&](int slot, bool half) {
-    float hk[4];
-    HQuad<Tin>::to_f32(hr[slot], hk);
-    if (half && j >= 2) {
-      // last half round (d % 16 == 8): chains 2 and 3 have no k left; their
-      // h values belong to the next row, their W_r values read zeros
+  for (int p = 0; p < HP; ++p) {
+    const int n = tid + p * NT;
+    const int r = n / (HROW / 8), lb = (n % (HROW / 8)) * 8;
+    hvo[p] = static_cast<uint32_t>(r) * d * S + lb;
+    hlo[p] = r * HROW + (((lb / UG) ^ (r & 15)) * UG) + lb % UG;
+  }
 #pragma unroll
-      for (int s = 0; s < 4; ++s) hk[s] = 0.0f;
+  for (int u = 0; u < WL; ++u) {
+    const int f = 4 * (tid + u * NT);
+    wvo[u] = (static_cast<uint32_t>(f / EP) * E + f % EP) * 4;
+  }
+  uint2 hreg[RD][HP];
+  float4 wreg[RD][WL];
+  // Stage st into register slot rs (a constant: the loops over slots are
+  // unrolled). Stages past the end read zeros or values that are never used.
+  auto load_stage = [&](int st, int rs) {
+#pragma unroll
+    for (int p = 0; p < HP; ++p) {
+      typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+      const u2 v = __builtin_amdgcn_raw_buffer_load_b64(hbuf, static_cast<int>(hvo[p]), st * kMfmaBK * S, 0);
+      hreg[rs][p] = make_uint2(v.x, v.y);
     }
-    bcast_round(acc, wr[slot], hk);
+#pragma unroll
+    for (int u = 0; u < WL; ++u) {
+      typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+      const u4 v = __builtin_amdgcn_raw_buffer_load_b128(wbuf, static_cast<int>(wvo[u]), st * kMfmaBK * E * 4, 0);
+      wreg[rs][u] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+    }
+  };
+  auto store_stage = [&](int rs, int b) {
+#pragma unroll
+    for (int p = 0; p < HP; ++p) *reinterpret_cast<uint2*>(hslot(b) + hlo[p]) = hreg[rs][p];
+#pragma unroll
+    for (int u = 0; u < WL; ++u) *reinterpret_cast<float4*>(wslot(b) + 4 * (tid + u * NT)) = wreg[rs][u];
   };
 
-  const int nm = d / 16;          // whole rounds of the four chains
-  const bool half = (d % 16) != 0;  // d % 8 == 0: then a half round, chains 0 and 1
+  f32x16_t acc;
 #pragma unroll
-  for (int r = 0; r < R; ++r) load_round(r, r);
-  int m0 = 0;
-  for (; m0 + R <= nm; m0 += R) {
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  // MFMAs of stage st (ring slot b): rounds of 16 k; chain j's group of four
+  // k of a round exists when it starts before d (d is a multiple of 8).
+  // Operands of one stage for this wave: per round of 16 k, the A values of
+  // k 4j + q and 4j + 2 + q (lane q = l / 32) and the matching B values.
+  struct Ops {
+    float a0[4], a1[4], b0[4], b1[4];
+  };
+  Ops ops[2];
+  auto read_ops = [&](int b, Ops& o) {
+    const char* hrow = hslot(b) + li * HROW;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      compute_round(r, false);
-      load_round(m0 + r + R, r);
-      // keep the refill here: sunk to the end of the loop body, the whole
-      // ring would be reissued at once and drained at the next round 0
-      __builtin_amdgcn_sched_barrier(0);
+    for (int mm = 0; mm < kMfmaBK / 16; ++mm) {
+      const int unit = (4 * mm + j) ^ (li & 15);
+      if constexpr (S == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(hrow + unit * UG);
+        o.a0[mm] = __uint_as_float(q ? (v.x & 0xFFFF0000u) : (v.x << 16));
+        o.a1[mm] = __uint_as_float(q ? (v.y & 0xFFFF0000u) : (v.y << 16));
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(hrow + unit * UG);
+        o.a0[mm] = q ? v.y : v.x;
+        o.a1[mm] = q ? v.w : v.z;
+      }
+      const float* wrow = wslot(b) + (16 * mm + 4 * j + q) * EP + 32 * eh + li;
+      o.b0[mm] = wrow[0];
+      o.b1[mm] = wrow[2 * EP];
     }
-  }
-  // fewer than R whole rounds and the half round: all already in their slots
+  };
+  // MFMAs of stage st: chain j's group of four k of a round exists when it
+  // starts before d (d is a multiple of 8).
+  auto mfmas = [&](auto full, int st, const Ops& o) {
+    const int kv = d - st * kMfmaBK;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (m0 + r < nm) compute_round(r, false);
-    else if (m0 + r == nm && half) compute_round(r, true);
-  }
+    for (int mm = 0; mm < kMfmaBK / 16; ++mm) {
+      if (decltype(full)::value || 16 * mm + 4 * j < kv) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a0[mm], o.b0[mm], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(o.a1[mm], o.b1[mm], acc, 0, 0, 0);
+      }
+    }
+  };
 
-  // (c0 + c1) + (c2 + c3) in chain row 0; to LDS for the epilogue
+  // Stage x lives in register slot x % RD from its load until its store, then
+  // in LDS slot x % 3. Each stage st: a barrier (every wave is done with the
+  // reads of stage st - 1, made during stage st - 2, so its LDS slot may be
+  // overwritten, and the stores of stage st + 1 are visible), the store of
+  // stage st + 2 from its registers, the loads of stage st + 2 + RD into the
+  // registers just freed, then the operand reads of stage st + 1 and the MFMAs
+  // of stage st (whose operands were read during stage st - 1), which the
+  // reads overlap. Loads run RD + 2 stages ahead of their MFMAs. The main loop
+  // runs whole groups of U full stages with no condition; the tail, at most U
+  // stages, has the conditions.
+  constexpr int U = RD * 2;  // a multiple of RD, 3 and 2 (RD = 3)
+  static_assert(RD == 3, "unroll factor");
+  auto stage = [&](auto full, int st, int r) {
+    __syncthreads();
+    store_stage((r + 2) % RD, (r + 2) % 3);
+    load_stage(st + 2 + RD, (r + 2) % RD);
+    // keep the loads here: sunk to the end of the stage, the next stage's
+    // stores would wait for them
+    __builtin_amdgcn_sched_barrier(0);
+    read_ops((r + 1) % 3, ops[(r + 1) % 2]);
+    mfmas(full, st, ops[r % 2]);
+  };
+  const int nst = (d + kMfmaBK - 1) / kMfmaBK;  // stages
+  const int nfull = d / kMfmaBK;                // stages of a whole 64 k
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const float c01 = acc[q] + __shfl_xor(acc[q], 16);
-    acc[q] = c01 + __shfl_xor(c01, 32);
-  }
-  if (j == 0) {
-#pragma unroll
-    for (int q = 0; q < 16; q += 4)
-      *reinterpret_cast<float4*>(&lg_s[ts * 16 + i][eg * 16 + q]) =
-          make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
-  }
+  for (int r = 0; r < RD; ++r) load_stage(r, r);
+  store_stage(0, 0);
+  store_stage(1, 1);
+  load_stage(RD, 0);
+  load_stage(RD + 1, 1);
   __syncthreads();
-  const int tg = tid / LG;
-  const int cj = (tid % LG) / LE;
+  read_ops(0, ops[0]);
+  int s0 = 0;
+  for (; s0 + U <= nfull; s0 += U) {
+#pragma unroll
+    for (int r = 0; r < U; ++r) stage(std::true_type{}, s0 + r, r);
+  }
+#pragma unroll
+  for (int r = 0; r < U; ++r)
+    if (s0 + r < nst) stage(std::false_type{}, s0 + r, r);
+  // chain sums: accumulator register rg holds token 8 (rg / 4) + 4 q + rg % 4
+#pragma unroll
+  for (int rg = 0; rg < 16; ++rg) cs[j][8 * (rg / 4) + 4 * q + rg % 4][32 * eh + li] = acc[rg];
+  __syncthreads();
+  const int tg = tid / LE;
+  const int cj = 0;
   const int el = tid % LE;
-  auto expert_of = [&](int q) { return el * 4 + q; };  // TE == 4: experts 4 el .. 4 el + 3
+  auto expert_of = [&](int qq) { return el * 4 + qq; };
   float lsum[TPT][TE];
 #pragma unroll
   for (int u = 0; u < TPT; ++u) {
-    const float4 v = *reinterpret_cast<const float4*>(&lg_s[tg + u * G][el * 4]);
-    lsum[u][0] = v.x; lsum[u][1] = v.y; lsum[u][2] = v.z; lsum[u][3] = v.w;
+    const int row = tg + u * G;
+    const float4 c0 = *reinterpret_cast<const float4*>(&cs[0][row][el * 4]);
+    const float4 c1 = *reinterpret_cast<const float4*>(&cs[1][row][el * 4]);
+    const float4 c2 = *reinterpret_cast<const float4*>(&cs[2][row][el * 4]);
+    const float4 c3 = *reinterpret_cast<const float4*>(&cs[3][row][el * 4]);
+    lsum[u][0] = (c0.x + c1.x) + (c2.x + c3.x);
+    lsum[u][1] = (c0.y + c1.y) + (c2.y + c3.y);
+    lsum[u][2] = (c0.z + c1.z) + (c2.z + c3.z);
+    lsum[u][3] = (c0.w + c1.w) + (c2.w + c3.w);
   }
   const RouteOut o{br, noise, T, E, K, gate_mode, bias_select, topk_idx, topk_gate, logits_out,
                    blk_hist, blk_psum, blk_z};
@@ -975,8 +1013,8 @@ hipError_t launch_route_wide(const RouteArgs& a, const RouteTiling& rt, hipStrea
 }
 
 template <typename Tin, int EP>
-hipError_t launch_route_bcast(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
-  hipLaunchKernelGGL((route_bcast_kernel<Tin, EP>), dim3(rt.NB), dim3(kRouteThreads), 0, st,
+hipError_t launch_route_mfma(const RouteArgs& a, const RouteTiling& rt, hipStream_t st) {
+  hipLaunchKernelGGL((route_mfma_kernel<Tin, EP>), dim3(rt.NB), dim3(mfma_threads<EP>()), 0, st,
                      static_cast<const Tin*>(a.h), a.Wr, a.br, a.noise, a.T, a.d, a.E, a.K, a.gate, a.topk_idx,
                      a.topk_gate, a.logits, a.blk_hist, a.blk_psum, a.blk_z, a.bias_select);
   return hipGetLastError();
@@ -1003,8 +1041,8 @@ hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStre
   switch (rt.EP) {  // wide layout: wide_tb<EP>() tokens x EP experts per block of 256 threads
     case 8: return launch_route_wide<Tin, 8, WideCfg<8>::TE, WideCfg<8>::TPT, WideCfg<8>::BK, 2>(a, rt, st);
     case 16: return launch_route_wide<Tin, 16, WideCfg<16>::TE, WideCfg<16>::TPT, WideCfg<16>::BK, 2>(a, rt, st);
-    case 32: return launch_route_bcast<Tin, 32>(a, rt, st);
-    default: return launch_route_bcast<Tin, 64>(a, rt, st);
+    case 32: return launch_route_mfma<Tin, 32>(a, rt, st);
+    default: return launch_route_mfma<Tin, 64>(a, rt, st);
   }
 }
 
@@ -1012,8 +1050,8 @@ hipError_t launch_route_dtype(const RouteArgs& a, const RouteTiling& rt, hipStre
 
 // Narrow layout for small batches of few experts (T <= 256, E <= 16), where the
 // wide layout leaves most compute units idle: one token per wave, 4 waves per
-// block. Otherwise the wide layout (up to 16 experts) or the broadcast layout
-// (17..64), wide_tb<EP>() tokens per block.
+// block. Otherwise the wide layout (up to 16 experts, wide_tb<EP>() tokens per
+// block) or the MFMA layout (17..64 experts, kMfmaTB tokens per block).
 constexpr int64_t kNarrowMaxT = 256;
 
 RouteTiling route_tiling(int64_t T, int64_t E) {
@@ -1024,7 +1062,7 @@ RouteTiling route_tiling(int64_t T, int64_t E) {
     rt.TB = kNarrowNW;
   } else {
     rt.NW = 0;  // wide or broadcast layout
-    rt.TB = rt.EP == 8 ? wide_tb<8>() : rt.EP == 16 ? wide_tb<16>() : rt.EP == 32 ? wide_tb<32>() : wide_tb<64>();
+    rt.TB = rt.EP == 8 ? wide_tb<8>() : rt.EP == 16 ? wide_tb<16>() : kMfmaTB;
   }
   rt.NB = static_cast<int>((T + rt.TB - 1) / rt.TB);
   return rt;
