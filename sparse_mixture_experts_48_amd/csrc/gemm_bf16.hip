@@ -204,7 +204,7 @@ constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x
 // only): the x operand stored [S][M] with the grouped slots as rows; each
 // expert's reduction then runs over its own slots [beg, end) (expert_rows),
 // rows past end reading zeros.
-template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false>
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false, bool PERSIST = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
@@ -271,30 +271,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const int n_nt = (p.N + NCOLS - 1) / NCOLS;
   WaveTiles wt{};
   if constexpr (!WGRAD) wt = wave_tiles(p.offsets, p.E, p.S, p.cap, BM);
-  const int n_mt = WGRAD ? p.n_mt : min(p.n_mt, wt.total);
+  // wave-uniform values kept in scalar registers (a lane shuffle's result is
+  // not known to be uniform, and the persistent tile loop branches on them)
+  const int n_mt = __builtin_amdgcn_readfirstlane(WGRAD ? p.n_mt : min(p.n_mt, wt.total));
   const int n_t = n_nt * n_mt;
   const int per_xcd = (n_t + 7) / 8;
   const int xi = static_cast<int>(blockIdx.x / 8);
   if (xi >= per_xcd) return;
-  const int t = static_cast<int>(blockIdx.x % 8) * per_xcd + xi;
-  if (t >= n_t) return;
-  // logical tile t -> (n-tile group g of up to kNG n-tiles, m-tile, n-tile in group)
-  const int g = t / (kNG * n_mt);
-  const int gs = min(kNG, n_nt - g * kNG);
-  const int rem = t - g * kNG * n_mt;
-  const int mt = rem / gs;
-  const int nt = g * kNG + rem % gs;
-  int e, row0, rows;
-  if constexpr (WGRAD) {  // fixed M rows for every expert: m-tile mt = (expert, tile)
-    const int n_mte = (p.M + BM - 1) / BM;
-    e = mt / n_mte;
-    row0 = (mt % n_mte) * BM;
-    rows = min(BM, p.M - row0);
-    if (e >= p.E) return;
-  } else {
-    wave_tile_owner(wt, BM, mt, &e, &row0, &rows);
-  }
-  const int n0 = nt * NCOLS;
+  // PERSIST: the grid holds one block per CU (a multiple of 8, so every XCD
+  // gets gridDim.x / 8 of them); the block at index xi of its XCD takes the
+  // tiles xi, xi + gridDim.x / 8, ... of that XCD's run, and issues the first
+  // loads of its next tile before the epilogue of the current one.
+  const int t_end = min(n_t, (static_cast<int>(blockIdx.x % 8) + 1) * per_xcd);
+  int t = static_cast<int>(blockIdx.x % 8) * per_xcd + xi;
+  if (t >= t_end) return;
+  int e = 0, row0 = 0, rows = 0, n0 = 0;
+  // logical tile tt -> (n-tile group g of up to kNG n-tiles, m-tile, n-tile in
+  // group) -> expert, rows, first output column; false for a tile past the
+  // last expert (weight-gradient grids)
+  auto decode = [&](int tt) {
+    const int g = tt / (kNG * n_mt);
+    const int gs = min(kNG, n_nt - g * kNG);
+    const int rem = tt - g * kNG * n_mt;
+    const int mt = rem / gs;
+    const int ntl = g * kNG + rem % gs;
+    n0 = ntl * NCOLS;
+    if constexpr (WGRAD) {  // fixed M rows for every expert: m-tile mt = (expert, tile)
+      const int n_mte = (p.M + BM - 1) / BM;
+      e = mt / n_mte;
+      row0 = (mt % n_mte) * BM;
+      rows = min(BM, p.M - row0);
+      return e < p.E;
+    } else {
+      wave_tile_owner(wt, BM, mt, &e, &row0, &rows);
+      e = __builtin_amdgcn_readfirstlane(e);
+      row0 = __builtin_amdgcn_readfirstlane(row0);
+      rows = __builtin_amdgcn_readfirstlane(rows);
+      return true;
+    }
+  };
+  if (!decode(t)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid % 64;
@@ -323,13 +339,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // over expert e's padded range of rows of length ldk, a whole number of
   // stages (so its last stage needs no zero fill).
   const int stride = WGRAD ? p.ldk : Kd;
-  const int kb = WGRAD ? p.kofs[e] : 0;
-  const int nk = WGRAD ? (p.kofs[e + 1] - kb) / kBK : (Kd + kBK - 1) / kBK;
-  // k-major weight-gradient operands: expert e's grouped slots (the same
-  // count of stages as its padded range kofs[e] .. kofs[e+1])
-  int kbeg = 0, kend = 0;
-  if constexpr (XT) expert_rows(p.offsets, e, p.S, p.cap, &kbeg, &kend);
-  const int k_last = WGRAD ? (1 << 30) : (nk - 1) * kBK;  // first k of the last stage
+  // per tile: k range (weight-gradient GEMMs), buffers and per-lane offsets
+  int kb = 0, nk = 0, kbeg = 0, kend = 0, k_last = 0;
   const uint32_t a_bytes = XT ? static_cast<uint32_t>(p.S) * static_cast<uint32_t>(p.M) * 2u
                               : static_cast<uint32_t>(WGRAD ? p.M : p.x_nrows) * static_cast<uint32_t>(stride) * 2u;
   const uint32_t b_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(stride) * 2u;
@@ -337,14 +348,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // k-major weights: Kd1 rows of B per expert (then as many of B3)
   const int Kd1 = (BT && p.kb3 > 0) ? p.kb3 : Kd;
   const uint32_t bt_bytes = static_cast<uint32_t>(WGRAD ? p.S : Kd1) * static_cast<uint32_t>(N) * 2u;
-  const __amdgpu_buffer_rsrc_t rb1 =
-      BT ? buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * Kd1 * N), bt_bytes)
-         : buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * N * Kd), b_bytes);
-  const __amdgpu_buffer_rsrc_t rb3 =
-      (NMAT == 2) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * N * Kd, b_bytes)
-                  : ((BT && p.kb3 > 0) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * Kd1 * N, bt_bytes) : rb1);
+  __amdgpu_buffer_rsrc_t rb1 = ra, rb3 = ra;
   // per lane: offset for every stage, and for the last one (out of range past the end of k)
   uint32_t a_vo[A_IN], a_vl[A_IN], b_vo[B_IN], b_vl[B_IN];
+  auto setup = [&]() {
+  kb = WGRAD ? p.kofs[e] : 0;
+  nk = WGRAD ? (p.kofs[e + 1] - kb) / kBK : (Kd + kBK - 1) / kBK;
+  // k-major weight-gradient operands: expert e's grouped slots (the same
+  // count of stages as its padded range kofs[e] .. kofs[e+1])
+  if constexpr (XT) expert_rows(p.offsets, e, p.S, p.cap, &kbeg, &kend);
+  k_last = WGRAD ? (1 << 30) : (nk - 1) * kBK;  // first k of the last stage
+  rb1 = BT ? buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * Kd1 * N), bt_bytes)
+           : buffer_rsrc(p.B + (WGRAD ? size_t{0} : static_cast<size_t>(e) * N * Kd), b_bytes);
+  rb3 = (NMAT == 2) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * N * Kd, b_bytes)
+                    : ((BT && p.kb3 > 0) ? buffer_rsrc(p.B3 + static_cast<size_t>(e) * Kd1 * N, bt_bytes) : rb1);
 #pragma unroll
   for (int u = 0; u < A_IN; ++u) {
     if constexpr (XT) {  // the slot layout of k-major weights, over the block's M columns
@@ -386,6 +403,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       b_vl[u] = (WGRAD || k_last + kc < Kd) ? b_vo[u] : b_bytes;
     }
   }
+  };
+  setup();
   // k-major slot rows: the lane's row kbeg + k0 + (first row of instruction
   // u) + lane / CPR, zeros (an offset past the buffer) at or past kend
   auto kmajor_off = [&](uint32_t vo, int rbase, int lr, uint32_t ld, uint32_t bytes) {
@@ -427,13 +446,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     }
   };
 
-  f32x16_t acc[TN][TM];
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+  f32x16_t acc[TN][TM];  // zeroed at the start of every tile
 
   const int frow = lane % 32;
   const int fsub = lane / 32;  // which of the two 8-wide k chunks of a 16-k step
@@ -576,7 +589,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // waves past its rows without work: they skip the fragment reads and MFMAs
   // (wave-uniform choice, once per tile).
   auto run = [&](auto nt) {
-    prologue(nt);
+    if constexpr (!PERSIST) prologue(nt);
     if (wm * WTM < rows) {
       ring(std::true_type{}, nt);
       if constexpr (kDefer) {
@@ -595,17 +608,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // slower with it (0.229 -> 0.244 ms), and all-non-temporal weight loads were
   // slower everywhere (first GEMM 0.335 -> 0.366 ms, prefill 1.64 -> 1.79 ms).
   constexpr bool kNtOnce = BM == 128 && BN == 256 && !BT && (MODE == G1_SWIGLU || MODE == G1_GELU);
-  if constexpr (kNtOnce) {
-    if (__shfl(wt.cnt, e) <= BM) run(std::true_type{});
-    else run(std::false_type{});
-  } else {
-    run(std::false_type{});
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
-  asm volatile("" ::: "memory");
+  static_assert(!PERSIST || !kNtOnce, "persistent tiles use the default weight-load policy");
 
-  // Epilogue. Accumulator (j, i), register r: token = i*32 + lane%32 of the
-  // wave's rows; weight row = j*32 + (r/4)*8 + (lane/32)*4 + r%4.
+  // Epilogue of the tile (e, row0, rows, n0). Accumulator (j, i), register r:
+  // token = i*32 + lane%32 of the wave's rows; weight row = j*32 + (r/4)*8 +
+  // (lane/32)*4 + r%4.
+  auto epilogue = [&](const int e, const int row0, const int rows, const int n0) {
   constexpr int TNO = TN / NMAT;  // output column tiles per wave
   constexpr bool DZ = (MODE == G2_DZ_SWIGLU || MODE == G2_DZ_GELU);
   // gate-gradient terms of a row: column tiles j hold columns j*32 .. j*32+31
@@ -812,6 +820,46 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
           if (c0 < N) p.dgp[static_cast<size_t>(c0 / kDgpCols) * p.S + row0 + rl] = dgs[i][b];
         }
       }
+    }
+  }
+  };
+
+  if constexpr (PERSIST) prologue(std::false_type{});
+  for (;;) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+    if constexpr (kNtOnce) {
+      if (__shfl(wt.cnt, e) <= BM) run(std::true_type{});
+      else run(std::false_type{});
+    } else {
+      run(std::false_type{});
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
+    asm volatile("" ::: "memory");
+    const int te = e, trow0 = row0, trows = rows, tn0 = n0;
+    bool more = false;
+    if constexpr (PERSIST) {
+      t += static_cast<int>(gridDim.x / 8);
+      more = t < t_end;
+      if (more) {
+        // every wave has read its last fragments of this tile: the next
+        // tile's first stages may go into the slots
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        decode(t);
+        setup();
+        prologue(std::false_type{});
+      }
+    }
+    epilogue(te, trow0, trows, tn0);
+    if constexpr (!PERSIST) {
+      break;
+    } else {
+      if (!more) break;
     }
   }
 }
@@ -1114,14 +1162,31 @@ __global__ __launch_bounds__(64) void gemm_slab_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------- launch
 
-template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false>
+// Compute units of the current device (cached per device; 0 if the query fails).
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false, bool PERSIST = false>
 hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   p.n_mt = MODE == G_WGRAD ? p.E * ((p.M + BM - 1) / BM) : (S + BM - 1) / BM + min(p.E, S);
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
   const size_t total = static_cast<size_t>(n_nt) * p.n_mt;
-  const size_t grid = (total + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE, BT, XT>), dim3(static_cast<unsigned>(grid)),
+  size_t grid = (total + 7) / 8 * 8;
+  if (PERSIST) {  // one block per CU, a multiple of 8 (every XCD the same count)
+    const size_t cus = static_cast<size_t>(device_cu_count()) / 8 * 8;
+    if (cus >= 8 && cus < grid) grid = cus;
+  }
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE, BT, XT, PERSIST>), dim3(static_cast<unsigned>(grid)),
                      dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
 }
@@ -1147,7 +1212,8 @@ hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
     return static_cast<long>((S + bm - 1) / bm + min(p.E, S)) * ((p.N + bn / NMAT - 1) / (bn / NMAT));
   };
   if (mean_rows >= 512 && blocks(256, 256) >= 2 * 256) {
-    return launch_tile<256, 256, 4, 2, MODE, BT>(p, S, st);
+    if constexpr (MODE == G1_SWIGLU && !BT) return launch_tile<256, 256, 4, 2, MODE, BT, false, true>(p, S, st);
+    else return launch_tile<256, 256, 4, 2, MODE, BT>(p, S, st);
   }
   if (blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, 4, 2, MODE, BT>(p, S, st);
   return launch_tile<128, 128, 2, 2, MODE, BT>(p, S, st);
