@@ -52,7 +52,7 @@ struct Plan {
   size_t blk_hist, blk_psum, blk_base, blk_z;
   size_t topk_idx, topk_gate, token_slot, slot_token;
   size_t counts, offsets, pmean, aux;
-  size_t act, o_perm;
+  size_t act, o_perm, tail_part;
   size_t total;
 };
 
@@ -82,6 +82,13 @@ Plan make_plan(const moe_desc& d) {
   p.aux = take(4);
   p.act = take(S * d.width * bpe);
   p.o_perm = take(d.K > 1 || d.capacity > 0 ? S * d.d * 4 : 0);  // K = 1 dropless writes y directly
+  // float32 partial rows of the second GEMM's split tails (moe_expert_ffn never
+  // fuses the scatter, so the region is sized as if it did not)
+  const int64_t max_rows = std::min<int64_t>(d.T, d.capacity > 0 ? d.capacity : INT_MAX);
+  p.tail_part = take(d.dtype == MOE_BF16 ? moe::gemm2_tail_bytes(static_cast<int>(S), static_cast<int>(d.E),
+                                                                   static_cast<int>(d.d), static_cast<int>(d.width),
+                                                                   static_cast<int>(max_rows), false)
+                                         : 0);
   p.total = off;
   return p;
 }
@@ -334,6 +341,7 @@ int enqueue_forward(const moe_desc& d, const Plan& pl, const void* h, const floa
   f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
   f.a = at<char>(ws, pl.act);
   f.o_perm = at<float>(ws, pl.o_perm);
+  f.tail_part = at<float>(ws, pl.tail_part);
   f.fused_y = K == 1 && d.capacity == 0;  // with drops, the combine writes the tokens that lost their slot
   f.y = y;
   f.slot_token = slot_token;
@@ -596,6 +604,7 @@ int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expe
   f.W1 = W1; f.b1 = b1; f.W3 = W3; f.W2 = W2; f.b2 = b2;
   f.a = at<char>(ws, pl.act);
   f.o_perm = o_perm;
+  f.tail_part = at<float>(ws, pl.tail_part);
   f.fused_y = false;
   f.cap = cap_of(d);
   f.max_rows_per_expert = static_cast<int>(std::min<int64_t>(d.T, f.cap));

@@ -75,8 +75,15 @@ struct WaveTiles {
   int total;           // m-tiles over all experts (wave-uniform)
 };
 
+// ks > 1: an expert whose last m-tile holds at most tail_max rows (a short
+// tail) has that tile split into ks tiles, each over one part of the reduction.
+__device__ __forceinline__ int expert_mtiles(int cnt, int bm, int ks, int tail_max) {
+  const int rem = cnt % bm;
+  return (cnt + bm - 1) / bm + ((ks > 1 && rem > 0 && rem <= tail_max) ? ks - 1 : 0);
+}
+
 __device__ __forceinline__ WaveTiles wave_tiles(const int32_t* __restrict__ offsets, int E, int S, int cap,
-                                                int bm) {
+                                                int bm, int ks = 1, int tail_max = 0) {
   const int lane = static_cast<int>(threadIdx.x % 64);
   WaveTiles w{0, 0, 0, 0};
   int nt = 0;
@@ -85,7 +92,7 @@ __device__ __forceinline__ WaveTiles wave_tiles(const int32_t* __restrict__ offs
     expert_rows(offsets, lane, S, cap, &b, &e);
     w.beg = b;
     w.cnt = e - b;
-    nt = (w.cnt + bm - 1) / bm;
+    nt = expert_mtiles(w.cnt, bm, ks, tail_max);
   }
   int incl = nt;
 #pragma unroll
@@ -98,17 +105,27 @@ __device__ __forceinline__ WaveTiles wave_tiles(const int32_t* __restrict__ offs
   return w;
 }
 
-// Owner of m-tile mt (wave-uniform, 0 <= mt < w.total).
+// Owner of m-tile mt (wave-uniform, 0 <= mt < w.total). With split tails
+// (ks > 1, as passed to wave_tiles), *split is the part of the reduction a
+// tile of a split tail takes (0 .. ks-1), and -1 for every other tile.
 __device__ __forceinline__ void wave_tile_owner(const WaveTiles& w, int bm, int mt, int* expert, int* row0,
-                                                int* rows) {
+                                                int* rows, int ks = 1, int tail_max = 0, int* split = nullptr) {
   // tile counts are non-negative, so the lanes whose tiles all lie at or
   // before mt form a prefix of the wave
   const int e = __popcll(__ballot(w.incl <= mt));
-  const int first = __shfl(w.incl, e) - (__shfl(w.cnt, e) + bm - 1) / bm;
-  const int local = mt - first;
+  const int cnt = __shfl(w.cnt, e);
+  const int first = __shfl(w.incl, e) - expert_mtiles(cnt, bm, ks, tail_max);
+  int local = mt - first;
+  const int full = cnt / bm;
+  int sp = -1;
+  if (ks > 1 && local >= full && cnt % bm > 0 && cnt % bm <= tail_max) {
+    sp = local - full;
+    local = full;
+  }
   *expert = e;
   *row0 = __shfl(w.beg, e) + local * bm;
-  *rows = min(bm, __shfl(w.cnt, e) - local * bm);
+  *rows = min(bm, cnt - local * bm);
+  if (split != nullptr) *split = sp;
 }
 
 }  // namespace moe

@@ -82,6 +82,13 @@ struct GemmParams {
   // B is [E][Kd1][N] with N contiguous, Kd1 = kb3 > 0 rows of B followed by
   // kb3 rows of B3 (the SwiGLU input gradient dZ [W1; W3]), or Kd1 = Kd.
   int kb3;
+  // G2_OPERM with split tails (gemm_tile_kernel<..., TS = true>): an expert's
+  // last m-tile of at most BM / WM rows is computed as ks tiles, part j over
+  // stages [j q, (j + 1) q) of the reduction (q = ceil(stages / ks)); part j
+  // writes its rows r (0 .. 63) to tail_part[(j E + e) 64 + r][N] (float32,
+  // the bias in part 0), which tail_sum_kernel adds into o_perm.
+  float* tail_part;
+  int ks;
 };
 constexpr int kDgpCols = 64;  // columns per partial sum of the dZ GEMM's gate-gradient terms
 
@@ -204,12 +211,14 @@ constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x
 // only): the x operand stored [S][M] with the grouped slots as rows; each
 // expert's reduction then runs over its own slots [beg, end) (expert_rows),
 // rows past end reading zeros.
-template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false, bool PERSIST = false>
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false, bool PERSIST = false,
+          bool TS = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   static_assert(!BT || NMAT == 1, "k-major weights: single-matrix modes");
   static_assert(!XT || MODE == G_WGRAD, "k-major x: weight-gradient GEMMs");
+  static_assert(!TS || (MODE == G2_OPERM && !BT && !PERSIST), "split tails: second GEMM into o_perm");
   static_assert(MODE != G_WGRAD || !BT || XT, "k-major weights of a weight-gradient GEMM need k-major x");
   constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_SWIGLU_Z || MODE == G1_GELU_Z);
   constexpr bool WGRAD = (MODE == G_WGRAD);
@@ -270,7 +279,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int kNG = (!G1 && !WGRAD && BM == 128) ? 2 * kTileGroupN : kTileGroupN;
   const int n_nt = (p.N + NCOLS - 1) / NCOLS;
   WaveTiles wt{};
-  if constexpr (!WGRAD) wt = wave_tiles(p.offsets, p.E, p.S, p.cap, BM);
+  const int ks = TS ? p.ks : 1;
+  if constexpr (!WGRAD) wt = wave_tiles(p.offsets, p.E, p.S, p.cap, BM, ks, WTM);
   // wave-uniform values kept in scalar registers (a lane shuffle's result is
   // not known to be uniform, and the persistent tile loop branches on them)
   const int n_mt = __builtin_amdgcn_readfirstlane(WGRAD ? p.n_mt : min(p.n_mt, wt.total));
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   const int t_end = min(n_t, (static_cast<int>(blockIdx.x % 8) + 1) * per_xcd);
   int t = static_cast<int>(blockIdx.x % 8) * per_xcd + xi;
   if (t >= t_end) return;
-  int e = 0, row0 = 0, rows = 0, n0 = 0;
+  int e = 0, row0 = 0, rows = 0, n0 = 0, split = -1;
   // logical tile tt -> (n-tile group g of up to kNG n-tiles, m-tile, n-tile in
   // group) -> expert, rows, first output column; false for a tile past the
   // last expert (weight-gradient grids)
@@ -303,8 +313,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       rows = min(BM, p.M - row0);
       return e < p.E;
     } else {
-      wave_tile_owner(wt, BM, mt, &e, &row0, &rows);
+      wave_tile_owner(wt, BM, mt, &e, &row0, &rows, ks, WTM, &split);
       e = __builtin_amdgcn_readfirstlane(e);
+      split = __builtin_amdgcn_readfirstlane(split);
       row0 = __builtin_amdgcn_readfirstlane(row0);
       rows = __builtin_amdgcn_readfirstlane(rows);
       return true;
@@ -354,6 +365,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   auto setup = [&]() {
   kb = WGRAD ? p.kofs[e] : 0;
   nk = WGRAD ? (p.kofs[e + 1] - kb) / kBK : (Kd + kBK - 1) / kBK;
+  if (TS && split >= 0) {  // one part of the reduction (the host keeps every part non-empty)
+    const int q = (nk + ks - 1) / ks;
+    kb = split * q * kBK;
+    nk = min(q, nk - split * q);
+  }
   // k-major weight-gradient operands: expert e's grouped slots (the same
   // count of stages as its padded range kofs[e] .. kofs[e+1])
   if constexpr (XT) expert_rows(p.offsets, e, p.S, p.cap, &kbeg, &kend);
@@ -377,7 +393,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       const int s = row0 + min(r, rows - 1);
       const int src_row = (p.x_rows != nullptr) ? p.x_rows[s] : s;
       a_vo[u] = (static_cast<uint32_t>(src_row) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
-      a_vl[u] = (WGRAD || k_last + kc < Kd) ? a_vo[u] : a_bytes;
+      a_vl[u] = (WGRAD || kb + k_last + kc < Kd) ? a_vo[u] : a_bytes;
     }
   }
 #pragma unroll
@@ -400,7 +416,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       const int kc = ((lane % kCH) ^ swz_key(r)) * 8;
       const int n = min(brow_col(r, &mat), N - 1);
       b_vo[u] = (static_cast<uint32_t>(n) * static_cast<uint32_t>(stride) + static_cast<uint32_t>(kc)) * 2u;
-      b_vl[u] = (WGRAD || k_last + kc < Kd) ? b_vo[u] : b_bytes;
+      b_vl[u] = (WGRAD || kb + k_last + kc < Kd) ? b_vo[u] : b_bytes;
     }
   }
   };
@@ -613,7 +629,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // Epilogue of the tile (e, row0, rows, n0). Accumulator (j, i), register r:
   // token = i*32 + lane%32 of the wave's rows; weight row = j*32 + (r/4)*8 +
   // (lane/32)*4 + r%4.
-  auto epilogue = [&](const int e, const int row0, const int rows, const int n0) {
+  auto epilogue = [&](const int e, const int row0, const int rows, const int n0, const int split) {
   constexpr int TNO = TN / NMAT;  // output column tiles per wave
   constexpr bool DZ = (MODE == G2_DZ_SWIGLU || MODE == G2_DZ_GELU);
   // gate-gradient terms of a row: column tiles j hold columns j*32 .. j*32+31
@@ -718,7 +734,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   // (four 2-byte loads per group, each after the stores before it, took most
   // of a short reduction's tile).
   constexpr bool BIAS = MODE == G1_GELU || MODE == G1_GELU_Z || MODE == G2_OPERM || MODE == G2_FUSED_Y;
-  const bool has_bias = BIAS && p.bias != nullptr;
+  const bool has_bias = BIAS && p.bias != nullptr && split <= 0;  // split tails: the bias in part 0
   u32x2_t bias4[BIAS ? TNO : 1][4];
   if constexpr (BIAS) {
     if (has_bias) {
@@ -789,8 +805,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
                            : p.out2 + (static_cast<size_t>(e) * (p.M - p.split) + (s - p.split)) * N + n;
           *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
         } else if (MODE == G2_OPERM) {
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + static_cast<size_t>(s) * N + n) =
-              f32x4_t{v[0], v[1], v[2], v[3]};
+          float* dst = static_cast<float*>(p.out) + static_cast<size_t>(s) * N + n;
+          if (TS && split >= 0) dst = p.tail_part + (static_cast<size_t>(split * p.E + e) * 64 + rl) * N + n;
+          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
         } else {
           const int t = fy_t[i];
           const float gt = fy_g[i];
@@ -840,7 +857,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
     asm volatile("" ::: "memory");
-    const int te = e, trow0 = row0, trows = rows, tn0 = n0;
+    const int te = e, trow0 = row0, trows = rows, tn0 = n0, tsplit = split;
     bool more = false;
     if constexpr (PERSIST) {
       t += static_cast<int>(gridDim.x / 8);
@@ -855,7 +872,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
         prologue(std::false_type{});
       }
     }
-    epilogue(te, trow0, trows, tn0);
+    epilogue(te, trow0, trows, tn0, tsplit);
     if constexpr (!PERSIST) {
       break;
     } else {
@@ -1175,10 +1192,12 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false, bool PERSIST = false>
+template <int BM, int BN, int WM, int WN, int MODE, bool BT = false, bool XT = false, bool PERSIST = false,
+          bool TS = false>
 hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   p.n_mt = MODE == G_WGRAD ? p.E * ((p.M + BM - 1) / BM) : (S + BM - 1) / BM + min(p.E, S);
+  if (TS) p.n_mt += p.E * (p.ks - 1);  // at most one split tail per expert
   const int n_nt = (p.N + BN / NMAT - 1) / (BN / NMAT);
   const size_t total = static_cast<size_t>(n_nt) * p.n_mt;
   size_t grid = (total + 7) / 8 * 8;
@@ -1186,9 +1205,47 @@ hipError_t launch_tile(GemmParams p, int S, hipStream_t st) {
     const size_t cus = static_cast<size_t>(device_cu_count()) / 8 * 8;
     if (cus >= 8 && cus < grid) grid = cus;
   }
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE, BT, XT, PERSIST>), dim3(static_cast<unsigned>(grid)),
-                     dim3(WM * WN * 64), 0, st, p);
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WM, WN, MODE, BT, XT, PERSIST, TS>),
+                     dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), 0, st, p);
   return hipGetLastError();
+}
+
+// 256 x 256 tiles: about 1k rows per expert and at least two tiles per CU.
+bool tiles_256(int S, int E, int N, int nmat) {
+  const long bn = 256 / nmat;
+  const long blocks = static_cast<long>((S + 255) / 256 + min(E, S)) * ((N + bn - 1) / bn);
+  return S / max(E, 1) >= 512 && blocks >= 2 * 256;
+}
+
+// Split tails of the second GEMM. On 256 x 256 tiles a tail of at most 64 rows
+// (the last m-tile of an expert) keeps one of four wave rows busy but streams a
+// whole weight slice over the full reduction; at the prefill shape the 64 tail
+// tiles beside 512 full ones made a third, mostly idle round (second GEMM
+// 0.96 ms against 0.80 ms for the same rows in whole tiles). Split into
+// kTailSplit parts along k they run as short tiles among the full ones; part j
+// writes float32 partial rows, and tail_sum_kernel adds the parts in order
+// 0, 1, ... into o_perm (fixed order: the same bits every run).
+constexpr int kTailSplit = 4;
+constexpr int kTailRows = 64;  // rows of one wave row of a 256 x 256 tile (4 x 2 waves)
+
+__global__ __launch_bounds__(256) void tail_sum_kernel(const float* __restrict__ part, float* __restrict__ o_perm,
+                                                       const int32_t* __restrict__ offsets, int S, int cap, int E,
+                                                       int N, int ks) {
+  const int e = static_cast<int>(blockIdx.x) / kTailRows, r = static_cast<int>(blockIdx.x) % kTailRows;
+  int b, en;
+  expert_rows(offsets, e, S, cap, &b, &en);
+  const int cnt = en - b, rem = cnt % 256;
+  if (rem == 0 || rem > kTailRows || r >= rem) return;
+  float* dst = o_perm + static_cast<size_t>(b + cnt - rem + r) * N;
+  for (int c = static_cast<int>(threadIdx.x) * 4; c < N; c += 256 * 4) {
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + (static_cast<size_t>(e) * kTailRows + r) * N + c);
+    for (int j = 1; j < ks; ++j) {
+      const f32x4_t w = *reinterpret_cast<const f32x4_t*>(
+          part + (static_cast<size_t>(j * E + e) * kTailRows + r) * N + c);
+      v = f32x4_t{v[0] + w[0], v[1] + w[1], v[2] + w[2], v[3] + w[3]};
+    }
+    *reinterpret_cast<f32x4_t*>(dst + c) = v;
+  }
 }
 
 // Tile shape from the mean rows per expert (S / E): with about 1k rows per
@@ -1212,8 +1269,14 @@ hipError_t launch_tile_auto(GemmParams p, int S, hipStream_t st) {
     return static_cast<long>((S + bm - 1) / bm + min(p.E, S)) * ((p.N + bn / NMAT - 1) / (bn / NMAT));
   };
   if (mean_rows >= 512 && blocks(256, 256) >= 2 * 256) {
-    if constexpr (MODE == G1_SWIGLU && !BT) return launch_tile<256, 256, 4, 2, MODE, BT, false, true>(p, S, st);
-    else return launch_tile<256, 256, 4, 2, MODE, BT>(p, S, st);
+    // persistent tiles where the epilogue reads nothing (measured: prefill first
+    // GEMM -2 %, backward recompute -1 %; the second GEMM, 2.25 tiles per CU,
+    // +2.5 % with the static tile order)
+    if constexpr ((MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) && !BT) {
+      return launch_tile<256, 256, 4, 2, MODE, BT, false, true>(p, S, st);
+    } else {
+      return launch_tile<256, 256, 4, 2, MODE, BT>(p, S, st);
+    }
   }
   if (blocks(128, 256) >= 2 * 256) return launch_tile<128, 256, 4, 2, MODE, BT>(p, S, st);
   return launch_tile<128, 128, 2, 2, MODE, BT>(p, S, st);
@@ -1273,6 +1336,12 @@ hipError_t launch_gemm1_bf16(const FfnArgs& f, hipStream_t st) {
   return swiglu ? launch_tile_auto<G1_SWIGLU>(p, f.S, st) : launch_tile_auto<G1_GELU>(p, f.S, st);
 }
 
+size_t gemm2_tail_bytes(int S, int E, int d, int width, int max_rows_per_expert, bool fused_y) {
+  if (fused_y || max_rows_per_expert <= kSlabMaxRows || !tiles_256(S, E, d, 1)) return 0;
+  if ((width + 63) / 64 < 4 * kTailSplit) return 0;  // every part at least four stages
+  return static_cast<size_t>(kTailSplit) * E * kTailRows * d * 4;
+}
+
 hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
   GemmParams p{};
   p.x = static_cast<const bf16_t*>(f.a);
@@ -1296,6 +1365,15 @@ hipError_t launch_gemm2_bf16(const FfnArgs& f, hipStream_t st) {
   if (f.max_rows_per_expert <= kSlabMaxRows) {
     return f.fused_y ? launch_slab<G2_FUSED_Y, kSlabBuf2>(p, f.max_rows_per_expert, st)
                      : launch_slab<G2_OPERM, kSlabBuf2>(p, f.max_rows_per_expert, st);
+  }
+  if (f.tail_part != nullptr && gemm2_tail_bytes(f.S, f.E, f.d, f.width, f.max_rows_per_expert, f.fused_y) > 0) {
+    p.tail_part = f.tail_part;
+    p.ks = kTailSplit;
+    const hipError_t err = launch_tile<256, 256, 4, 2, G2_OPERM, false, false, false, true>(p, f.S, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(tail_sum_kernel, dim3(static_cast<unsigned>(f.E * kTailRows)), dim3(256), 0, st,
+                       static_cast<const float*>(f.tail_part), f.o_perm, f.offsets, f.S, f.cap, f.E, f.d, kTailSplit);
+    return hipGetLastError();
   }
   return f.fused_y ? launch_tile_auto<G2_FUSED_Y>(p, f.S, st) : launch_tile_auto<G2_OPERM>(p, f.S, st);
 }

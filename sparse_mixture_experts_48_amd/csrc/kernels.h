@@ -86,7 +86,10 @@ struct FfnArgs {
   const float* topk_gate;
   int max_rows_per_expert;     // host-known bound (min(T, cap)) used to pick the kernel family
   int cap;                     // rows each expert processes at most (INT_MAX: dropless)
+  float* tail_part;            // nullable: gemm2_tail_bytes of workspace for split tails (bfloat16)
 };
+// Workspace the bfloat16 second GEMM uses for split tails (0: none are split).
+size_t gemm2_tail_bytes(int S, int E, int d, int width, int max_rows_per_expert, bool fused_y);
 hipError_t launch_gemm1(const FfnArgs& f, hipStream_t st);
 hipError_t launch_gemm2(const FfnArgs& f, hipStream_t st);
 

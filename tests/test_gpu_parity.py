@@ -331,6 +331,52 @@ def test_group_size_boundaries(act):
             assert err <= H.Y_TOL[cfg.dtype], (e, n, err)
 
 
+def _tiles_256(S, E, N, nmat):
+    """The library's choice of 256 x 256 tiles for a grouped GEMM: about 1k rows
+    per expert and at least two tiles per CU."""
+    bn = 256 // nmat
+    return S // E >= 512 and ((S + 255) // 256 + min(E, S)) * ((N + bn - 1) // bn) >= 2 * 256
+
+
+@pytest.mark.parametrize("act", [W.ACT_SWIGLU, W.ACT_GELU])
+def test_split_tails_256(act):
+    """Second GEMM on 256 x 256 tiles with experts whose last m-tile holds at
+    most 64 rows: those tails run as four tiles over quarters of the reduction
+    and are summed into o_perm afterwards. Tails of 1, 63 and 64 rows, an
+    expert of 40 rows (its only tile split), a tail of 65 rows and a whole
+    number of tiles (not split). Every tail row and the first and last rows of
+    every whole tile are compared with the oracle (GELU: the bias b2 enters
+    once); o_perm is bitwise the same on a second call."""
+    sizes = [2049, 1087, 1344, 1089, 1024, 40]
+    T, d, width = int(sum(sizes)), 4096, 1024
+    assert _tiles_256(T, len(sizes), d, 1) and (width + 63) // 64 >= 16
+    cfg = L("split_tails", T, d, len(sizes), 1, width, act, W.GATE_RAW, W.DT_BF16, "none", 61)
+    H.say("[gpu] split tails %s" % (cfg,))
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    offs_d = torch.from_numpy(offs).cuda()
+    desc = moe.desc_of(cfg)
+    o1 = moe.expert_ffn(desc, dev["h"], offs_d, dev["W1"], dev["b1"], dev["W3"], dev["W2"], dev["b2"])
+    o2 = moe.expert_ffn(desc, dev["h"], offs_d, dev["W1"], dev["b1"], dev["W3"], dev["W2"], dev["b2"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)), "o_perm differs between two calls"
+    o = H.to_np(o1)
+    p = H.oracle_params(inp)
+    for e, n in enumerate(sizes):
+        full, rem = divmod(n, 256)
+        rows = set()
+        for m in range(full):
+            rows.update((m * 256, m * 256 + 255))
+        rows.update(range(full * 256, n))
+        rows = np.array(sorted(rows), dtype=np.int64) + offs[e]
+        ref = O.expert_ffn(p["h"][rows], e, p, act)
+        err = H.rel_err(o[rows], ref)
+        H.record("o", "split_tails_%s_e%d" % ("swiglu" if act == W.ACT_SWIGLU else "gelu", e), rows=len(rows),
+                 tail=rem, err=err, bar=H.Y_TOL[cfg.dtype])
+        assert err <= H.Y_TOL[cfg.dtype], (e, n, err)
+
+
 def test_max_operand_size():
     """The largest layer the 32-bit offsets allow: T*K*d = 2^31 - 2^22 elements
     of h rows read through the grouping (T = 261632 tokens, d = 4096, top-2),
