@@ -192,7 +192,10 @@ int moe_permute(const moe_desc* desc, const int32_t* topk_idx, const void* h,
  * expert_offsets must be non-decreasing from 0 to S = T*K (as moe_permute
  * writes them); otherwise the outputs are unspecified, but every expert's row
  * range is clamped into [0, S), so no access leaves the buffers.
- * Returns a moe_status. */
+ * ws is scratch: the hidden activations and, for bfloat16 layers on large
+ * groups, float32 partial rows of the experts' short last row tiles, whose
+ * reduction is split in parts and summed in a fixed order (same bits every
+ * call). Returns a moe_status. */
 int moe_expert_ffn(const moe_desc* desc, const void* h_perm, const int32_t* expert_offsets,
                    const void* W1, const void* b1, const void* W3, const void* W2,
                    const void* b2, float* o_perm, void* ws, size_t ws_bytes, void* stream);
