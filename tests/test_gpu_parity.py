@@ -377,6 +377,35 @@ def test_split_tails_256(act):
         assert err <= H.Y_TOL[cfg.dtype], (e, n, err)
 
 
+@pytest.mark.parametrize("capacity", [0, 1])
+def test_forward_equals_composition(capacity):
+    """moe_forward against the four entry points in a row (moe_route,
+    moe_permute, moe_expert_ffn, moe_combine) on the Mixtral-shaped prefill
+    layer, whose second GEMM splits four experts' short tails: the fused path
+    (h read through the grouping, workspace-resident o_perm) and the composition
+    (gathered h_perm, caller's o_perm) must give y bit for bit the same
+    (dropless, and with a capacity of T*K/E slots per expert)."""
+    cfg = W.WORKLOADS["mixtral_prefill"]
+    cap = moe.capacity_slots(1.0, cfg.T, cfg.K, cfg.E) if capacity else 0
+    H.say("[gpu] forward vs composition %s capacity=%d" % (cfg.name, cap))
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    desc = moe.desc_of(cfg, capacity=cap)
+    y, _, _ = moe.forward(desc, dev["h"], dev["W_r"], dev["b_r"], dev["W1"], dev["b1"], dev["W3"], dev["W2"],
+                          dev["b2"])
+    g = moe.route(desc, dev["h"], dev["W_r"], dev["b_r"])
+    pm = moe.permute(desc, g["topk_idx"], dev["h"])
+    o = moe.expert_ffn(desc, pm["h_perm"], pm["offsets"], dev["W1"], dev["b1"], dev["W3"], dev["W2"], dev["b2"])
+    y2 = moe.combine(desc, o, pm["token_slot"], g["topk_gate"], y.dtype)
+    torch.cuda.synchronize()
+    counts = np.diff(H.to_np(pm["offsets"]).astype(np.int64))
+    kept = np.minimum(counts, cap) if cap else counts
+    assert ((kept % 256 > 0) & (kept % 256 <= 64)).any() or cap, "no split tail in this layer"
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "moe_forward differs from the composition"
+    del dev
+    torch.cuda.empty_cache()
+
+
 def test_max_operand_size():
     """The largest layer the 32-bit offsets allow: T*K*d = 2^31 - 2^22 elements
     of h rows read through the grouping (T = 261632 tokens, d = 4096, top-2),
