@@ -131,3 +131,30 @@ def test_capacity_full_workload(name):
     assert (~r["keep"]).any(), "factor 1.0 should drop slots on this layer"
     del dev
     torch.cuda.empty_cache()
+
+
+def _tiles_256(S, E, N, nmat):
+    """The library's choice of 256 x 256 tiles for a grouped GEMM: about 1k rows
+    per expert (by S / E) and at least two tiles per CU in its grid bound."""
+    bn = 256 // nmat
+    return S // E >= 512 and ((S + 255) // 256 + min(E, S)) * ((N + bn - 1) // bn) >= 2 * 256
+
+
+@pytest.mark.parametrize("C", [200, 300])
+def test_capacity_large_tiles(C):
+    """A layer on 256 x 256 tiles (the first GEMM persistent, one block per CU)
+    with a capacity far below the mean group: C = 200 leaves 8 x 22 = 176 tiles
+    of the first GEMM for 256 blocks (blocks with no tile, blocks with one);
+    C = 300 gives every expert a 44-row tail that the second GEMM splits along
+    k. Every token against the oracle, bitwise reproducible."""
+    cfg = L("cap_large_tiles", 4096, 4096, 8, 2, 2816, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none", 50)
+    assert _tiles_256(cfg.S, cfg.E, 2 * cfg.width, 2) and _tiles_256(cfg.S, cfg.E, cfg.d, 1)
+    assert (cfg.width + 63) // 64 >= 16
+    H.say("[gpu] capacity on 256-row tiles C=%d %s" % (C, cfg))
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    r = _check_case(cfg, inp, dev, C)
+    kept = np.minimum(r["counts"], C)
+    assert (kept == C).all(), "every expert should be capped in this case"
+    del dev
+    torch.cuda.empty_cache()
