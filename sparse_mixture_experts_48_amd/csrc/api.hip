@@ -103,6 +103,7 @@ struct BwdPlan {
   size_t blk_hist, blk_psum, blk_base, blk_z, topk_idx, topk_gate, token_slot, slot_token, counts, offsets, aux,
       logits;
   size_t z, a, rgate, dyb, dgp, dgs, dO, dZ, dX, kofs, xT, dl, wr_part;
+  size_t dx_tail;  // float32 partial rows of the dX GEMM's split tails (bfloat16 layers)
   size_t u;  // float32 layers: dy W2 of the grouped rows
   size_t total;
 };
@@ -163,6 +164,8 @@ BwdPlan make_bwd_plan(const moe_desc& d) {
   p.xT = take(dd * ldk * 2);
   p.dl = take(static_cast<size_t>(d.T) * E * 4);
   p.wr_part = take(static_cast<size_t>(p.nwr) * dd * E * 4);
+  p.dx_tail = take(moe::bwd_dx_tail_bytes(static_cast<int>(S), static_cast<int>(E), static_cast<int>(dd),
+                                          static_cast<int>(Zw)));
   p.total = off;
   return p;
 }
@@ -775,7 +778,8 @@ int moe_backward(const moe_desc* desc, const void* h, const float* W_r, const fl
   MOE_LAUNCH(MOE_K_BWD, st,
              moe::launch_dgate_sum(dgp, (Wd + moe::kDgpColsHost - 1) / moe::kDgpColsHost, S, dgs, st));
   MOE_LAUNCH(MOE_K_GEMM1, st,
-             moe::launch_bwd_dx_bf16(dZ, S, offsets, cap, E_, W1, swiglu ? W3 : nullptr, D, Wd, dX, st));
+             moe::launch_bwd_dx_bf16(dZ, S, offsets, cap, E_, W1, swiglu ? W3 : nullptr, D, Wd, dX,
+                                     at<float>(ws, pl.dx_tail), st));
 
   // router, dh, dW_r, db_r
   float* dl = at<float>(ws, pl.dl);

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
   constexpr int NMAT = (MODE == G1_SWIGLU || MODE == G1_SWIGLU_Z) ? 2 : 1;
   static_assert(!BT || NMAT == 1, "k-major weights: single-matrix modes");
   static_assert(!XT || MODE == G_WGRAD, "k-major x: weight-gradient GEMMs");
-  static_assert(!TS || (MODE == G2_OPERM && !BT && !PERSIST), "split tails: second GEMM into o_perm");
+  static_assert(!TS || (MODE == G2_OPERM && !PERSIST), "split tails: second GEMM or dX GEMM into float32 rows");
   static_assert(MODE != G_WGRAD || !BT || XT, "k-major weights of a weight-gradient GEMM need k-major x");
   constexpr bool G1 = (MODE == G1_SWIGLU || MODE == G1_GELU || MODE == G1_SWIGLU_Z || MODE == G1_GELU_Z);
   constexpr bool WGRAD = (MODE == G_WGRAD);
@@ -440,9 +440,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_tile_kernel(GemmParams p) {
       const int rbase = k0 + (wid * B_IN + u) * kBtRows<BN>;
       lds_load16(rb1, kmajor_off(b_vo[u], rbase, lane / kBtCPR<BN>, N, bt_bytes), 0, Bs + (wid * B_IN + u) * 64);
     } else if constexpr (BT) {
-      // rows k0 + (wid * B_IN + u) * RB .. of the reduction: all in B, all in
-      // B3 (Kd1 is a multiple of 8, RB <= 4) or all past Kd (zeros, no traffic)
-      const int kr = k0 + (wid * B_IN + u) * kBtRows<BN>;
+      // rows kb + k0 + (wid * B_IN + u) * RB .. of the reduction (kb: the first
+      // k of a split tail's part, else 0): all in B, all in B3 (Kd1 is a
+      // multiple of 8, RB <= 4) or all past Kd (zeros, no traffic)
+      const int kr = kb + k0 + (wid * B_IN + u) * kBtRows<BN>;
       const bool second = p.kb3 > 0 && kr >= Kd1;
       // byte offsets below 2^32 (the matrix bytes are); passed on as the same 32 bits
       const uint32_t soff = kr >= Kd ? bt_bytes : static_cast<uint32_t>(second ? kr - Kd1 : kr) * N * 2u;
@@ -1403,8 +1404,13 @@ hipError_t launch_bwd_z_bf16(const FfnArgs& f, void* z, void* a, hipStream_t st)
   return f.act == 1 ? launch_tile_auto<G1_SWIGLU_Z>(p, f.S, st) : launch_tile_auto<G1_GELU_Z>(p, f.S, st);
 }
 
+size_t bwd_dx_tail_bytes(int S, int E, int d, int Kd) {
+  if (!tiles_256(S, E, d, 1) || (Kd + 63) / 64 < 4 * kTailSplit) return 0;
+  return static_cast<size_t>(kTailSplit) * E * kTailRows * d * 4;
+}
+
 hipError_t launch_bwd_dx_bf16(const void* dZ, int S, const int32_t* offsets, int cap, int E, const void* W1,
-                              const void* W3, int N, int Kd1, float* out, hipStream_t st) {
+                              const void* W3, int N, int Kd1, float* out, float* tail_part, hipStream_t st) {
   GemmParams p{};
   p.x = static_cast<const bf16_t*>(dZ);
   p.x_nrows = S;
@@ -1418,6 +1424,17 @@ hipError_t launch_bwd_dx_bf16(const void* dZ, int S, const int32_t* offsets, int
   p.N = N;
   p.Kd = W3 != nullptr ? 2 * Kd1 : Kd1;
   p.S = S;
+  // split tails as in the forward's second GEMM (the same 2.25 rounds of 256 x
+  // 256 tiles at the prefill shape, over a reduction of 2 width)
+  if (tail_part != nullptr && bwd_dx_tail_bytes(S, E, N, p.Kd) > 0) {
+    p.tail_part = tail_part;
+    p.ks = kTailSplit;
+    const hipError_t err = launch_tile<256, 256, 4, 2, G2_OPERM, true, false, false, true>(p, S, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(tail_sum_kernel, dim3(static_cast<unsigned>(E * kTailRows)), dim3(256), 0, st,
+                       static_cast<const float*>(tail_part), out, offsets, S, cap, E, N, kTailSplit);
+    return hipGetLastError();
+  }
   return launch_tile_auto<G2_OPERM, true>(p, S, st);
 }
 

@@ -114,7 +114,9 @@ hipError_t launch_bwd_dz_bf16(const void* dy, int T, const int32_t* slot_token, 
 // [E][Kd1 = width][N = d], read with k as the row index; dZ rows of 2 Kd1
 // (SwiGLU, [dz1 | dz3]) or Kd1 (W3 null).
 hipError_t launch_bwd_dx_bf16(const void* dZ, int S, const int32_t* offsets, int cap, int E, const void* W1,
-                              const void* W3, int N, int Kd1, float* out, hipStream_t st);
+                              const void* W3, int N, int Kd1, float* out, float* tail_part, hipStream_t st);
+// Workspace the dX GEMM uses for split tails (tail_part of launch_bwd_dx_bf16; 0: none are split).
+size_t bwd_dx_tail_bytes(int S, int E, int d, int Kd);
 // Weight gradients: C_e[m][n] = sum over expert e's kept grouped slots s of X[s][m] B[s][n]
 // (X [S][M] bfloat16, read with the slots as rows). B is either the same kind
 // of k-major matrix [S][N] (b_kmajor) or a transposed copy [N][ldk] in which

@@ -64,6 +64,10 @@ CASES = {
     # ... and the dX GEMM on 256 x 256 (d = 4096)
     "tiles_256_dx_gelu": (L("bw_t256dx", 4096, 4096, 4, 2, 512, W.ACT_GELU, W.GATE_RENORM, W.DT_BF16, "normal2", 94),
                           0.1, 0, 0),
+    # ... and with a reduction of 2 width = 1024 (four stages per part), so that
+    # the dX GEMM splits the experts' short tails along k
+    "tiles_256_dx_split": (L("bw_t256split", 4096, 4096, 8, 2, 512, W.ACT_SWIGLU, W.GATE_RENORM, W.DT_BF16, "none",
+                             97), 0.2, 0, 0),
     # float32 layers: the micro workload itself (GELU with biases), SwiGLU with
     # raw gates and capacity drops, top-1 with a selection-only bias
     "f32_micro": (W.WORKLOADS["micro"], 0.5, 0, 0),
@@ -79,7 +83,21 @@ TILES = {
     "tiles_256_swiglu": ((256, 256), (256, 256), (128, 128)),
     "tiles_128x256_k1": ((128, 256), (128, 256), (128, 128)),
     "tiles_256_dx_gelu": ((128, 128), (128, 128), (256, 256)),
+    "tiles_256_dx_split": ((128, 128), (128, 128), (256, 256)),
 }
+
+
+def test_dx_split_tails_case():
+    """The tiles_256_dx_split case has experts whose last 256-row tile holds
+    at most 64 rows, which the dX GEMM (reduction 2 width = 1024, at least 16
+    stages) splits into four parts."""
+    cfg = CASES["tiles_256_dx_split"][0]
+    assert (2 * cfg.width + 63) // 64 >= 16
+    inp = W.make_inputs(cfg)
+    dev = H.to_dev(inp)
+    g = moe.route(moe.desc_of(cfg), dev["h"], dev["W_r"], dev["b_r"])
+    counts = H.to_np(g["counts"]).astype(np.int64)
+    assert ((counts % 256 > 0) & (counts % 256 <= 64)).any(), counts
 
 
 def _tile(S, E, N, nmat):
